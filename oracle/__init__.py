@@ -1,0 +1,15 @@
+"""Float64 CPU oracle of the DSA hot path (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  It is independent of the HIP library.
+"""
+from .dsa_oracle import (  # noqa: F401
+    attention_row,
+    decode_bf16,
+    decode_e4m3fn,
+    dsa_row,
+    indexer_row,
+    indexer_scores,
+    select_topk,
+    sparse_attention,
+)

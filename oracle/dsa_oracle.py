@@ -1,0 +1,172 @@
+"""Float64 CPU oracle for the DeepSeek Sparse Attention (DSA) hot path.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or link
+this module: it is used by ``tests/``, by ``__graft_entry__.smoke()`` and by the
+``cpu_baseline`` leg of ``bench.py``, and by nothing else.  It shares no code with
+the HIP library and imports nothing from it.
+
+What it computes, and where the definition comes from
+------------------------------------------------------
+Sources are the web pages on DeepSeek-V3.2-Exp.  "V3.2-Exp paper" below means the
+full Chinese translation of the DeepSeek-V3.2-Exp paper carried on the page
+"重磅！DeepSeek-V3.2-Exp 发布百万输出仅3元｜附完整论文中文翻译" (m.163.com); on that
+page every equation was an image and is lost, so each step follows the paper's
+prose around the lost equation.  "nsmao report" means the page
+"DeepSeek-V3.2开源技术报告" (nsmao.com).
+
+1. Indexer score (V3.2-Exp paper, §1 Architecture, "DSA prototype", Eq. 1):
+   I[t,s] = sum_{j < H_I} w[t,j] * ReLU(q[t,j] . k[s]); q[t,j] and w[t,j] come from
+   the query token, k[s] from a preceding token; ReLU is the activation; few heads;
+   FP8 arithmetic is allowed.  Reading: no extra constant factor; "preceding" is
+   inclusive, s <= t (0-indexed positions).
+2. Fine-grained selection (V3.2-Exp paper, §1, text after Eq. 1, and §2.1 "sparse
+   training stage"): S_t = the positions of the top-k indexer scores, k = 2048.
+   Reading: exactly n = min(k, t+1) positions, equal scores broken toward the lower
+   position.
+3. Sparse attention (V3.2-Exp paper, §1, Eq. 2): u_t = Attn(h_t, {c_s | s in S_t}).
+   Instantiated under MLA in MQA mode (§1 "Instantiate DSA under MLA"; App. A,
+   Fig. 4): every selected latent entry c_s is shared by all query heads; the key is
+   the whole entry (latent + rope part) and the value is its latent part (the first
+   D_v columns).  Reading: plain softmax attention with a given softmax scale, no
+   bias, no sink.  The nsmao report ("DSA principle") gives the cache widths: 128 per
+   token for the indexer key, 512 for the latent.
+
+Inputs are the exact byte images the GPU receives: e4m3fn codes with fp32 scales
+(dequantised value = decode(code) * scale), bf16 bit patterns, or plain fp32.  The
+oracle decodes them with its own decoders and computes every step in float64.
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import numpy as np
+
+__all__ = [
+    "decode_e4m3fn", "decode_bf16", "indexer_scores", "select_topk",
+    "sparse_attention", "indexer_row", "attention_row", "dsa_row",
+]
+
+
+# ---------------------------------------------------------------------------
+# O0: storage decoders
+# ---------------------------------------------------------------------------
+
+def decode_e4m3fn(codes: np.ndarray) -> np.ndarray:
+    """OCP 8-bit float E4M3 ("fn": finite, NaN at S.1111.111, no infinities).
+
+    Bit layout s eeee mmm, exponent bias 7:
+      e > 0: (-1)^s * 2^(e-7) * (1 + m/8)
+      e = 0: (-1)^s * 2^(-6) * (m/8)           (subnormals)
+      e = 15 and m = 7: NaN.
+    (The pages name only "FP8"; the e4m3fn flavour is the reading adopted.)
+    """
+    c = np.asarray(codes).astype(np.int64)
+    s = (c >> 7) & 1
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    normal = np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int64))
+    subnormal = np.ldexp(m / 8.0, -6)
+    mag = np.where(e > 0, normal, subnormal)
+    val = np.where(s == 1, -mag, mag)
+    return np.where((c & 0x7F) == 0x7F, np.nan, val).astype(np.float64)
+
+
+def decode_bf16(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) -> float64: the bf16 word is the top half of
+    an IEEE binary32 word."""
+    b = np.asarray(bits).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# O1-O3: the three steps, on dequantised float64 operands
+# ---------------------------------------------------------------------------
+
+def indexer_scores(q: np.ndarray, w: np.ndarray, k: np.ndarray) -> np.ndarray:
+    """Lightning-indexer scores of one query token against a set of keys.
+
+    q: [H_I, d_I] indexer queries q[t,j]; w: [H_I] head weights w[t,j];
+    k: [n, d_I] indexer keys k[s].  Returns I[s] = sum_j w[j] * max(0, q[j].k[s]).
+    (V3.2-Exp paper, §1, Eq. 1 prose.)
+    """
+    dots = q @ k.T                       # [H_I, n]: q[t,j] . k[s]
+    return w @ np.maximum(dots, 0.0)     # ReLU, then the w-weighted head sum
+
+
+def select_topk(scores: np.ndarray, n: int) -> np.ndarray:
+    """Positions of the n largest scores, equal scores toward the lower position,
+    returned in ascending position order.  (V3.2-Exp paper, §1 selection of the
+    top-k key-value entries; §2.1 S_t definition and k = 2048.)"""
+    scores = np.asarray(scores, dtype=np.float64)
+    pos = np.arange(scores.shape[0])
+    order = np.lexsort((pos, -scores))   # primary key -I ascending, then s ascending
+    return np.sort(order[:n])
+
+
+def sparse_attention(q: np.ndarray, entries: np.ndarray, scale: float,
+                     v_dim: int) -> Tuple[np.ndarray, np.ndarray]:
+    """MQA-mode attention of one query token over its selected latent entries.
+
+    q: [H, D_k] per-head absorbed queries; entries: [n, D_k] the selected latent
+    entries c_s (keys are whole entries, values their first v_dim columns).
+    Returns (o [H, v_dim], lse [H]) with
+      z[h,s] = scale * q[h].c_s,  o[h] = sum_s softmax_s(z[h,:]) c_s[:v_dim],
+      lse[h] = log sum_s exp(z[h,s]).
+    (V3.2-Exp paper, §1 Eq. 2 prose and "Instantiate DSA under MLA"; App. A.)
+    """
+    z = scale * (q @ entries.T)                  # [H, n]
+    m = z.max(axis=1, keepdims=True)
+    e = np.exp(z - m)
+    Z = e.sum(axis=1, keepdims=True)
+    o = (e / Z) @ entries[:, :v_dim]
+    lse = m[:, 0] + np.log(Z[:, 0])
+    return o, lse
+
+
+# ---------------------------------------------------------------------------
+# row drivers on raw input images
+# ---------------------------------------------------------------------------
+
+def _dequant(x: np.ndarray, scale: Optional[np.ndarray], fp8: bool) -> np.ndarray:
+    v = decode_e4m3fn(x) if fp8 else np.asarray(x, dtype=np.float64)
+    if scale is not None:
+        v = v * np.asarray(scale, dtype=np.float64)[..., None]
+    return v
+
+
+def indexer_row(q_idx: np.ndarray, q_scale: Optional[np.ndarray], w: np.ndarray,
+                k_idx: np.ndarray, k_scale: Optional[np.ndarray], t: int,
+                fp8: bool) -> np.ndarray:
+    """Scores I[0..t] of one query row at position t.
+
+    q_idx: [H_I, d_I] (e4m3fn codes if fp8 else fp32), q_scale: [H_I] or None;
+    w: [H_I]; k_idx: [>= t+1, d_I] the sequence's indexer keys, k_scale: [>= t+1]
+    or None.  Only keys s <= t are candidates.
+    """
+    qf = _dequant(q_idx, q_scale, fp8)
+    kf = _dequant(k_idx[: t + 1], None if k_scale is None else k_scale[: t + 1], fp8)
+    return indexer_scores(qf, np.asarray(w, dtype=np.float64), kf)
+
+
+def _decode_attn(x: np.ndarray, bf16: bool) -> np.ndarray:
+    return decode_bf16(x) if bf16 else np.asarray(x, dtype=np.float64)
+
+
+def attention_row(q: np.ndarray, entries: np.ndarray, scale: float, v_dim: int,
+                  bf16: bool) -> Tuple[np.ndarray, np.ndarray]:
+    """Attention for one row; q: [H, D_k], entries: [n, D_k] (bf16 bits or fp32)."""
+    return sparse_attention(_decode_attn(q, bf16), _decode_attn(entries, bf16),
+                            scale, v_dim)
+
+
+def dsa_row(q_idx, q_scale, w, k_idx, k_scale, q, latent, t: int, topk: int,
+            scale: float, v_dim: int, quantised: bool):
+    """The whole path for one row at position t: scores, selected set, output.
+
+    latent: [>= t+1, D_k] the sequence's latent cache.  Returns
+    (scores [t+1], S ascending [min(topk, t+1)], o [H, v_dim], lse [H]).
+    """
+    I = indexer_row(q_idx, q_scale, w, k_idx, k_scale, t, quantised)
+    S = select_topk(I, min(topk, t + 1))
+    o, lse = attention_row(q, latent[S], scale, v_dim, quantised)
+    return I, S, o, lse

@@ -1,0 +1,318 @@
+"""Pins of the float64 oracle to facts outside itself.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with a
+hand-worked example, a published table, a library routine, a brute-force
+enumeration, a closed form or an invariant.  ``test_oracle.py`` runs them as
+they are; ``test_oracle_mutations.py`` plants plausible mistakes in the oracle
+and checks that at least one pin fails for each.
+
+All pins call the oracle through the module attribute ``oracle.dsa_oracle.X`` so
+that a planted mistake is seen by every pin.
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+import oracle.dsa_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------- P1 decoders
+
+def pin_e4m3fn_golden():
+    """Published OFP8 E4M3 values (tests/golden/e4m3fn_codes.txt)."""
+    with open(os.path.join(GOLDEN, "e4m3fn_codes.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            code_s, val_s = line.split()
+            code = int(code_s, 16)
+            got = O.decode_e4m3fn(np.array([code], dtype=np.uint8))[0]
+            if val_s == "nan":
+                assert np.isnan(got), (hex(code), got)
+            else:
+                want = float(val_s)
+                assert got == want and math.copysign(1, got) == math.copysign(1, want), \
+                    (hex(code), got, want)
+
+
+def pin_e4m3fn_library():
+    """All 256 codes against torch's float8_e4m3fn decode (a library routine)."""
+    codes = np.arange(256, dtype=np.uint8)
+    ours = O.decode_e4m3fn(codes)
+    lib = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    both_nan = np.isnan(ours) & np.isnan(lib)
+    assert np.array_equal(np.isnan(ours), np.isnan(lib))
+    assert np.all((ours == lib) | both_nan)
+    assert np.array_equal(np.signbit(ours[~both_nan]), np.signbit(lib[~both_nan]))
+    # strictly increasing over the non-negative finite codes
+    pos = ours[:0x7F]
+    assert np.all(np.diff(pos) > 0)
+    assert pos.max() == 448.0 and ours[1] == 2.0 ** -9
+
+
+def pin_bf16():
+    """bf16 decode: closed-form words and torch's bfloat16 (library routine)."""
+    words = np.array([0x3F80, 0xC000, 0x0001, 0x7F7F, 0x8000, 0x4049], dtype=np.uint16)
+    got = O.decode_bf16(words)
+    want = [1.0, -2.0, 2.0 ** -133, (2 - 2.0 ** -7) * 2.0 ** 127, -0.0, 3.140625]
+    for g, w in zip(got, want):
+        assert g == w and math.copysign(1, g) == math.copysign(1, w), (g, w)
+    r = _rng(1).integers(0, 1 << 16, size=4096, dtype=np.uint16)
+    r = r[(r & 0x7F80) != 0x7F80]  # drop inf / nan words
+    lib = torch.from_numpy(r.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(O.decode_bf16(r), lib)
+
+
+# ---------------------------------------------------------------- P2 indexer
+
+def pin_indexer_hand_example():
+    """Hand-worked example (tests/golden/indexer_hand_example.json), float and fp8."""
+    with open(os.path.join(GOLDEN, "indexer_hand_example.json")) as f:
+        ex = json.load(f)
+    got = O.indexer_scores(np.array(ex["q"]), np.array(ex["w"]), np.array(ex["k"]))
+    assert np.array_equal(got, np.array(ex["expected"])), got
+    f8 = ex["fp8_case"]
+    k_codes = np.array(f8["k_codes"], dtype=np.uint8)
+    got8 = O.indexer_row(np.array(f8["q_codes"], dtype=np.uint8), np.array(f8["q_scale"]),
+                         np.array(ex["w"]), k_codes, np.array(f8["k_scale"]),
+                         t=len(k_codes) - 1, fp8=True)
+    assert np.array_equal(got8, np.array(f8["expected"])), got8
+
+
+def _brute_indexer(q, w, k):
+    H, d = q.shape
+    out = []
+    for s in range(k.shape[0]):
+        acc = 0.0
+        for j in range(H):
+            dot = 0.0
+            for i in range(d):
+                dot += float(q[j, i]) * float(k[s, i])
+            acc += float(w[j]) * (dot if dot > 0.0 else 0.0)
+        out.append(acc)
+    return np.array(out)
+
+
+def pin_indexer_bruteforce():
+    """Pure-Python loops on small non-square shapes (catches transposed operands)."""
+    r = _rng(2)
+    for H, d, n in [(3, 5, 7), (1, 4, 9), (4, 32, 11), (2, 1, 3)]:
+        q = r.standard_normal((H, d))
+        w = r.standard_normal(H)
+        k = r.standard_normal((n, d))
+        got = O.indexer_scores(q, w, k)
+        assert got.shape == (n,)
+        np.testing.assert_allclose(got, _brute_indexer(q, w, k), rtol=1e-12, atol=1e-12)
+
+
+def pin_indexer_invariants():
+    r = _rng(3)
+    H, d, n = 6, 16, 40
+    q = r.standard_normal((H, d))
+    w = r.standard_normal(H)
+    k = r.standard_normal((n, d))
+    base = O.indexer_scores(q, w, k)
+    # a permutation of the heads (with their weights) leaves I unchanged
+    p = r.permutation(H)
+    np.testing.assert_allclose(O.indexer_scores(q[p], w[p], k), base, rtol=1e-12, atol=1e-12)
+    # I is linear in w
+    np.testing.assert_allclose(O.indexer_scores(q, 2.5 * w, k), 2.5 * base, rtol=1e-12, atol=1e-12)
+    # every q.k <= 0 gives exactly zero scores (ReLU)
+    kneg = -np.abs(k)
+    assert np.all(O.indexer_scores(np.abs(q), np.abs(w) + 0.1, kneg) == 0.0)
+    # H_I = 1, w = 1 reduces to ReLU of a single dot product
+    one = O.indexer_scores(q[:1], np.ones(1), k)
+    np.testing.assert_allclose(one, np.maximum(k @ q[0], 0.0), rtol=1e-12, atol=1e-12)
+
+
+def pin_indexer_row_causal_and_scales():
+    """indexer_row: exactly t+1 candidates (s <= t); trading a positive constant
+    between the q and k scales leaves I unchanged; keys after t do not matter."""
+    r = _rng(4)
+    H, d, L = 4, 8, 12
+    q_codes = r.integers(0, 0x7E, size=(H, d), dtype=np.uint8) ^ (r.integers(0, 2, size=(H, d), dtype=np.uint8) << 7)
+    k_codes = r.integers(0, 0x7E, size=(L, d), dtype=np.uint8) ^ (r.integers(0, 2, size=(L, d), dtype=np.uint8) << 7)
+    qs = np.exp2(r.integers(-8, 2, size=H)).astype(np.float64)
+    ks = np.exp2(r.integers(-8, 2, size=L)).astype(np.float64)
+    w = r.standard_normal(H)
+    for t in [0, 1, 5, L - 1]:
+        I = O.indexer_row(q_codes, qs, w, k_codes, ks, t, fp8=True)
+        assert I.shape == (t + 1,)
+        k2 = k_codes.copy()
+        k2[t + 1:] = 0x7E
+        np.testing.assert_array_equal(O.indexer_row(q_codes, qs, w, k2, ks, t, True), I)
+        I2 = O.indexer_row(q_codes, qs * 4.0, w, k_codes, ks / 4.0, t, True)
+        np.testing.assert_allclose(I2, I, rtol=1e-12, atol=1e-300)
+        # dequantised brute force
+        qf = O.decode_e4m3fn(q_codes) * qs[:, None]
+        kf = O.decode_e4m3fn(k_codes[: t + 1]) * ks[: t + 1, None]
+        np.testing.assert_allclose(I, _brute_indexer(qf, w, kf), rtol=1e-12, atol=1e-300)
+    # t = 0 scores the query's own position only
+    I0 = O.indexer_row(q_codes, qs, w, k_codes, ks, 0, True)
+    qf = O.decode_e4m3fn(q_codes) * qs[:, None]
+    kf0 = O.decode_e4m3fn(k_codes[0]) * ks[0]
+    assert np.isclose(I0[0], float(np.sum(w * np.maximum(qf @ kf0, 0.0))), rtol=1e-12)
+
+
+# ---------------------------------------------------------------- P3 top-k
+
+def _brute_topk(I, n):
+    return sorted(sorted(range(len(I)), key=lambda s: (-I[s], s))[:n])
+
+
+def pin_topk_bruteforce():
+    r = _rng(5)
+    for L, n in [(1, 1), (5, 3), (17, 17), (40, 7), (64, 64), (100, 10)]:
+        for kind in ("normal", "dupes", "negative"):
+            if kind == "normal":
+                I = r.standard_normal(L)
+            elif kind == "dupes":
+                I = r.integers(-2, 3, size=L).astype(np.float64)
+            else:
+                I = -np.abs(r.standard_normal(L)) - 1.0
+            got = O.select_topk(I, n)
+            assert list(got) == _brute_topk(I, n), (L, n, kind)
+
+
+def pin_topk_special_rows():
+    # all-zero row (every ReLU zero): the n lowest positions
+    assert list(O.select_topk(np.zeros(50), 8)) == list(range(8))
+    # exact tie straddling the cut: the lower position wins
+    I = np.array([5.0, 1.0, 3.0, 2.0, 3.0, 0.5])
+    assert list(O.select_topk(I, 2)) == [0, 2]
+    # only m < n positive scores: those, then the lowest-position zeros
+    I = np.zeros(20)
+    I[[7, 13, 19]] = [1.0, 2.0, 3.0]
+    assert list(O.select_topk(I, 6)) == [0, 1, 2, 7, 13, 19]
+    # n >= L selects everything
+    assert list(O.select_topk(np.array([3.0, -1.0, 2.0]), 3)) == [0, 1, 2]
+    # -0.0 and +0.0 are equal scores
+    I = np.array([0.0, -0.0, 1.0, -0.0, 0.0])
+    assert list(O.select_topk(I, 3)) == [0, 1, 2]
+
+
+# ---------------------------------------------------------------- P4 attention
+
+def pin_attention_hand_example():
+    with open(os.path.join(GOLDEN, "attention_hand_example.json")) as f:
+        ex = json.load(f)
+    o, lse = O.sparse_attention(np.array(ex["q"]), np.array(ex["entries"]), ex["scale"],
+                                ex["v_dim"])
+    assert o.shape == (2, ex["v_dim"])
+    np.testing.assert_allclose(o[0], ex["expected_o_head0"], rtol=1e-13)
+    np.testing.assert_allclose(o[1], ex["expected_o_head1"], rtol=1e-13)
+    np.testing.assert_allclose(lse, [ex["expected_lse_head0"], ex["expected_lse_head1"]],
+                               rtol=1e-13)
+
+
+def pin_attention_dense_equivalence():
+    """Rows with t+1 <= k select every prior position, so the path must equal dense
+    causal MQA attention; the dense side is torch's scaled_dot_product_attention
+    in float64 (a library routine) with a causal mask."""
+    r = _rng(6)
+    H, Dk, Dv, L, k = 3, 10, 6, 9, 16
+    q = r.standard_normal((L, H, Dk))
+    c = r.standard_normal((L, Dk))
+    scale = 0.37
+    qt = torch.from_numpy(q).permute(1, 0, 2).contiguous()          # [H, L, Dk]
+    kt = torch.from_numpy(c).unsqueeze(0).expand(H, L, Dk).contiguous()
+    vt = torch.from_numpy(c[:, :Dv]).unsqueeze(0).expand(H, L, Dv).contiguous()
+    dense = torch.nn.functional.scaled_dot_product_attention(
+        qt, kt, vt, is_causal=True, scale=scale).permute(1, 0, 2).numpy()  # [L, H, Dv]
+    for t in range(L):
+        S = O.select_topk(np.zeros(t + 1), min(k, t + 1))
+        assert list(S) == list(range(t + 1))
+        o, lse = O.sparse_attention(q[t], c[S], scale, Dv)
+        np.testing.assert_allclose(o, dense[t], rtol=1e-12, atol=1e-12)
+        z = scale * (q[t] @ c[: t + 1].T)
+        from scipy.special import logsumexp
+        np.testing.assert_allclose(lse, logsumexp(z, axis=1), rtol=1e-12, atol=1e-12)
+
+
+def pin_attention_closed_forms():
+    r = _rng(7)
+    H, Dk, Dv = 4, 12, 8
+    q = r.standard_normal((H, Dk))
+    c = r.standard_normal((5, Dk))
+    # single entry: o is that entry's value part, lse = scale * q.c
+    o, lse = O.sparse_attention(q, c[:1], 0.3, Dv)
+    assert np.array_equal(o, np.broadcast_to(c[0, :Dv], (H, Dv)))
+    np.testing.assert_allclose(lse, 0.3 * (q @ c[0]), rtol=1e-14)
+    # identical entries: o equals the entry
+    same = np.repeat(c[2:3], 7, axis=0)
+    o, lse = O.sparse_attention(q, same, 0.3, Dv)
+    np.testing.assert_allclose(o, np.broadcast_to(c[2, :Dv], (H, Dv)), rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(lse, 0.3 * (q @ c[2]) + np.log(7.0), rtol=1e-13)
+    # scale 0: plain mean of the values, lse = log n
+    o, lse = O.sparse_attention(q, c, 0.0, Dv)
+    np.testing.assert_allclose(o, np.broadcast_to(c[:, :Dv].mean(0), (H, Dv)), rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(lse, np.log(5.0), rtol=1e-14)
+    # convex combination: every output coordinate lies within the values' range
+    o, _ = O.sparse_attention(q * 3, c, 1.0, Dv)
+    lo, hi = c[:, :Dv].min(0), c[:, :Dv].max(0)
+    assert np.all(o >= lo - 1e-12) and np.all(o <= hi + 1e-12)
+    # order of the selected entries does not matter
+    p = r.permutation(5)
+    o1, l1 = O.sparse_attention(q, c, 0.7, Dv)
+    o2, l2 = O.sparse_attention(q, c[p], 0.7, Dv)
+    np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(l1, l2, rtol=1e-12)
+
+
+def pin_attention_bruteforce():
+    """Softmax attention by explicit loops with math.exp on a tiny case."""
+    r = _rng(8)
+    H, Dk, Dv, n = 2, 3, 2, 4
+    q = r.standard_normal((H, Dk))
+    c = r.standard_normal((n, Dk))
+    o, lse = O.sparse_attention(q, c, 0.9, Dv)
+    for h in range(H):
+        z = [0.9 * sum(q[h, i] * c[s, i] for i in range(Dk)) for s in range(n)]
+        den = sum(math.exp(v) for v in z)
+        for d in range(Dv):
+            num = sum(math.exp(z[s]) * c[s, d] for s in range(n))
+            assert abs(o[h, d] - num / den) < 1e-12
+        assert abs(lse[h] - math.log(den)) < 1e-12
+
+
+# ---------------------------------------------------------------- P5 composition
+
+def pin_dsa_row_composition():
+    """dsa_row = indexer -> top-k -> attention; with k >= t+1 the output is dense
+    causal attention; with k < t+1 it is attention over the brute-force top-k."""
+    r = _rng(9)
+    H_I, d_I, H, Dk, Dv, L = 2, 4, 3, 6, 4, 12
+    q_idx = r.standard_normal((L, H_I, d_I)).astype(np.float32)
+    w = r.random((L, H_I)).astype(np.float32)
+    k_idx = r.standard_normal((L, d_I)).astype(np.float32)
+    q = r.standard_normal((L, H, Dk)).astype(np.float32)
+    lat = r.standard_normal((L, Dk)).astype(np.float32)
+    for t in range(L):
+        for k in (L, 5):
+            I, S, o, lse = O.dsa_row(q_idx[t], None, w[t], k_idx, None, q[t], lat, t, k,
+                                     0.5, Dv, quantised=False)
+            Ib = _brute_indexer(q_idx[t].astype(np.float64), w[t].astype(np.float64),
+                                k_idx[: t + 1].astype(np.float64))
+            np.testing.assert_allclose(I, Ib, rtol=1e-12, atol=1e-12)
+            Sb = _brute_topk(list(Ib), min(k, t + 1))
+            assert list(S) == Sb
+            zz = 0.5 * (q[t].astype(np.float64) @ lat[Sb].astype(np.float64).T)
+            ww = np.exp(zz - zz.max(1, keepdims=True))
+            ww /= ww.sum(1, keepdims=True)
+            np.testing.assert_allclose(o, ww @ lat[Sb, :Dv].astype(np.float64), rtol=1e-12, atol=1e-12)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

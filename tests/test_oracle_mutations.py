@@ -1,0 +1,122 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that the pins
+catch every one of them: a pin suite that passes a broken oracle pins nothing."""
+import numpy as np
+import pytest
+
+import oracle.dsa_oracle as O
+import oracle_pins
+
+_orig = {name: getattr(O, name) for name in
+         ["indexer_scores", "select_topk", "sparse_attention", "decode_e4m3fn",
+          "decode_bf16", "indexer_row"]}
+
+
+def _no_relu(q, w, k):
+    return w @ (q @ k.T)
+
+
+def _relu_after_sum(q, w, k):
+    return np.maximum(w @ (q @ k.T), 0.0)
+
+
+def _w_per_key(q, w, k):
+    return np.maximum(q @ k.T, 0.0).sum(0) * w.mean()
+
+
+def _scaled_by_sqrt_d(q, w, k):
+    return _orig["indexer_scores"](q, w, k) / np.sqrt(q.shape[1])
+
+
+def _ties_high(scores, n):
+    scores = np.asarray(scores, dtype=np.float64)
+    pos = np.arange(scores.shape[0])
+    order = np.lexsort((-pos, -scores))
+    return np.sort(order[:n])
+
+
+def _smallest(scores, n):
+    return np.sort(np.argsort(scores, kind="stable")[:n])
+
+
+def _unstable(scores, n):
+    return np.sort(np.argsort(-np.asarray(scores), kind="quicksort")[:n][::-1])
+
+
+def _value_last_cols(q, e, scale, v_dim):
+    z = scale * (q @ e.T)
+    m = z.max(1, keepdims=True)
+    p = np.exp(z - m)
+    Z = p.sum(1, keepdims=True)
+    return (p / Z) @ e[:, -v_dim:], m[:, 0] + np.log(Z[:, 0])
+
+
+def _no_scale(q, e, scale, v_dim):
+    return _orig["sparse_attention"](q, e, 1.0, v_dim)
+
+
+def _lse_no_max(q, e, scale, v_dim):
+    o, lse = _orig["sparse_attention"](q, e, scale, v_dim)
+    z = scale * (q @ e.T)
+    return o, lse - z.max(1)
+
+
+def _no_softmax_norm(q, e, scale, v_dim):
+    z = scale * (q @ e.T)
+    p = np.exp(z - z.max(1, keepdims=True))
+    return p @ e[:, :v_dim], np.log(p.sum(1)) + z.max(1)
+
+
+def _fnuz_bias(codes):
+    return _orig["decode_e4m3fn"](codes) / 2.0
+
+
+def _no_subnormals(codes):
+    v = _orig["decode_e4m3fn"](codes)
+    c = np.asarray(codes).astype(np.int64)
+    return np.where(((c >> 3) & 0xF) == 0, 0.0 * v, v)
+
+
+def _bf16_low_half(bits):
+    b = np.asarray(bits).astype(np.uint32)
+    return (b | (b << 16)).view(np.float32).astype(np.float64)
+
+
+def _exclusive_causal(q_idx, q_scale, w, k_idx, k_scale, t, fp8):
+    full = _orig["indexer_row"](q_idx, q_scale, w, k_idx, k_scale, t, fp8)
+    return full[:t] if t > 0 else full
+
+
+def _scale_ignored(q_idx, q_scale, w, k_idx, k_scale, t, fp8):
+    return _orig["indexer_row"](q_idx, None, w, k_idx, None, t, fp8)
+
+
+MUTANTS = [
+    ("indexer_scores", _no_relu),
+    ("indexer_scores", _relu_after_sum),
+    ("indexer_scores", _w_per_key),
+    ("indexer_scores", _scaled_by_sqrt_d),
+    ("select_topk", _ties_high),
+    ("select_topk", _smallest),
+    ("select_topk", _unstable),
+    ("sparse_attention", _value_last_cols),
+    ("sparse_attention", _no_scale),
+    ("sparse_attention", _lse_no_max),
+    ("sparse_attention", _no_softmax_norm),
+    ("decode_e4m3fn", _fnuz_bias),
+    ("decode_e4m3fn", _no_subnormals),
+    ("decode_bf16", _bf16_low_half),
+    ("indexer_row", _exclusive_causal),
+    ("indexer_row", _scale_ignored),
+]
+
+
+@pytest.mark.parametrize("name,mutant", MUTANTS, ids=lambda x: getattr(x, "__name__", x))
+def test_pins_catch_mutant(monkeypatch, name, mutant):
+    monkeypatch.setattr(O, name, mutant)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin()
+        except Exception:  # AssertionError or a shape error both count as caught
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches the planted mistake {mutant.__name__} in {name}"
