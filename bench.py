@@ -1,0 +1,208 @@
+"""Benchmark of the DSA hot path on one MI355X.
+
+A step is one pass of the whole path (indexer scores -> top-k -> sparse MLA
+attention) over one batch of synthetic input already resident in HBM.  The
+headline workload is decode at 32K context, batch 32 (one new token per
+sequence); 4 independent input sets are rotated so the 256 MB MALL cannot serve
+a step from the previous one.
+
+Prints one JSON line.  Per-step kernel times come from HIP events recorded on the
+stream the library launches on, around each of the three C-ABI calls inside the
+timed region.
+
+    python bench.py [--steps K] [--warmup W] [--workload decode32k] [--extra]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "DSA decode tokens/s @32K ctx; 128K prefill tokens/s; % HBM/MFMA peak"
+HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+# Algorithmic work per unit (documented in the design doc):
+IDX_BYTES_PER_PAIR = 132          # fp8 key (128 B) + fp32 scale per (row, candidate key)
+IDX_FLOP_PER_PAIR = 2 * 64 * 128  # 64 heads x 128-wide fp8 dot per (row, key)
+TOPK_BYTES_PER_PAIR = 4           # one fp32 score read per (row, candidate)
+ATTN_BYTES_PER_ENTRY = 1152       # one gathered 576-wide bf16 latent row per (row, selected)
+ATTN_BYTES_PER_ROW = 128 * 576 * 2 + 128 * 512 * 2  # q in + out
+ATTN_FLOP_PER_ENTRY = 2 * 128 * (576 + 512)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="decode32k")
+    p.add_argument("--sets", type=int, default=4)
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--extra", action="store_true",
+                   help="also time decode128k, prefill8k and prefill128k")
+    return p.parse_args()
+
+
+def _pairs(cfg):
+    """(row, candidate key) pairs and (row, selected entry) pairs of one step."""
+    seq, pos = cfg.row_seq_pos()
+    cand = int((pos.astype("int64") + 1).sum())
+    sel = int(sum(min(cfg.topk, int(t) + 1) for t in pos))
+    return cand, sel
+
+
+class Step:
+    """Device buffers and the three C-ABI calls of one input set."""
+
+    def __init__(self, dsa, di, cfg, set_id, r0=0, r1=None):
+        import torch
+
+        self.cfg = cfg
+        self.inp = di.make_inputs(cfg, set_id, device="cuda", rows=(r0, r1 or cfg.num_rows))
+        R = self.inp.row_pos.numel()
+        self.rows = dsa.rows_struct(self.inp.row_seq, self.inp.row_pos, cfg.num_seqs,
+                                    cfg.max_ctx, cfg.kv_len - 1)
+        self.dims = dsa.Dims.from_config(cfg)
+        self.ld = (cfg.kv_len + 63) // 64 * 64
+        self.scores = torch.empty(R, self.ld, dtype=torch.float32, device="cuda")
+        self.idx = torch.empty(R, cfg.topk, dtype=torch.int32, device="cuda")
+        self.out = torch.empty(R, cfg.n_heads, cfg.v_dim, dtype=torch.bfloat16, device="cuda")
+        self.lse = torch.empty(R, cfg.n_heads, dtype=torch.float32, device="cuda")
+        need = dsa.sparse_mla_attn_workspace_size(self.rows, self.dims)
+        self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+        self.dsa = dsa
+
+    def run(self, ev=None):
+        d, i = self.dsa, self.inp
+        if ev: ev[0].record()
+        d.indexer_scores(self.rows, self.dims, i.q_idx, i.q_scale, i.w, i.k_idx, i.k_scale,
+                         scores=self.scores)
+        if ev: ev[1].record()
+        d.topk(self.rows, self.cfg.topk, self.scores, indices=self.idx)
+        if ev: ev[2].record()
+        d.sparse_mla_attn(self.rows, self.dims, i.q, i.latent, self.idx, self.cfg.scale,
+                          out=self.out, lse=self.lse, workspace=self.ws)
+        if ev: ev[3].record()
+
+
+def time_steps(steps, K, W):
+    import torch
+
+    for i in range(W):
+        steps[i % len(steps)].run()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        steps[i % len(steps)].run(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    k_ms = [[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in evs]
+    avg = [sum(x[j] for x in k_ms) / K for j in range(3)]
+    return wall / K * 1e3, avg
+
+
+def cpu_baseline(di, cfg, budget_s=20.0):
+    """The float64 oracle on a bounded sample of the workload's rows, host cores."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    g = di.Generator(cfg, 0)
+    seq, pos = cfg.row_seq_pos()
+    rows = di.sample_rows(cfg, 64)
+    done, spent = 0, 0.0
+    for r in rows:
+        b, t = int(seq[r]), int(pos[r])
+        qc, qs = g.q_idx(int(r), int(r) + 1)
+        kc, ks = g.k_idx(b, 0, t + 1)
+        qv = g.q(int(r), int(r) + 1)[0]
+        lat = g.latent(b, 0, t + 1)
+        args = (qc[0].numpy(), qs[0].numpy().astype(np.float64),
+                g.w(int(r), int(r) + 1)[0].numpy().astype(np.float64), kc.numpy(),
+                ks.numpy().astype(np.float64), di.bf16_bits(qv), di.bf16_bits(lat))
+        t0 = time.perf_counter()
+        oracle.dsa_row(*args, t, cfg.topk, cfg.scale, cfg.v_dim, quantised=True)
+        spent += time.perf_counter() - t0
+        done += 1
+        if spent >= budget_s:
+            break
+    return {"value": done / spent, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {cfg.num_rows} query rows of {cfg.name} (full indexer, top-k "
+                      f"and attention per row, float64 numpy), {spent:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path is "
+              f"single-GPU; see DESIGN.md for how it would shard)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import dsa_inputs as di
+    import sparse_attention_fp8_amd as dsa
+
+    cfg = di.CONFIGS[args.workload]
+    print(f"[bench] generating {args.sets} input sets of {cfg.name}", file=sys.stderr, flush=True)
+    steps = [Step(dsa, di, cfg, s) for s in range(args.sets)]
+    torch.cuda.synchronize()
+    print("[bench] timing", file=sys.stderr, flush=True)
+    ms, k_ms = time_steps(steps, args.steps, args.warmup)
+
+    cand, sel = _pairs(cfg)
+    R = cfg.num_rows
+    idx_bytes = cand * IDX_BYTES_PER_PAIR
+    topk_bytes = cand * TOPK_BYTES_PER_PAIR
+    attn_bytes = sel * ATTN_BYTES_PER_ENTRY + R * ATTN_BYTES_PER_ROW
+    kernels = {
+        "indexer": {"ms": k_ms[0], "bytes": idx_bytes,
+                    "gbs": idx_bytes / k_ms[0] / 1e6, "tflops": cand * IDX_FLOP_PER_PAIR / k_ms[0] / 1e9},
+        "topk": {"ms": k_ms[1], "bytes": topk_bytes, "gbs": topk_bytes / k_ms[1] / 1e6},
+        "attention": {"ms": k_ms[2], "bytes": attn_bytes, "gbs": attn_bytes / k_ms[2] / 1e6,
+                      "tflops": sel * ATTN_FLOP_PER_ENTRY / k_ms[2] / 1e9},
+    }
+    dom = max(kernels, key=lambda k: kernels[k]["ms"])
+    kd = kernels[dom]
+    step_bytes = idx_bytes + attn_bytes
+    line = {
+        "metric": METRIC,
+        "value": R / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3+bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.description}", "batch": cfg.num_seqs,
+                   "context": cfg.kv_len, "topk": cfg.topk, "input_sets": args.sets},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": kd["gbs"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": kd["gbs"] / HBM_PEAK_GBS, "traffic": None},
+        "step_hbm_frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "kernels": kernels,
+    }
+    if not args.no_cpu:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(di, cfg)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,176 @@
+/*
+ * dsa.h - C ABI of the DeepSeek Sparse Attention (DSA) hot path on AMD MI355X (gfx950).
+ *
+ * The path has three steps, each a hand-written HIP kernel family:
+ *   1. lightning-indexer scores   I[t,s] = sum_j w[t,j] * ReLU(q[t,j] . k[s]),  s <= t
+ *      (DeepSeek-V3.2-Exp paper as translated on the m.163.com page, section 1
+ *      "Architecture", Eq. 1 and the prose around it: few indexer heads, ReLU,
+ *      FP8 arithmetic);
+ *   2. fine-grained top-k selection of the k highest-scoring positions per query
+ *      (same paper, section 1 text after Eq. 1, and section 2.1 "sparse training
+ *      stage": S_t and k = 2048);
+ *   3. sparse MLA attention in MQA mode over the selected latent entries, every
+ *      entry shared by all query heads (same paper, section 1 Eq. 2 and
+ *      "Instantiate DSA under MLA"; Appendix A, Fig. 4).  Key = the whole
+ *      qk_dim-wide entry (latent + rope part), value = its first v_dim columns.
+ *      The page "DeepSeek-V3.2开源技术报告" (nsmao.com, "DSA principle") gives the
+ *      cache widths: 128 per token for the indexer key, 512 for the latent.
+ *
+ * Conventions (all entry points):
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller; tensors are
+ *     dense, row-major, 16-byte aligned.  The library allocates nothing: scratch
+ *     comes from the caller's workspace.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the null
+ *     stream).  No call synchronises the device.
+ *   - Arguments are validated on the host before anything is enqueued; on any
+ *     status other than DSA_OK nothing was enqueued, except DSA_E_HIP, which
+ *     reports a failed launch (earlier launches of the same call may have run).
+ *     Device-side faults surface at the caller's next synchronisation.
+ *   - Thread-safe and re-entrant: no global mutable state except the per-thread
+ *     text behind dsa_last_error().
+ *   - No C++ exception crosses this interface.
+ *
+ * Row model: a call processes R query rows.  Row r belongs to sequence
+ * row_seq[r] (in [0, B)) and sits at position t = row_pos[r] (in [0, max_pos]) of
+ * that sequence; its candidates are the positions 0..t (inclusive).  Caches are
+ * per sequence with capacity N = max_ctx entries.  Rows whose row_seq or row_pos
+ * is out of range are not processed (their outputs are left unspecified) and
+ * cause no out-of-bounds access.
+ *
+ * Supported dimension sets (anything else returns DSA_E_UNSUPPORTED):
+ *   - production: H_I = 64, d_I = 128, fp8 e4m3fn indexer operands with fp32
+ *     scales; H = 128, D_k = 576, D_v = 512, bf16 attention operands; topk = 2048.
+ *   - fp32: idx_dtype = attn_dtype = DSA_F32 with H_I <= 64, d_I <= 128,
+ *     H <= 128, D_v <= D_k <= 576, topk <= 2048 (correctness configuration; plain
+ *     fp32 vector kernels).
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_API_VERSION 1
+
+typedef enum dsa_status {
+  DSA_OK = 0,
+  DSA_E_INVALID = 1,     /* null pointer, negative or inconsistent size */
+  DSA_E_UNSUPPORTED = 2, /* dimension / dtype combination with no kernel */
+  DSA_E_WORKSPACE = 3,   /* workspace missing or smaller than required */
+  DSA_E_HIP = 4          /* a HIP runtime call or launch failed */
+} dsa_status;
+
+typedef enum dsa_dtype {
+  DSA_F32 = 0,
+  DSA_BF16 = 1,
+  DSA_FP8_E4M3FN = 2 /* OCP 8-bit E4M3, finite-only ("fn"), bias 7, max 448 */
+} dsa_dtype;
+
+/* Query rows of one call.  The two arrays live in device memory; every other
+ * field is a host value. */
+typedef struct dsa_rows {
+  int32_t num_rows;       /* R >= 0 */
+  int32_t num_seqs;       /* B >= 1 */
+  int32_t max_ctx;        /* N >= 1: cache capacity per sequence, in entries */
+  int32_t max_pos;        /* host upper bound of row_pos[*]: 0 <= max_pos < N */
+  const int32_t* row_seq; /* device [R] */
+  const int32_t* row_pos; /* device [R] */
+} dsa_rows;
+
+typedef struct dsa_dims {
+  int32_t n_idx_heads; /* H_I: indexer heads */
+  int32_t idx_dim;     /* d_I: indexer query/key width */
+  int32_t n_heads;     /* H: attention query heads (all share each latent entry) */
+  int32_t qk_dim;      /* D_k: latent entry width (latent + rope) */
+  int32_t v_dim;       /* D_v: value width = leading columns of the entry */
+  int32_t topk;        /* k: positions selected per row */
+  dsa_dtype idx_dtype; /* DSA_FP8_E4M3FN or DSA_F32 */
+  dsa_dtype attn_dtype;/* DSA_BF16 or DSA_F32 */
+} dsa_dims;
+
+/* ---------------------------------------------------------------------------
+ * Step 1: indexer scores.
+ *   q_idx   [R, H_I, d_I]  fp8 codes (uint8) or fp32, per idx_dtype
+ *   q_scale [R, H_I]  fp32 > 0, dequantisation scale of each q vector (fp8 only;
+ *                     ignored and may be NULL for fp32)
+ *   w       [R, H_I]  fp32 head weights (any sign)
+ *   k_idx   [B, N, d_I] fp8 codes or fp32
+ *   k_scale [B, N]    fp32 > 0 (fp8 only; may be NULL for fp32)
+ *   scores  [R, ld_scores] fp32 output, ld_scores >= max_pos + 1
+ * For row r with t = row_pos[r], b = row_seq[r] and every s in [0, t]:
+ *   scores[r*ld + s] = sum_j w[r,j] * max(0, (q_scale[r,j] q_idx[r,j,:]) . (k_scale[b,s] k_idx[b,s,:]))
+ * computed with exact fp8 products and fp32 accumulation.  Entries s > t are not
+ * candidates: the call may write -inf to some of them and leaves the rest
+ * untouched.  Positive scales are required (they are folded through the ReLU).
+ * ------------------------------------------------------------------------- */
+dsa_status dsa_indexer_scores(const dsa_rows* rows, const dsa_dims* dims,
+                              const void* q_idx, const float* q_scale, const float* w,
+                              const void* k_idx, const float* k_scale,
+                              float* scores, int64_t ld_scores, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Step 2: top-k selection.
+ *   scores  [R, ld_scores] fp32 (only s <= row_pos[r] is read)
+ *   indices [R, topk] int32 output
+ * Row r selects exactly n = min(topk, t+1) positions: those with the largest
+ * scores, equal scores taken from the lowest position first (-0.0 equals +0.0).
+ * indices[r, 0..n) hold them in ascending order, indices[r, n..topk) hold -1.
+ * Supports topk in [1, 4096] and any t.  Scores must not be NaN (a NaN row gives
+ * an unspecified but in-range selection).
+ * ------------------------------------------------------------------------- */
+dsa_status dsa_topk(const dsa_rows* rows, int32_t topk, const float* scores,
+                    int64_t ld_scores, int32_t* indices, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Step 3: sparse MLA attention (MQA mode).
+ *   q       [R, H, D_k]  bf16 or fp32 per attn_dtype
+ *   latent  [B, N, D_k]  bf16 or fp32
+ *   indices [R, topk] int32: positions to attend; entries < 0 or >= N are padding
+ *   out     [R, H, D_v]  bf16 or fp32 output
+ *   lse     [R, H] fp32 output (natural log of the softmax denominator), or NULL
+ * For each row r and head h over the listed positions S:
+ *   z[s] = softmax_scale * q[r,h,:] . latent[b,s,:]
+ *   out[r,h,:] = sum_s softmax(z)[s] * latent[b,s,0:D_v],  lse[r,h] = log sum_s e^z[s]
+ * A listed position counts once per occurrence.  A row with no valid position
+ * gets out = 0 and lse = -inf.  bf16 path: bf16 products, fp32 accumulation and
+ * softmax, softmax weights rounded to bf16 for the value product, out rounded to
+ * nearest-even bf16.  The workspace holds split partial results
+ * (see dsa_sparse_mla_attn_workspace_size).
+ * ------------------------------------------------------------------------- */
+size_t dsa_sparse_mla_attn_workspace_size(const dsa_rows* rows, const dsa_dims* dims);
+
+dsa_status dsa_sparse_mla_attn(const dsa_rows* rows, const dsa_dims* dims,
+                               const void* q, const void* latent, const int32_t* indices,
+                               float softmax_scale, void* out, float* lse,
+                               void* workspace, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Whole path: step 1 -> step 2 -> step 3 for all R rows, processed in chunks of
+ * chunk_rows rows (0 = all rows at once) so the score workspace stays bounded.
+ * Inputs are those of the three steps; outputs out/lse as in step 3, plus the
+ * selected positions in indices_out [R, topk] when it is not NULL.  The workspace
+ * must be at least dsa_forward_workspace_size(rows, dims, chunk_rows) bytes.
+ * ------------------------------------------------------------------------- */
+size_t dsa_forward_workspace_size(const dsa_rows* rows, const dsa_dims* dims, int32_t chunk_rows);
+
+dsa_status dsa_forward(const dsa_rows* rows, const dsa_dims* dims,
+                       const void* q_idx, const float* q_scale, const float* w,
+                       const void* k_idx, const float* k_scale,
+                       const void* q, const void* latent, float softmax_scale,
+                       void* out, float* lse, int32_t* indices_out,
+                       int32_t chunk_rows, void* workspace, size_t ws_bytes, void* stream);
+
+/* Status text, and the detail of the last failure on the calling thread. */
+const char* dsa_status_string(dsa_status status);
+const char* dsa_last_error(void);
+int32_t dsa_api_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

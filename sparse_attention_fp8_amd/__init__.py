@@ -1,0 +1,234 @@
+"""Python binding of libdsa.so, the HIP implementation of the DeepSeek Sparse
+Attention (DSA) hot path for MI355X (gfx950).
+
+Every function here only marshals arguments (torch tensors -> device pointers,
+the current HIP stream) into the C ABI declared in ``include/dsa.h``; all the
+computation runs in the library's kernels.  Importing this package loads the
+library and raises if it is missing: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "LIB_PATH", "lib", "Dims", "PRODUCTION_DIMS", "rows_struct", "dims_struct",
+    "indexer_scores", "topk", "sparse_mla_attn", "forward", "forward_workspace_size",
+    "sparse_mla_attn_workspace_size", "DSAError", "EXPORTED_SYMBOLS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
+
+DSA_OK, DSA_E_INVALID, DSA_E_UNSUPPORTED, DSA_E_WORKSPACE, DSA_E_HIP = range(5)
+DSA_F32, DSA_BF16, DSA_FP8_E4M3FN = range(3)
+
+EXPORTED_SYMBOLS = [
+    "dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_attn_workspace_size",
+    "dsa_sparse_mla_attn", "dsa_forward_workspace_size", "dsa_forward",
+    "dsa_status_string", "dsa_last_error", "dsa_api_version",
+]
+
+
+class DSAError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{detail} (status {status})")
+        self.status = status
+
+
+class _Rows(ctypes.Structure):
+    _fields_ = [("num_rows", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
+                ("max_ctx", ctypes.c_int32), ("max_pos", ctypes.c_int32),
+                ("row_seq", ctypes.c_void_p), ("row_pos", ctypes.c_void_p)]
+
+
+class _Dims(ctypes.Structure):
+    _fields_ = [("n_idx_heads", ctypes.c_int32), ("idx_dim", ctypes.c_int32),
+                ("n_heads", ctypes.c_int32), ("qk_dim", ctypes.c_int32),
+                ("v_dim", ctypes.c_int32), ("topk", ctypes.c_int32),
+                ("idx_dtype", ctypes.c_int32), ("attn_dtype", ctypes.c_int32)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it first (python -m sparse_attention_fp8_amd.build)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                             ctypes.c_size_t)
+    R, D = ctypes.POINTER(_Rows), ctypes.POINTER(_Dims)
+    L.dsa_indexer_scores.argtypes = [R, D, vp, vp, vp, vp, vp, vp, i64, vp]
+    L.dsa_topk.argtypes = [R, i32, vp, i64, vp, vp]
+    L.dsa_sparse_mla_attn_workspace_size.argtypes = [R, D]
+    L.dsa_sparse_mla_attn_workspace_size.restype = sz
+    L.dsa_sparse_mla_attn.argtypes = [R, D, vp, vp, vp, f32, vp, vp, vp, sz, vp]
+    L.dsa_forward_workspace_size.argtypes = [R, D, i32]
+    L.dsa_forward_workspace_size.restype = sz
+    L.dsa_forward.argtypes = [R, D, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, i32, vp, sz, vp]
+    for name in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_attn", "dsa_forward"):
+        getattr(L, name).restype = ctypes.c_int
+    L.dsa_status_string.argtypes = [ctypes.c_int]
+    L.dsa_status_string.restype = ctypes.c_char_p
+    L.dsa_last_error.restype = ctypes.c_char_p
+    L.dsa_api_version.restype = ctypes.c_int32
+    return L
+
+
+lib = _load()
+
+
+class Dims:
+    """Dimension set of a DSA layer (mirrors dsa_dims)."""
+
+    def __init__(self, n_idx_heads, idx_dim, n_heads, qk_dim, v_dim, topk, fp32: bool):
+        self.n_idx_heads, self.idx_dim, self.n_heads = n_idx_heads, idx_dim, n_heads
+        self.qk_dim, self.v_dim, self.topk, self.fp32 = qk_dim, v_dim, topk, fp32
+
+    @classmethod
+    def from_config(cls, cfg) -> "Dims":
+        return cls(cfg.n_idx_heads, cfg.idx_dim, cfg.n_heads, cfg.qk_dim, cfg.v_dim, cfg.topk,
+                   cfg.fp32)
+
+
+PRODUCTION_DIMS = Dims(64, 128, 128, 576, 512, 2048, False)
+
+
+def dims_struct(d: Dims) -> _Dims:
+    return _Dims(d.n_idx_heads, d.idx_dim, d.n_heads, d.qk_dim, d.v_dim, d.topk,
+                 DSA_F32 if d.fp32 else DSA_FP8_E4M3FN, DSA_F32 if d.fp32 else DSA_BF16)
+
+
+def rows_struct(row_seq: torch.Tensor, row_pos: torch.Tensor, num_seqs: int, max_ctx: int,
+                max_pos: int) -> _Rows:
+    _dev(row_seq, torch.int32, "row_seq")
+    _dev(row_pos, torch.int32, "row_pos")
+    return _Rows(row_pos.numel(), num_seqs, max_ctx, max_pos, _ptr(row_seq), _ptr(row_pos))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: Optional[torch.Tensor], dtype, name):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(status: int):
+    if status != DSA_OK:
+        raise DSAError(status, lib.dsa_last_error().decode() or lib.dsa_status_string(status).decode())
+
+
+def _idx_dtype(d: Dims):
+    return torch.float32 if d.fp32 else torch.uint8
+
+
+def _attn_dtype(d: Dims):
+    return torch.float32 if d.fp32 else torch.bfloat16
+
+
+def indexer_scores(rows: _Rows, dims: Dims, q_idx, q_scale, w, k_idx, k_scale,
+                   scores: Optional[torch.Tensor] = None, ld: Optional[int] = None) -> torch.Tensor:
+    """dsa_indexer_scores: returns scores [R, ld] (entries s > t unspecified)."""
+    _dev(q_idx, _idx_dtype(dims), "q_idx")
+    _dev(k_idx, _idx_dtype(dims), "k_idx")
+    _dev(w, torch.float32, "w")
+    _dev(q_scale, torch.float32, "q_scale")
+    _dev(k_scale, torch.float32, "k_scale")
+    if scores is None:
+        ld = ld or rows.max_pos + 1
+        scores = torch.empty(rows.num_rows, ld, dtype=torch.float32, device=q_idx.device)
+    _dev(scores, torch.float32, "scores")
+    ds = dims_struct(dims)
+    _check(lib.dsa_indexer_scores(ctypes.byref(rows), ctypes.byref(ds), _ptr(q_idx), _ptr(q_scale),
+                                  _ptr(w), _ptr(k_idx), _ptr(k_scale), _ptr(scores),
+                                  scores.shape[1], _stream()))
+    return scores
+
+
+def topk(rows: _Rows, k: int, scores: torch.Tensor,
+         indices: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """dsa_topk: returns indices [R, k] int32 (ascending, -1 padded)."""
+    _dev(scores, torch.float32, "scores")
+    if indices is None:
+        indices = torch.empty(rows.num_rows, k, dtype=torch.int32, device=scores.device)
+    _dev(indices, torch.int32, "indices")
+    _check(lib.dsa_topk(ctypes.byref(rows), k, _ptr(scores), scores.shape[1], _ptr(indices),
+                        _stream()))
+    return indices
+
+
+def sparse_mla_attn_workspace_size(rows: _Rows, dims: Dims) -> int:
+    ds = dims_struct(dims)
+    return int(lib.dsa_sparse_mla_attn_workspace_size(ctypes.byref(rows), ctypes.byref(ds)))
+
+
+def sparse_mla_attn(rows: _Rows, dims: Dims, q, latent, indices, softmax_scale: float,
+                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """dsa_sparse_mla_attn: returns (out [R,H,D_v], lse [R,H])."""
+    adt = _attn_dtype(dims)
+    _dev(q, adt, "q")
+    _dev(latent, adt, "latent")
+    _dev(indices, torch.int32, "indices")
+    R = rows.num_rows
+    if out is None:
+        out = torch.empty(R, dims.n_heads, dims.v_dim, dtype=adt, device=q.device)
+    if lse is None:
+        lse = torch.empty(R, dims.n_heads, dtype=torch.float32, device=q.device)
+    _dev(out, adt, "out")
+    _dev(lse, torch.float32, "lse")
+    need = sparse_mla_attn_workspace_size(rows, dims)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    ds = dims_struct(dims)
+    _check(lib.dsa_sparse_mla_attn(ctypes.byref(rows), ctypes.byref(ds), _ptr(q), _ptr(latent),
+                                   _ptr(indices), float(softmax_scale), _ptr(out), _ptr(lse),
+                                   _ptr(workspace), ws_bytes, _stream()))
+    return out, lse
+
+
+def forward_workspace_size(rows: _Rows, dims: Dims, chunk_rows: int = 0) -> int:
+    ds = dims_struct(dims)
+    return int(lib.dsa_forward_workspace_size(ctypes.byref(rows), ctypes.byref(ds), chunk_rows))
+
+
+def forward(rows: _Rows, dims: Dims, q_idx, q_scale, w, k_idx, k_scale, q, latent,
+            softmax_scale: float, out=None, lse=None, indices_out=None, chunk_rows: int = 0,
+            workspace: Optional[torch.Tensor] = None):
+    """dsa_forward: indexer -> top-k -> attention.  Returns (out, lse, indices_out)."""
+    adt = _attn_dtype(dims)
+    for t, dt, name in ((q_idx, _idx_dtype(dims), "q_idx"), (k_idx, _idx_dtype(dims), "k_idx"),
+                        (w, torch.float32, "w"), (q_scale, torch.float32, "q_scale"),
+                        (k_scale, torch.float32, "k_scale"), (q, adt, "q"), (latent, adt, "latent")):
+        _dev(t, dt, name)
+    R = rows.num_rows
+    if out is None:
+        out = torch.empty(R, dims.n_heads, dims.v_dim, dtype=adt, device=q.device)
+    if lse is None:
+        lse = torch.empty(R, dims.n_heads, dtype=torch.float32, device=q.device)
+    _dev(out, adt, "out")
+    _dev(lse, torch.float32, "lse")
+    _dev(indices_out, torch.int32, "indices_out")
+    need = forward_workspace_size(rows, dims, chunk_rows)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ds = dims_struct(dims)
+    _check(lib.dsa_forward(ctypes.byref(rows), ctypes.byref(ds), _ptr(q_idx), _ptr(q_scale),
+                           _ptr(w), _ptr(k_idx), _ptr(k_scale), _ptr(q), _ptr(latent),
+                           float(softmax_scale), _ptr(out), _ptr(lse), _ptr(indices_out),
+                           int(chunk_rows), _ptr(workspace), workspace.numel(), _stream()))
+    return out, lse, indices_out

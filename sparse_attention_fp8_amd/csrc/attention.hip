@@ -1,0 +1,475 @@
+// Sparse MLA attention in MQA mode on gfx950.
+//
+// For query row r (sequence b) and head h over the selected positions S_r:
+//   z[s] = scale * q[r,h,:] . c[b,s,:]          (576 = 512 latent + 64 rope)
+//   o[r,h,:] = sum_s softmax(z)[s] * c[b,s,0:512],  lse[r,h] = log sum_s e^z[s]
+// (DeepSeek-V3.2-Exp paper, section 1 Eq. 2 prose and "Instantiate DSA under MLA":
+// every latent entry is shared by all query heads of the token; Appendix A, Fig. 4:
+// MQA mode of MLA.)
+//
+// Kernel design (bf16 path, H = 128, D_k = 576, D_v = 512):
+// * one 256-thread block (4 waves x 32 heads) per (row, split); a split is a
+//   contiguous slice of the row's selected positions.  Splits of a row are mapped
+//   to one XCD so the row's queries are fetched from HBM once per XCD L2.
+// * the wave's 32 queries live in registers for the whole block (B operand of
+//   S^T = C q^T, 144 VGPRs); the 32 x 512 fp32 output accumulators are MFMA
+//   accumulators (256 registers).
+// * positions are processed 32 at a time.  The 32 gathered latent rows (36 KB) are
+//   copied HBM -> LDS by direct global_load_lds (no registers), double-buffered so
+//   the next block's gather overlaps this block's MFMAs.  A swizzle of the 16-byte
+//   chunks inside each row keeps the MFMA operand reads free of bank conflicts.
+//   The value part is then re-laid out in LDS as [dim][position] so the P.V
+//   contraction over positions reads contiguous 8-byte runs.
+// * S^T tiles (M = 16 positions, N = 16 heads) leave each lane with 4 consecutive
+//   positions of one head, which is exactly the P operand of the P.V MFMA
+//   (M = 16 heads, K = 32 positions) after a bf16 cast: no shuffles.
+// * online softmax in the exp2 domain with a stale-max rule: the running max is
+//   only raised (and the accumulators rescaled) when a block's max exceeds it by
+//   more than 2^8, which keeps every exponent <= 2^8 and skips nearly all rescales.
+#include "dsa_device.h"
+#include "dsa_internal.h"
+
+namespace dsa {
+namespace {
+
+constexpr int H = kHeads;           // 128
+constexpr int DK = kQkDim;          // 576
+constexpr int DV = kVDim;           // 512
+constexpr int BE = 32;              // positions per block
+constexpr int KROW = DK * 2;        // 1152 bytes per latent row
+constexpr int KCH = KROW / 16;      // 72 chunks of 16 bytes
+constexpr int VS = 72;              // bytes per [dim] row of the transposed value tile
+constexpr int KBUF = BE * KROW;     // 36864
+constexpr int VBUF = DV * VS;       // 36864
+constexpr int STAGE = KBUF + VBUF;  // 73728
+constexpr int NT = 256;
+constexpr int LOADS_PER_WAVE = KBUF / 1024 / 4;  // 9 direct loads of 1 KB per wave
+constexpr float kStaleMax = 8.0f;   // log2 headroom of the stale running max
+constexpr float kLn2 = 0.69314718055994530942f;
+
+static_assert(KBUF % 4096 == 0, "block gather must split evenly over 4 waves");
+
+// physical 16-byte slot of logical chunk c of entry e inside its 1152-byte row
+__device__ __forceinline__ int kswz(int e, int c) { return (c & ~7) | ((c ^ e) & 7); }
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ lds_ptr_t to_lds(void* p) {
+  return (lds_ptr_t)(p);
+}
+
+__global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ latent,
+    const int32_t* __restrict__ indices, const int32_t* __restrict__ row_seq,
+    const int32_t* __restrict__ row_pos, int R, int B, int N, int topk, int splits,
+    float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
+    float* __restrict__ o_part, float* __restrict__ lse_part) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+  __shared__ int sidx[kTopk];
+
+  const int tid = threadIdx.x, l = lane_id(), wv = tid >> 6, g = l >> 4, nn = l & 15;
+  // XCD-aware decode of the block id: all splits of row r run on XCD r % 8.
+  const int xcd = blockIdx.x & 7;
+  const int rest = blockIdx.x >> 3;
+  const int sp = rest % splits;
+  const int r = (rest / splits) * 8 + xcd;
+  if (r >= R) return;
+  const int b = row_seq[r], t = row_pos[r];
+  if (b < 0 || b >= B || t < 0 || t >= N) return;
+
+  const int ES = topk / splits;  // positions of this split
+  const int nblk = ES / BE;
+  const int32_t* irow = indices + (size_t)r * topk + (size_t)sp * ES;
+  for (int i = tid; i < ES; i += NT) {
+    const int p = irow[i];
+    sidx[i] = (p >= 0 && p < N) ? p : -1;
+  }
+
+  const uint16_t* lat = latent + (size_t)b * N * DK;
+
+  // queries of this wave's 32 heads: B operand of S^T = C q^T
+  i32x4 qr[2][18];
+  {
+    const uint16_t* qrow = q + ((size_t)r * H + 32 * wv) * DK;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int ks = 0; ks < 18; ++ks)
+        qr[nt][ks] = *reinterpret_cast<const i32x4*>(qrow + (16 * nt + nn) * DK + 32 * ks + 8 * g);
+  }
+  __syncthreads();  // sidx visible
+
+  // gather of block `blk` into stage `st`: each lane fetches one 16-byte chunk per
+  // 1 KB direct load; the chunk it fetches is the one whose swizzled slot equals
+  // its lane-linear LDS address.
+  auto issue_gather = [&](int blk, int st) {
+    uint8_t* kb = smem + st * STAGE;
+#pragma unroll
+    for (int i = 0; i < LOADS_PER_WAVE; ++i) {
+      const int base = (wv * LOADS_PER_WAVE + i) * 1024;
+      const int P = (base >> 4) + l;  // physical slot
+      const int e = P / KCH;
+      const int pc = P - e * KCH;
+      const int c = (pc & ~7) | ((pc ^ e) & 7);
+      const int pos = sidx[blk * BE + e];
+      const uint16_t* src = lat + (size_t)(pos >= 0 ? pos : 0) * DK + c * 8;
+      __builtin_amdgcn_global_load_lds(src, to_lds(kb + base), 16, 0, 0);
+    }
+  };
+
+  // value part re-laid out as [dim][position] (bf16 pairs of positions 2p, 2p+1)
+  auto build_vt = [&](int st) {
+    const uint8_t* kb = smem + st * STAGE;
+    uint8_t* vt = smem + st * STAGE + KBUF;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int p = l & 15;
+      const int c = 16 * it + 4 * wv + (l >> 4);  // value chunk 0..63
+      const int e0 = 2 * p, e1 = 2 * p + 1;
+      const i32x4 a = *reinterpret_cast<const i32x4*>(kb + e0 * KROW + kswz(e0, c) * 16);
+      const i32x4 bq = *reinterpret_cast<const i32x4*>(kb + e1 * KROW + kswz(e1, c) * 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t wa = (uint32_t)a[i], wb = (uint32_t)bq[i];
+        const uint32_t lo = (wa & 0xffffu) | (wb << 16);          // dim 8c+2i
+        const uint32_t hi = (wa >> 16) | (wb & 0xffff0000u);      // dim 8c+2i+1
+        *reinterpret_cast<uint32_t*>(vt + (8 * c + 2 * i) * VS + 4 * p) = lo;
+        *reinterpret_cast<uint32_t*>(vt + (8 * c + 2 * i + 1) * VS + 4 * p) = hi;
+      }
+    }
+  };
+
+  f32x4 O[2][32];
+#pragma unroll
+  for (int hm = 0; hm < 2; ++hm)
+#pragma unroll
+    for (int dt = 0; dt < 32; ++dt) O[hm][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY};
+  float l_part[2] = {0.f, 0.f};
+
+  if (nblk > 0) issue_gather(0, 0);
+
+  for (int blk = 0; blk < nblk; ++blk) {
+    const int st = blk & 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // block blk's rows are in LDS; previous block's compute done
+    build_vt(st);
+    __syncthreads();
+    if (blk + 1 < nblk) issue_gather(blk + 1, st ^ 1);
+
+    const uint8_t* kb = smem + st * STAGE;
+    const uint8_t* vt = kb + KBUF;
+
+    // ---- S^T = C q^T : acc[mt][nt] lane holds S^T[16mt + 4g + v][16nt + nn]
+    f32x4 acc[2][2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) {
+      bf16x8 a[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const int e = 16 * mt + nn;
+        a[mt] = as_bf16x8(
+            *reinterpret_cast<const i32x4*>(kb + e * KROW + kswz(e, 4 * ks + g) * 16));
+      }
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+          acc[mt][nt] = mfma_bf16_16x16x32(a[mt], as_bf16x8(qr[nt][ks]), acc[mt][nt]);
+    }
+
+    // ---- online softmax (exp2 domain) for the lane's heads 16nt + nn
+    bool valid[2][4];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) valid[mt][v] = sidx[blk * BE + 16 * mt + 4 * g + v] >= 0;
+
+    float sv[2][2][4];  // [nt][mt][v]
+    float bm[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float s = valid[mt][v] ? acc[mt][nt][v] * scale_log2 : -INFINITY;
+          sv[nt][mt][v] = s;
+          mx = fmaxf(mx, s);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      bm[nt] = mx;
+    }
+    const bool raise = (bm[0] > m_run[0] + kStaleMax) || (bm[1] > m_run[1] + kStaleMax);
+    if (__any(raise)) {
+      float alpha[2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const float mnew = fmaxf(m_run[nt], bm[nt]);
+        alpha[nt] = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[nt] - mnew);
+        l_part[nt] *= alpha[nt];
+        m_run[nt] = mnew;
+      }
+#pragma unroll
+      for (int hm = 0; hm < 2; ++hm)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float a = __shfl(alpha[hm], 4 * g + v);
+#pragma unroll
+          for (int dt = 0; dt < 32; ++dt) O[hm][dt][v] *= a;
+        }
+    }
+    bf16x8 pa[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const float mref = (m_run[nt] == -INFINITY) ? 0.f : m_run[nt];
+      float p[2][4];
+      float sum = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          p[mt][v] = __builtin_amdgcn_exp2f(sv[nt][mt][v] - mref);
+          sum += p[mt][v];
+        }
+      l_part[nt] += sum;
+      i32x4 pk;
+      pk[0] = (int)pack_bf16x2(p[0][0], p[0][1]);
+      pk[1] = (int)pack_bf16x2(p[0][2], p[0][3]);
+      pk[2] = (int)pack_bf16x2(p[1][0], p[1][1]);
+      pk[3] = (int)pack_bf16x2(p[1][2], p[1][3]);
+      pa[nt] = as_bf16x8(pk);
+    }
+
+    // ---- O += P V : B operand = values of positions {4g..4g+3, 16+4g..16+4g+3}
+#pragma unroll
+    for (int dt = 0; dt < 32; ++dt) {
+      const uint8_t* vrow = vt + (16 * dt + nn) * VS;
+      const i32x2 v0 = *reinterpret_cast<const i32x2*>(vrow + 8 * g);
+      const i32x2 v1 = *reinterpret_cast<const i32x2*>(vrow + 32 + 8 * g);
+      const i32x4 vv = {v0[0], v0[1], v1[0], v1[1]};
+      const bf16x8 bv = as_bf16x8(vv);
+      O[0][dt] = mfma_bf16_16x16x32(pa[0], bv, O[0][dt]);
+      O[1][dt] = mfma_bf16_16x16x32(pa[1], bv, O[1][dt]);
+    }
+  }
+
+  // ---- finalize: normalise by the softmax denominator of each output head
+  float l_tot[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    float s = l_part[nt];
+    s += __shfl_xor(s, 16);
+    s += __shfl_xor(s, 32);
+    l_tot[nt] = s;
+  }
+#pragma unroll
+  for (int hm = 0; hm < 2; ++hm)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float L = __shfl(l_tot[hm], 4 * g + v);
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+      for (int dt = 0; dt < 32; ++dt) O[hm][dt][v] *= inv;
+    }
+  const int head0 = 32 * wv;
+  if (splits == 1) {
+    uint16_t* orow = out + (size_t)r * H * DV;
+#pragma unroll
+    for (int hm = 0; hm < 2; ++hm)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        uint16_t* oh = orow + (size_t)(head0 + 16 * hm + 4 * g + v) * DV + nn;
+#pragma unroll
+        for (int dt = 0; dt < 32; ++dt) oh[16 * dt] = (uint16_t)f32_to_bf16_bits(O[hm][dt][v]);
+      }
+    if (lse != nullptr && g == 0) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+        lse[(size_t)r * H + head0 + 16 * nt + nn] =
+            l_tot[nt] > 0.f ? (m_run[nt] + __log2f(l_tot[nt])) * kLn2 : -INFINITY;
+    }
+  } else {
+    float* prow = o_part + ((size_t)r * splits + sp) * H * DV;
+#pragma unroll
+    for (int hm = 0; hm < 2; ++hm)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        float* ph = prow + (size_t)(head0 + 16 * hm + 4 * g + v) * DV + nn;
+#pragma unroll
+        for (int dt = 0; dt < 32; ++dt) ph[16 * dt] = O[hm][dt][v];
+      }
+    if (g == 0) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+        lse_part[((size_t)r * splits + sp) * H + head0 + 16 * nt + nn] =
+            l_tot[nt] > 0.f ? (m_run[nt] + __log2f(l_tot[nt])) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+// LSE-weighted merge of the splits: out = sum_i e^{lse_i - LSE} o_i.
+__global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ o_part,
+                                                           const float* __restrict__ lse_part,
+                                                           int R, int splits,
+                                                           uint16_t* __restrict__ out,
+                                                           float* __restrict__ lse) {
+  const int rh = blockIdx.x;
+  const int r = rh / H, h = rh - (rh / H) * H;
+  if (r >= R) return;
+  const float* lp = lse_part + (size_t)r * splits * H + h;
+  float M = -INFINITY;
+  for (int s = 0; s < splits; ++s) M = fmaxf(M, lp[(size_t)s * H]);
+  float den = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    const float x = lp[(size_t)s * H];
+    den += (x == -INFINITY) ? 0.f : __expf(x - M);
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < splits; ++s) {
+    const float x = lp[(size_t)s * H];
+    if (x == -INFINITY) continue;
+    const float wgt = __expf(x - M) * inv;
+    const f32x4 v = *reinterpret_cast<const f32x4*>(
+        o_part + (((size_t)r * splits + s) * H + h) * DV + 4 * threadIdx.x);
+    acc += wgt * v;
+  }
+  uint2 pk;
+  pk.x = pack_bf16x2(acc[0], acc[1]);
+  pk.y = pack_bf16x2(acc[2], acc[3]);
+  *reinterpret_cast<uint2*>(out + ((size_t)r * H + h) * DV + 4 * threadIdx.x) = pk;
+  if (lse != nullptr && threadIdx.x == 0)
+    lse[(size_t)r * H + h] = den > 0.f ? M + __logf(den) : -INFINITY;
+}
+
+// ---------------------------------------------------------------------------
+// fp32 correctness path (any H <= 128, D_v <= D_k <= 576, topk <= 2048):
+// one block per (row, head), two-pass softmax.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void attn_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ latent,
+    const int32_t* __restrict__ indices, const int32_t* __restrict__ row_seq,
+    const int32_t* __restrict__ row_pos, int B, int N, int nh, int dk, int dv, int topk,
+    float scale, float* __restrict__ out, float* __restrict__ lse) {
+  __shared__ float z[kTopk];
+  __shared__ int pos[kTopk];
+  __shared__ float qs[kQkDim];
+  __shared__ float red[8];
+  const int r = blockIdx.x / nh, h = blockIdx.x - (blockIdx.x / nh) * nh;
+  const int b = row_seq[r], t = row_pos[r];
+  if (b < 0 || b >= B || t < 0 || t >= N) return;
+  const int tid = threadIdx.x, l = lane_id(), wv = tid >> 6;
+  for (int d = tid; d < dk; d += 256) qs[d] = q[((size_t)r * nh + h) * dk + d];
+  __syncthreads();
+  const float* lat = latent + (size_t)b * N * dk;
+  float mx = -INFINITY;
+  for (int i = tid; i < topk; i += 256) {
+    const int p = indices[(size_t)r * topk + i];
+    const bool ok = p >= 0 && p < N;
+    float s = -INFINITY;
+    if (ok) {
+      float dot = 0.f;
+      for (int d = 0; d < dk; ++d) dot = fmaf(qs[d], lat[(size_t)p * dk + d], dot);
+      s = dot * scale;
+    }
+    z[i] = s;
+    pos[i] = ok ? p : -1;
+    mx = fmaxf(mx, s);
+  }
+  mx = wave_max(mx);
+  if (l == 0) red[wv] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  float sum = 0.f;
+  for (int i = tid; i < topk; i += 256) {
+    const float e = pos[i] >= 0 ? expf(z[i] - mx) : 0.f;
+    z[i] = e;
+    sum += e;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+  if (l == 0) red[4 + wv] = sum;
+  __syncthreads();
+  sum = red[4] + red[5] + red[6] + red[7];
+  const float inv = sum > 0.f ? 1.f / sum : 0.f;
+  for (int d = tid; d < dv; d += 256) {
+    float acc = 0.f;
+    for (int i = 0; i < topk; ++i)
+      if (pos[i] >= 0) acc = fmaf(z[i], lat[(size_t)pos[i] * dk + d], acc);
+    out[((size_t)r * nh + h) * dv + d] = acc * inv;
+  }
+  if (lse != nullptr && tid == 0)
+    lse[(size_t)r * nh + h] = sum > 0.f ? mx + logf(sum) : -INFINITY;
+}
+
+int splits_override() {
+  static const int v = [] {
+    const char* e = getenv("DSA_ATTN_SPLITS");
+    return e ? atoi(e) : 0;
+  }();
+  return v;
+}
+
+}  // namespace
+
+int attn_num_splits(int num_rows, int topk) {
+  const int nblk = topk / BE;
+  int s = splits_override();
+  if (s <= 0) {
+    // one block per CU in flight: aim for >= 256 blocks
+    s = 1;
+    while (s < nblk && (int64_t)num_rows * s < 256) s <<= 1;
+  }
+  while (s > 1 && (nblk % s) != 0) s >>= 1;
+  return s < 1 ? 1 : s;
+}
+
+size_t attn_workspace_bytes(int num_rows, const dsa_dims& dims) {
+  if (dims.attn_dtype != DSA_BF16) return 0;
+  const int s = attn_num_splits(num_rows, dims.topk);
+  if (s <= 1) return 0;
+  return (size_t)num_rows * s * H * (DV + 1) * sizeof(float);
+}
+
+hipError_t launch_attn_bf16(const dsa_rows& rows, const void* q, const void* latent,
+                            const int32_t* indices, float softmax_scale, void* out, float* lse,
+                            void* workspace, hipStream_t stream) {
+  const int R = rows.num_rows;
+  const int S = attn_num_splits(R, kTopk);
+  float* o_part = nullptr;
+  float* lse_part = nullptr;
+  if (S > 1) {
+    o_part = static_cast<float*>(workspace);
+    lse_part = o_part + (size_t)R * S * H * DV;
+  }
+  const int row_groups = (R + 7) / 8;
+  const float scale_log2 = softmax_scale * 1.44269504088896340736f;
+  hipLaunchKernelGGL(attn_bf16_kernel, dim3(row_groups * 8 * S), dim3(NT), 0, stream,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(latent), indices,
+                     rows.row_seq, rows.row_pos, R, rows.num_seqs, rows.max_ctx, kTopk, S,
+                     scale_log2, static_cast<uint16_t*>(out), lse, o_part, lse_part);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || S == 1) return err;
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(R * H), dim3(DV / 4), 0, stream, o_part, lse_part,
+                     R, S, static_cast<uint16_t*>(out), lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_f32(const dsa_rows& rows, const dsa_dims& dims, const float* q,
+                           const float* latent, const int32_t* indices, float softmax_scale,
+                           float* out, float* lse, hipStream_t stream) {
+  hipLaunchKernelGGL(attn_f32_kernel, dim3(rows.num_rows * dims.n_heads), dim3(256), 0, stream, q,
+                     latent, indices, rows.row_seq, rows.row_pos, rows.num_seqs, rows.max_ctx,
+                     dims.n_heads, dims.qk_dim, dims.v_dim, dims.topk, softmax_scale, out, lse);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -1,0 +1,245 @@
+// C ABI of the DSA library: argument validation, workspace layout, launches.
+// The steps and their sources are documented in include/dsa.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "dsa.h"
+#include "dsa_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+dsa_status fail(dsa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+dsa_status hip_fail(hipError_t err, const char* what) {
+  return fail(DSA_E_HIP, "%s: %s", what, hipGetErrorString(err));
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+dsa_status check_rows(const dsa_rows* rows) {
+  if (rows == nullptr) return fail(DSA_E_INVALID, "rows is NULL");
+  if (rows->num_rows < 0) return fail(DSA_E_INVALID, "num_rows < 0");
+  if (rows->num_seqs < 1) return fail(DSA_E_INVALID, "num_seqs < 1");
+  if (rows->max_ctx < 1) return fail(DSA_E_INVALID, "max_ctx < 1");
+  if (rows->max_pos < 0 || rows->max_pos >= rows->max_ctx)
+    return fail(DSA_E_INVALID, "max_pos must lie in [0, max_ctx)");
+  if (rows->num_rows > 0 && (rows->row_seq == nullptr || rows->row_pos == nullptr))
+    return fail(DSA_E_INVALID, "row_seq / row_pos is NULL");
+  return DSA_OK;
+}
+
+bool is_production(const dsa_dims& d) {
+  return d.n_idx_heads == dsa::kIdxHeads && d.idx_dim == dsa::kIdxDim &&
+         d.n_heads == dsa::kHeads && d.qk_dim == dsa::kQkDim && d.v_dim == dsa::kVDim &&
+         d.topk == dsa::kTopk && d.idx_dtype == DSA_FP8_E4M3FN && d.attn_dtype == DSA_BF16;
+}
+
+bool is_fp32(const dsa_dims& d) {
+  return d.idx_dtype == DSA_F32 && d.attn_dtype == DSA_F32 && d.n_idx_heads >= 1 &&
+         d.n_idx_heads <= 64 && d.idx_dim >= 1 && d.idx_dim <= 128 && d.n_heads >= 1 &&
+         d.n_heads <= 128 && d.qk_dim >= 1 && d.qk_dim <= dsa::kQkDim && d.v_dim >= 1 &&
+         d.v_dim <= d.qk_dim && d.topk >= 1 && d.topk <= dsa::kTopk;
+}
+
+dsa_status check_dims(const dsa_dims* dims) {
+  if (dims == nullptr) return fail(DSA_E_INVALID, "dims is NULL");
+  if (is_production(*dims) || is_fp32(*dims)) return DSA_OK;
+  return fail(DSA_E_UNSUPPORTED,
+              "unsupported dims (H_I=%d d_I=%d H=%d D_k=%d D_v=%d topk=%d idx_dtype=%d "
+              "attn_dtype=%d)",
+              dims->n_idx_heads, dims->idx_dim, dims->n_heads, dims->qk_dim, dims->v_dim,
+              dims->topk, (int)dims->idx_dtype, (int)dims->attn_dtype);
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+// --- step launchers shared by the public calls and dsa_forward -----------------
+
+dsa_status run_indexer(const dsa_rows& rows, const dsa_dims& dims, const void* q_idx,
+                       const float* q_scale, const float* w, const void* k_idx,
+                       const float* k_scale, float* scores, int64_t ld, hipStream_t stream) {
+  hipError_t err;
+  if (dims.idx_dtype == DSA_FP8_E4M3FN)
+    err = dsa::launch_indexer_fp8(rows, static_cast<const uint8_t*>(q_idx), q_scale, w,
+                                  static_cast<const uint8_t*>(k_idx), k_scale, scores, ld, stream);
+  else
+    err = dsa::launch_indexer_f32(rows, dims, static_cast<const float*>(q_idx), w,
+                                  static_cast<const float*>(k_idx), scores, ld, stream);
+  return err == hipSuccess ? DSA_OK : hip_fail(err, "indexer launch");
+}
+
+dsa_status run_topk(const dsa_rows& rows, int topk, const float* scores, int64_t ld,
+                    int32_t* indices, hipStream_t stream) {
+  const hipError_t err = dsa::launch_topk(rows, topk, scores, ld, indices, stream);
+  return err == hipSuccess ? DSA_OK : hip_fail(err, "top-k launch");
+}
+
+dsa_status run_attn(const dsa_rows& rows, const dsa_dims& dims, const void* q,
+                    const void* latent, const int32_t* indices, float scale, void* out,
+                    float* lse, void* ws, hipStream_t stream) {
+  hipError_t err;
+  if (dims.attn_dtype == DSA_BF16)
+    err = dsa::launch_attn_bf16(rows, q, latent, indices, scale, out, lse, ws, stream);
+  else
+    err = dsa::launch_attn_f32(rows, dims, static_cast<const float*>(q),
+                               static_cast<const float*>(latent), indices, scale,
+                               static_cast<float*>(out), lse, stream);
+  return err == hipSuccess ? DSA_OK : hip_fail(err, "attention launch");
+}
+
+size_t elem_bytes(dsa_dtype t) { return t == DSA_FP8_E4M3FN ? 1 : (t == DSA_BF16 ? 2 : 4); }
+
+int64_t scores_ld(const dsa_rows& rows) { return (int64_t)align_up((size_t)rows.max_pos + 1, 64); }
+
+}  // namespace
+
+extern "C" {
+
+int32_t dsa_api_version(void) { return DSA_API_VERSION; }
+
+const char* dsa_status_string(dsa_status status) {
+  switch (status) {
+    case DSA_OK: return "DSA_OK";
+    case DSA_E_INVALID: return "DSA_E_INVALID: invalid argument";
+    case DSA_E_UNSUPPORTED: return "DSA_E_UNSUPPORTED: unsupported dimensions or dtype";
+    case DSA_E_WORKSPACE: return "DSA_E_WORKSPACE: workspace missing or too small";
+    case DSA_E_HIP: return "DSA_E_HIP: HIP runtime error";
+  }
+  return "unknown dsa_status";
+}
+
+const char* dsa_last_error(void) { return g_last_error; }
+
+dsa_status dsa_indexer_scores(const dsa_rows* rows, const dsa_dims* dims, const void* q_idx,
+                              const float* q_scale, const float* w, const void* k_idx,
+                              const float* k_scale, float* scores, int64_t ld_scores,
+                              void* stream) {
+  dsa_status st = check_rows(rows);
+  if (st != DSA_OK) return st;
+  if ((st = check_dims(dims)) != DSA_OK) return st;
+  if (rows->num_rows == 0) return DSA_OK;
+  if (!q_idx || !w || !k_idx || !scores) return fail(DSA_E_INVALID, "NULL tensor pointer");
+  if (dims->idx_dtype == DSA_FP8_E4M3FN && (!q_scale || !k_scale))
+    return fail(DSA_E_INVALID, "fp8 indexer needs q_scale and k_scale");
+  if (ld_scores < (int64_t)rows->max_pos + 1)
+    return fail(DSA_E_INVALID, "ld_scores < max_pos + 1");
+  return run_indexer(*rows, *dims, q_idx, q_scale, w, k_idx, k_scale, scores, ld_scores,
+                     as_stream(stream));
+}
+
+dsa_status dsa_topk(const dsa_rows* rows, int32_t topk, const float* scores, int64_t ld_scores,
+                    int32_t* indices, void* stream) {
+  dsa_status st = check_rows(rows);
+  if (st != DSA_OK) return st;
+  if (topk < 1 || topk > 4096) return fail(DSA_E_UNSUPPORTED, "topk must lie in [1, 4096]");
+  if (rows->num_rows == 0) return DSA_OK;
+  if (!scores || !indices) return fail(DSA_E_INVALID, "NULL tensor pointer");
+  if (ld_scores < (int64_t)rows->max_pos + 1)
+    return fail(DSA_E_INVALID, "ld_scores < max_pos + 1");
+  return run_topk(*rows, topk, scores, ld_scores, indices, as_stream(stream));
+}
+
+size_t dsa_sparse_mla_attn_workspace_size(const dsa_rows* rows, const dsa_dims* dims) {
+  if (check_rows(rows) != DSA_OK || check_dims(dims) != DSA_OK) return 0;
+  return dsa::attn_workspace_bytes(rows->num_rows, *dims);
+}
+
+dsa_status dsa_sparse_mla_attn(const dsa_rows* rows, const dsa_dims* dims, const void* q,
+                               const void* latent, const int32_t* indices, float softmax_scale,
+                               void* out, float* lse, void* workspace, size_t ws_bytes,
+                               void* stream) {
+  dsa_status st = check_rows(rows);
+  if (st != DSA_OK) return st;
+  if ((st = check_dims(dims)) != DSA_OK) return st;
+  if (rows->num_rows == 0) return DSA_OK;
+  if (!q || !latent || !indices || !out) return fail(DSA_E_INVALID, "NULL tensor pointer");
+  const size_t need = dsa::attn_workspace_bytes(rows->num_rows, *dims);
+  if (need > 0 && (workspace == nullptr || ws_bytes < need))
+    return fail(DSA_E_WORKSPACE, "attention needs %zu workspace bytes, got %zu", need, ws_bytes);
+  return run_attn(*rows, *dims, q, latent, indices, softmax_scale, out, lse, workspace,
+                  as_stream(stream));
+}
+
+size_t dsa_forward_workspace_size(const dsa_rows* rows, const dsa_dims* dims, int32_t chunk_rows) {
+  if (check_rows(rows) != DSA_OK || check_dims(dims) != DSA_OK || chunk_rows < 0) return 0;
+  const int R = rows->num_rows;
+  const int CH = (chunk_rows > 0 && chunk_rows < R) ? chunk_rows : R;
+  if (CH == 0) return 0;
+  const int64_t ld = scores_ld(*rows);
+  size_t bytes = align_up((size_t)CH * ld * sizeof(float), 256);
+  bytes += align_up((size_t)CH * dims->topk * sizeof(int32_t), 256);
+  // the last chunk may hold fewer rows and therefore use more attention splits
+  const int last = R - (R - 1) / CH * CH;
+  const size_t attn = dsa::attn_workspace_bytes(CH, *dims);
+  const size_t attn_last = dsa::attn_workspace_bytes(last, *dims);
+  bytes += align_up(attn > attn_last ? attn : attn_last, 256);
+  return bytes;
+}
+
+dsa_status dsa_forward(const dsa_rows* rows, const dsa_dims* dims, const void* q_idx,
+                       const float* q_scale, const float* w, const void* k_idx,
+                       const float* k_scale, const void* q, const void* latent,
+                       float softmax_scale, void* out, float* lse, int32_t* indices_out,
+                       int32_t chunk_rows, void* workspace, size_t ws_bytes, void* stream) {
+  dsa_status st = check_rows(rows);
+  if (st != DSA_OK) return st;
+  if ((st = check_dims(dims)) != DSA_OK) return st;
+  if (chunk_rows < 0) return fail(DSA_E_INVALID, "chunk_rows < 0");
+  const int R = rows->num_rows;
+  if (R == 0) return DSA_OK;
+  if (!q_idx || !w || !k_idx || !q || !latent || !out)
+    return fail(DSA_E_INVALID, "NULL tensor pointer");
+  if (dims->idx_dtype == DSA_FP8_E4M3FN && (!q_scale || !k_scale))
+    return fail(DSA_E_INVALID, "fp8 indexer needs q_scale and k_scale");
+  const size_t need = dsa_forward_workspace_size(rows, dims, chunk_rows);
+  if (workspace == nullptr || ws_bytes < need)
+    return fail(DSA_E_WORKSPACE, "dsa_forward needs %zu workspace bytes, got %zu", need,
+                ws_bytes);
+
+  const int CH = (chunk_rows > 0 && chunk_rows < R) ? chunk_rows : R;
+  const int64_t ld = scores_ld(*rows);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* scores = reinterpret_cast<float*>(ws);
+  ws += align_up((size_t)CH * ld * sizeof(float), 256);
+  int32_t* idx_ws = reinterpret_cast<int32_t*>(ws);
+  ws += align_up((size_t)CH * dims->topk * sizeof(int32_t), 256);
+  void* attn_ws = ws;
+  const hipStream_t s = as_stream(stream);
+
+  const size_t qi_row = (size_t)dims->n_idx_heads * dims->idx_dim * elem_bytes(dims->idx_dtype);
+  const size_t q_row = (size_t)dims->n_heads * dims->qk_dim * elem_bytes(dims->attn_dtype);
+  const size_t o_row = (size_t)dims->n_heads * dims->v_dim * elem_bytes(dims->attn_dtype);
+  const size_t hi = (size_t)dims->n_idx_heads;
+
+  for (int r0 = 0; r0 < R; r0 += CH) {
+    dsa_rows sub = *rows;
+    sub.num_rows = (R - r0) < CH ? (R - r0) : CH;
+    sub.row_seq = rows->row_seq + r0;
+    sub.row_pos = rows->row_pos + r0;
+    int32_t* idx = indices_out ? indices_out + (size_t)r0 * dims->topk : idx_ws;
+    st = run_indexer(sub, *dims, static_cast<const uint8_t*>(q_idx) + r0 * qi_row,
+                     q_scale ? q_scale + r0 * hi : nullptr, w + r0 * hi, k_idx, k_scale, scores,
+                     ld, s);
+    if (st != DSA_OK) return st;
+    st = run_topk(sub, dims->topk, scores, ld, idx, s);
+    if (st != DSA_OK) return st;
+    st = run_attn(sub, *dims, static_cast<const uint8_t*>(q) + r0 * q_row, latent, idx,
+                  softmax_scale, static_cast<uint8_t*>(out) + r0 * o_row,
+                  lse ? lse + (size_t)r0 * dims->n_heads : nullptr, attn_ws, s);
+    if (st != DSA_OK) return st;
+  }
+  return DSA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,42 @@
+// Host-side declarations shared by the launch code of the DSA library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dsa.h"
+
+namespace dsa {
+
+// production dimensions (fp8 indexer, bf16 attention)
+constexpr int kIdxHeads = 64;
+constexpr int kIdxDim = 128;
+constexpr int kHeads = 128;
+constexpr int kQkDim = 576;
+constexpr int kVDim = 512;
+constexpr int kTopk = 2048;
+
+hipError_t launch_indexer_fp8(const dsa_rows& rows, const uint8_t* q_idx, const float* q_scale,
+                              const float* w, const uint8_t* k_idx, const float* k_scale,
+                              float* scores, int64_t ld, hipStream_t stream);
+
+hipError_t launch_indexer_f32(const dsa_rows& rows, const dsa_dims& dims, const float* q_idx,
+                              const float* w, const float* k_idx, float* scores, int64_t ld,
+                              hipStream_t stream);
+
+hipError_t launch_topk(const dsa_rows& rows, int topk, const float* scores, int64_t ld,
+                       int32_t* indices, hipStream_t stream);
+
+// Number of splits of each row's selected set used by the bf16 attention for R rows.
+int attn_num_splits(int num_rows, int topk);
+size_t attn_workspace_bytes(int num_rows, const dsa_dims& dims);
+
+hipError_t launch_attn_bf16(const dsa_rows& rows, const void* q, const void* latent,
+                            const int32_t* indices, float softmax_scale, void* out, float* lse,
+                            void* workspace, hipStream_t stream);
+
+hipError_t launch_attn_f32(const dsa_rows& rows, const dsa_dims& dims, const float* q,
+                           const float* latent, const int32_t* indices, float softmax_scale,
+                           float* out, float* lse, hipStream_t stream);
+
+}  // namespace dsa

@@ -1,0 +1,310 @@
+// Lightning-indexer scores on gfx950.
+//
+// I[t,s] = sum_j w[t,j] * ReLU(q[t,j] . k[s]) over positions s <= t
+// (DeepSeek-V3.2-Exp paper, section 1 "Architecture", Eq. 1 and its prose; the
+// paper notes the indexer has few heads and can run in FP8).
+//
+// FP8 path: q and k are e4m3fn codes with one positive fp32 scale per 128-wide
+// vector.  Because a positive scale commutes with ReLU,
+//   I[t,s] = k_scale[s] * sum_j (w[t,j] * q_scale[t,j]) * ReLU(q8[t,j] . k8[s]),
+// so the fp8 dot products run unscaled on the 16x16x128 fp8 MFMA (exact products,
+// fp32 accumulation: d_I = 128 is exactly one MFMA contraction) and the scales,
+// ReLU and the weighted head sum form the fp32 epilogue.
+//
+// MFMA tile: M = 16 indexer heads, N = 16 keys.  Four tiles cover the 64 heads, so
+// each lane ends with 16 heads of one key and the head sum is 16 in-lane FMAs
+// plus a 3-shuffle reduce-scatter across the four lane groups.
+#include "dsa_device.h"
+#include "dsa_internal.h"
+
+namespace dsa {
+namespace {
+
+constexpr int IH = kIdxHeads;  // 64
+constexpr int ID = kIdxDim;    // 128
+
+__device__ __forceinline__ i32x8 load_frag32(const uint8_t* p) {
+  const i32x4* v = reinterpret_cast<const i32x4*>(p);
+  i32x4 a = v[0];
+  i32x4 b = v[1];
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Lane partial of sum_j wq[j] * ReLU(dot[j, key]) over the lane's 16 heads for the
+// 16-key tile `kb` (key = lane & 15).
+__device__ __forceinline__ float head_partial(const i32x8 (&qa)[4], const float (&wq)[16],
+                                              i32x8 kb) {
+  float p = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    f32x4 acc = mfma_fp8_16x16x128(qa[mt], kb, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+    for (int v = 0; v < 4; ++v) p = fmaf(wq[mt * 4 + v], fmaxf(acc[v], 0.f), p);
+  }
+  return p;
+}
+
+// p_i is the lane's partial for key tile i (keys 16i..16i+15 of a 64-key group,
+// key = lane & 15).  Returns the full head sum for key `lane` of the group:
+// exchange halves across lanes l^32, then across l^16 (reduce-scatter).
+__device__ __forceinline__ float reduce_groups(float p0, float p1, float p2, float p3) {
+  const int l = lane_id();
+  const bool hi = l >= 32;
+  float keep0 = hi ? p2 : p0, keep1 = hi ? p3 : p1;
+  const float send0 = hi ? p0 : p2, send1 = hi ? p1 : p3;
+  keep0 += __shfl_xor(send0, 32);
+  keep1 += __shfl_xor(send1, 32);
+  const bool odd = (l >> 4) & 1;
+  const float send = odd ? keep0 : keep1;
+  const float keep = odd ? keep1 : keep0;
+  return keep + __shfl_xor(send, 16);
+}
+
+__device__ __forceinline__ void load_query(const uint8_t* __restrict__ q_idx,
+                                           const float* __restrict__ q_scale,
+                                           const float* __restrict__ w, int r, i32x8 (&qa)[4],
+                                           float (&wq)[16]) {
+  const int l = lane_id(), g = l >> 4, n = l & 15;
+  const uint8_t* qr = q_idx + (size_t)r * IH * ID;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) qa[mt] = load_frag32(qr + (16 * mt + n) * ID + 32 * g);
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int h = 16 * mt + 4 * g + v;
+      wq[mt * 4 + v] = w[(size_t)r * IH + h] * q_scale[(size_t)r * IH + h];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Decode tiling: one query row per block row, keys streamed from HBM.  Each wave
+// walks 64-key groups (interleaved across the block's waves) with the next
+// group's fragments prefetched while the current one is multiplied.
+// Grid: num_rows * key_blocks blocks (row-major), WAVES waves each.
+// ---------------------------------------------------------------------------
+template <int WAVES, int KPB>
+__global__ __launch_bounds__(WAVES * 64) void indexer_fp8_decode_kernel(
+    const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale,
+    const float* __restrict__ w, const uint8_t* __restrict__ k_idx,
+    const float* __restrict__ k_scale, const int32_t* __restrict__ row_seq,
+    const int32_t* __restrict__ row_pos, int B, int N, int nkb, float* __restrict__ scores,
+    int64_t ld) {
+  const int r = blockIdx.x / nkb;
+  const int kb0 = (blockIdx.x - r * nkb) * KPB;
+  const int b = row_seq[r], t = row_pos[r];
+  if (b < 0 || b >= B || t < 0 || t >= N || (int64_t)t >= ld || kb0 > t) return;
+  const int kend = min(kb0 + KPB, t + 1);
+  const int l = lane_id(), wv = threadIdx.x >> 6, g = l >> 4, n = l & 15;
+
+  int k0 = kb0 + 64 * wv;
+  if (k0 >= kend) return;
+
+  i32x8 qa[4];
+  float wq[16];
+  load_query(q_idx, q_scale, w, r, qa, wq);
+
+  const uint8_t* kc = k_idx + (size_t)b * N * ID;
+  const float* ksc = k_scale + (size_t)b * N;
+  float* out = scores + (size_t)r * ld;
+
+  i32x8 cur[4];
+  float ks_cur;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt)
+    cur[kt] = load_frag32(kc + (size_t)min(k0 + 16 * kt + n, t) * ID + 32 * g);
+  ks_cur = ksc[min(k0 + l, t)];
+
+  for (; k0 < kend; k0 += 64 * WAVES) {
+    const int kn = k0 + 64 * WAVES;
+    i32x8 nxt[4];
+    float ks_nxt = 0.f;
+    if (kn < kend) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+        nxt[kt] = load_frag32(kc + (size_t)min(kn + 16 * kt + n, t) * ID + 32 * g);
+      ks_nxt = ksc[min(kn + l, t)];
+    }
+    const float p0 = head_partial(qa, wq, cur[0]);
+    const float p1 = head_partial(qa, wq, cur[1]);
+    const float p2 = head_partial(qa, wq, cur[2]);
+    const float p3 = head_partial(qa, wq, cur[3]);
+    const float s = reduce_groups(p0, p1, p2, p3) * ks_cur;
+    if (k0 + l < kend) out[k0 + l] = s;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) cur[kt] = nxt[kt];
+    ks_cur = ks_nxt;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Prefill tiling: each wave owns RW consecutive query rows (their fp8 queries stay
+// in registers) and walks the block's key range; every 16-key fragment feeds the
+// MFMAs of all RW rows.  The four waves of a block read the same keys, which the
+// L1/L2 serve.  Rows of a wave that belong to different sequences fall back to one
+// row at a time.  Grid: row_tiles * key_blocks blocks.
+// ---------------------------------------------------------------------------
+template <int NR>
+__device__ __forceinline__ void prefill_rows(const uint8_t* __restrict__ q_idx,
+                                             const float* __restrict__ q_scale,
+                                             const float* __restrict__ w,
+                                             const uint8_t* __restrict__ kc,
+                                             const float* __restrict__ ksc, const int* rr,
+                                             const int* tt, int kb0, int kend,
+                                             float* __restrict__ scores, int64_t ld) {
+  const int l = lane_id(), g = l >> 4, n = l & 15;
+  i32x8 qa[NR][4];
+  float wq[NR][16];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) load_query(q_idx, q_scale, w, rr[i], qa[i], wq[i]);
+  const int klast = kend - 1;
+
+  i32x8 cur[4];
+  float ks_cur;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt)
+    cur[kt] = load_frag32(kc + (size_t)min(kb0 + 16 * kt + n, klast) * ID + 32 * g);
+  ks_cur = ksc[min(kb0 + l, klast)];
+
+  for (int k0 = kb0; k0 < kend; k0 += 64) {
+    const int kn = k0 + 64;
+    i32x8 nxt[4];
+    float ks_nxt = 0.f;
+    if (kn < kend) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+        nxt[kt] = load_frag32(kc + (size_t)min(kn + 16 * kt + n, klast) * ID + 32 * g);
+      ks_nxt = ksc[min(kn + l, klast)];
+    }
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      if (k0 > tt[i]) continue;  // wave-uniform
+      const float p0 = head_partial(qa[i], wq[i], cur[0]);
+      const float p1 = head_partial(qa[i], wq[i], cur[1]);
+      const float p2 = head_partial(qa[i], wq[i], cur[2]);
+      const float p3 = head_partial(qa[i], wq[i], cur[3]);
+      const float s = reduce_groups(p0, p1, p2, p3) * ks_cur;
+      if (k0 + l <= tt[i]) scores[(size_t)rr[i] * ld + k0 + l] = s;
+    }
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) cur[kt] = nxt[kt];
+    ks_cur = ks_nxt;
+  }
+}
+
+template <int RW, int KPB>
+__global__ __launch_bounds__(256) void indexer_fp8_prefill_kernel(
+    const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale,
+    const float* __restrict__ w, const uint8_t* __restrict__ k_idx,
+    const float* __restrict__ k_scale, const int32_t* __restrict__ row_seq,
+    const int32_t* __restrict__ row_pos, int R, int B, int N, int nkb,
+    float* __restrict__ scores, int64_t ld) {
+  const int tile = blockIdx.x / nkb;
+  const int kb0 = (blockIdx.x - tile * nkb) * KPB;
+  const int wv = threadIdx.x >> 6;
+  const int rbase = (tile * 4 + wv) * RW;
+
+  int rr[RW], tt[RW], bs[RW];
+  int nvalid = 0, tmax = -1, b0 = -1;
+  bool uniform = true;
+#pragma unroll
+  for (int i = 0; i < RW; ++i) {
+    const int r = rbase + i;
+    int b = -1, t = -1;
+    if (r < R) {
+      b = row_seq[r];
+      t = row_pos[r];
+      if (b < 0 || b >= B || t < 0 || t >= N || (int64_t)t >= ld) t = -1;
+    }
+    rr[i] = r < R ? r : 0;
+    tt[i] = t;
+    bs[i] = b;
+    if (t >= 0) {
+      if (b0 < 0) b0 = b;
+      uniform = uniform && (b == b0);
+      tmax = max(tmax, t);
+      ++nvalid;
+    }
+  }
+  if (nvalid == 0 || kb0 > tmax) return;
+
+  if (uniform) {
+    const int kend = min(kb0 + KPB, tmax + 1);
+    prefill_rows<RW>(q_idx, q_scale, w, k_idx + (size_t)b0 * N * ID, k_scale + (size_t)b0 * N,
+                     rr, tt, kb0, kend, scores, ld);
+  } else {
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      if (tt[i] < kb0) continue;
+      const int kend = min(kb0 + KPB, tt[i] + 1);
+      prefill_rows<1>(q_idx, q_scale, w, k_idx + (size_t)bs[i] * N * ID,
+                      k_scale + (size_t)bs[i] * N, &rr[i], &tt[i], kb0, kend, scores, ld);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 correctness path (any H_I <= 64, d_I <= 128): one thread per key.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void indexer_f32_kernel(
+    const float* __restrict__ q_idx, const float* __restrict__ w,
+    const float* __restrict__ k_idx, const int32_t* __restrict__ row_seq,
+    const int32_t* __restrict__ row_pos, int B, int N, int HI, int DI, int nkb,
+    float* __restrict__ scores, int64_t ld) {
+  __shared__ float qs[64 * 128];
+  __shared__ float ws[64];
+  const int r = blockIdx.x / nkb;
+  const int s0 = (blockIdx.x - r * nkb) * 256;
+  const int b = row_seq[r], t = row_pos[r];
+  if (b < 0 || b >= B || t < 0 || t >= N || (int64_t)t >= ld || s0 > t) return;
+  for (int i = threadIdx.x; i < HI * DI; i += 256) qs[i] = q_idx[(size_t)r * HI * DI + i];
+  for (int i = threadIdx.x; i < HI; i += 256) ws[i] = w[(size_t)r * HI + i];
+  __syncthreads();
+  const int s = s0 + threadIdx.x;
+  if (s > t) return;
+  const float* kv = k_idx + ((size_t)b * N + s) * DI;
+  float acc = 0.f;
+  for (int j = 0; j < HI; ++j) {
+    float dot = 0.f;
+    for (int d = 0; d < DI; ++d) dot = fmaf(qs[j * DI + d], kv[d], dot);
+    acc = fmaf(ws[j], fmaxf(dot, 0.f), acc);
+  }
+  scores[(size_t)r * ld + s] = acc;
+}
+
+}  // namespace
+
+hipError_t launch_indexer_fp8(const dsa_rows& rows, const uint8_t* q_idx, const float* q_scale,
+                              const float* w, const uint8_t* k_idx, const float* k_scale,
+                              float* scores, int64_t ld, hipStream_t stream) {
+  const int R = rows.num_rows;
+  const int L = rows.max_pos + 1;
+  if (R >= 8 && R >= 4 * rows.num_seqs) {
+    constexpr int RW = 2, KPB = 512;
+    const int nkb = (L + KPB - 1) / KPB;
+    const int tiles = (R + 4 * RW - 1) / (4 * RW);
+    hipLaunchKernelGGL((indexer_fp8_prefill_kernel<RW, KPB>), dim3(tiles * nkb), dim3(256), 0,
+                       stream, q_idx, q_scale, w, k_idx, k_scale, rows.row_seq, rows.row_pos, R,
+                       rows.num_seqs, rows.max_ctx, nkb, scores, ld);
+  } else {
+    constexpr int WAVES = 4, KPB = 1024;
+    const int nkb = (L + KPB - 1) / KPB;
+    hipLaunchKernelGGL((indexer_fp8_decode_kernel<WAVES, KPB>), dim3(R * nkb), dim3(WAVES * 64),
+                       0, stream, q_idx, q_scale, w, k_idx, k_scale, rows.row_seq, rows.row_pos,
+                       rows.num_seqs, rows.max_ctx, nkb, scores, ld);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_indexer_f32(const dsa_rows& rows, const dsa_dims& dims, const float* q_idx,
+                              const float* w, const float* k_idx, float* scores, int64_t ld,
+                              hipStream_t stream) {
+  const int L = rows.max_pos + 1;
+  const int nkb = (L + 255) / 256;
+  hipLaunchKernelGGL(indexer_f32_kernel, dim3(rows.num_rows * nkb), dim3(256), 0, stream, q_idx,
+                     w, k_idx, rows.row_seq, rows.row_pos, rows.num_seqs, rows.max_ctx,
+                     dims.n_idx_heads, dims.idx_dim, nkb, scores, ld);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -1,0 +1,151 @@
+"""Test helpers: run the float64 oracle on host-regenerated inputs and compare the
+HIP path's outputs with it.
+
+Oracle inputs are always regenerated on the host from the seeded generator; they
+never come from the GPU.  The three comparison rules follow the tolerances the
+hot path is held to:
+
+* C1 scores:  |I_gpu - I_ref| <= 2e-2 * max(|I_ref|, 1e-3 * max_s |I_ref|)
+* C2 indices: the GPU set has n = min(k, t+1) unique positions in [0, t], ascending,
+  -1 padded; it equals the oracle's set outside the tie band
+  A = {s : |I_ref[s] - tau| <= 1e-3 |tau|}, tau = the n-th largest oracle score.
+* C3 attention (bf16): max |o_gpu - o_ref| <= 2e-2 and mean <= 2e-3.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+import torch
+
+import dsa_inputs as di
+import oracle
+
+SCORE_RTOL = 2e-2
+SCORE_FLOOR = 1e-3
+BAND = 1e-3
+ATTN_MAX_ABS = 2e-2
+ATTN_MEAN_ABS = 2e-3
+
+
+@dataclasses.dataclass
+class HostRow:
+    """Raw input images of one query row, regenerated on the host."""
+    r: int
+    b: int
+    t: int
+    q_idx: np.ndarray
+    q_scale: Optional[np.ndarray]
+    w: np.ndarray
+    q: np.ndarray
+
+
+class HostInputs:
+    """Lazily regenerates host copies of a workload's inputs."""
+
+    def __init__(self, cfg: di.Config, set_id: int = 0):
+        self.cfg = cfg
+        self.gen = di.Generator(cfg, set_id)
+        self.seq, self.pos = cfg.row_seq_pos()
+        self._k: Dict[int, tuple] = {}
+        self._kf: Dict[int, np.ndarray] = {}
+
+    def row(self, r: int) -> HostRow:
+        c = self.cfg
+        codes, sc = self.gen.q_idx(r, r + 1)
+        w = self.gen.w(r, r + 1)[0].numpy().astype(np.float64)
+        q = self.gen.q(r, r + 1)[0]
+        if c.fp32:
+            return HostRow(r, int(self.seq[r]), int(self.pos[r]), codes[0].numpy(), None, w,
+                           q.numpy())
+        return HostRow(r, int(self.seq[r]), int(self.pos[r]), codes[0].numpy(),
+                       sc[0].numpy().astype(np.float64), w, di.bf16_bits(q))
+
+    def keys(self, b: int, upto: int):
+        """Indexer key codes / scales of sequence b for positions [0, upto)."""
+        have = self._k.get(b)
+        if have is None or have[0].shape[0] < upto:
+            codes, sc = self.gen.k_idx(b, 0, upto)
+            self._k[b] = (codes.numpy(), None if self.cfg.fp32 else sc.numpy().astype(np.float64))
+        codes, sc = self._k[b]
+        return codes[:upto], (None if sc is None else sc[:upto])
+
+    def latent_rows(self, b: int, positions: np.ndarray) -> np.ndarray:
+        x = self.gen.latent_rows(b, torch.from_numpy(np.asarray(positions, dtype=np.int64)))
+        return x.numpy() if self.cfg.fp32 else di.bf16_bits(x)
+
+    def scores(self, row: HostRow) -> np.ndarray:
+        """Oracle scores I[0..t] of one row.  The sequence's dequantised keys are
+        cached (oracle decoder times scale, exactly what oracle.indexer_row does per
+        call) so long sequences are decoded once."""
+        if row.t + 1 <= 4096:
+            codes, sc = self.keys(row.b, row.t + 1)
+            return oracle.indexer_row(row.q_idx, row.q_scale, row.w, codes, sc, row.t,
+                                      not self.cfg.fp32)
+        kf = self._kf.get(row.b)
+        if kf is None or kf.shape[0] < row.t + 1:
+            codes, sc = self.keys(row.b, self.cfg.max_ctx)
+            kf = (oracle.decode_e4m3fn(codes) * sc[:, None]) if sc is not None \
+                else codes.astype(np.float64)
+            self._kf[row.b] = kf
+        qf = (oracle.decode_e4m3fn(row.q_idx) * row.q_scale[:, None]) if row.q_scale is not None \
+            else row.q_idx.astype(np.float64)
+        return oracle.indexer_scores(qf, row.w, kf[: row.t + 1])
+
+    def attention(self, row: HostRow, positions: np.ndarray):
+        ent = self.latent_rows(row.b, positions)
+        return oracle.attention_row(row.q, ent, self.cfg.scale, self.cfg.v_dim, not self.cfg.fp32)
+
+
+def check_scores(gpu: np.ndarray, ref: np.ndarray) -> float:
+    """C1; returns the worst ratio |err| / allowed (must be <= 1)."""
+    gpu = np.asarray(gpu, dtype=np.float64)
+    floor = SCORE_FLOOR * np.max(np.abs(ref)) if ref.size else 0.0
+    allowed = SCORE_RTOL * np.maximum(np.abs(ref), floor)
+    err = np.abs(gpu - ref)
+    ok = (err <= allowed) | ((err == 0) & (allowed == 0))
+    assert np.all(np.isfinite(gpu)), "non-finite GPU score"
+    assert ok.all(), (f"score mismatch at {np.nonzero(~ok)[0][:8]}: gpu {gpu[~ok][:4]} "
+                      f"ref {ref[~ok][:4]}")
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(allowed > 0, err / allowed, 0.0)
+    return float(ratio.max()) if ratio.size else 0.0
+
+
+def check_selection(gpu_idx: np.ndarray, ref_scores: np.ndarray, t: int, k: int) -> int:
+    """C2; returns the size of the tie band."""
+    n = min(k, t + 1)
+    g = np.asarray(gpu_idx)
+    assert g.shape == (k,)
+    assert np.all(g[n:] == -1), "padding must be -1"
+    sel = g[:n]
+    assert np.all((sel >= 0) & (sel <= t)), "selected position out of [0, t]"
+    assert np.all(np.diff(sel) > 0), "selection must be strictly ascending (unique)"
+    ref_sel = oracle.select_topk(ref_scores, n)
+    tau = np.min(ref_scores[ref_sel])
+    band = np.abs(ref_scores - tau) <= BAND * abs(tau)
+    gs = set(sel.tolist())
+    rs = set(ref_sel.tolist())
+    outside_g = {s for s in gs if not band[s]}
+    outside_r = {s for s in rs if not band[s]}
+    assert outside_g == outside_r, (
+        f"selection differs outside the tie band: gpu-only {sorted(outside_g - outside_r)[:8]} "
+        f"ref-only {sorted(outside_r - outside_g)[:8]}")
+    return int(band.sum())
+
+
+def attn_errors(gpu_o: np.ndarray, ref_o: np.ndarray):
+    d = np.abs(np.asarray(gpu_o, dtype=np.float64) - ref_o)
+    return float(d.max()), float(d.mean())
+
+
+def check_attention(gpu_o: np.ndarray, ref_o: np.ndarray):
+    mx, mean = attn_errors(gpu_o, ref_o)
+    assert np.all(np.isfinite(gpu_o)), "non-finite attention output"
+    assert mx <= ATTN_MAX_ABS and mean <= ATTN_MEAN_ABS, (mx, mean)
+    return mx, mean
+
+
+def to_f64(x: torch.Tensor) -> np.ndarray:
+    return x.detach().float().cpu().numpy().astype(np.float64)

@@ -1,0 +1,100 @@
+"""The C ABI without a GPU: the library loads, exports every entry point that
+include/dsa.h declares, and rejects invalid arguments on the host before anything
+is enqueued (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+
+@pytest.fixture(scope="module")
+def m():
+    import sparse_attention_fp8_amd as mod
+    return mod
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points(m):
+    names = declared_functions()
+    for required in ["dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_attn", "dsa_forward"]:
+        assert required in names
+    assert sorted(m.EXPORTED_SYMBOLS) == names
+
+
+def test_library_exports_every_declared_symbol(m):
+    for name in declared_functions():
+        assert hasattr(m.lib, name), name
+
+
+def test_status_strings_and_version(m):
+    assert m.lib.dsa_api_version() == 1
+    for st in range(5):
+        assert m.lib.dsa_status_string(st).decode().startswith("DSA_")
+
+
+def _rows(m, R=4, B=2, N=64, max_pos=63, seq=1, pos=1):
+    return m._Rows(R, B, N, max_pos, seq, pos)  # dummy non-NULL "device" addresses
+
+
+def test_invalid_arguments_rejected_on_host(m):
+    L = m.lib
+    d = m.dims_struct(m.PRODUCTION_DIMS)
+    r = _rows(m)
+    p = ctypes.c_void_p(16)
+    # NULL rows / dims
+    assert L.dsa_topk(None, 2048, p, 64, p, None) == m.DSA_E_INVALID
+    assert L.dsa_indexer_scores(ctypes.byref(r), None, p, p, p, p, p, p, 64, None) == m.DSA_E_INVALID
+    # max_pos outside [0, N)
+    bad = _rows(m, max_pos=64)
+    assert L.dsa_topk(ctypes.byref(bad), 2048, p, 64, p, None) == m.DSA_E_INVALID
+    # ld too small
+    assert L.dsa_topk(ctypes.byref(r), 2048, p, 63, p, None) == m.DSA_E_INVALID
+    # topk out of range
+    assert L.dsa_topk(ctypes.byref(r), 0, p, 64, p, None) == m.DSA_E_UNSUPPORTED
+    assert L.dsa_topk(ctypes.byref(r), 5000, p, 64, p, None) == m.DSA_E_UNSUPPORTED
+    # NULL tensors
+    assert L.dsa_topk(ctypes.byref(r), 2048, None, 64, p, None) == m.DSA_E_INVALID
+    # fp8 indexer without scales
+    assert L.dsa_indexer_scores(ctypes.byref(r), ctypes.byref(d), p, None, p, p, None, p, 64,
+                                None) == m.DSA_E_INVALID
+    assert "scale" in L.dsa_last_error().decode()
+    # unsupported dims
+    odd = m.dims_struct(m.Dims(32, 128, 128, 576, 512, 2048, False))
+    assert L.dsa_indexer_scores(ctypes.byref(r), ctypes.byref(odd), p, p, p, p, p, p, 64,
+                                None) == m.DSA_E_UNSUPPORTED
+    # workspace too small
+    rows_dec = _rows(m, R=32, B=32, N=32768, max_pos=32767)
+    need = L.dsa_sparse_mla_attn_workspace_size(ctypes.byref(rows_dec), ctypes.byref(d))
+    assert need > 0
+    assert L.dsa_sparse_mla_attn(ctypes.byref(rows_dec), ctypes.byref(d), p, p, p, 0.1, p, p, p,
+                                 need - 1, None) == m.DSA_E_WORKSPACE
+    assert L.dsa_forward(ctypes.byref(rows_dec), ctypes.byref(d), p, p, p, p, p, p, p, 0.1, p, p,
+                         None, 0, p, 16, None) == m.DSA_E_WORKSPACE
+    # zero rows: nothing to do
+    empty = _rows(m, R=0, seq=None, pos=None)
+    assert L.dsa_topk(ctypes.byref(empty), 2048, None, 64, None, None) == m.DSA_OK
+
+
+def test_workspace_sizes(m):
+    L = m.lib
+    d = m.dims_struct(m.PRODUCTION_DIMS)
+    dec = _rows(m, R=32, B=32, N=32768, max_pos=32767)
+    attn = L.dsa_sparse_mla_attn_workspace_size(ctypes.byref(dec), ctypes.byref(d))
+    assert attn == 32 * 8 * 128 * 513 * 4   # 8 splits of fp32 partial outputs + lse
+    fwd = L.dsa_forward_workspace_size(ctypes.byref(dec), ctypes.byref(d), 0)
+    assert fwd >= attn + 32 * 32768 * 4 + 32 * 2048 * 4
+    pre = _rows(m, R=131072, B=1, N=131072, max_pos=131071)
+    w = L.dsa_forward_workspace_size(ctypes.byref(pre), ctypes.byref(d), 8192)
+    assert w >= 8192 * 131072 * 4 and w < 8192 * 131072 * 4 + 8192 * 2048 * 4 + (1 << 20)
+    f32 = m.dims_struct(m.Dims(4, 32, 16, 80, 64, 64, True))
+    tiny = _rows(m, R=256, B=1, N=256, max_pos=255)
+    assert L.dsa_sparse_mla_attn_workspace_size(ctypes.byref(tiny), ctypes.byref(f32)) == 0
