@@ -8,24 +8,28 @@
 // MQA mode of MLA.)
 //
 // Kernel design (bf16 path, H = 128, D_k = 576, D_v = 512):
-// * one 256-thread block (4 waves x 32 heads) per (row, split); a split is a
-//   contiguous slice of the row's selected positions.  Splits of a row are mapped
-//   to one XCD so the row's queries are fetched from HBM once per XCD L2.
-// * the wave's 32 queries live in registers for the whole block (B operand of
-//   S^T = C q^T, 144 VGPRs); the 32 x 512 fp32 output accumulators are MFMA
-//   accumulators (256 registers).
-// * positions are processed 32 at a time.  The 32 gathered latent rows (36 KB) are
-//   copied HBM -> LDS by direct global_load_lds (no registers), double-buffered so
-//   the next block's gather overlaps this block's MFMAs.  A swizzle of the 16-byte
-//   chunks inside each row keeps the MFMA operand reads free of bank conflicts.
-//   The value part is then re-laid out in LDS as [dim][position] so the P.V
-//   contraction over positions reads contiguous 8-byte runs.
+// * one 512-thread block (8 waves) per (row, split); a split is a contiguous slice
+//   of the row's selected positions.  Splits of a row are mapped to one XCD so
+//   the row's queries come from HBM once per XCD L2.
+// * wave w owns head group hg = w/2 (32 heads) and half hf = w%2.  It keeps the
+//   queries of its 32 heads for contraction dims [288 hf, 288 hf + 288) in
+//   registers (72 VGPRs) and accumulates the output columns [256 hf, 256 hf + 256)
+//   (128 accumulator registers).  The two halves of S = q c^T are summed through
+//   LDS, so both waves of a pair see the same fp32 logits.
+// * positions are processed 32 at a time.  The 32 gathered latent rows (36 KB)
+//   are copied HBM -> LDS by direct global_load_lds, double-buffered, so the next
+//   gather overlaps this block's MFMAs.  A 16-byte chunk swizzle inside each row
+//   keeps the operand reads spread over the LDS banks.
 // * S^T tiles (M = 16 positions, N = 16 heads) leave each lane with 4 consecutive
-//   positions of one head, which is exactly the P operand of the P.V MFMA
-//   (M = 16 heads, K = 32 positions) after a bf16 cast: no shuffles.
+//   positions of one head: exactly the P operand of the P.V MFMA (M = 16 heads,
+//   K = 32 positions) after a bf16 cast, with no shuffles.  The V operand needs
+//   the row-major tile read column-wise; ds_read_b64_tr_b16 does that: within
+//   each 16-lane group, lane L receives element L%4 of the 8-byte chunks addressed
+//   by lanes 4i + L/4 (i = 0..3), so lanes pointing at V[e_i][d0 + 4j .. +3]
+//   deliver V[e_0..e_3][d0 + L] to lane L.
 // * online softmax in the exp2 domain with a stale-max rule: the running max is
-//   only raised (and the accumulators rescaled) when a block's max exceeds it by
-//   more than 2^8, which keeps every exponent <= 2^8 and skips nearly all rescales.
+//   raised (and the accumulators rescaled) only when a block's max exceeds it by
+//   more than 2^8, which bounds every weight by 2^8 and skips nearly all rescales.
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
@@ -38,24 +42,32 @@ constexpr int DV = kVDim;           // 512
 constexpr int BE = 32;              // positions per block
 constexpr int KROW = DK * 2;        // 1152 bytes per latent row
 constexpr int KCH = KROW / 16;      // 72 chunks of 16 bytes
-constexpr int VS = 72;              // bytes per [dim] row of the transposed value tile
-constexpr int KBUF = BE * KROW;     // 36864
-constexpr int VBUF = DV * VS;       // 36864
-constexpr int STAGE = KBUF + VBUF;  // 73728
-constexpr int NT = 256;
-constexpr int LOADS_PER_WAVE = KBUF / 1024 / 4;  // 9 direct loads of 1 KB per wave
+constexpr int STAGE = BE * KROW;    // 36864 bytes per gathered block
+constexpr int NT = 512;             // 8 waves
+constexpr int NWAVE = NT / 64;
+constexpr int LOADS = STAGE / 1024; // 36 direct loads of 1 KB per block
+constexpr int KS_HALF = DK / 32 / 2;  // 9 contraction steps of 32 per half
+constexpr int DT_HALF = DV / 16 / 2;  // 16 output column tiles per half
 constexpr float kStaleMax = 8.0f;   // log2 headroom of the stale running max
 constexpr float kLn2 = 0.69314718055994530942f;
 
-static_assert(KBUF % 4096 == 0, "block gather must split evenly over 4 waves");
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4_t;
 
 // physical 16-byte slot of logical chunk c of entry e inside its 1152-byte row
 __device__ __forceinline__ int kswz(int e, int c) { return (c & ~7) | ((c ^ e) & 7); }
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
+// byte offset of dim d (multiple of 4) of entry e inside a gathered block
+__device__ __forceinline__ int koff(int e, int d) {
+  return e * KROW + kswz(e, d >> 3) * 16 + (d & 4) * 2;
+}
 
-__device__ __forceinline__ lds_ptr_t to_lds(void* p) {
-  return (lds_ptr_t)(p);
+__device__ __forceinline__ lds_ptr_t to_lds(void* p) { return (lds_ptr_t)(p); }
+
+__device__ __forceinline__ i32x2 ds_read_tr16(const uint8_t* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)(p));
+  return __builtin_bit_cast(i32x2, v);
 }
 
 __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
@@ -65,9 +77,11 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
     float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ o_part, float* __restrict__ lse_part) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+  __shared__ __attribute__((aligned(16))) float xbuf[NWAVE][16][64];  // S partials
   __shared__ int sidx[kTopk];
 
   const int tid = threadIdx.x, l = lane_id(), wv = tid >> 6, g = l >> 4, nn = l & 15;
+  const int hg = wv >> 1, hf = wv & 1;
   // XCD-aware decode of the block id: all splits of row r run on XCD r % 8.
   const int xcd = blockIdx.x & 7;
   const int rest = blockIdx.x >> 3;
@@ -84,66 +98,41 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
     const int p = irow[i];
     sidx[i] = (p >= 0 && p < N) ? p : -1;
   }
-
   const uint16_t* lat = latent + (size_t)b * N * DK;
 
-  // queries of this wave's 32 heads: B operand of S^T = C q^T
-  i32x4 qr[2][18];
+  // queries of heads 32hg + 16nt + nn, dims 288hf + 32ks + 8g .. +7 (B operand of S^T)
+  i32x4 qr[2][KS_HALF];
   {
-    const uint16_t* qrow = q + ((size_t)r * H + 32 * wv) * DK;
+    const uint16_t* qrow = q + ((size_t)r * H + 32 * hg) * DK + 288 * hf;
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int ks = 0; ks < 18; ++ks)
+      for (int ks = 0; ks < KS_HALF; ++ks)
         qr[nt][ks] = *reinterpret_cast<const i32x4*>(qrow + (16 * nt + nn) * DK + 32 * ks + 8 * g);
   }
   __syncthreads();  // sidx visible
 
-  // gather of block `blk` into stage `st`: each lane fetches one 16-byte chunk per
-  // 1 KB direct load; the chunk it fetches is the one whose swizzled slot equals
-  // its lane-linear LDS address.
+  // gather of block blk into stage st: direct load i fills LDS bytes
+  // [1024 i, 1024 i + 1024); each lane fetches the chunk whose swizzled slot is its
+  // lane-linear destination.
   auto issue_gather = [&](int blk, int st) {
     uint8_t* kb = smem + st * STAGE;
-#pragma unroll
-    for (int i = 0; i < LOADS_PER_WAVE; ++i) {
-      const int base = (wv * LOADS_PER_WAVE + i) * 1024;
-      const int P = (base >> 4) + l;  // physical slot
+    for (int i = wv; i < LOADS; i += NWAVE) {
+      const int P = i * 64 + l;  // physical slot
       const int e = P / KCH;
       const int pc = P - e * KCH;
       const int c = (pc & ~7) | ((pc ^ e) & 7);
       const int pos = sidx[blk * BE + e];
       const uint16_t* src = lat + (size_t)(pos >= 0 ? pos : 0) * DK + c * 8;
-      __builtin_amdgcn_global_load_lds(src, to_lds(kb + base), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(src, to_lds(kb + i * 1024), 16, 0, 0);
     }
   };
 
-  // value part re-laid out as [dim][position] (bf16 pairs of positions 2p, 2p+1)
-  auto build_vt = [&](int st) {
-    const uint8_t* kb = smem + st * STAGE;
-    uint8_t* vt = smem + st * STAGE + KBUF;
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int p = l & 15;
-      const int c = 16 * it + 4 * wv + (l >> 4);  // value chunk 0..63
-      const int e0 = 2 * p, e1 = 2 * p + 1;
-      const i32x4 a = *reinterpret_cast<const i32x4*>(kb + e0 * KROW + kswz(e0, c) * 16);
-      const i32x4 bq = *reinterpret_cast<const i32x4*>(kb + e1 * KROW + kswz(e1, c) * 16);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t wa = (uint32_t)a[i], wb = (uint32_t)bq[i];
-        const uint32_t lo = (wa & 0xffffu) | (wb << 16);          // dim 8c+2i
-        const uint32_t hi = (wa >> 16) | (wb & 0xffff0000u);      // dim 8c+2i+1
-        *reinterpret_cast<uint32_t*>(vt + (8 * c + 2 * i) * VS + 4 * p) = lo;
-        *reinterpret_cast<uint32_t*>(vt + (8 * c + 2 * i + 1) * VS + 4 * p) = hi;
-      }
-    }
-  };
-
-  f32x4 O[2][32];
+  f32x4 O[2][DT_HALF];
 #pragma unroll
   for (int hm = 0; hm < 2; ++hm)
 #pragma unroll
-    for (int dt = 0; dt < 32; ++dt) O[hm][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < DT_HALF; ++dt) O[hm][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run[2] = {-INFINITY, -INFINITY};
   float l_part[2] = {0.f, 0.f};
 
@@ -152,28 +141,25 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
   for (int blk = 0; blk < nblk; ++blk) {
     const int st = blk & 1;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // block blk's rows are in LDS; previous block's compute done
-    build_vt(st);
-    __syncthreads();
+    __syncthreads();  // block blk in LDS; everyone is done with block blk-1
     if (blk + 1 < nblk) issue_gather(blk + 1, st ^ 1);
-
     const uint8_t* kb = smem + st * STAGE;
-    const uint8_t* vt = kb + KBUF;
 
-    // ---- S^T = C q^T : acc[mt][nt] lane holds S^T[16mt + 4g + v][16nt + nn]
+    // ---- partial S^T over this wave's contraction half:
+    //      acc[mt][nt] lane holds S^T[16mt + 4g + v][16nt + nn]
     f32x4 acc[2][2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 18; ++ks) {
+    for (int ks = 0; ks < KS_HALF; ++ks) {
       bf16x8 a[2];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
         const int e = 16 * mt + nn;
-        a[mt] = as_bf16x8(
-            *reinterpret_cast<const i32x4*>(kb + e * KROW + kswz(e, 4 * ks + g) * 16));
+        a[mt] = as_bf16x8(*reinterpret_cast<const i32x4*>(
+            kb + e * KROW + kswz(e, 36 * hf + 4 * ks + g) * 16));
       }
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
@@ -181,6 +167,25 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
         for (int mt = 0; mt < 2; ++mt)
           acc[mt][nt] = mfma_bf16_16x16x32(a[mt], as_bf16x8(qr[nt][ks]), acc[mt][nt]);
     }
+    // ---- sum the two halves through LDS (same addition order in both waves)
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) xbuf[wv][(mt * 2 + nt) * 4 + v][l] = acc[mt][nt][v];
+    __syncthreads();
+    float sfull[2][2][4];  // [mt][nt][v]
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float other = xbuf[wv ^ 1][(mt * 2 + nt) * 4 + v][l];
+          const float mine = acc[mt][nt][v];
+          sfull[mt][nt][v] = hf == 0 ? mine + other : other + mine;
+        }
 
     // ---- online softmax (exp2 domain) for the lane's heads 16nt + nn
     bool valid[2][4];
@@ -189,7 +194,6 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
 #pragma unroll
       for (int v = 0; v < 4; ++v) valid[mt][v] = sidx[blk * BE + 16 * mt + 4 * g + v] >= 0;
 
-    float sv[2][2][4];  // [nt][mt][v]
     float bm[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
@@ -198,8 +202,8 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float s = valid[mt][v] ? acc[mt][nt][v] * scale_log2 : -INFINITY;
-          sv[nt][mt][v] = s;
+          const float s = valid[mt][v] ? sfull[mt][nt][v] * scale_log2 : -INFINITY;
+          sfull[mt][nt][v] = s;
           mx = fmaxf(mx, s);
         }
       mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -222,7 +226,7 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
         for (int v = 0; v < 4; ++v) {
           const float a = __shfl(alpha[hm], 4 * g + v);
 #pragma unroll
-          for (int dt = 0; dt < 32; ++dt) O[hm][dt][v] *= a;
+          for (int dt = 0; dt < DT_HALF; ++dt) O[hm][dt][v] *= a;
         }
     }
     bf16x8 pa[2];
@@ -235,7 +239,7 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          p[mt][v] = __builtin_amdgcn_exp2f(sv[nt][mt][v] - mref);
+          p[mt][v] = __builtin_amdgcn_exp2f(sfull[mt][nt][v] - mref);
           sum += p[mt][v];
         }
       l_part[nt] += sum;
@@ -247,12 +251,15 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
       pa[nt] = as_bf16x8(pk);
     }
 
-    // ---- O += P V : B operand = values of positions {4g..4g+3, 16+4g..16+4g+3}
+    // ---- O += P V for output columns 256hf + 16dt + nn.  B operand slots 0..3 are
+    //      positions 4g..4g+3, slots 4..7 positions 16+4g..16+4g+3 (the P layout).
+    const int ei = 4 * g + (nn >> 2);   // position read by this lane (first half)
+    const int dj = 4 * (nn & 3);        // dim quad read by this lane
 #pragma unroll
-    for (int dt = 0; dt < 32; ++dt) {
-      const uint8_t* vrow = vt + (16 * dt + nn) * VS;
-      const i32x2 v0 = *reinterpret_cast<const i32x2*>(vrow + 8 * g);
-      const i32x2 v1 = *reinterpret_cast<const i32x2*>(vrow + 32 + 8 * g);
+    for (int dt = 0; dt < DT_HALF; ++dt) {
+      const int d0 = 256 * hf + 16 * dt + dj;
+      const i32x2 v0 = ds_read_tr16(kb + koff(ei, d0));
+      const i32x2 v1 = ds_read_tr16(kb + koff(ei + 16, d0));
       const i32x4 vv = {v0[0], v0[1], v1[0], v1[1]};
       const bf16x8 bv = as_bf16x8(vv);
       O[0][dt] = mfma_bf16_16x16x32(pa[0], bv, O[0][dt]);
@@ -276,20 +283,21 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
       const float L = __shfl(l_tot[hm], 4 * g + v);
       const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
-      for (int dt = 0; dt < 32; ++dt) O[hm][dt][v] *= inv;
+      for (int dt = 0; dt < DT_HALF; ++dt) O[hm][dt][v] *= inv;
     }
-  const int head0 = 32 * wv;
+  const int head0 = 32 * hg;
+  const int col0 = 256 * hf + nn;
   if (splits == 1) {
     uint16_t* orow = out + (size_t)r * H * DV;
 #pragma unroll
     for (int hm = 0; hm < 2; ++hm)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        uint16_t* oh = orow + (size_t)(head0 + 16 * hm + 4 * g + v) * DV + nn;
+        uint16_t* oh = orow + (size_t)(head0 + 16 * hm + 4 * g + v) * DV + col0;
 #pragma unroll
-        for (int dt = 0; dt < 32; ++dt) oh[16 * dt] = (uint16_t)f32_to_bf16_bits(O[hm][dt][v]);
+        for (int dt = 0; dt < DT_HALF; ++dt) oh[16 * dt] = (uint16_t)f32_to_bf16_bits(O[hm][dt][v]);
       }
-    if (lse != nullptr && g == 0) {
+    if (lse != nullptr && g == 0 && hf == 0) {
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
         lse[(size_t)r * H + head0 + 16 * nt + nn] =
@@ -301,11 +309,11 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
     for (int hm = 0; hm < 2; ++hm)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        float* ph = prow + (size_t)(head0 + 16 * hm + 4 * g + v) * DV + nn;
+        float* ph = prow + (size_t)(head0 + 16 * hm + 4 * g + v) * DV + col0;
 #pragma unroll
-        for (int dt = 0; dt < 32; ++dt) ph[16 * dt] = O[hm][dt][v];
+        for (int dt = 0; dt < DT_HALF; ++dt) ph[16 * dt] = O[hm][dt][v];
       }
-    if (g == 0) {
+    if (g == 0 && hf == 0) {
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
         lse_part[((size_t)r * splits + sp) * H + head0 + 16 * nt + nn] =
