@@ -5,7 +5,13 @@ Oracle inputs are always regenerated on the host from the seeded generator; they
 never come from the GPU.  The three comparison rules follow the tolerances the
 hot path is held to:
 
-* C1 scores:  |I_gpu - I_ref| <= 2e-2 * max(|I_ref|, 1e-3 * max_s |I_ref|)
+* C1 scores:  |I_gpu - I_ref| <= 2e-2 * max(|I_ref|, 1e-2 * max_s |I_ref|).
+  The floor exists because w has both signs, so single scores can cancel to ~0.
+  Its level follows the arithmetic: the gfx950 fp8 MFMA accumulates a 128-wide
+  dot product with an error of up to ~2.6e-4 of its largest product (measured
+  on the device against exact sums), which puts score errors near 1e-4 of the
+  row's largest score; the allowance 2e-4 * max|I| stays below the selection tie
+  band (1e-3 * tau) whenever tau >= 0.2 * max|I|.
 * C2 indices: the GPU set has n = min(k, t+1) unique positions in [0, t], ascending,
   -1 padded; it equals the oracle's set outside the tie band
   A = {s : |I_ref[s] - tau| <= 1e-3 |tau|}, tau = the n-th largest oracle score.
@@ -23,7 +29,7 @@ import dsa_inputs as di
 import oracle
 
 SCORE_RTOL = 2e-2
-SCORE_FLOOR = 1e-3
+SCORE_FLOOR = 1e-2
 BAND = 1e-3
 ATTN_MAX_ABS = 2e-2
 ATTN_MEAN_ABS = 2e-3

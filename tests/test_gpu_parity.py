@@ -93,7 +93,7 @@ def test_indexer_parity(dsa, name):
     rows = sample(cfg)
     dims = dsa.Dims.from_config(cfg)
     ld = (cfg.kv_len + 63) // 64 * 64
-    worst = 0.0
+    worst, rel_row = 0.0, 0.0
     for a, b in chunks(cfg):
         want = rows[(rows >= a) & (rows < b)]
         if want.size == 0:
@@ -108,7 +108,10 @@ def test_indexer_parity(dsa, name):
             row = host.row(int(r))
             ref = host.scores(row)
             worst = max(worst, check_scores(got[i, : row.t + 1], ref))
-    print(f"[indexer] {name}: worst error / allowed = {worst:.3e}")
+            rel_row = max(rel_row, float(np.max(np.abs(got[i, : row.t + 1] - ref))
+                                         / max(np.max(np.abs(ref)), 1e-30)))
+    print(f"[indexer] {name}: worst error / allowed = {worst:.3e}, "
+          f"worst |error| / max|score| of its row = {rel_row:.3e}")
 
 
 # ---------------------------------------------------------------- step 2
