@@ -19,6 +19,11 @@ LIB = os.path.join(PKG, "libdsa.so")
 ARCH = "gfx950"
 
 SOURCES = ["indexer.hip", "topk.hip", "attention.hip", "dsa_api.cpp"]
+# per-source code generation options
+EXTRA = {
+    # keep MFMA results in VGPRs: the indexer epilogue reads every result with VALU
+    "indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def _hipcc() -> str:
@@ -40,7 +45,7 @@ def _flags(extra_debug: bool = False):
 
 def _compile(src: str, hipcc: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc, *_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc, *_flags(), *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -11,11 +11,14 @@
 // * one 512-thread block (8 waves) per (row, split); a split is a contiguous slice
 //   of the row's selected positions.  Splits of a row are mapped to one XCD so
 //   the row's queries come from HBM once per XCD L2.
-// * wave w owns head group hg = w/2 (32 heads) and half hf = w%2.  It keeps the
-//   queries of its 32 heads for contraction dims [288 hf, 288 hf + 288) in
-//   registers (72 VGPRs) and accumulates the output columns [256 hf, 256 hf + 256)
-//   (128 accumulator registers).  The two halves of S = q c^T are summed through
-//   LDS, so both waves of a pair see the same fp32 logits.
+// * wave w owns head group hg = w/2 (32 heads) and half hf = w%2.  Its share of
+//   the 576-long contraction is latent dims [256 hf, 256 hf + 256), whose queries
+//   stay in registers (64 VGPRs), plus rope dims [512 + 32 hf, +32), read from a
+//   16 KB LDS copy of the row's rope queries.  It accumulates output columns
+//   [256 hf, 256 hf + 256) (128 registers).  The two halves of S = q c^T are
+//   summed through LDS, so both waves of a pair see the same fp32 logits.  The
+//   kernel fits 255 VGPRs with no scratch: a spill reload inside the loop would
+//   wait on the in-flight gather (vmcnt is in order) and serialise the pipeline.
 // * positions are processed 32 at a time.  The 32 gathered latent rows (36 KB)
 //   are copied HBM -> LDS by direct global_load_lds, double-buffered, so the next
 //   gather overlaps this block's MFMAs.  A 16-byte chunk swizzle inside each row
@@ -46,7 +49,9 @@ constexpr int STAGE = BE * KROW;    // 36864 bytes per gathered block
 constexpr int NT = 512;             // 8 waves
 constexpr int NWAVE = NT / 64;
 constexpr int LOADS = STAGE / 1024; // 36 direct loads of 1 KB per block
-constexpr int KS_HALF = DK / 32 / 2;  // 9 contraction steps of 32 per half
+constexpr int KS_LAT = DV / 32 / 2;   // 8 latent contraction steps of 32 per half
+constexpr int RD = DK - DV;           // 64 rope dims
+constexpr int QR_STRIDE = RD * 2 + 16;  // bytes per head row of the rope queries in LDS
 constexpr int DT_HALF = DV / 16 / 2;  // 16 output column tiles per half
 constexpr float kStaleMax = 8.0f;   // log2 headroom of the stale running max
 constexpr float kLn2 = 0.69314718055994530942f;
@@ -57,11 +62,6 @@ typedef __attribute__((address_space(3))) s16x4* lds_s16x4_t;
 
 // physical 16-byte slot of logical chunk c of entry e inside its 1152-byte row
 __device__ __forceinline__ int kswz(int e, int c) { return (c & ~7) | ((c ^ e) & 7); }
-
-// byte offset of dim d (multiple of 4) of entry e inside a gathered block
-__device__ __forceinline__ int koff(int e, int d) {
-  return e * KROW + kswz(e, d >> 3) * 16 + (d & 4) * 2;
-}
 
 __device__ __forceinline__ lds_ptr_t to_lds(void* p) { return (lds_ptr_t)(p); }
 
@@ -79,8 +79,15 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
   __shared__ __attribute__((aligned(16))) float xbuf[NWAVE][16][64];  // S partials
   __shared__ int sidx[kTopk];
+  // rope part of the 128 queries (q[r, h, 512:576]), rows padded to spread banks
+  __shared__ __attribute__((aligned(16))) uint8_t qrope[H * QR_STRIDE];
+  // per-thread gather table: (entry << 16 | byte offset in row) of each direct load;
+  // kept in LDS so the loop does not hold it in registers
+  __shared__ uint32_t gtab[(STAGE / 1024 + NT / 64 - 1) / (NT / 64)][NT];
 
-  const int tid = threadIdx.x, l = lane_id(), wv = tid >> 6, g = l >> 4, nn = l & 15;
+  const int tid = threadIdx.x, l = lane_id(), g = l >> 4, nn = l & 15;
+  // wave-uniform indices live in scalar registers
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hg = wv >> 1, hf = wv & 1;
   // XCD-aware decode of the block id: all splits of row r run on XCD r % 8.
   const int xcd = blockIdx.x & 7;
@@ -99,34 +106,79 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
     sidx[i] = (p >= 0 && p < N) ? p : -1;
   }
   const uint16_t* lat = latent + (size_t)b * N * DK;
+  const uint8_t* lat_bytes = reinterpret_cast<const uint8_t*>(lat);
 
-  // queries of heads 32hg + 16nt + nn, dims 288hf + 32ks + 8g .. +7 (B operand of S^T)
-  i32x4 qr[2][KS_HALF];
+  // Contraction split: half hf owns latent dims [256 hf, 256 hf + 256) (k-steps
+  // 8 hf .. 8 hf + 7, queries in registers) and rope dims [512 + 32 hf, +32)
+  // (k-step 16 + hf, queries read from LDS).
+  // registers: queries of heads 32hg + 16nt + nn, dims 256hf + 32ks + 8g .. +7
+  i32x4 qr[2][KS_LAT];
   {
-    const uint16_t* qrow = q + ((size_t)r * H + 32 * hg) * DK + 288 * hf;
+    const uint16_t* qrow = q + ((size_t)r * H + 32 * hg) * DK + 256 * hf;
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int ks = 0; ks < KS_HALF; ++ks)
+      for (int ks = 0; ks < KS_LAT; ++ks)
         qr[nt][ks] = *reinterpret_cast<const i32x4*>(qrow + (16 * nt + nn) * DK + 32 * ks + 8 * g);
+  }
+  // LDS: rope queries of all 128 heads, 8 chunks of 16 bytes per head
+  for (int c = tid; c < H * (RD / 8); c += NT) {
+    const int h = c >> 3, j = c & 7;
+    *reinterpret_cast<i32x4*>(qrope + h * QR_STRIDE + 16 * j) =
+        *reinterpret_cast<const i32x4*>(q + ((size_t)r * H + h) * DK + DV + 8 * j);
   }
   __syncthreads();  // sidx visible
 
   // gather of block blk into stage st: direct load i fills LDS bytes
-  // [1024 i, 1024 i + 1024); each lane fetches the chunk whose swizzled slot is its
-  // lane-linear destination.
+  // [1024 i, 1024 i + 1024); each lane fetches the 16-byte chunk whose swizzled
+  // slot is its lane-linear destination.  The (entry, chunk) of each of the wave's
+  // loads is fixed, so it is computed once: packed as entry << 16 | chunk * 16.
+  constexpr int MAXL = (LOADS + NWAVE - 1) / NWAVE;  // 5
+#pragma unroll
+  for (int j = 0; j < MAXL; ++j) {
+    const int i = wv + j * NWAVE;
+    const int P = (i < LOADS ? i : 0) * 64 + l;  // physical slot
+    const int e = P / KCH;
+    const int pc = P - e * KCH;
+    gtab[j][tid] = ((uint32_t)e << 16) | (uint32_t)(kswz(e, pc) * 16);  // kswz is an involution
+  }
   auto issue_gather = [&](int blk, int st) {
     uint8_t* kb = smem + st * STAGE;
-    for (int i = wv; i < LOADS; i += NWAVE) {
-      const int P = i * 64 + l;  // physical slot
-      const int e = P / KCH;
-      const int pc = P - e * KCH;
-      const int c = (pc & ~7) | ((pc ^ e) & 7);
-      const int pos = sidx[blk * BE + e];
-      const uint16_t* src = lat + (size_t)(pos >= 0 ? pos : 0) * DK + c * 8;
-      __builtin_amdgcn_global_load_lds(src, to_lds(kb + i * 1024), 16, 0, 0);
+    const int* bidx = sidx + blk * BE;
+#pragma unroll
+    for (int j = 0; j < MAXL; ++j) {
+      const int i = wv + j * NWAVE;
+      if (i < LOADS) {
+        const uint32_t ent = gtab[j][tid];
+        const int pos = bidx[ent >> 16];
+        // 32-bit offset from the sequence base (a sequence's cache is < 4 GiB)
+        const uint32_t off = (uint32_t)(pos >= 0 ? pos : 0) * (uint32_t)KROW + (ent & 0xffffu);
+        const uint8_t* src = lat_bytes + off;
+        __builtin_amdgcn_global_load_lds(src, to_lds(kb + i * 1024), 16, 0, 0);
+      }
     }
   };
+
+  // Per-lane LDS base offsets.  With x = e & 7 the swizzled slot of chunk c = 4k + u
+  // (u < 4) is c ^ x = 4 (k ^ (x >> 2)) + (u ^ (x & 3)), and k ^ (x >> 2) is
+  // k + (x >> 2) for even k and k - (x >> 2) for odd k; so every operand address
+  // below is one of a few per-lane bases plus a compile-time offset.
+  // QK^T A operand: entry 16 mt + nn, latent chunk 4 (8 hf + ks) + g (k = 8 hf + ks
+  // has the parity of ks); rope chunk 4 (16 + hf) + g.
+  const int xq = nn & 7;
+  const int qa_base = nn * KROW + 16 * (g ^ (xq & 3)) + 512 * hf;
+  const int qa_even = qa_base + 64 * (xq >> 2);  // ks even
+  const int qa_odd = qa_base - 64 * (xq >> 2);   // ks odd
+  const int qa_rope = hf ? qa_odd + 576 : qa_even + 1024;
+  const int qb_rope = (32 * hg + nn) * QR_STRIDE + 64 * hf + 16 * g;  // B operand, nt = 0
+  // P.V B operand (transposed reads): entry ei (+16), dims 256 hf + 16 dt + 4 (nn & 3),
+  // chunk 32 hf + 8 (dt >> 2) + (2 (dt & 3) + hh), hh = (nn >> 1) & 1.
+  const int ei = 4 * g + (nn >> 2);
+  const int xv = ei & 7;
+  const int hh = (nn >> 1) & 1;
+  // slot (2j + hh) ^ xv = 2 (j ^ (xv >> 1)) + (hh ^ (xv & 1)) for column tile group j
+  const int tr_base = ei * KROW + 512 * hf + 16 * (hh ^ (xv & 1)) + 8 * (nn & 1);
+  const int tr_x = xv >> 1;
 
   f32x4 O[2][DT_HALF];
 #pragma unroll
@@ -153,19 +205,23 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < KS_HALF; ++ks) {
+    for (int ks = 0; ks <= KS_LAT; ++ks) {
+      const bool rope = ks == KS_LAT;
+      const uint8_t* ap = kb + (rope ? qa_rope : (((ks & 1) ? qa_odd : qa_even) + 64 * ks));
       bf16x8 a[2];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const int e = 16 * mt + nn;
-        a[mt] = as_bf16x8(*reinterpret_cast<const i32x4*>(
-            kb + e * KROW + kswz(e, 36 * hf + 4 * ks + g) * 16));
-      }
+      for (int mt = 0; mt < 2; ++mt)
+        a[mt] = as_bf16x8(*reinterpret_cast<const i32x4*>(ap + 16 * KROW * mt));
+      bf16x8 bq[2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+        bq[nt] = rope ? as_bf16x8(*reinterpret_cast<const i32x4*>(qrope + qb_rope + 16 * QR_STRIDE * nt))
+                      : as_bf16x8(qr[nt][rope ? 0 : ks]);
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
-          acc[mt][nt] = mfma_bf16_16x16x32(a[mt], as_bf16x8(qr[nt][ks]), acc[mt][nt]);
+          acc[mt][nt] = mfma_bf16_16x16x32(a[mt], bq[nt], acc[mt][nt]);
     }
     // ---- sum the two halves through LDS (same addition order in both waves)
 #pragma unroll
@@ -188,11 +244,12 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
         }
 
     // ---- online softmax (exp2 domain) for the lane's heads 16nt + nn
-    bool valid[2][4];
+    uint32_t valid = 0;  // bit 4 mt + v: position 16 mt + 4 g + v is not padding
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) valid[mt][v] = sidx[blk * BE + 16 * mt + 4 * g + v] >= 0;
+      for (int v = 0; v < 4; ++v)
+        valid |= (sidx[blk * BE + 16 * mt + 4 * g + v] >= 0 ? 1u : 0u) << (4 * mt + v);
 
     float bm[2];
 #pragma unroll
@@ -202,7 +259,7 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float s = valid[mt][v] ? sfull[mt][nt][v] * scale_log2 : -INFINITY;
+          const float s = ((valid >> (4 * mt + v)) & 1u) ? sfull[mt][nt][v] * scale_log2 : -INFINITY;
           sfull[mt][nt][v] = s;
           mx = fmaxf(mx, s);
         }
@@ -253,13 +310,11 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
 
     // ---- O += P V for output columns 256hf + 16dt + nn.  B operand slots 0..3 are
     //      positions 4g..4g+3, slots 4..7 positions 16+4g..16+4g+3 (the P layout).
-    const int ei = 4 * g + (nn >> 2);   // position read by this lane (first half)
-    const int dj = 4 * (nn & 3);        // dim quad read by this lane
 #pragma unroll
     for (int dt = 0; dt < DT_HALF; ++dt) {
-      const int d0 = 256 * hf + 16 * dt + dj;
-      const i32x2 v0 = ds_read_tr16(kb + koff(ei, d0));
-      const i32x2 v1 = ds_read_tr16(kb + koff(ei + 16, d0));
+      const uint8_t* vp = kb + tr_base + 32 * ((dt & 3) ^ tr_x) + 128 * (dt >> 2);
+      const i32x2 v0 = ds_read_tr16(vp);
+      const i32x2 v1 = ds_read_tr16(vp + 16 * KROW);
       const i32x4 vv = {v0[0], v0[1], v1[0], v1[1]};
       const bf16x8 bv = as_bf16x8(vv);
       O[0][dt] = mfma_bf16_16x16x32(pa[0], bv, O[0][dt]);
@@ -295,7 +350,7 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
       for (int v = 0; v < 4; ++v) {
         uint16_t* oh = orow + (size_t)(head0 + 16 * hm + 4 * g + v) * DV + col0;
 #pragma unroll
-        for (int dt = 0; dt < DT_HALF; ++dt) oh[16 * dt] = (uint16_t)f32_to_bf16_bits(O[hm][dt][v]);
+        for (int dt = 0; dt < DT_HALF; ++dt) oh[16 * dt] = bf16_bits(O[hm][dt][v]);
       }
     if (lse != nullptr && g == 0 && hf == 0) {
 #pragma unroll

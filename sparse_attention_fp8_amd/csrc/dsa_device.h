@@ -35,16 +35,23 @@ __device__ __forceinline__ f32x4 mfma_bf16_16x16x32(bf16x8 a, bf16x8 b, f32x4 c)
 __device__ __forceinline__ bf16x8 as_bf16x8(i32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // ---------------------------------------------------------------- conversions
-// float -> bf16 bits, round to nearest even (NaN kept quiet).
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+// float -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t bf16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
+// Two floats -> packed bf16 pair (lo in bits 0..15), round to nearest even; on
+// gfx950 this is the single v_cvt_pk_bf16_f32 instruction.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// max(x, 0) for an IEEE float as one integer max on its bits: non-negative floats
+// order like their bit patterns and every negative float has a negative pattern.
+__device__ __forceinline__ float relu_bits(float x) {
+  return __builtin_bit_cast(float, max(__builtin_bit_cast(int, x), 0));
 }
 
 // Order-preserving map of a float to uint32 (larger float -> larger key).

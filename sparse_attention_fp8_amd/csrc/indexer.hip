@@ -39,7 +39,7 @@ __device__ __forceinline__ float head_partial(const i32x8 (&qa)[4], const float 
   for (int mt = 0; mt < 4; ++mt) {
     f32x4 acc = mfma_fp8_16x16x128(qa[mt], kb, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-    for (int v = 0; v < 4; ++v) p = fmaf(wq[mt * 4 + v], fmaxf(acc[v], 0.f), p);
+    for (int v = 0; v < 4; ++v) p = fmaf(wq[mt * 4 + v], relu_bits(acc[v]), p);
   }
   return p;
 }
@@ -108,32 +108,36 @@ __global__ __launch_bounds__(WAVES * 64) void indexer_fp8_decode_kernel(
   const float* ksc = k_scale + (size_t)b * N;
   float* out = scores + (size_t)r * ld;
 
-  i32x8 cur[4];
-  float ks_cur;
+  auto load_group = [&](int k, i32x8(&kb)[4], float& ks) {
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt)
-    cur[kt] = load_frag32(kc + (size_t)min(k0 + 16 * kt + n, t) * ID + 32 * g);
-  ks_cur = ksc[min(k0 + l, t)];
-
-  for (; k0 < kend; k0 += 64 * WAVES) {
-    const int kn = k0 + 64 * WAVES;
-    i32x8 nxt[4];
-    float ks_nxt = 0.f;
-    if (kn < kend) {
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-        nxt[kt] = load_frag32(kc + (size_t)min(kn + 16 * kt + n, t) * ID + 32 * g);
-      ks_nxt = ksc[min(kn + l, t)];
-    }
-    const float p0 = head_partial(qa, wq, cur[0]);
-    const float p1 = head_partial(qa, wq, cur[1]);
-    const float p2 = head_partial(qa, wq, cur[2]);
-    const float p3 = head_partial(qa, wq, cur[3]);
-    const float s = reduce_groups(p0, p1, p2, p3) * ks_cur;
-    if (k0 + l < kend) out[k0 + l] = s;
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) cur[kt] = nxt[kt];
-    ks_cur = ks_nxt;
+    for (int kt = 0; kt < 4; ++kt)
+      kb[kt] = load_frag32(kc + (size_t)min(k + 16 * kt + n, t) * ID + 32 * g);
+    ks = ksc[min(k + l, t)];
+  };
+  auto compute = [&](int k, const i32x8(&kb)[4], float ks) {
+    const float p0 = head_partial(qa, wq, kb[0]);
+    const float p1 = head_partial(qa, wq, kb[1]);
+    const float p2 = head_partial(qa, wq, kb[2]);
+    const float p3 = head_partial(qa, wq, kb[3]);
+    const float s = reduce_groups(p0, p1, p2, p3) * ks;
+    if (k + l < kend) out[k + l] = s;
+  };
+  // two register sets in ping-pong: the next group's loads are in flight while the
+  // current group is multiplied
+  constexpr int STEP = 64 * WAVES;
+  i32x8 ka[4], kb[4];
+  float sa, sb;
+  load_group(k0, ka, sa);
+  for (;;) {
+    const int k1 = k0 + STEP;
+    if (k1 < kend) load_group(k1, kb, sb);
+    compute(k0, ka, sa);
+    if (k1 >= kend) break;
+    const int k2 = k1 + STEP;
+    if (k2 < kend) load_group(k2, ka, sa);
+    compute(k1, kb, sb);
+    if (k2 >= kend) break;
+    k0 = k2;
   }
 }
 
@@ -158,37 +162,38 @@ __device__ __forceinline__ void prefill_rows(const uint8_t* __restrict__ q_idx,
 #pragma unroll
   for (int i = 0; i < NR; ++i) load_query(q_idx, q_scale, w, rr[i], qa[i], wq[i]);
   const int klast = kend - 1;
-
-  i32x8 cur[4];
-  float ks_cur;
+  auto load_group = [&](int k, i32x8(&kb)[4], float& ks) {
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt)
-    cur[kt] = load_frag32(kc + (size_t)min(kb0 + 16 * kt + n, klast) * ID + 32 * g);
-  ks_cur = ksc[min(kb0 + l, klast)];
-
-  for (int k0 = kb0; k0 < kend; k0 += 64) {
-    const int kn = k0 + 64;
-    i32x8 nxt[4];
-    float ks_nxt = 0.f;
-    if (kn < kend) {
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-        nxt[kt] = load_frag32(kc + (size_t)min(kn + 16 * kt + n, klast) * ID + 32 * g);
-      ks_nxt = ksc[min(kn + l, klast)];
-    }
+    for (int kt = 0; kt < 4; ++kt)
+      kb[kt] = load_frag32(kc + (size_t)min(k + 16 * kt + n, klast) * ID + 32 * g);
+    ks = ksc[min(k + l, klast)];
+  };
+  auto compute = [&](int k, const i32x8(&kb)[4], float ks) {
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
-      if (k0 > tt[i]) continue;  // wave-uniform
-      const float p0 = head_partial(qa[i], wq[i], cur[0]);
-      const float p1 = head_partial(qa[i], wq[i], cur[1]);
-      const float p2 = head_partial(qa[i], wq[i], cur[2]);
-      const float p3 = head_partial(qa[i], wq[i], cur[3]);
-      const float s = reduce_groups(p0, p1, p2, p3) * ks_cur;
-      if (k0 + l <= tt[i]) scores[(size_t)rr[i] * ld + k0 + l] = s;
+      if (k > tt[i]) continue;  // wave-uniform
+      const float p0 = head_partial(qa[i], wq[i], kb[0]);
+      const float p1 = head_partial(qa[i], wq[i], kb[1]);
+      const float p2 = head_partial(qa[i], wq[i], kb[2]);
+      const float p3 = head_partial(qa[i], wq[i], kb[3]);
+      const float s = reduce_groups(p0, p1, p2, p3) * ks;
+      if (k + l <= tt[i]) scores[(size_t)rr[i] * ld + k + l] = s;
     }
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) cur[kt] = nxt[kt];
-    ks_cur = ks_nxt;
+  };
+  i32x8 ka[4], kb[4];
+  float sa, sb;
+  int k0 = kb0;
+  load_group(k0, ka, sa);
+  for (;;) {
+    const int k1 = k0 + 64;
+    if (k1 < kend) load_group(k1, kb, sb);
+    compute(k0, ka, sa);
+    if (k1 >= kend) break;
+    const int k2 = k1 + 64;
+    if (k2 < kend) load_group(k2, ka, sa);
+    compute(k1, kb, sb);
+    if (k2 >= kend) break;
+    k0 = k2;
   }
 }
 
