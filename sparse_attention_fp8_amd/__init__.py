@@ -102,9 +102,15 @@ def dims_struct(d: Dims) -> _Dims:
 
 def rows_struct(row_seq: torch.Tensor, row_pos: torch.Tensor, num_seqs: int, max_ctx: int,
                 max_pos: int) -> _Rows:
+    """dsa_rows for R rows.  The struct keeps references to both tensors, so their
+    device memory stays alive as long as the struct does."""
     _dev(row_seq, torch.int32, "row_seq")
     _dev(row_pos, torch.int32, "row_pos")
-    return _Rows(row_pos.numel(), num_seqs, max_ctx, max_pos, _ptr(row_seq), _ptr(row_pos))
+    if row_seq.numel() != row_pos.numel():
+        raise ValueError("row_seq and row_pos must have the same length")
+    rs = _Rows(row_pos.numel(), num_seqs, max_ctx, max_pos, _ptr(row_seq), _ptr(row_pos))
+    rs._keep = (row_seq, row_pos)
+    return rs
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -120,6 +126,20 @@ def _dev(t: Optional[torch.Tensor], dtype, name):
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _shape(t: Optional[torch.Tensor], shape, name):
+    """Check a tensor's leading dims (None = any) so a mismatch fails on the host."""
+    if t is None:
+        return
+    if t.dim() != len(shape) or any(w is not None and a != w for a, w in zip(t.shape, shape)):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
+
+
+def _caches(rows: _Rows, dims: Dims, k_idx, k_scale, latent=None):
+    _shape(k_idx, (rows.num_seqs, rows.max_ctx, dims.idx_dim), "k_idx")
+    _shape(k_scale, (rows.num_seqs, rows.max_ctx), "k_scale")
+    _shape(latent, (rows.num_seqs, rows.max_ctx, dims.qk_dim), "latent")
 
 
 def _stream():
@@ -147,10 +167,16 @@ def indexer_scores(rows: _Rows, dims: Dims, q_idx, q_scale, w, k_idx, k_scale,
     _dev(w, torch.float32, "w")
     _dev(q_scale, torch.float32, "q_scale")
     _dev(k_scale, torch.float32, "k_scale")
+    R = rows.num_rows
+    _shape(q_idx, (R, dims.n_idx_heads, dims.idx_dim), "q_idx")
+    _shape(q_scale, (R, dims.n_idx_heads), "q_scale")
+    _shape(w, (R, dims.n_idx_heads), "w")
+    _caches(rows, dims, k_idx, k_scale)
     if scores is None:
         ld = ld or rows.max_pos + 1
         scores = torch.empty(rows.num_rows, ld, dtype=torch.float32, device=q_idx.device)
     _dev(scores, torch.float32, "scores")
+    _shape(scores, (R, None), "scores")
     ds = dims_struct(dims)
     _check(lib.dsa_indexer_scores(ctypes.byref(rows), ctypes.byref(ds), _ptr(q_idx), _ptr(q_scale),
                                   _ptr(w), _ptr(k_idx), _ptr(k_scale), _ptr(scores),
@@ -165,6 +191,8 @@ def topk(rows: _Rows, k: int, scores: torch.Tensor,
     if indices is None:
         indices = torch.empty(rows.num_rows, k, dtype=torch.int32, device=scores.device)
     _dev(indices, torch.int32, "indices")
+    _shape(scores, (rows.num_rows, None), "scores")
+    _shape(indices, (rows.num_rows, k), "indices")
     _check(lib.dsa_topk(ctypes.byref(rows), k, _ptr(scores), scores.shape[1], _ptr(indices),
                         _stream()))
     return indices
@@ -190,6 +218,11 @@ def sparse_mla_attn(rows: _Rows, dims: Dims, q, latent, indices, softmax_scale: 
         lse = torch.empty(R, dims.n_heads, dtype=torch.float32, device=q.device)
     _dev(out, adt, "out")
     _dev(lse, torch.float32, "lse")
+    _shape(q, (R, dims.n_heads, dims.qk_dim), "q")
+    _shape(indices, (R, dims.topk), "indices")
+    _shape(out, (R, dims.n_heads, dims.v_dim), "out")
+    _shape(lse, (R, dims.n_heads), "lse")
+    _caches(rows, dims, None, None, latent)
     need = sparse_mla_attn_workspace_size(rows, dims)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -223,9 +256,18 @@ def forward(rows: _Rows, dims: Dims, q_idx, q_scale, w, k_idx, k_scale, q, laten
     _dev(out, adt, "out")
     _dev(lse, torch.float32, "lse")
     _dev(indices_out, torch.int32, "indices_out")
+    _shape(q_idx, (R, dims.n_idx_heads, dims.idx_dim), "q_idx")
+    _shape(q_scale, (R, dims.n_idx_heads), "q_scale")
+    _shape(w, (R, dims.n_idx_heads), "w")
+    _shape(q, (R, dims.n_heads, dims.qk_dim), "q")
+    _shape(out, (R, dims.n_heads, dims.v_dim), "out")
+    _shape(lse, (R, dims.n_heads), "lse")
+    _shape(indices_out, (R, dims.topk), "indices_out")
+    _caches(rows, dims, k_idx, k_scale, latent)
     need = forward_workspace_size(rows, dims, chunk_rows)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _dev(workspace, torch.uint8, "workspace")
     ds = dims_struct(dims)
     _check(lib.dsa_forward(ctypes.byref(rows), ctypes.byref(ds), _ptr(q_idx), _ptr(q_scale),
                            _ptr(w), _ptr(k_idx), _ptr(k_scale), _ptr(q), _ptr(latent),

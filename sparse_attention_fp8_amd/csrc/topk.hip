@@ -6,18 +6,25 @@
 // are taken from the lowest position first, so the set is unique; it is written in
 // ascending position order and padded with -1.
 //
-// One 1024-thread block per row.  The row is held in registers when it fits
-// (L <= 1024 * JC) and streamed from global memory once per pass otherwise.
-//   pass 0  min / max of the row
-//   pass 1  histogram of 2048 equal-width value bins over [min, max] in LDS.  The
-//           bin map is monotone in the score, so every bin above the one holding the
-//           n-th largest score is selected outright.  Equal-width bins spread real
-//           score rows evenly, which keeps LDS atomic collisions rare.
-//   pass 2  exact 32-bit threshold T inside that bin: four 8-bit radix rounds over
-//           the order-preserving keys of its members.
-//   pass 3  ordered compaction: ballots and a block scan give every selected
-//           position its rank; positions with key > T are taken, and of those with
-//           key == T the lowest (n - #{key > T}) positions.
+// One 1024-thread block per row, reading four consecutive scores per thread and
+// step.  Rows of up to 32768 positions are staged once in LDS (128 KB) and every
+// pass reads them there; longer rows (up to 131072) are streamed from global memory
+// once per pass.
+//   1. min / max of the row (while staging it).
+//   2. histogram of 2048 equal-width value bins over [min, max] in LDS.  The bin
+//      map is monotone in the score, so every bin above the one holding the n-th
+//      largest score (found by a block-wide scan) is selected outright.  Equal-width
+//      bins spread real score rows evenly, which keeps LDS atomic collisions rare.
+//   3. positions in higher bins are marked in an LDS position bitmap; the members
+//      of the threshold bin (typically a few dozen) are ranked exactly by (score
+//      descending, position ascending) and the winners marked too.  Bins with more
+//      than 256 members (mass ties) fall back to four 8-bit radix rounds over
+//      order-preserving keys, which yield the exact threshold key T; positions with
+//      key > T are marked selected and those with key == T as ties, of which the
+//      lowest positions are taken.
+//   4. output: one block scan over the bitmap words' popcounts gives every thread
+//      the output slot of its first marked position; marked positions are written
+//      in ascending order.
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
@@ -27,14 +34,17 @@ namespace {
 constexpr int TK_T = 1024;
 constexpr int TK_W = TK_T / 64;
 constexpr int NBIN = 2048;
-constexpr int JC_MAX = 32;
+constexpr int CMAX = 256;              // threshold-bin members ranked directly
+constexpr int BITMAP_POS = 131072;     // positions covered by the streaming bitmap
 
 struct TopkShared {
   uint32_t hist[NBIN];
-  uint32_t cg[JC_MAX * TK_W];
-  uint32_t ce[JC_MAX * TK_W];
+  uint32_t cg[TK_T];
+  uint32_t ce[TK_T];
   uint32_t wtot[2][TK_W];
   float fred[2][TK_W];
+  uint32_t ckey[CMAX];
+  int cpos[CMAX];
   int misc[8];
 };
 
@@ -66,6 +76,24 @@ __device__ __forceinline__ void find_bin_desc(const uint32_t* hist, uint32_t nee
       acc += c;
     }
   }
+}
+
+// Inclusive block-wide scan of one value per thread; returns the inclusive prefix.
+__device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* wtot) {
+  const int l = lane_id(), wv = threadIdx.x >> 6;
+  uint32_t inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t u = __shfl_up(inc, o);
+    if (l >= o) inc += u;
+  }
+  if (l == 63) wtot[wv] = inc;
+  __syncthreads();
+  uint32_t base = 0;
+#pragma unroll
+  for (int i = 0; i < TK_W; ++i)
+    if (i < wv) base += wtot[i];
+  return base + inc;
 }
 
 // Exclusive scan, in place, of a[0..M) and b[0..M) (M <= TK_T); returns totals.
@@ -106,16 +134,29 @@ __device__ __forceinline__ uint2 block_scan2(uint32_t* a, uint32_t* b, int M,
   return make_uint2(ta, tb);
 }
 
-template <int JC, bool CACHED>
+// Positions are visited in chunks of CH = 4 * 1024 * JV: within a chunk, thread tid
+// owns the float4 groups j * 1024 + tid (j < JV), i.e. positions
+// c * CH + 4 (j * 1024 + tid) + e, e < 4.  Selected positions are marked in LDS
+// bitmaps and the ordered output is produced from the bitmaps, so no pass depends
+// on which thread owns a position.
+constexpr int kResidentMax = 32768;  // longest row staged in LDS (128 KB)
+
+template <bool RESIDENT, int JV>
 __global__ __launch_bounds__(TK_T) void topk_kernel(const float* __restrict__ scores, int64_t ld,
                                                     const int32_t* __restrict__ row_pos,
-                                                    int max_pos, int topk,
+                                                    int max_pos, int topk, int vec_ok,
                                                     int32_t* __restrict__ out) {
+  constexpr int CH = 4 * TK_T * JV;
+  constexpr int CAP = RESIDENT ? CH : BITMAP_POS;  // positions the bitmaps cover
+  constexpr int BM_WORDS = CAP / 32;
   __shared__ TopkShared sh;
+  __shared__ uint32_t sel[BM_WORDS];   // positions selected outright
+  __shared__ uint32_t tie[BM_WORDS];   // fallback: positions whose key equals T
+  __shared__ f32x4 srow[RESIDENT ? TK_T * JV : 1];  // the row (RESIDENT)
   const int r = blockIdx.x, tid = threadIdx.x, l = lane_id(), wv = tid >> 6;
   const int t = row_pos[r];
   int32_t* orow = out + (size_t)r * topk;
-  if (t < 0 || t > max_pos || (int64_t)t >= ld) {
+  if (t < 0 || t > max_pos || (int64_t)t >= ld || t >= CAP) {
     for (int i = tid; i < topk; i += TK_T) orow[i] = -1;
     return;
   }
@@ -127,36 +168,69 @@ __global__ __launch_bounds__(TK_T) void topk_kernel(const float* __restrict__ sc
   }
   const float* row = scores + (size_t)r * ld;
   if (tid < 8) sh.misc[tid] = 0;
-  constexpr int CH = JC * TK_T;
-  const int nchunks = CACHED ? 1 : (L + CH - 1) / CH;
+  const int nchunks = (L + CH - 1) / CH;
+  const int words = (L + 31) >> 5;
 
-  float x[JC];
-  auto load = [&](int c0) {
+  // four consecutive scores starting at position s (s % 4 == 0); lanes past the
+  // row end read as -inf and are masked by position everywhere
+  auto fetch = [&](int s) -> f32x4 {
+    f32x4 v;
+    if (RESIDENT) return srow[s >> 2];
+    if (vec_ok && s + 3 < L) {
+      v = *reinterpret_cast<const f32x4*>(row + s);
+    } else {
 #pragma unroll
-    for (int j = 0; j < JC; ++j) {
-      const int s = c0 + j * TK_T + tid;
-      const float v = s < L ? row[s] : 0.f;
-      x[j] = (v != v) ? -INFINITY : v;
+      for (int e = 0; e < 4; ++e) v[e] = s + e < L ? row[s + e] : -INFINITY;
     }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (v[e] != v[e]) ? -INFINITY : v[e];
+    return v;
   };
-  if (CACHED) load(0);
 
-  // ---- pass 0: min / max
+  // ---- 1. (stage the row and) min / max
   float mn = INFINITY, mx = -INFINITY;
   for (int c = 0; c < nchunks; ++c) {
-    if (!CACHED) load(c * CH);
+    f32x4 v[JV];
 #pragma unroll
-    for (int j = 0; j < JC; ++j)
-      if (c * CH + j * TK_T + tid < L) {
-        mn = fminf(mn, x[j]);
-        mx = fmaxf(mx, x[j]);
+    for (int j = 0; j < JV; ++j) {
+      const int s = c * CH + 4 * (j * TK_T + tid);
+      if (s < L) {
+        if (vec_ok && s + 3 < L) {
+          v[j] = *reinterpret_cast<const f32x4*>(row + s);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[j][e] = s + e < L ? row[s + e] : -INFINITY;
+        }
       }
+    }
+#pragma unroll
+    for (int j = 0; j < JV; ++j) {
+      const int s = c * CH + 4 * (j * TK_T + tid);
+      if (s < L) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float x = v[j][e];
+          x = (x != x) ? -INFINITY : x;
+          v[j][e] = x;
+          if (s + e < L) {
+            mn = fminf(mn, x);
+            mx = fmaxf(mx, x);
+          }
+        }
+        if (RESIDENT) srow[j * TK_T + tid] = v[j];
+      }
+    }
   }
   mn = wave_min(mn);
   mx = wave_max(mx);
   if (l == 0) {
     sh.fred[0][wv] = mn;
     sh.fred[1][wv] = mx;
+  }
+  for (int i = tid; i < NBIN; i += TK_T) sh.hist[i] = 0u;
+  for (int i = tid; i < words; i += TK_T) {
+    sel[i] = 0u;
+    tie[i] = 0u;
   }
   __syncthreads();
   mn = sh.fred[0][0];
@@ -166,107 +240,148 @@ __global__ __launch_bounds__(TK_T) void topk_kernel(const float* __restrict__ sc
     mn = fminf(mn, sh.fred[0][i]);
     mx = fmaxf(mx, sh.fred[1][i]);
   }
-
-  uint32_t T, cnt_gt;
   if (!(mx > mn)) {  // all candidates equal: the n lowest positions
-    T = float_key(mx);
-    cnt_gt = 0;
-  } else {
-    float inv = (float)NBIN / (mx - mn);
-    if (!(inv < INFINITY)) inv = 0.f;
-    auto bin_of = [&](float v) -> int {
-      const float f = (v - mn) * inv;
-      if (f < (float)(NBIN - 1)) return (int)f;
-      return (f != f) ? 0 : NBIN - 1;
-    };
-    // ---- pass 1: equal-width value histogram
-    for (int i = tid; i < NBIN; i += TK_T) sh.hist[i] = 0u;
-    __syncthreads();
-    for (int c = 0; c < nchunks; ++c) {
-      if (!CACHED) load(c * CH);
-#pragma unroll
-      for (int j = 0; j < JC; ++j)
-        if (c * CH + j * TK_T + tid < L) atomicAdd(&sh.hist[bin_of(x[j])], 1u);
-    }
-    __syncthreads();
-    if (wv == 0) find_bin_desc<NBIN>(sh.hist, (uint32_t)n, sh.misc);
-    __syncthreads();
-    const int bstar = sh.misc[0];
-    cnt_gt = (uint32_t)sh.misc[1];
-    uint32_t need = (uint32_t)n - cnt_gt;
+    for (int i = tid; i < topk; i += TK_T) orow[i] = i < n ? i : -1;
+    return;
+  }
 
-    uint32_t cand = 0u;  // bit j: element j of the cached row lies in bin bstar
-    if (CACHED) {
+  float inv = (float)NBIN / (mx - mn);
+  if (!(inv < INFINITY)) inv = 0.f;
+  auto bin_of = [&](float v) -> int {
+    const float f = (v - mn) * inv;
+    if (f < (float)(NBIN - 1)) return (int)f;
+    return (f != f) ? 0 : NBIN - 1;
+  };
+  // visit every valid position: fn(s, value)
+  auto for_each = [&](auto&& fn) {
+    for (int c = 0; c < nchunks; ++c) {
+#pragma unroll 4
+      for (int j = 0; j < JV; ++j) {
+        const int s = c * CH + 4 * (j * TK_T + tid);
+        if (s < L) {
+          const f32x4 v = fetch(s);
 #pragma unroll
-      for (int j = 0; j < JC; ++j)
-        if (j * TK_T + tid < L && bin_of(x[j]) == bstar) cand |= 1u << j;
+          for (int e = 0; e < 4; ++e)
+            if (s + e < L) fn(s + e, v[e]);
+        }
+      }
     }
-    // ---- pass 2: exact threshold key inside bin bstar
-    uint32_t prefix = 0u, pmask = 0u;
+  };
+
+  // ---- 2. equal-width value histogram and the bin of the n-th largest score
+  for_each([&](int, float v) { atomicAdd(&sh.hist[bin_of(v)], 1u); });
+  __syncthreads();
+  {
+    const int hi = NBIN - 1 - 2 * tid;  // this thread's bins, from the top down
+    const uint32_t c1 = sh.hist[hi], c0 = sh.hist[hi - 1];
+    const uint32_t incl = block_incl_scan(c0 + c1, sh.wtot[0]);
+    const uint32_t excl = incl - c0 - c1;
+    if (excl < (uint32_t)n && (uint32_t)n <= incl) {
+      const bool upper = excl + c1 >= (uint32_t)n;
+      sh.misc[0] = upper ? hi : hi - 1;
+      sh.misc[1] = (int)(upper ? excl : excl + c1);
+    }
+  }
+  __syncthreads();
+  const int bstar = sh.misc[0];
+  const uint32_t above = (uint32_t)sh.misc[1];
+  const uint32_t need = (uint32_t)n - above;  // members of bin bstar to take
+  const uint32_t cnt_b = sh.hist[bstar];
+  const bool fast = cnt_b <= (uint32_t)CMAX;
+
+  uint32_t m_ties = 0u;
+  if (fast) {
+    // ---- 3a. mark the bins above bstar; rank bstar's members exactly
+    for_each([&](int s, float v) {
+      const int bn = bin_of(v);
+      if (bn > bstar) {
+        atomicOr(&sel[s >> 5], 1u << (s & 31));
+      } else if (bn == bstar) {
+        const int slot = atomicAdd(&sh.misc[4], 1);
+        sh.ckey[slot] = float_key(v);
+        sh.cpos[slot] = s;
+      }
+    });
+    __syncthreads();
+    for (int c = tid; c < (int)cnt_b; c += TK_T) {
+      const uint32_t k = sh.ckey[c];
+      const int p = sh.cpos[c];
+      uint32_t rank = 0;
+      for (int u = 0; u < (int)cnt_b; ++u) {
+        const uint32_t ku = sh.ckey[u];
+        rank += (ku > k) || (ku == k && sh.cpos[u] < p);
+      }
+      if (rank < need) atomicOr(&sel[p >> 5], 1u << (p & 31));
+    }
+  } else {
+    // ---- 3b. exact threshold key T inside bin bstar by 8-bit radix rounds, then
+    //          mark key > T as selected and key == T as ties
+    uint32_t prefix = 0u, pmask = 0u, rem = need, gt = above;
 #pragma unroll 1
     for (int shift = 24; shift >= 0; shift -= 8) {
       __syncthreads();
       if (tid < 256) sh.hist[tid] = 0u;
       __syncthreads();
-      for (int c = 0; c < nchunks; ++c) {
-        if (!CACHED) load(c * CH);
-#pragma unroll
-        for (int j = 0; j < JC; ++j) {
-          const bool in = CACHED ? ((cand >> j) & 1u)
-                                 : (c * CH + j * TK_T + tid < L && bin_of(x[j]) == bstar);
-          if (in) {
-            const uint32_t k = float_key(x[j]);
-            if ((k & pmask) == prefix) atomicAdd(&sh.hist[(k >> shift) & 255u], 1u);
-          }
+      for_each([&](int, float v) {
+        if (bin_of(v) == bstar) {
+          const uint32_t k = float_key(v);
+          if ((k & pmask) == prefix) atomicAdd(&sh.hist[(k >> shift) & 255u], 1u);
         }
-      }
+      });
       __syncthreads();
-      if (wv == 0) find_bin_desc<256>(sh.hist, need, sh.misc + 2);
+      if (wv == 0) find_bin_desc<256>(sh.hist, rem, sh.misc + 2);
       __syncthreads();
       const uint32_t d = (uint32_t)sh.misc[2], ab = (uint32_t)sh.misc[3];
       prefix |= d << shift;
       pmask |= 255u << shift;
-      need -= ab;
-      cnt_gt += ab;
+      rem -= ab;
+      gt += ab;
     }
-    T = prefix;
+    const uint32_t T = prefix;
+    m_ties = (uint32_t)n - gt;  // positions with key == T to take, lowest first
+    for_each([&](int s, float v) {
+      const uint32_t k = float_key(v);
+      if (k > T) atomicOr(&sel[s >> 5], 1u << (s & 31));
+      else if (k == T) atomicOr(&tie[s >> 5], 1u << (s & 31));
+    });
   }
-  const uint32_t m = (uint32_t)n - cnt_gt;  // positions with key == T to take
+  __syncthreads();
 
-  // ---- pass 3: ordered compaction (position order = chunk, slot j, wave, lane)
-  const uint64_t lt = lanemask_lt();
-  uint32_t carry_g = 0u, carry_e = 0u;
-  for (int c = 0; c < nchunks; ++c) {
-    if (!CACHED) load(c * CH);
+  // ---- 4. ordered output from the bitmaps: thread tid owns words [tid*WPT, +WPT).
+  // Output slot of a position = #selected before + min(#ties before, m_ties).
+  constexpr int WPT = BM_WORDS > TK_T ? BM_WORDS / TK_T : 1;  // words per thread
+  uint32_t sw[WPT], tw[WPT], ns = 0u, nt = 0u;
 #pragma unroll
-    for (int j = 0; j < JC; ++j) {
-      const bool valid = c * CH + j * TK_T + tid < L;
-      const uint32_t k = float_key(x[j]);
-      const uint64_t bg = __ballot(valid && k > T);
-      const uint64_t be = __ballot(valid && k == T);
-      if (l == 0) {
-        sh.cg[j * TK_W + wv] = (uint32_t)__popcll(bg);
-        sh.ce[j * TK_W + wv] = (uint32_t)__popcll(be);
+  for (int i = 0; i < WPT; ++i) {
+    const int w = tid * WPT + i;
+    sw[i] = w < words ? sel[w] : 0u;
+    tw[i] = w < words ? tie[w] : 0u;
+    ns += (uint32_t)__popc(sw[i]);
+    nt += (uint32_t)__popc(tw[i]);
+  }
+  sh.cg[tid] = ns;
+  sh.ce[tid] = nt;
+  __syncthreads();
+  block_scan2(sh.cg, sh.ce, TK_T, sh.wtot);
+  uint32_t S = sh.cg[tid], E = sh.ce[tid];
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    uint32_t a = sw[i], b = tw[i];
+    const int base = (tid * WPT + i) * 32;
+    while (a | b) {
+      const uint32_t la = a ? (uint32_t)__ffs(a) - 1u : 32u;
+      const uint32_t lb = b ? (uint32_t)__ffs(b) - 1u : 32u;
+      if (la < lb) {  // next set position is a selected one
+        const uint32_t at = S + min(E, m_ties);
+        if (at < (uint32_t)n) orow[at] = base + (int)la;
+        ++S;
+        a &= a - 1u;
+      } else {        // next set position is a tie
+        if (E < m_ties && S + E < (uint32_t)n) orow[S + E] = base + (int)lb;
+        ++E;
+        b &= b - 1u;
       }
     }
-    __syncthreads();
-    const uint2 tot = block_scan2(sh.cg, sh.ce, JC * TK_W, sh.wtot);
-#pragma unroll
-    for (int j = 0; j < JC; ++j) {
-      const int s = c * CH + j * TK_T + tid;
-      const bool valid = s < L;
-      const uint32_t k = float_key(x[j]);
-      const bool gt = valid && k > T, eq = valid && k == T;
-      const uint64_t bg = __ballot(gt);
-      const uint64_t be = __ballot(eq);
-      const uint32_t G = carry_g + sh.cg[j * TK_W + wv] + (uint32_t)__popcll(bg & lt);
-      const uint32_t E = carry_e + sh.ce[j * TK_W + wv] + (uint32_t)__popcll(be & lt);
-      const uint32_t at = G + min(E, m);
-      if ((gt || (eq && E < m)) && at < (uint32_t)n) orow[at] = s;
-    }
-    carry_g += tot.x;
-    carry_e += tot.y;
-    __syncthreads();
   }
   for (int i = n + tid; i < topk; i += TK_T) orow[i] = -1;
 }
@@ -277,15 +392,18 @@ hipError_t launch_topk(const dsa_rows& rows, int topk, const float* scores, int6
                        int32_t* indices, hipStream_t stream) {
   const int R = rows.num_rows;
   const int L = rows.max_pos + 1;
-  if (L <= 8 * TK_T) {
-    hipLaunchKernelGGL((topk_kernel<8, true>), dim3(R), dim3(TK_T), 0, stream, scores, ld,
-                       rows.row_pos, rows.max_pos, topk, indices);
-  } else if (L <= 32 * TK_T) {
-    hipLaunchKernelGGL((topk_kernel<32, true>), dim3(R), dim3(TK_T), 0, stream, scores, ld,
-                       rows.row_pos, rows.max_pos, topk, indices);
+  const int vec_ok = (ld % 4 == 0) && (reinterpret_cast<uintptr_t>(scores) % 16 == 0);
+  if (L <= 4 * TK_T * 2) {
+    hipLaunchKernelGGL((topk_kernel<true, 2>), dim3(R), dim3(TK_T), 0, stream, scores, ld,
+                       rows.row_pos, rows.max_pos, topk, vec_ok, indices);
+  } else if (L <= kResidentMax) {
+    hipLaunchKernelGGL((topk_kernel<true, 8>), dim3(R), dim3(TK_T), 0, stream, scores, ld,
+                       rows.row_pos, rows.max_pos, topk, vec_ok, indices);
+  } else if (L <= BITMAP_POS) {
+    hipLaunchKernelGGL((topk_kernel<false, 4>), dim3(R), dim3(TK_T), 0, stream, scores, ld,
+                       rows.row_pos, rows.max_pos, topk, vec_ok, indices);
   } else {
-    hipLaunchKernelGGL((topk_kernel<16, false>), dim3(R), dim3(TK_T), 0, stream, scores, ld,
-                       rows.row_pos, rows.max_pos, topk, indices);
+    return hipErrorInvalidValue;  // rows longer than the bitmap capacity
   }
   return hipGetLastError();
 }

@@ -180,7 +180,10 @@ def test_topk_single_regime_per_launch(dsa):
         for i in range(R):
             t = int(pos[i])
             n = min(2048, t + 1)
-            assert np.array_equal(idx[i, :n], oracle.select_topk(host[i, : t + 1].astype(np.float64), n))
+            want = oracle.select_topk(host[i, : t + 1].astype(np.float64), n)
+            assert np.array_equal(idx[i, :n], want), (
+                f"L={L} row {i} t={t}: {np.sum(idx[i, :n] != want)} slots differ; "
+                f"first gpu {idx[i, :6]} want {want[:6]}")
 
 
 # ---------------------------------------------------------------- step 3
