@@ -110,6 +110,46 @@ def time_steps(steps, K, W):
     return wall / K * 1e3, avg
 
 
+def time_workload(dsa, di, cfg, reps):
+    """Whole-path throughput of one more workload through dsa_forward (chunked like
+    the library's prefill loop), with MFMA/HBM fractions of its algorithmic work."""
+    import torch
+
+    print(f"[bench] extra workload {cfg.name}", file=sys.stderr, flush=True)
+    inp = di.make_inputs(cfg, 0, device="cuda")
+    R = cfg.num_rows
+    rows = dsa.rows_struct(inp.row_seq, inp.row_pos, cfg.num_seqs, cfg.max_ctx, cfg.kv_len - 1)
+    dims = dsa.Dims.from_config(cfg)
+    out = torch.empty(R, cfg.n_heads, cfg.v_dim, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(R, cfg.n_heads, dtype=torch.float32, device="cuda")
+    chunk = cfg.chunk_rows if 0 < cfg.chunk_rows < R else 0
+    ws = torch.empty(max(dsa.forward_workspace_size(rows, dims, chunk), 1), dtype=torch.uint8,
+                     device="cuda")
+    run = lambda: dsa.forward(rows, dims, inp.q_idx, inp.q_scale, inp.w, inp.k_idx, inp.k_scale,
+                              inp.q, inp.latent, cfg.scale, out=out, lse=lse, chunk_rows=chunk,
+                              workspace=ws)
+    run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        run()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / reps * 1e3
+    cand, sel = _pairs(cfg)
+    fp8_tf = cand * IDX_FLOP_PER_PAIR / 1e12
+    bf16_tf = sel * ATTN_FLOP_PER_ENTRY / 1e12
+    hbm = (cand * IDX_BYTES_PER_PAIR + sel * ATTN_BYTES_PER_ENTRY + R * ATTN_BYTES_PER_ROW) / 1e9
+    s = ms * 1e-3
+    res = {"tokens_per_s": R / s, "ms": ms, "rows": R, "reps": reps,
+           "fp8_tflop": fp8_tf, "bf16_tflop": bf16_tf,
+           # time-weighted MFMA fraction: ideal time at both peaks over measured time
+           "mfma_frac": (fp8_tf / FP8_PEAK_TFLOPS + bf16_tf / BF16_PEAK_TFLOPS) / s,
+           "hbm_frac": hbm / s / HBM_PEAK_GBS}
+    del inp, out, lse, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(di, cfg, budget_s=20.0):
     """The float64 oracle on a bounded sample of the workload's rows, host cores."""
     import numpy as np
@@ -198,6 +238,12 @@ def main():
         "step_hbm_frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "kernels": kernels,
     }
+    if args.extra:
+        del steps
+        torch.cuda.empty_cache()
+        line["extra"] = {name: time_workload(dsa, di, di.CONFIGS[name], reps)
+                         for name, reps in (("decode128k", 20), ("prefill8k", 5),
+                                            ("prefill128k", 2))}
     if not args.no_cpu:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(di, cfg)

@@ -175,7 +175,7 @@ class Config:
     max_ctx: int           # N: per-sequence cache capacity
     q_len: int             # query rows per sequence
     kv_len: int            # cache length per sequence; row i sits at kv_len - q_len + i
-    chunk_rows: int        # rows per dsa_forward call in the chunked prefill
+    chunk_rows: int        # rows per internal chunk of dsa_forward (0 = all rows at once)
     n_idx_heads: int       # H_I
     idx_dim: int           # d_I
     n_heads: int           # H
@@ -204,13 +204,13 @@ CONFIGS: Dict[str, Config] = {
         Config("tiny", 1, 1, 256, 256, 256, 256, 4, 32, 16, 80, 64, 64,
                1.0 / math.sqrt(80.0), True, True,
                "tiny causal prefill, fp32 throughout"),
-        Config("decode32k", 2, 32, 32768, 1, 32768, 1, 64, 128, 128, 576, 512, 2048,
+        Config("decode32k", 2, 32, 32768, 1, 32768, 0, 64, 128, 128, 576, 512, 2048,
                1.0 / math.sqrt(192.0), False, False,
                "decode, batch 32, one query each at context 32768"),
         Config("prefill8k", 3, 1, 8192, 8192, 8192, 8192, 64, 128, 128, 576, 512, 2048,
                1.0 / math.sqrt(192.0), False, False,
                "causal prefill of one 8192-token sequence"),
-        Config("decode128k", 4, 8, 131072, 1, 131072, 1, 64, 128, 128, 576, 512, 2048,
+        Config("decode128k", 4, 8, 131072, 1, 131072, 0, 64, 128, 128, 576, 512, 2048,
                1.0 / math.sqrt(192.0), False, False,
                "decode, batch 8, one query each at context 131072"),
         Config("prefill128k", 5, 1, 131072, 131072, 131072, 8192, 64, 128, 128, 576, 512,

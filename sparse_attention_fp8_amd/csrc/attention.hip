@@ -377,33 +377,43 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
   }
 }
 
-// LSE-weighted merge of the splits: out = sum_i e^{lse_i - LSE} o_i.
+// LSE-weighted merge of the splits: out = sum_i e^{lse_i - LSE} o_i.  One block of
+// 128 threads per (row, head); each thread merges 4 output columns.  The split
+// partials are loaded 8 at a time before any is used, so their latencies overlap.
 __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ o_part,
                                                            const float* __restrict__ lse_part,
                                                            int R, int splits,
                                                            uint16_t* __restrict__ out,
                                                            float* __restrict__ lse) {
+  constexpr int B8 = 8;
   const int rh = blockIdx.x;
   const int r = rh / H, h = rh - (rh / H) * H;
   if (r >= R) return;
   const float* lp = lse_part + (size_t)r * splits * H + h;
+  const float* op = o_part + ((size_t)r * splits * H + h) * DV + 4 * threadIdx.x;
+  const size_t ostride = (size_t)H * DV;
   float M = -INFINITY;
   for (int s = 0; s < splits; ++s) M = fmaxf(M, lp[(size_t)s * H]);
   float den = 0.f;
-  for (int s = 0; s < splits; ++s) {
-    const float x = lp[(size_t)s * H];
-    den += (x == -INFINITY) ? 0.f : __expf(x - M);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < splits; s0 += B8) {
+    f32x4 v[B8];
+    float x[B8];
+#pragma unroll
+    for (int i = 0; i < B8; ++i) {
+      const int s = min(s0 + i, splits - 1);
+      x[i] = s0 + i < splits ? lp[(size_t)s * H] : -INFINITY;
+      v[i] = *reinterpret_cast<const f32x4*>(op + (size_t)s * ostride);
+    }
+#pragma unroll
+    for (int i = 0; i < B8; ++i) {
+      const float wgt = (x[i] == -INFINITY) ? 0.f : __expf(x[i] - M);
+      den += wgt;
+      acc += wgt * v[i];
+    }
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < splits; ++s) {
-    const float x = lp[(size_t)s * H];
-    if (x == -INFINITY) continue;
-    const float wgt = __expf(x - M) * inv;
-    const f32x4 v = *reinterpret_cast<const f32x4*>(
-        o_part + (((size_t)r * splits + s) * H + h) * DV + 4 * threadIdx.x);
-    acc += wgt * v;
-  }
+  acc *= inv;
   uint2 pk;
   pk.x = pack_bf16x2(acc[0], acc[1]);
   pk.y = pack_bf16x2(acc[2], acc[3]);

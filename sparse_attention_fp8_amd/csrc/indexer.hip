@@ -292,7 +292,7 @@ hipError_t launch_indexer_fp8(const dsa_rows& rows, const uint8_t* q_idx, const 
                        stream, q_idx, q_scale, w, k_idx, k_scale, rows.row_seq, rows.row_pos, R,
                        rows.num_seqs, rows.max_ctx, nkb, scores, ld);
   } else {
-    constexpr int WAVES = 4, KPB = 1024;
+    constexpr int WAVES = 4, KPB = 2048;
     const int nkb = (L + KPB - 1) / KPB;
     hipLaunchKernelGGL((indexer_fp8_decode_kernel<WAVES, KPB>), dim3(R * nkb), dim3(WAVES * 64),
                        0, stream, q_idx, q_scale, w, k_idx, k_scale, rows.row_seq, rows.row_pos,
