@@ -55,6 +55,7 @@ constexpr int QR_STRIDE = RD * 2 + 16;  // bytes per head row of the rope querie
 constexpr int DT_HALF = DV / 16 / 2;  // 16 output column tiles per half
 constexpr float kStaleMax = 8.0f;   // log2 headroom of the stale running max
 constexpr float kLn2 = 0.69314718055994530942f;
+static_assert(((LOADS * 64 - 1) * 3641 >> 18) == (LOADS * 64 - 1) / KCH, "slot / 72 by multiply");
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -63,7 +64,37 @@ typedef __attribute__((address_space(3))) s16x4* lds_s16x4_t;
 // physical 16-byte slot of logical chunk c of entry e inside its 1152-byte row
 __device__ __forceinline__ int kswz(int e, int c) { return (c & ~7) | ((c ^ e) & 7); }
 
-__device__ __forceinline__ lds_ptr_t to_lds(void* p) { return (lds_ptr_t)(p); }
+// Direct 16-byte global -> LDS load: lane l's 16 bytes from base + off go to LDS
+// bytes [lds + 16 l, lds + 16 l + 16) (lds is wave-uniform, passed in M0).  It is
+// written as inline asm so that the compiler does not order later LDS reads (of
+// other stage buffers) behind it: the kernel orders the gathers itself, with
+// s_waitcnt vmcnt and barriers.  It writes no register; M0 is restored.
+__device__ __forceinline__ void gather16(const uint8_t* base, uint32_t off, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off), "s"(base), "s"(lds)
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)(p));
+}
+
+// max of v over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the same nn, every g):
+// v_permlane16_swap(x, x) leaves {x[l & ~16], x[l | 16]} and v_permlane32_swap
+// {x[l & ~32], x[l | 32]} in its two results, so each swap pairs l with its partner
+// without a trip through LDS.
+__device__ __forceinline__ float max_over_g(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 
 __device__ __forceinline__ i32x2 ds_read_tr16(const uint8_t* p) {
   const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)(p));
@@ -81,9 +112,6 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
   __shared__ int sidx[kTopk];
   // rope part of the 128 queries (q[r, h, 512:576]), rows padded to spread banks
   __shared__ __attribute__((aligned(16))) uint8_t qrope[H * QR_STRIDE];
-  // per-thread gather table: (entry << 16 | byte offset in row) of each direct load;
-  // kept in LDS so the loop does not hold it in registers
-  __shared__ uint32_t gtab[(STAGE / 1024 + NT / 64 - 1) / (NT / 64)][NT];
 
   const int tid = threadIdx.x, l = lane_id(), g = l >> 4, nn = l & 15;
   // wave-uniform indices live in scalar registers
@@ -129,33 +157,37 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
   }
   __syncthreads();  // sidx visible
 
-  // gather of block blk into stage st: direct load i fills LDS bytes
-  // [1024 i, 1024 i + 1024); each lane fetches the 16-byte chunk whose swizzled
-  // slot is its lane-linear destination.  The (entry, chunk) of each of the wave's
-  // loads is fixed, so it is computed once: packed as entry << 16 | chunk * 16.
+  // Gather of block blk into stage buffer kb: direct load i (wave wv issues
+  // i = wv + 8 j) fills LDS bytes [1024 i, 1024 i + 1024); lane l fetches the
+  // 16-byte chunk whose swizzled slot is its lane-linear destination P = 64 i + l:
+  // entry P / 72, slot P % 72 (kswz is an involution, so the slot's chunk is kswz
+  // of the slot).  The source offsets are computed before the barrier that frees
+  // the buffer, so the loads issue right after it.
   constexpr int MAXL = (LOADS + NWAVE - 1) / NWAVE;  // 5
-#pragma unroll
-  for (int j = 0; j < MAXL; ++j) {
-    const int i = wv + j * NWAVE;
-    const int P = (i < LOADS ? i : 0) * 64 + l;  // physical slot
-    const int e = P / KCH;
-    const int pc = P - e * KCH;
-    gtab[j][tid] = ((uint32_t)e << 16) | (uint32_t)(kswz(e, pc) * 16);  // kswz is an involution
-  }
-  auto issue_gather = [&](int blk, int st) {
-    uint8_t* kb = smem + st * STAGE;
+  auto gather_offsets = [&](int blk, uint32_t (&off)[MAXL]) {
     const int* bidx = sidx + blk * BE;
+    // The per-lane slot arithmetic below is cheap; recomputing it every block
+    // (the empty asm hides that the lane id is loop-invariant) keeps ten
+    // loop-invariant registers free for the rest of the loop.
+    int lane = l;
+    asm volatile("" : "+v"(lane));
 #pragma unroll
     for (int j = 0; j < MAXL; ++j) {
       const int i = wv + j * NWAVE;
-      if (i < LOADS) {
-        const uint32_t ent = gtab[j][tid];
-        const int pos = bidx[ent >> 16];
-        // 32-bit offset from the sequence base (a sequence's cache is < 4 GiB)
-        const uint32_t off = (uint32_t)(pos >= 0 ? pos : 0) * (uint32_t)KROW + (ent & 0xffffu);
-        const uint8_t* src = lat_bytes + off;
-        __builtin_amdgcn_global_load_lds(src, to_lds(kb + i * 1024), 16, 0, 0);
-      }
+      const int P = (i < LOADS ? i : 0) * 64 + lane;
+      const int e = (P * 3641) >> 18;  // P / 72 for P < 2304
+      const int c = kswz(e, P - e * KCH);
+      const int pos = bidx[e];
+      // 32-bit offset from the sequence base (a sequence's cache is < 4 GiB and
+      // positions are < 2^24)
+      off[j] = __umul24((uint32_t)(pos >= 0 ? pos : 0), (uint32_t)KROW) + (uint32_t)(16 * c);
+    }
+  };
+  auto issue_gather = [&](const uint32_t (&off)[MAXL], uint8_t* kb) {
+#pragma unroll
+    for (int j = 0; j < MAXL; ++j) {
+      const int i = wv + j * NWAVE;
+      if (i < LOADS) gather16(lat_bytes, off[j], lds_addr(kb + i * 1024));
     }
   };
 
@@ -188,14 +220,26 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
   float m_run[2] = {-INFINITY, -INFINITY};
   float l_part[2] = {0.f, 0.f};
 
-  if (nblk > 0) issue_gather(0, 0);
+  if (nblk > 0) {
+    uint32_t off0[MAXL];
+    gather_offsets(0, off0);
+    issue_gather(off0, smem);
+  }
 
   for (int blk = 0; blk < nblk; ++blk) {
     const int st = blk & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // block blk in LDS; everyone is done with block blk-1
-    if (blk + 1 < nblk) issue_gather(blk + 1, st ^ 1);
+    const bool more = blk + 1 < nblk;
+    uint32_t offn[MAXL];
+    if (more) gather_offsets(blk + 1, offn);
+    // Block blk is in LDS and every wave is done with block blk-1.  A plain
+    // s_barrier: __syncthreads() would also wait for the gather issued below in
+    // the previous iteration, since that is an outstanding LDS write.
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    if (more) issue_gather(offn, smem + (st ^ 1) * STAGE);
     const uint8_t* kb = smem + st * STAGE;
+    // bit 16 mt + v of vbits: position 16 mt + 4 g + v of the block is not padding
+    const uint32_t vbits = (uint32_t)__ballot(sidx[blk * BE + (l & (BE - 1))] >= 0) >> (4 * g);
 
     // ---- partial S^T over this wave's contraction half:
     //      acc[mt][nt] lane holds S^T[16mt + 4g + v][16nt + nn]
@@ -230,7 +274,8 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
         for (int v = 0; v < 4; ++v) xbuf[wv][(mt * 2 + nt) * 4 + v][l] = acc[mt][nt][v];
-    __syncthreads();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
     float sfull[2][2][4];  // [mt][nt][v]
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -244,13 +289,6 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
         }
 
     // ---- online softmax (exp2 domain) for the lane's heads 16nt + nn
-    uint32_t valid = 0;  // bit 4 mt + v: position 16 mt + 4 g + v is not padding
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        valid |= (sidx[blk * BE + 16 * mt + 4 * g + v] >= 0 ? 1u : 0u) << (4 * mt + v);
-
     float bm[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
@@ -259,13 +297,11 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float s = ((valid >> (4 * mt + v)) & 1u) ? sfull[mt][nt][v] * scale_log2 : -INFINITY;
+          const float s = ((vbits >> (16 * mt + v)) & 1u) ? sfull[mt][nt][v] * scale_log2 : -INFINITY;
           sfull[mt][nt][v] = s;
           mx = fmaxf(mx, s);
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      bm[nt] = mx;
+      bm[nt] = max_over_g(mx);
     }
     const bool raise = (bm[0] > m_run[0] + kStaleMax) || (bm[1] > m_run[1] + kStaleMax);
     if (__any(raise)) {
