@@ -164,31 +164,40 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
   // of the slot).  The source offsets are computed before the barrier that frees
   // the buffer, so the loads issue right after it.
   constexpr int MAXL = (LOADS + NWAVE - 1) / NWAVE;  // 5
-  auto gather_offsets = [&](int blk, uint32_t (&off)[MAXL]) {
-    const int* bidx = sidx + blk * BE;
-    // The per-lane slot arithmetic below is cheap; recomputing it every block
-    // (the empty asm hides that the lane id is loop-invariant) keeps ten
-    // loop-invariant registers free for the rest of the loop.
-    int lane = l;
-    asm volatile("" : "+v"(lane));
-#pragma unroll
-    for (int j = 0; j < MAXL; ++j) {
-      const int i = wv + j * NWAVE;
-      const int P = (i < LOADS ? i : 0) * 64 + lane;
-      const int e = (P * 3641) >> 18;  // P / 72 for P < 2304
-      const int c = kswz(e, P - e * KCH);
-      const int pos = bidx[e];
-      // 32-bit offset from the sequence base (a sequence's cache is < 4 GiB and
-      // positions are < 2^24)
-      off[j] = __umul24((uint32_t)(pos >= 0 ? pos : 0), (uint32_t)KROW) + (uint32_t)(16 * c);
-    }
+  // source offset of load j of this wave for block blk, from a lane id read afresh
+  // (volatile asm, so that the compiler does not keep the loop-invariant slot
+  // arithmetic in registers across the loop: it is cheap to redo)
+  auto fresh_lane = [&]() {
+    int lane;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+    return lane;
   };
-  auto issue_gather = [&](const uint32_t (&off)[MAXL], uint8_t* kb) {
+  auto gather_offset = [&](int blk, int j, int lane) -> uint32_t {
+    const int i = wv + j * NWAVE;
+    const int P = (i < LOADS ? i : 0) * 64 + lane;
+    const int e = (P * 3641) >> 18;  // P / 72 for P < 2304
+    const int c = kswz(e, P - e * KCH);
+    const int pos = sidx[blk * BE + e];
+    // 32-bit offset from the sequence base (a sequence's cache is < 4 GiB and
+    // positions are < 2^24)
+    return __umul24((uint32_t)(pos >= 0 ? pos : 0), (uint32_t)KROW) + (uint32_t)(16 * c);
+  };
+  // The first MAXL - 1 offsets are computed before the barrier that frees the
+  // buffer; the last load (waves 0..3 only) computes its own when it issues.
+  auto gather_offsets = [&](int blk, uint32_t (&off)[MAXL - 1]) {
+    const int lane = fresh_lane();
 #pragma unroll
-    for (int j = 0; j < MAXL; ++j) {
-      const int i = wv + j * NWAVE;
-      if (i < LOADS) gather16(lat_bytes, off[j], lds_addr(kb + i * 1024));
-    }
+    for (int j = 0; j < MAXL - 1; ++j) off[j] = gather_offset(blk, j, lane);
+  };
+  auto issue_gather_one = [&](int blk, int j, const uint32_t (&off)[MAXL - 1], uint8_t* kb) {
+    const int i = wv + j * NWAVE;
+    if (i < LOADS)
+      gather16(lat_bytes, j < MAXL - 1 ? off[j] : gather_offset(blk, j, fresh_lane()),
+               lds_addr(kb + i * 1024));
+  };
+  auto issue_gather = [&](int blk, const uint32_t (&off)[MAXL - 1], uint8_t* kb) {
+#pragma unroll
+    for (int j = 0; j < MAXL; ++j) issue_gather_one(blk, j, off, kb);
   };
 
   // Per-lane LDS base offsets.  With x = e & 7 the swizzled slot of chunk c = 4k + u
@@ -221,22 +230,22 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
   float l_part[2] = {0.f, 0.f};
 
   if (nblk > 0) {
-    uint32_t off0[MAXL];
+    uint32_t off0[MAXL - 1];
     gather_offsets(0, off0);
-    issue_gather(off0, smem);
+    issue_gather(0, off0, smem);
   }
 
   for (int blk = 0; blk < nblk; ++blk) {
     const int st = blk & 1;
     const bool more = blk + 1 < nblk;
-    uint32_t offn[MAXL];
+    uint32_t offn[MAXL - 1];
     if (more) gather_offsets(blk + 1, offn);
     // Block blk is in LDS and every wave is done with block blk-1.  A plain
-    // s_barrier: __syncthreads() would also wait for the gather issued below in
-    // the previous iteration, since that is an outstanding LDS write.
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    if (more) issue_gather(offn, smem + (st ^ 1) * STAGE);
+    // s_barrier (in the asm, so no memory access moves across it): a fenced one
+    // would also wait for the gather issued in the previous iteration, since
+    // that is an outstanding LDS write.
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    uint8_t* const nxt = smem + (st ^ 1) * STAGE;
     const uint8_t* kb = smem + st * STAGE;
     // bit 16 mt + v of vbits: position 16 mt + 4 g + v of the block is not padding
     const uint32_t vbits = (uint32_t)__ballot(sidx[blk * BE + (l & (BE - 1))] >= 0) >> (4 * g);
@@ -266,6 +275,9 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
           acc[mt][nt] = mfma_bf16_16x16x32(a[mt], bq[nt], acc[mt][nt]);
+      // the next block's direct loads go out one per contraction step, so the
+      // address unit works through them while the MFMAs run
+      if (more && ks < MAXL) issue_gather_one(blk + 1, ks, offn, nxt);
     }
     // ---- sum the two halves through LDS (same addition order in both waves)
 #pragma unroll
@@ -274,8 +286,7 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
         for (int v = 0; v < 4; ++v) xbuf[wv][(mt * 2 + nt) * 4 + v][l] = acc[mt][nt][v];
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     float sfull[2][2][4];  // [mt][nt][v]
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -287,6 +298,17 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
           const float mine = acc[mt][nt][v];
           sfull[mt][nt][v] = hf == 0 ? mine + other : other + mine;
         }
+
+    // V operand of output column tile dt (transposed reads of the stage rows)
+    auto read_v = [&](int dt) {
+      const uint8_t* vp = kb + tr_base + 32 * ((dt & 3) ^ tr_x) + 128 * (dt >> 2);
+      const i32x2 v0 = ds_read_tr16(vp);
+      const i32x2 v1 = ds_read_tr16(vp + 16 * KROW);
+      const i32x4 vv = {v0[0], v0[1], v1[0], v1[1]};
+      return as_bf16x8(vv);
+    };
+    // the first tile's operands do not depend on P: read them before the softmax
+    bf16x8 vnext = read_v(0);
 
     // ---- online softmax (exp2 domain) for the lane's heads 16nt + nn
     float bm[2];
@@ -346,15 +368,16 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
 
     // ---- O += P V for output columns 256hf + 16dt + nn.  B operand slots 0..3 are
     //      positions 4g..4g+3, slots 4..7 positions 16+4g..16+4g+3 (the P layout).
+    //      The operands of tile dt + 1 are read while the MFMAs of tile dt run.
+    bf16x8 bv = vnext;
 #pragma unroll
     for (int dt = 0; dt < DT_HALF; ++dt) {
-      const uint8_t* vp = kb + tr_base + 32 * ((dt & 3) ^ tr_x) + 128 * (dt >> 2);
-      const i32x2 v0 = ds_read_tr16(vp);
-      const i32x2 v1 = ds_read_tr16(vp + 16 * KROW);
-      const i32x4 vv = {v0[0], v0[1], v1[0], v1[1]};
-      const bf16x8 bv = as_bf16x8(vv);
+      if (dt + 1 < DT_HALF) vnext = read_v(dt + 1);
       O[0][dt] = mfma_bf16_16x16x32(pa[0], bv, O[0][dt]);
       O[1][dt] = mfma_bf16_16x16x32(pa[1], bv, O[1][dt]);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // then 2 MFMAs
+      bv = vnext;
     }
   }
 
