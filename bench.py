@@ -38,6 +38,43 @@ ATTN_BYTES_PER_ROW = 128 * 576 * 2 + 128 * 512 * 2  # q in + out
 ATTN_FLOP_PER_ENTRY = 2 * 128 * (576 + 512)
 
 
+# Kernel sources whose digest ties a committed HBM-traffic measurement to the code
+# that is built now (a stale measurement is reported as null).
+_CALL_SOURCES = {"indexer": ["sparse_attention_fp8_amd/csrc/indexer.hip"],
+                 "topk": ["sparse_attention_fp8_amd/csrc/topk.hip"],
+                 "attention": ["sparse_attention_fp8_amd/csrc/attention.hip"]}
+_COMMON_SOURCES = ["sparse_attention_fp8_amd/csrc/dsa_device.h",
+                   "sparse_attention_fp8_amd/csrc/dsa_internal.h", "sparse_attention_fp8_amd/build.py"]
+
+
+def _sources_digest(call):
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in _CALL_SOURCES[call] + _COMMON_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, call):
+    """HBM bytes per launch of one C-ABI call from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary (copy-kernel calibrated), or None when there is none for this
+    workload or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    a, b = text.find("```json"), text.rfind("```")
+    try:
+        entry = json.loads(text[a + 7:b])["calls"][call]
+    except (ValueError, KeyError):
+        return None
+    if entry.get("sources_sha256_16") != _sources_digest(call):
+        return None
+    return entry["traffic_bytes"], entry["kernels"]
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -48,6 +85,10 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--extra", action="store_true",
                    help="also time decode128k, prefill8k and prefill128k")
+    p.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
+                   help="only run an fp32 elementwise copy (x * 1) that reads and writes MIB MiB, "
+                        "five times: the reference kernel of known traffic that scales the "
+                        "FETCH_SIZE / WRITE_SIZE counters")
     return p.parse_args()
 
 
@@ -193,6 +234,17 @@ def main():
         sys.exit(2)
     import torch
 
+    if args.copy_calib:
+        n = args.copy_calib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            torch.mul(a, 1.0, out=b)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calib_bytes_read": 4 * n, "copy_calib_bytes_written": 4 * n,
+                          "launches": 5}), flush=True)
+        return
+
     import dsa_inputs as di
     import sparse_attention_fp8_amd as dsa
 
@@ -217,6 +269,7 @@ def main():
     }
     dom = max(kernels, key=lambda k: kernels[k]["ms"])
     kd = kernels[dom]
+    mt = measured_traffic(cfg.name, dom)
     step_bytes = idx_bytes + attn_bytes
     line = {
         "metric": METRIC,
@@ -234,7 +287,10 @@ def main():
         "config": {"workload": f"{cfg.name}: {cfg.description}", "batch": cfg.num_seqs,
                    "context": cfg.kv_len, "topk": cfg.topk, "input_sets": args.sets},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": kd["gbs"], "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": kd["gbs"] / HBM_PEAK_GBS, "traffic": None},
+                     "unit": "GB/s", "frac": kd["gbs"] / HBM_PEAK_GBS,
+                     "traffic": mt[0] if mt else None,
+                     "traffic_kernels": mt[1] if mt else None,
+                     "algorithmic_bytes": kd["bytes"], "launch_ms": kd["ms"]},
         "step_hbm_frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "kernels": kernels,
     }
