@@ -138,8 +138,10 @@ dsa_status dsa_topk(const dsa_rows* rows, int32_t topk, const float* scores,
  * A listed position counts once per occurrence.  A row with no valid position
  * gets out = 0 and lse = -inf.  bf16 path: bf16 products, fp32 accumulation and
  * softmax, softmax weights rounded to bf16 for the value product, out rounded to
- * nearest-even bf16.  The workspace holds split partial results
- * (see dsa_sparse_mla_attn_workspace_size).
+ * nearest-even bf16.  When few rows cannot fill the GPU, a row's positions are
+ * split into S slices; the workspace then holds each slice's normalised output
+ * (bf16) and its lse (fp32), merged as out = sum_i e^(lse_i - LSE) out_i in fp32
+ * (see dsa_sparse_mla_attn_workspace_size; 0 bytes when no row is split).
  * ------------------------------------------------------------------------- */
 size_t dsa_sparse_mla_attn_workspace_size(const dsa_rows* rows, const dsa_dims* dims);
 

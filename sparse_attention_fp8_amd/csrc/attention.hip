@@ -106,7 +106,7 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
     const int32_t* __restrict__ indices, const int32_t* __restrict__ row_seq,
     const int32_t* __restrict__ row_pos, int R, int B, int N, int topk, int splits,
     float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
-    float* __restrict__ o_part, float* __restrict__ lse_part) {
+    uint16_t* __restrict__ o_part, float* __restrict__ lse_part) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
   __shared__ __attribute__((aligned(16))) float xbuf[NWAVE][16][64];  // S partials
   __shared__ int sidx[kTopk];
@@ -418,14 +418,15 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
             l_tot[nt] > 0.f ? (m_run[nt] + __log2f(l_tot[nt])) * kLn2 : -INFINITY;
     }
   } else {
-    float* prow = o_part + ((size_t)r * splits + sp) * H * DV;
+    // the split's normalised output, rounded to bf16 (its lse stays fp32)
+    uint16_t* prow = o_part + ((size_t)r * splits + sp) * H * DV;
 #pragma unroll
     for (int hm = 0; hm < 2; ++hm)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        float* ph = prow + (size_t)(head0 + 16 * hm + 4 * g + v) * DV + col0;
+        uint16_t* ph = prow + (size_t)(head0 + 16 * hm + 4 * g + v) * DV + col0;
 #pragma unroll
-        for (int dt = 0; dt < DT_HALF; ++dt) ph[16 * dt] = O[hm][dt][v];
+        for (int dt = 0; dt < DT_HALF; ++dt) ph[16 * dt] = bf16_bits(O[hm][dt][v]);
       }
     if (g == 0 && hf == 0) {
 #pragma unroll
@@ -438,8 +439,10 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
 
 // LSE-weighted merge of the splits: out = sum_i e^{lse_i - LSE} o_i.  One block of
 // 128 threads per (row, head); each thread merges 4 output columns.  The split
-// partials are loaded 8 at a time before any is used, so their latencies overlap.
-__global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ o_part,
+// outputs o_i are bf16 (normalised, so |o_i| <= max |value|), their lse_i fp32; the
+// merge runs in fp32.  The partials are loaded 8 at a time before any is used, so
+// their latencies overlap.
+__global__ __launch_bounds__(128) void attn_combine_kernel(const uint16_t* __restrict__ o_part,
                                                            const float* __restrict__ lse_part,
                                                            int R, int splits,
                                                            uint16_t* __restrict__ out,
@@ -449,26 +452,29 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restri
   const int r = rh / H, h = rh - (rh / H) * H;
   if (r >= R) return;
   const float* lp = lse_part + (size_t)r * splits * H + h;
-  const float* op = o_part + ((size_t)r * splits * H + h) * DV + 4 * threadIdx.x;
+  const uint16_t* op = o_part + ((size_t)r * splits * H + h) * DV + 4 * threadIdx.x;
   const size_t ostride = (size_t)H * DV;
   float M = -INFINITY;
   for (int s = 0; s < splits; ++s) M = fmaxf(M, lp[(size_t)s * H]);
   float den = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < splits; s0 += B8) {
-    f32x4 v[B8];
+    uint2 v[B8];
     float x[B8];
 #pragma unroll
     for (int i = 0; i < B8; ++i) {
       const int s = min(s0 + i, splits - 1);
       x[i] = s0 + i < splits ? lp[(size_t)s * H] : -INFINITY;
-      v[i] = *reinterpret_cast<const f32x4*>(op + (size_t)s * ostride);
+      v[i] = *reinterpret_cast<const uint2*>(op + (size_t)s * ostride);
     }
 #pragma unroll
     for (int i = 0; i < B8; ++i) {
       const float wgt = (x[i] == -INFINITY) ? 0.f : __expf(x[i] - M);
       den += wgt;
-      acc += wgt * v[i];
+      acc[0] += wgt * __uint_as_float(v[i].x << 16);
+      acc[1] += wgt * __uint_as_float(v[i].x & 0xffff0000u);
+      acc[2] += wgt * __uint_as_float(v[i].y << 16);
+      acc[3] += wgt * __uint_as_float(v[i].y & 0xffff0000u);
     }
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
@@ -568,7 +574,8 @@ size_t attn_workspace_bytes(int num_rows, const dsa_dims& dims) {
   if (dims.attn_dtype != DSA_BF16) return 0;
   const int s = attn_num_splits(num_rows, dims.topk);
   if (s <= 1) return 0;
-  return (size_t)num_rows * s * H * (DV + 1) * sizeof(float);
+  // bf16 split outputs [R, S, H, D_v] followed by fp32 split lse [R, S, H]
+  return (size_t)num_rows * s * H * (DV * sizeof(uint16_t) + sizeof(float));
 }
 
 hipError_t launch_attn_bf16(const dsa_rows& rows, const void* q, const void* latent,
@@ -576,11 +583,11 @@ hipError_t launch_attn_bf16(const dsa_rows& rows, const void* q, const void* lat
                             void* workspace, hipStream_t stream) {
   const int R = rows.num_rows;
   const int S = attn_num_splits(R, kTopk);
-  float* o_part = nullptr;
+  uint16_t* o_part = nullptr;
   float* lse_part = nullptr;
   if (S > 1) {
-    o_part = static_cast<float*>(workspace);
-    lse_part = o_part + (size_t)R * S * H * DV;
+    o_part = static_cast<uint16_t*>(workspace);
+    lse_part = reinterpret_cast<float*>(o_part + (size_t)R * S * H * DV);
   }
   const int row_groups = (R + 7) / 8;
   const float scale_log2 = softmax_scale * 1.44269504088896340736f;

@@ -89,7 +89,7 @@ def test_workspace_sizes(m):
     d = m.dims_struct(m.PRODUCTION_DIMS)
     dec = _rows(m, R=32, B=32, N=32768, max_pos=32767)
     attn = L.dsa_sparse_mla_attn_workspace_size(ctypes.byref(dec), ctypes.byref(d))
-    assert attn == 32 * 8 * 128 * 513 * 4   # 8 splits of fp32 partial outputs + lse
+    assert attn == 32 * 8 * 128 * (512 * 2 + 4)   # 8 splits of bf16 partial outputs + fp32 lse
     fwd = L.dsa_forward_workspace_size(ctypes.byref(dec), ctypes.byref(d), 0)
     assert fwd >= attn + 32 * 32768 * 4 + 32 * 2048 * 4
     pre = _rows(m, R=131072, B=1, N=131072, max_pos=131071)
