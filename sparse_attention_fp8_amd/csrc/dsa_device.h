@@ -64,19 +64,72 @@ __device__ __forceinline__ uint32_t float_key(float x) {
 }
 
 // ---------------------------------------------------------------- wave helpers
+// Cross-lane moves without LDS: DPP (row = 16 lanes) and the gfx950 permlane swaps.
+// dpp<CTRL, ROWS>(x): lane i receives x from the lane CTRL names; lanes whose
+// source lies outside the row, or whose row is not in ROWS, receive 0.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ uint32_t dpp(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROWS, 0xf, true);
+}
+constexpr int kDppXor1 = 0xB1;          // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;          // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;   // lane i <- 7 - i within each 8 lanes
+constexpr int kDppMirror = 0x140;       // lane i <- 15 - i within each row
+constexpr int kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr4 = 0x114, kDppShr8 = 0x118;
+constexpr int kDppBcast15 = 0x142;      // row r <- lane 15 of row r - 1
+constexpr int kDppBcast31 = 0x143;      // rows 2, 3 <- lane 31
+
+// the two halves of {x[l & ~16], x[l | 16]} and {x[l & ~32], x[l | 32]}
+__device__ __forceinline__ uint2 swap16(uint32_t x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return make_uint2(r[0], r[1]);
+}
+__device__ __forceinline__ uint2 swap32(uint32_t x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return make_uint2(r[0], r[1]);
+}
+
+// Reduction over the whole wave with a commutative, associative op: every lane
+// gets the result.  Each step pairs lanes that already hold equal partials, so a
+// mirror permutation serves as well as an xor one.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce_bits(uint32_t v, Op op) {
+  v = op(v, dpp<kDppXor1>(v));
+  v = op(v, dpp<kDppXor2>(v));
+  v = op(v, dpp<kDppHalfMirror>(v));
+  v = op(v, dpp<kDppMirror>(v));
+  uint2 s = swap16(v);
+  v = op(s.x, s.y);
+  s = swap32(v);
+  return op(s.x, s.y);
+}
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  return __uint_as_float(wave_reduce_bits(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+  }));
 }
 __device__ __forceinline__ float wave_min(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o));
-  return v;
+  return __uint_as_float(wave_reduce_bits(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(fminf(__uint_as_float(a), __uint_as_float(b)));
+  }));
 }
 __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return wave_reduce_bits(v, [](uint32_t a, uint32_t b) { return a + b; });
+}
+// OR over each aligned group of 8 lanes (every lane of the group gets it)
+__device__ __forceinline__ uint32_t or8(uint32_t v) {
+  v |= dpp<kDppXor1>(v);
+  v |= dpp<kDppXor2>(v);
+  return v | dpp<kDppHalfMirror>(v);
+}
+// Inclusive prefix sum over the wave (lane l gets v[0] + ... + v[l]).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += dpp<kDppShr1>(v);
+  v += dpp<kDppShr2>(v);
+  v += dpp<kDppShr4>(v);
+  v += dpp<kDppShr8>(v);
+  v += dpp<kDppBcast15, 0xa>(v);
+  v += dpp<kDppBcast31, 0xc>(v);
   return v;
 }
 

@@ -57,12 +57,9 @@ __device__ __forceinline__ void find_bin_desc(const uint32_t* hist, uint32_t nee
   uint32_t local = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) local += hist[l * PER + i];
-  uint32_t suf = local;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t v = __shfl_down(suf, o);
-    if (l + o < 64) suf += v;
-  }
+  const uint32_t incl = wave_incl_scan(local);
+  const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+  const uint32_t suf = total - incl + local;  // sum over lanes >= l
   const uint32_t above = suf - local;
   if (above < need && need <= suf) {
     uint32_t acc = above;
@@ -81,12 +78,7 @@ __device__ __forceinline__ void find_bin_desc(const uint32_t* hist, uint32_t nee
 // Inclusive block-wide scan of one value per thread; returns the inclusive prefix.
 __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* wtot) {
   const int l = lane_id(), wv = threadIdx.x >> 6;
-  uint32_t inc = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t u = __shfl_up(inc, o);
-    if (l >= o) inc += u;
-  }
+  const uint32_t inc = wave_incl_scan(v);
   if (l == 63) wtot[wv] = inc;
   __syncthreads();
   uint32_t base = 0;
@@ -101,15 +93,7 @@ __device__ __forceinline__ uint2 block_scan2(uint32_t* a, uint32_t* b, int M,
                                              uint32_t (*wtot)[TK_W]) {
   const int tid = threadIdx.x, l = lane_id(), wv = tid >> 6;
   const uint32_t va = tid < M ? a[tid] : 0u, vb = tid < M ? b[tid] : 0u;
-  uint32_t ia = va, ib = vb;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t ua = __shfl_up(ia, o), ub = __shfl_up(ib, o);
-    if (l >= o) {
-      ia += ua;
-      ib += ub;
-    }
-  }
+  const uint32_t ia = wave_incl_scan(va), ib = wave_incl_scan(vb);
   if (l == 63) {
     wtot[0][wv] = ia;
     wtot[1][wv] = ib;
@@ -152,7 +136,6 @@ __global__ __launch_bounds__(TK_T) void topk_kernel(const float* __restrict__ sc
   __shared__ TopkShared sh;
   __shared__ uint32_t sel[BM_WORDS];   // positions selected outright
   __shared__ uint32_t tie[BM_WORDS];   // fallback: positions whose key equals T
-  __shared__ f32x4 srow[RESIDENT ? TK_T * JV : 1];  // the row (RESIDENT)
   const int r = blockIdx.x, tid = threadIdx.x, l = lane_id(), wv = tid >> 6;
   const int t = row_pos[r];
   int32_t* orow = out + (size_t)r * topk;
@@ -175,7 +158,6 @@ __global__ __launch_bounds__(TK_T) void topk_kernel(const float* __restrict__ sc
   // row end read as -inf and are masked by position everywhere
   auto fetch = [&](int s) -> f32x4 {
     f32x4 v;
-    if (RESIDENT) return srow[s >> 2];
     if (vec_ok && s + 3 < L) {
       v = *reinterpret_cast<const f32x4*>(row + s);
     } else {
@@ -187,7 +169,9 @@ __global__ __launch_bounds__(TK_T) void topk_kernel(const float* __restrict__ sc
     return v;
   };
 
-  // ---- 1. (stage the row and) min / max
+  // ---- 1. (keep the row in registers and) min / max.  A resident row (one chunk)
+  //      stays in rv for every later pass: thread tid holds groups j * 1024 + tid.
+  f32x4 rv[RESIDENT ? JV : 1];
   float mn = INFINITY, mx = -INFINITY;
   for (int c = 0; c < nchunks; ++c) {
     f32x4 v[JV];
@@ -217,8 +201,8 @@ __global__ __launch_bounds__(TK_T) void topk_kernel(const float* __restrict__ sc
             mx = fmaxf(mx, x);
           }
         }
-        if (RESIDENT) srow[j * TK_T + tid] = v[j];
       }
+      if (RESIDENT) rv[j] = s < L ? v[j] : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     }
   }
   mn = wave_min(mn);
@@ -228,10 +212,6 @@ __global__ __launch_bounds__(TK_T) void topk_kernel(const float* __restrict__ sc
     sh.fred[1][wv] = mx;
   }
   for (int i = tid; i < NBIN; i += TK_T) sh.hist[i] = 0u;
-  for (int i = tid; i < words; i += TK_T) {
-    sel[i] = 0u;
-    tie[i] = 0u;
-  }
   __syncthreads();
   mn = sh.fred[0][0];
   mx = sh.fred[1][0];
@@ -247,29 +227,50 @@ __global__ __launch_bounds__(TK_T) void topk_kernel(const float* __restrict__ sc
 
   float inv = (float)NBIN / (mx - mn);
   if (!(inv < INFINITY)) inv = 0.f;
-  auto bin_of = [&](float v) -> int {
-    const float f = (v - mn) * inv;
-    if (f < (float)(NBIN - 1)) return (int)f;
-    return (f != f) ? 0 : NBIN - 1;
+  // bin of v: floor((v - lo) * sc) clamped to [0, NBIN); NaN (from inv = 0) and -inf
+  // land in bin 0.  Min / max / convert only, so no compare masks are made.
+  auto bin_with = [&](float v, float lo, float sc) -> int {
+    return (int)fminf(fmaxf((v - lo) * sc, 0.f), (float)(NBIN - 1));
   };
-  // visit every valid position: fn(s, value)
-  auto for_each = [&](auto&& fn) {
-    for (int c = 0; c < nchunks; ++c) {
-#pragma unroll 4
-      for (int j = 0; j < JV; ++j) {
-        const int s = c * CH + 4 * (j * TK_T + tid);
-        if (s < L) {
-          const f32x4 v = fetch(s);
+  // 1 if a < b (ints of either sign whose difference fits), as plain arithmetic
+  auto lt1 = [](int a, int b) -> uint32_t { return (uint32_t)(a - b) >> 31; };
+  auto bin_of = [&](float v) -> int { return bin_with(v, mn, inv); };
+  // visit every float4 group with all lanes (uniform control flow, for shuffles):
+  // fn(s, v) with s the group's first position; lanes past the row end see -inf
+  auto for_each_group = [&](auto&& fn) {
+    if constexpr (RESIDENT) {
+      // a fresh (opaque) position base per pass: otherwise the compiler keeps every
+      // position and its validity from one pass to the next, past the register file
+      int p0 = 4 * tid;
+      asm volatile("" : "+v"(p0));
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (s + e < L) fn(s + e, v[e]);
+      for (int j = 0; j < JV; ++j) fn(p0 + 4 * j * TK_T, rv[j]);
+    } else {
+      for (int c = 0; c < nchunks; ++c) {
+#pragma unroll 2
+        for (int j = 0; j < JV; ++j) {
+          const int s = c * CH + 4 * (j * TK_T + tid);
+          const f32x4 v = s < L ? fetch(s) : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+          fn(s, v);
         }
       }
     }
   };
+  // visit every valid position: fn(s, value)
+  auto for_each = [&](auto&& fn) {
+    for_each_group([&](int s, const f32x4 v) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (s + e < L) fn(s + e, v[e]);
+    });
+  };
 
   // ---- 2. equal-width value histogram and the bin of the n-th largest score
-  for_each([&](int, float v) { atomicAdd(&sh.hist[bin_of(v)], 1u); });
+  // branch-free: a position past the row end (value -inf, bin 0) adds 0
+  for_each_group([&](int s, const f32x4 v) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) atomicAdd(&sh.hist[bin_of(v[e])], lt1(s + e, L));
+  });
   __syncthreads();
   {
     const int hi = NBIN - 1 - 2 * tid;  // this thread's bins, from the top down
@@ -291,29 +292,74 @@ __global__ __launch_bounds__(TK_T) void topk_kernel(const float* __restrict__ sc
 
   uint32_t m_ties = 0u;
   if (fast) {
-    // ---- 3a. mark the bins above bstar; rank bstar's members exactly
-    for_each([&](int s, float v) {
-      const int bn = bin_of(v);
-      if (bn > bstar) {
-        atomicOr(&sel[s >> 5], 1u << (s & 31));
-      } else if (bn == bstar) {
-        const int slot = atomicAdd(&sh.misc[4], 1);
-        sh.ckey[slot] = float_key(v);
-        sh.cpos[slot] = s;
+    // ---- 3a. mark the bins above bstar; collect bstar's members.  The 8 lanes
+    //      whose 4-position groups make up one 32-bit bitmap word OR their nibbles
+    //      together and one of them stores the word (every word below the row end
+    //      is written once, so the bitmap needs no clearing and no atomics).  Bin
+    //      members take wave-aggregated slots: one LDS atomic per wave and group.
+    const uint64_t lt = lanemask_lt();
+    // the same bin scale through an opaque copy: recomputing the bins is cheaper
+    // than keeping the histogram pass's 32 bin indices alive in registers
+    float inv_m = inv, mn_m = mn;
+    asm volatile("" : "+v"(inv_m), "+v"(mn_m));
+    for_each_group([&](int s, const f32x4 v) {
+      uint32_t m = 0u, mem = 0u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int bn = bin_with(v[e], mn_m, inv_m);
+        const uint32_t ok = lt1(s + e, L);
+        m |= (lt1(bstar, bn) & ok) << e;                          // bn > bstar
+        mem |= ((((uint32_t)(bn ^ bstar)) - 1u) >> 31 & ok) << e;  // bn == bstar
+      }
+      const uint32_t wd = or8(m << (4 * (l & 7)));
+      if ((l & 7) == 0 && s < L) sel[s >> 5] = wd;
+      if (__ballot(mem != 0u) != 0ull) {  // wave-uniform; rare
+        uint32_t below = 0u, tot = 0u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint64_t bal = __ballot((mem >> e) & 1u);
+          below += (uint32_t)__popcll(bal & lt);
+          tot += (uint32_t)__popcll(bal);
+        }
+        int base = 0;
+        if (l == 0) base = atomicAdd(&sh.misc[4], (int)tot);
+        base = __builtin_amdgcn_readfirstlane(base) + (int)below;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if ((mem >> e) & 1u) {
+            sh.ckey[base] = float_key(v[e]);
+            sh.cpos[base] = s + e;
+            ++base;
+          }
       }
     });
     __syncthreads();
-    for (int c = tid; c < (int)cnt_b; c += TK_T) {
-      const uint32_t k = sh.ckey[c];
-      const int p = sh.cpos[c];
+    // exact rank of each member by (key desc, position asc); four threads per
+    // member, each over a quarter of the others
+    for (int c0 = 0; c0 < (int)cnt_b; c0 += TK_T / 4) {
+      const int c = c0 + (tid >> 2), part = tid & 3;
       uint32_t rank = 0;
-      for (int u = 0; u < (int)cnt_b; ++u) {
-        const uint32_t ku = sh.ckey[u];
-        rank += (ku > k) || (ku == k && sh.cpos[u] < p);
+      uint32_t k = 0;
+      int p = 0;
+      if (c < (int)cnt_b) {
+        k = sh.ckey[c];
+        p = sh.cpos[c];
+        for (int u = part; u < (int)cnt_b; u += 4) {
+          const uint32_t ku = sh.ckey[u];
+          rank += (ku > k) || (ku == k && sh.cpos[u] < p);
+        }
       }
-      if (rank < need) atomicOr(&sel[p >> 5], 1u << (p & 31));
+      rank += dpp<kDppXor1>(rank);
+      rank += dpp<kDppXor2>(rank);
+      if (c < (int)cnt_b && part == 0 && rank < need) atomicOr(&sel[p >> 5], 1u << (p & 31));
     }
   } else {
+    // the fallback marks with atomics: clear both bitmaps first (the radix rounds
+    // below start with a barrier)
+    for (int i = tid; i < words; i += TK_T) {
+      sel[i] = 0u;
+      tie[i] = 0u;
+    }
     // ---- 3b. exact threshold key T inside bin bstar by 8-bit radix rounds, then
     //          mark key > T as selected and key == T as ties
     uint32_t prefix = 0u, pmask = 0u, rem = need, gt = above;
@@ -355,7 +401,7 @@ __global__ __launch_bounds__(TK_T) void topk_kernel(const float* __restrict__ sc
   for (int i = 0; i < WPT; ++i) {
     const int w = tid * WPT + i;
     sw[i] = w < words ? sel[w] : 0u;
-    tw[i] = w < words ? tie[w] : 0u;
+    tw[i] = (w < words && !fast) ? tie[w] : 0u;  // no ties on the fast path
     ns += (uint32_t)__popc(sw[i]);
     nt += (uint32_t)__popc(tw[i]);
   }
