@@ -89,6 +89,16 @@ __device__ __forceinline__ uint2 swap32(uint32_t x) {
   return make_uint2(r[0], r[1]);
 }
 
+// x of lane l ^ 16 and of lane l ^ 32, through the permlane swaps
+__device__ __forceinline__ float xor16(float x) {
+  const uint2 r = swap16(__float_as_uint(x));
+  return __uint_as_float((threadIdx.x & 16) ? r.x : r.y);
+}
+__device__ __forceinline__ float xor32(float x) {
+  const uint2 r = swap32(__float_as_uint(x));
+  return __uint_as_float((threadIdx.x & 32) ? r.x : r.y);
+}
+
 // Reduction over the whole wave with a commutative, associative op: every lane
 // gets the result.  Each step pairs lanes that already hold equal partials, so a
 // mirror permutation serves as well as an xor one.

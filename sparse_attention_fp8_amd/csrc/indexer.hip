@@ -52,12 +52,12 @@ __device__ __forceinline__ float reduce_groups(float p0, float p1, float p2, flo
   const bool hi = l >= 32;
   float keep0 = hi ? p2 : p0, keep1 = hi ? p3 : p1;
   const float send0 = hi ? p0 : p2, send1 = hi ? p1 : p3;
-  keep0 += __shfl_xor(send0, 32);
-  keep1 += __shfl_xor(send1, 32);
+  keep0 += xor32(send0);
+  keep1 += xor32(send1);
   const bool odd = (l >> 4) & 1;
   const float send = odd ? keep0 : keep1;
   const float keep = odd ? keep1 : keep0;
-  return keep + __shfl_xor(send, 16);
+  return keep + xor16(send);
 }
 
 __device__ __forceinline__ void load_query(const uint8_t* __restrict__ q_idx,
@@ -197,24 +197,69 @@ __device__ __forceinline__ void prefill_rows(const uint8_t* __restrict__ q_idx,
   }
 }
 
-template <int RW, int KPB>
-__global__ __launch_bounds__(256) void indexer_fp8_prefill_kernel(
+// Direct global -> LDS loads for the block's key groups (inline asm: the kernel
+// orders them itself with s_waitcnt vmcnt and barriers, so the compiler must not
+// make later LDS reads wait for them).  They write no register; M0 is restored.
+__device__ __forceinline__ void lds_dma16(const uint8_t* base, uint32_t off, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off), "s"(base), "s"(lds)
+      : "memory");
+}
+__device__ __forceinline__ void lds_dma4(const uint8_t* base, uint32_t off, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "global_load_lds_dword %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off), "s"(base), "s"(lds)
+      : "memory");
+}
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)(p));
+}
+
+// Prefill block: PW waves x PRW query rows (fp8 queries in registers) over PKPB keys.
+// The keys are staged once per block, 64 at a time, HBM -> LDS by direct loads
+// into PNBUF buffers three groups ahead; every wave reads its MFMA fragments from
+// LDS, so the block fetches each key once instead of once per wave.  Inside a
+// group, the 16-byte chunk c of key e sits in slot e * 8 + (c ^ (e & 7)), which
+// spreads the 16 rows of a fragment read over the LDS banks.
+constexpr int PW = 8, PRW = 2, PROWS = PW * PRW, PKPB = 1024, PG = 64, PNBUF = 4;
+constexpr int PGB = PG * ID;  // 8192 bytes per group
+static_assert(PGB == PW * 1024, "one 1 KB direct load per wave and group");
+
+__global__ __launch_bounds__(PW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void indexer_fp8_prefill_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale,
     const float* __restrict__ w, const uint8_t* __restrict__ k_idx,
     const float* __restrict__ k_scale, const int32_t* __restrict__ row_seq,
-    const int32_t* __restrict__ row_pos, int R, int B, int N, int nkb,
+    const int32_t* __restrict__ row_pos, int R, int B, int N, int ksplit,
     float* __restrict__ scores, int64_t ld) {
-  const int tile = blockIdx.x / nkb;
-  const int kb0 = (blockIdx.x - tile * nkb) * KPB;
-  const int wv = threadIdx.x >> 6;
-  const int rbase = (tile * 4 + wv) * RW;
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf[PNBUF][PGB];
+  __shared__ float ksbuf[PNBUF][PG];
+  __shared__ __attribute__((aligned(16))) float sbuf[PROWS][PKPB];  // one key block's scores
+  __shared__ int info[PW][3];
+  // block (tile, ks) walks key blocks ks, ks + ksplit, ... up to its rows' last
+  // position, so the grid does not depend on a bound of the positions
+  const int tile = blockIdx.x / ksplit;
+  const int ks = blockIdx.x - tile * ksplit;
+  const int l = lane_id(), g = l >> 4, n = l & 15;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  int rr[RW], tt[RW], bs[RW];
-  int nvalid = 0, tmax = -1, b0 = -1;
-  bool uniform = true;
+  int rr[PRW], tt[PRW], bs[PRW];
+  int bmin = 1 << 30, bmax = -1, tmax = -1;
 #pragma unroll
-  for (int i = 0; i < RW; ++i) {
-    const int r = rbase + i;
+  for (int i = 0; i < PRW; ++i) {
+    const int r = tile * PROWS + wv * PRW + i;
     int b = -1, t = -1;
     if (r < R) {
       b = row_seq[r];
@@ -225,25 +270,144 @@ __global__ __launch_bounds__(256) void indexer_fp8_prefill_kernel(
     tt[i] = t;
     bs[i] = b;
     if (t >= 0) {
-      if (b0 < 0) b0 = b;
-      uniform = uniform && (b == b0);
+      bmin = min(bmin, b);
+      bmax = max(bmax, b);
       tmax = max(tmax, t);
-      ++nvalid;
     }
   }
-  if (nvalid == 0 || kb0 > tmax) return;
-
-  if (uniform) {
-    const int kend = min(kb0 + KPB, tmax + 1);
-    prefill_rows<RW>(q_idx, q_scale, w, k_idx + (size_t)b0 * N * ID, k_scale + (size_t)b0 * N,
-                     rr, tt, kb0, kend, scores, ld);
-  } else {
+  if (l == 0) {
+    info[wv][0] = bmin;
+    info[wv][1] = bmax;
+    info[wv][2] = tmax;
+  }
+  __syncthreads();
+  int Bmin = 1 << 30, Bmax = -1, Tmax = -1;
 #pragma unroll
-    for (int i = 0; i < RW; ++i) {
-      if (tt[i] < kb0) continue;
-      const int kend = min(kb0 + KPB, tt[i] + 1);
-      prefill_rows<1>(q_idx, q_scale, w, k_idx + (size_t)bs[i] * N * ID,
-                      k_scale + (size_t)bs[i] * N, &rr[i], &tt[i], kb0, kend, scores, ld);
+  for (int i = 0; i < PW; ++i) {
+    Bmin = min(Bmin, info[i][0]);
+    Bmax = max(Bmax, info[i][1]);
+    Tmax = max(Tmax, info[i][2]);
+  }
+  if (Tmax < ks * PKPB) return;  // block-uniform
+
+  if (Bmin != Bmax) {
+    // rows of several sequences: each wave walks its own rows' keys from global memory
+    for (int kb0 = ks * PKPB; kb0 <= Tmax; kb0 += ksplit * PKPB) {
+#pragma unroll
+      for (int i = 0; i < PRW; ++i) {
+        if (tt[i] < kb0) continue;
+        const int kend = min(kb0 + PKPB, tt[i] + 1);
+        prefill_rows<1>(q_idx, q_scale, w, k_idx + (size_t)bs[i] * N * ID,
+                        k_scale + (size_t)bs[i] * N, &rr[i], &tt[i], kb0, kend, scores, ld);
+      }
+    }
+    return;
+  }
+
+  const uint8_t* kc = k_idx + (size_t)Bmin * N * ID;
+  const uint8_t* ksc = reinterpret_cast<const uint8_t*>(k_scale + (size_t)Bmin * N);
+
+  i32x8 qa[PRW][4];
+  float wq[PRW][16];
+#pragma unroll
+  for (int i = 0; i < PRW; ++i) load_query(q_idx, q_scale, w, rr[i], qa[i], wq[i]);
+
+  // B fragment of key tile kt: row e = 16 kt + n, bytes [32 g, 32 g + 32) = chunks
+  // 2 g and 2 g + 1, each at its swizzled slot
+  const int x = n & 7;  // e & 7 for every tile
+  const int c0 = (2 * g) ^ x, c1 = (2 * g + 1) ^ x;
+
+  for (int kb0 = ks * PKPB; kb0 <= Tmax; kb0 += ksplit * PKPB) {
+    const int kend = min(kb0 + PKPB, Tmax + 1);
+    const int ngroups = (kend - kb0 + PG - 1) / PG;
+    const int klast = kend - 1;
+    // group gi of this key block: wave wv fetches LDS slots [64 wv, 64 wv + 64) of
+    // the keys and the scales of keys [8 wv, 8 wv + 8)
+    auto issue_group = [&](int gi) {
+      const int k0 = kb0 + gi * PG;
+      const int P = 64 * wv + l;
+      const int e = P >> 3;
+      const int c = (P & 7) ^ (e & 7);
+      const uint32_t off = (uint32_t)min(k0 + e, klast) * (uint32_t)ID + (uint32_t)(16 * c);
+      lds_dma16(kc, off, lds_u32(&kbuf[gi % PNBUF][1024 * wv]));
+      if (l < 8)
+        lds_dma4(ksc, (uint32_t)min(k0 + 8 * wv + l, klast) * 4u,
+                 lds_u32(&ksbuf[gi % PNBUF][8 * wv]));
+    };
+    // every wave is past the previous key block's reads of kbuf and sbuf
+    __syncthreads();
+    for (int gi = 0; gi < 3 && gi < ngroups; ++gi) issue_group(gi);
+
+    for (int gi = 0; gi < ngroups; ++gi) {
+      // this wave's two loads of group gi are done once at most those of the (up
+      // to two) later groups in flight remain
+      const int later = min(ngroups - 1 - gi, 2);
+      if (later == 2)
+        asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      else if (later == 1)
+        asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (gi + 3 < ngroups) issue_group(gi + 3);
+      const uint8_t* kg = kbuf[gi % PNBUF];
+      const int k = kb0 + gi * PG;
+      i32x8 kf[4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const uint8_t* row = kg + (16 * kt + n) * ID;
+        const i32x4 a = *reinterpret_cast<const i32x4*>(row + 16 * c0);
+        const i32x4 b = *reinterpret_cast<const i32x4*>(row + 16 * c1);
+        kf[kt] = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+      const float ksv = ksbuf[gi % PNBUF][l];
+#pragma unroll
+      for (int i = 0; i < PRW; ++i) {
+        if (k > tt[i]) continue;  // wave-uniform
+        // all 16 MFMAs of the row first (distinct accumulators keep the matrix pipe
+        // busy), then the ReLU / weighted head-sum epilogue
+        f32x4 acc[4][4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+            acc[kt][mt] = mfma_fp8_16x16x128(qa[i][mt], kf[kt], f32x4{0.f, 0.f, 0.f, 0.f});
+        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  // the 16 MFMAs first
+        float p[4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          float a = 0.f;
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) a = fmaf(wq[i][mt * 4 + v], relu_bits(acc[kt][mt][v]), a);
+          p[kt] = a;
+        }
+        sbuf[wv * PRW + i][gi * PG + l] = reduce_groups(p[0], p[1], p[2], p[3]) * ksv;
+      }
+    }
+    // The key block's scores leave LDS after its loop, so that no vector-memory
+    // store sits between the direct loads whose completion the loop counts with
+    // vmcnt.  Each valid row writes keys [kb0, kend) (entries past its own
+    // position are left unspecified, as the interface allows).
+    __syncthreads();
+    constexpr int V4 = PKPB / 4;
+    const int nv4 = (kend - kb0 + 3) / 4;
+    for (int idx = threadIdx.x; idx < PROWS * V4; idx += PW * 64) {
+      const int row = idx / V4, c4 = idx - row * V4;
+      const int r = tile * PROWS + row;
+      if (c4 >= nv4 || r >= R) continue;
+      const int t = row_pos[r];
+      const int s0 = kb0 + 4 * c4;
+      if (t < s0) continue;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(&sbuf[row][4 * c4]);
+      float* dst = scores + (size_t)r * ld + s0;
+      if (s0 + 4 <= kend && ((reinterpret_cast<uintptr_t>(dst) & 15) == 0)) {
+        *reinterpret_cast<f32x4*>(dst) = v;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (s0 + e < kend) dst[e] = v[e];
+      }
     }
   }
 }
@@ -285,12 +449,15 @@ hipError_t launch_indexer_fp8(const dsa_rows& rows, const uint8_t* q_idx, const 
   const int R = rows.num_rows;
   const int L = rows.max_pos + 1;
   if (R >= 8 && R >= 4 * rows.num_seqs) {
-    constexpr int RW = 2, KPB = 512;
-    const int nkb = (L + KPB - 1) / KPB;
-    const int tiles = (R + 4 * RW - 1) / (4 * RW);
-    hipLaunchKernelGGL((indexer_fp8_prefill_kernel<RW, KPB>), dim3(tiles * nkb), dim3(256), 0,
+    // key blocks are split over ksplit blocks per row tile (enough blocks to fill
+    // the GPU several times over); each block loops over its share
+    const int nkb = (L + PKPB - 1) / PKPB;
+    const int tiles = (R + PROWS - 1) / PROWS;
+    int ksplit = 1;
+    while (ksplit < nkb && (int64_t)tiles * ksplit < 2048) ksplit <<= 1;
+    hipLaunchKernelGGL(indexer_fp8_prefill_kernel, dim3(tiles * ksplit), dim3(PW * 64), 0,
                        stream, q_idx, q_scale, w, k_idx, k_scale, rows.row_seq, rows.row_pos, R,
-                       rows.num_seqs, rows.max_ctx, nkb, scores, ld);
+                       rows.num_seqs, rows.max_ctx, ksplit, scores, ld);
   } else {
     constexpr int WAVES = 4, KPB = 2048;
     const int nkb = (L + KPB - 1) / KPB;
