@@ -129,13 +129,31 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
   const int ES = topk / splits;  // positions of this split
   const int nblk = ES / BE;
   const int32_t* irow = indices + (size_t)r * topk + (size_t)sp * ES;
-  for (int i = tid; i < ES; i += NT) {
-    const int p = irow[i];
-    sidx[i] = (p >= 0 && p < N) ? p : -1;
-  }
   const uint16_t* lat = latent + (size_t)b * N * DK;
   const uint8_t* lat_bytes = reinterpret_cast<const uint8_t*>(lat);
 
+  // Prologue, ordered so that three memory latencies do not add up: the first
+  // block's gather positions are read straight from the index row, the rest of the
+  // row and the queries are requested at the same time, and the first gather is
+  // issued as soon as its positions arrive, before the queries have.
+  constexpr int MAXL = (LOADS + NWAVE - 1) / NWAVE;  // 5 direct loads per wave and block
+  uint32_t off_first[MAXL];
+#pragma unroll
+  for (int j = 0; j < MAXL; ++j) {
+    const int i = wv + j * NWAVE;
+    const int P = (i < LOADS ? i : 0) * 64 + l;
+    const int e = (P * 3641) >> 18;  // P / 72 for P < 2304
+    const int c = kswz(e, P - e * KCH);
+    const int p = nblk > 0 ? irow[e] : 0;
+    off_first[j] = __umul24((uint32_t)((p >= 0 && p < N) ? p : 0), (uint32_t)KROW) + (uint32_t)(16 * c);
+  }
+  constexpr int IPT = kTopk / NT;  // selected positions per thread (at most)
+  int pv[IPT];
+#pragma unroll
+  for (int k = 0; k < IPT; ++k) {
+    const int i = tid + NT * k;
+    pv[k] = i < ES ? irow[i] : -1;
+  }
   // Contraction split: half hf owns latent dims [256 hf, 256 hf + 256) (k-steps
   // 8 hf .. 8 hf + 7, queries in registers) and rope dims [512 + 32 hf, +32)
   // (k-step 16 + hf, queries read from LDS).
@@ -149,13 +167,34 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
       for (int ks = 0; ks < KS_LAT; ++ks)
         qr[nt][ks] = *reinterpret_cast<const i32x4*>(qrow + (16 * nt + nn) * DK + 32 * ks + 8 * g);
   }
-  // LDS: rope queries of all 128 heads, 8 chunks of 16 bytes per head
-  for (int c = tid; c < H * (RD / 8); c += NT) {
-    const int h = c >> 3, j = c & 7;
-    *reinterpret_cast<i32x4*>(qrope + h * QR_STRIDE + 16 * j) =
-        *reinterpret_cast<const i32x4*>(q + ((size_t)r * H + h) * DK + DV + 8 * j);
+  // rope queries of all 128 heads (8 chunks of 16 bytes per head), bound for LDS
+  constexpr int QRC = H * (RD / 8) / NT;  // 2 chunks per thread
+  i32x4 qrv[QRC];
+#pragma unroll
+  for (int k = 0; k < QRC; ++k) {
+    const int c = tid + NT * k, h = c >> 3, j = c & 7;
+    qrv[k] = *reinterpret_cast<const i32x4*>(q + ((size_t)r * H + h) * DK + DV + 8 * j);
   }
-  __syncthreads();  // sidx visible
+  if (nblk > 0) {
+#pragma unroll
+    for (int j = 0; j < MAXL; ++j) {
+      const int i = wv + j * NWAVE;
+      if (i < LOADS) gather16(lat_bytes, off_first[j], lds_addr(smem + i * 1024));
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < IPT; ++k) {
+    const int i = tid + NT * k;
+    if (i < ES) sidx[i] = (pv[k] >= 0 && pv[k] < N) ? pv[k] : -1;
+  }
+#pragma unroll
+  for (int k = 0; k < QRC; ++k) {
+    const int c = tid + NT * k, h = c >> 3, j = c & 7;
+    *reinterpret_cast<i32x4*>(qrope + h * QR_STRIDE + 16 * j) = qrv[k];
+  }
+  // sidx and the rope queries visible; an unfenced barrier, so the gather and the
+  // query loads stay in flight
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
   // Gather of block blk into stage buffer kb: direct load i (wave wv issues
   // i = wv + 8 j) fills LDS bytes [1024 i, 1024 i + 1024); lane l fetches the
@@ -163,7 +202,6 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
   // entry P / 72, slot P % 72 (kswz is an involution, so the slot's chunk is kswz
   // of the slot).  The source offsets are computed before the barrier that frees
   // the buffer, so the loads issue right after it.
-  constexpr int MAXL = (LOADS + NWAVE - 1) / NWAVE;  // 5
   // source offset of load j of this wave for block blk, from a lane id read afresh
   // (volatile asm, so that the compiler does not keep the loop-invariant slot
   // arithmetic in registers across the loop: it is cheap to redo)
@@ -195,10 +233,6 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
       gather16(lat_bytes, j < MAXL - 1 ? off[j] : gather_offset(blk, j, fresh_lane()),
                lds_addr(kb + i * 1024));
   };
-  auto issue_gather = [&](int blk, const uint32_t (&off)[MAXL - 1], uint8_t* kb) {
-#pragma unroll
-    for (int j = 0; j < MAXL; ++j) issue_gather_one(blk, j, off, kb);
-  };
 
   // Per-lane LDS base offsets.  With x = e & 7 the swizzled slot of chunk c = 4k + u
   // (u < 4) is c ^ x = 4 (k ^ (x >> 2)) + (u ^ (x & 3)), and k ^ (x >> 2) is
@@ -228,12 +262,6 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
     for (int dt = 0; dt < DT_HALF; ++dt) O[hm][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run[2] = {-INFINITY, -INFINITY};
   float l_part[2] = {0.f, 0.f};
-
-  if (nblk > 0) {
-    uint32_t off0[MAXL - 1];
-    gather_offsets(0, off0);
-    issue_gather(0, off0, smem);
-  }
 
   for (int blk = 0; blk < nblk; ++blk) {
     const int st = blk & 1;
@@ -437,53 +465,58 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
   }
 }
 
-// LSE-weighted merge of the splits: out = sum_i e^{lse_i - LSE} o_i.  One block of
-// 128 threads per (row, head); each thread merges 4 output columns.  The split
-// outputs o_i are bf16 (normalised, so |o_i| <= max |value|), their lse_i fp32; the
-// merge runs in fp32.  The partials are loaded 8 at a time before any is used, so
-// their latencies overlap.
-__global__ __launch_bounds__(128) void attn_combine_kernel(const uint16_t* __restrict__ o_part,
-                                                           const float* __restrict__ lse_part,
-                                                           int R, int splits,
-                                                           uint16_t* __restrict__ out,
-                                                           float* __restrict__ lse) {
+// LSE-weighted merge of the splits: out = sum_i e^{lse_i - LSE} o_i.  64 threads per
+// (row, head), four (row, head) pairs per block; each thread merges 8 output
+// columns with 16-byte loads.  The split outputs o_i are bf16 (normalised, so
+// |o_i| <= max |value|), their lse_i fp32; the merge runs in fp32.  The partials
+// are loaded 8 at a time before any is used, so their latencies overlap.
+constexpr int CMB_T = 64;                 // threads per (row, head)
+constexpr int CMB_RH = 4;                 // (row, head) pairs per block
+static_assert(DV == CMB_T * 8, "8 columns per thread");
+__global__ __launch_bounds__(CMB_T * CMB_RH) void attn_combine_kernel(
+    const uint16_t* __restrict__ o_part, const float* __restrict__ lse_part, int R, int splits,
+    uint16_t* __restrict__ out, float* __restrict__ lse) {
   constexpr int B8 = 8;
-  const int rh = blockIdx.x;
+  const int rh = blockIdx.x * CMB_RH + (threadIdx.x / CMB_T);
+  const int c8 = threadIdx.x % CMB_T;
   const int r = rh / H, h = rh - (rh / H) * H;
   if (r >= R) return;
   const float* lp = lse_part + (size_t)r * splits * H + h;
-  const uint16_t* op = o_part + ((size_t)r * splits * H + h) * DV + 4 * threadIdx.x;
+  const uint16_t* op = o_part + ((size_t)r * splits * H + h) * DV + 8 * c8;
   const size_t ostride = (size_t)H * DV;
   float M = -INFINITY;
   for (int s = 0; s < splits; ++s) M = fmaxf(M, lp[(size_t)s * H]);
   float den = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < splits; s0 += B8) {
-    uint2 v[B8];
+    uint4 v[B8];
     float x[B8];
 #pragma unroll
     for (int i = 0; i < B8; ++i) {
       const int s = min(s0 + i, splits - 1);
       x[i] = s0 + i < splits ? lp[(size_t)s * H] : -INFINITY;
-      v[i] = *reinterpret_cast<const uint2*>(op + (size_t)s * ostride);
+      v[i] = *reinterpret_cast<const uint4*>(op + (size_t)s * ostride);
     }
 #pragma unroll
     for (int i = 0; i < B8; ++i) {
       const float wgt = (x[i] == -INFINITY) ? 0.f : __expf(x[i] - M);
       den += wgt;
-      acc[0] += wgt * __uint_as_float(v[i].x << 16);
-      acc[1] += wgt * __uint_as_float(v[i].x & 0xffff0000u);
-      acc[2] += wgt * __uint_as_float(v[i].y << 16);
-      acc[3] += wgt * __uint_as_float(v[i].y & 0xffff0000u);
+      const uint32_t u[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        acc[2 * k] += wgt * __uint_as_float(u[k] << 16);
+        acc[2 * k + 1] += wgt * __uint_as_float(u[k] & 0xffff0000u);
+      }
     }
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
-  acc *= inv;
-  uint2 pk;
-  pk.x = pack_bf16x2(acc[0], acc[1]);
-  pk.y = pack_bf16x2(acc[2], acc[3]);
-  *reinterpret_cast<uint2*>(out + ((size_t)r * H + h) * DV + 4 * threadIdx.x) = pk;
-  if (lse != nullptr && threadIdx.x == 0)
+  uint4 pk;
+  pk.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  pk.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  pk.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
+  pk.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
+  *reinterpret_cast<uint4*>(out + ((size_t)r * H + h) * DV + 8 * c8) = pk;
+  if (lse != nullptr && c8 == 0)
     lse[(size_t)r * H + h] = den > 0.f ? M + __logf(den) : -INFINITY;
 }
 
@@ -597,8 +630,8 @@ hipError_t launch_attn_bf16(const dsa_rows& rows, const void* q, const void* lat
                      scale_log2, static_cast<uint16_t*>(out), lse, o_part, lse_part);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || S == 1) return err;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(R * H), dim3(DV / 4), 0, stream, o_part, lse_part,
-                     R, S, static_cast<uint16_t*>(out), lse);
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((R * H + CMB_RH - 1) / CMB_RH), dim3(CMB_T * CMB_RH),
+                     0, stream, o_part, lse_part, R, S, static_cast<uint16_t*>(out), lse);
   return hipGetLastError();
 }
 

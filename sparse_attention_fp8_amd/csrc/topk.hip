@@ -125,31 +125,22 @@ __device__ __forceinline__ uint2 block_scan2(uint32_t* a, uint32_t* b, int M,
 // on which thread owns a position.
 constexpr int kResidentMax = 32768;  // longest row staged in LDS (128 KB)
 
+// One row at position t (0 <= t < CAP): row = its scores, orow = its k outputs.
+// sel / tie are LDS bitmaps covering CAP positions.
 template <bool RESIDENT, int JV>
-__global__ __launch_bounds__(TK_T) void topk_kernel(const float* __restrict__ scores, int64_t ld,
-                                                    const int32_t* __restrict__ row_pos,
-                                                    int max_pos, int topk, int vec_ok,
-                                                    int32_t* __restrict__ out) {
+__device__ __forceinline__ void topk_row(const float* __restrict__ row, int t, int topk,
+                                         int vec_ok, int32_t* __restrict__ orow,
+                                         TopkShared& sh, uint32_t* sel, uint32_t* tie) {
   constexpr int CH = 4 * TK_T * JV;
   constexpr int CAP = RESIDENT ? CH : BITMAP_POS;  // positions the bitmaps cover
   constexpr int BM_WORDS = CAP / 32;
-  __shared__ TopkShared sh;
-  __shared__ uint32_t sel[BM_WORDS];   // positions selected outright
-  __shared__ uint32_t tie[BM_WORDS];   // fallback: positions whose key equals T
-  const int r = blockIdx.x, tid = threadIdx.x, l = lane_id(), wv = tid >> 6;
-  const int t = row_pos[r];
-  int32_t* orow = out + (size_t)r * topk;
-  if (t < 0 || t > max_pos || (int64_t)t >= ld || t >= CAP) {
-    for (int i = tid; i < topk; i += TK_T) orow[i] = -1;
-    return;
-  }
+  const int tid = threadIdx.x, l = lane_id(), wv = tid >> 6;
   const int L = t + 1;
   const int n = min(topk, L);
   if (n == L) {  // every candidate is selected
     for (int i = tid; i < topk; i += TK_T) orow[i] = i < L ? i : -1;
     return;
   }
-  const float* row = scores + (size_t)r * ld;
   if (tid < 8) sh.misc[tid] = 0;
   const int nchunks = (L + CH - 1) / CH;
   const int words = (L + 31) >> 5;
@@ -432,6 +423,53 @@ __global__ __launch_bounds__(TK_T) void topk_kernel(const float* __restrict__ sc
   for (int i = n + tid; i < topk; i += TK_T) orow[i] = -1;
 }
 
+// One 1024-thread block per row, for rows shorter than 4 * 1024 * JV positions
+// (RESIDENT) or up to BITMAP_POS (streamed).
+template <bool RESIDENT, int JV>
+__global__ __launch_bounds__(TK_T) void topk_kernel(const float* __restrict__ scores, int64_t ld,
+                                                    const int32_t* __restrict__ row_pos,
+                                                    int max_pos, int topk, int vec_ok,
+                                                    int32_t* __restrict__ out) {
+  constexpr int CAP = RESIDENT ? 4 * TK_T * JV : BITMAP_POS;
+  __shared__ TopkShared sh;
+  __shared__ uint32_t sel[CAP / 32];   // positions selected outright
+  __shared__ uint32_t tie[CAP / 32];   // fallback: positions whose key equals T
+  const int r = blockIdx.x;
+  const int t = row_pos[r];
+  int32_t* orow = out + (size_t)r * topk;
+  if (t < 0 || t > max_pos || (int64_t)t >= ld || t >= CAP) {
+    for (int i = threadIdx.x; i < topk; i += TK_T) orow[i] = -1;
+    return;
+  }
+  topk_row<RESIDENT, JV>(scores + (size_t)r * ld, t, topk, vec_ok, orow, sh, sel, tie);
+}
+
+// Rows of any length up to BITMAP_POS, chosen per row: a row of at most
+// kResidentMax positions is held in registers, a longer one is streamed.  Used when
+// the host bound on the positions is above kResidentMax, since a looser bound (a
+// chunk of a long prefill, say) says nothing about each row's own length.
+__global__ __launch_bounds__(TK_T) void topk_kernel_any(const float* __restrict__ scores,
+                                                        int64_t ld,
+                                                        const int32_t* __restrict__ row_pos,
+                                                        int max_pos, int topk, int vec_ok,
+                                                        int32_t* __restrict__ out) {
+  __shared__ TopkShared sh;
+  __shared__ uint32_t sel[BITMAP_POS / 32];
+  __shared__ uint32_t tie[BITMAP_POS / 32];
+  const int r = blockIdx.x;
+  const int t = row_pos[r];
+  int32_t* orow = out + (size_t)r * topk;
+  if (t < 0 || t > max_pos || (int64_t)t >= ld || t >= BITMAP_POS) {
+    for (int i = threadIdx.x; i < topk; i += TK_T) orow[i] = -1;
+    return;
+  }
+  const float* row = scores + (size_t)r * ld;
+  if (t < kResidentMax)  // block-uniform
+    topk_row<true, kResidentMax / (4 * TK_T)>(row, t, topk, vec_ok, orow, sh, sel, tie);
+  else
+    topk_row<false, 4>(row, t, topk, vec_ok, orow, sh, sel, tie);
+}
+
 }  // namespace
 
 hipError_t launch_topk(const dsa_rows& rows, int topk, const float* scores, int64_t ld,
@@ -446,8 +484,8 @@ hipError_t launch_topk(const dsa_rows& rows, int topk, const float* scores, int6
     hipLaunchKernelGGL((topk_kernel<true, 8>), dim3(R), dim3(TK_T), 0, stream, scores, ld,
                        rows.row_pos, rows.max_pos, topk, vec_ok, indices);
   } else if (L <= BITMAP_POS) {
-    hipLaunchKernelGGL((topk_kernel<false, 4>), dim3(R), dim3(TK_T), 0, stream, scores, ld,
-                       rows.row_pos, rows.max_pos, topk, vec_ok, indices);
+    hipLaunchKernelGGL(topk_kernel_any, dim3(R), dim3(TK_T), 0, stream, scores, ld, rows.row_pos,
+                       rows.max_pos, topk, vec_ok, indices);
   } else {
     return hipErrorInvalidValue;  // rows longer than the bitmap capacity
   }
