@@ -34,14 +34,16 @@ __device__ __forceinline__ i32x8 load_frag32(const uint8_t* p) {
 // 16-key tile `kb` (key = lane & 15).
 __device__ __forceinline__ float head_partial(const i32x8 (&qa)[4], const float (&wq)[16],
                                               i32x8 kb) {
-  float p = 0.f;
+  // one accumulation chain per head tile, summed at the end (independent FMAs)
+  float p[4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
-    f32x4 acc = mfma_fp8_16x16x128(qa[mt], kb, f32x4{0.f, 0.f, 0.f, 0.f});
+    const f32x4 acc = mfma_fp8_16x16x128(qa[mt], kb, f32x4{0.f, 0.f, 0.f, 0.f});
+    p[mt] = wq[mt * 4] * relu_bits(acc[0]);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) p = fmaf(wq[mt * 4 + v], relu_bits(acc[v]), p);
+    for (int v = 1; v < 4; ++v) p[mt] = fmaf(wq[mt * 4 + v], relu_bits(acc[v]), p[mt]);
   }
-  return p;
+  return (p[0] + p[1]) + (p[2] + p[3]);
 }
 
 // p_i is the lane's partial for key tile i (keys 16i..16i+15 of a 64-key group,
@@ -233,9 +235,10 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p) {
 // LDS, so the block fetches each key once instead of once per wave.  Inside a
 // group, the 16-byte chunk c of key e sits in slot e * 8 + (c ^ (e & 7)), which
 // spreads the 16 rows of a fragment read over the LDS banks.
-constexpr int PW = 8, PRW = 2, PROWS = PW * PRW, PKPB = 1024, PG = 64, PNBUF = 4;
-constexpr int PGB = PG * ID;  // 8192 bytes per group
-static_assert(PGB == PW * 1024, "one 1 KB direct load per wave and group");
+constexpr int PW = 8, PRW = 2, PROWS = PW * PRW, PKPB = 1024, PG = 128, PNBUF = 4;
+constexpr int PGB = PG * ID;  // 16 KB per group
+static_assert(PGB == PW * 2048, "two 1 KB direct loads per wave and group");
+static_assert(PG == PW * 16, "16 key scales per wave and group");
 
 __global__ __launch_bounds__(PW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void indexer_fp8_prefill_kernel(
@@ -321,69 +324,105 @@ void indexer_fp8_prefill_kernel(
     const int kend = min(kb0 + PKPB, Tmax + 1);
     const int ngroups = (kend - kb0 + PG - 1) / PG;
     const int klast = kend - 1;
-    // group gi of this key block: wave wv fetches LDS slots [64 wv, 64 wv + 64) of
-    // the keys and the scales of keys [8 wv, 8 wv + 8)
+    // group gi of this key block (128 keys): wave wv fetches LDS slots
+    // [128 wv, 128 wv + 128) of the keys and the scales of keys [16 wv, 16 wv + 16)
     auto issue_group = [&](int gi) {
       const int k0 = kb0 + gi * PG;
-      const int P = 64 * wv + l;
-      const int e = P >> 3;
-      const int c = (P & 7) ^ (e & 7);
-      const uint32_t off = (uint32_t)min(k0 + e, klast) * (uint32_t)ID + (uint32_t)(16 * c);
-      lds_dma16(kc, off, lds_u32(&kbuf[gi % PNBUF][1024 * wv]));
-      if (l < 8)
-        lds_dma4(ksc, (uint32_t)min(k0 + 8 * wv + l, klast) * 4u,
-                 lds_u32(&ksbuf[gi % PNBUF][8 * wv]));
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int P = 64 * (2 * wv + h) + l;
+        const int e = P >> 3;
+        const int c = (P & 7) ^ (e & 7);
+        const uint32_t off = (uint32_t)min(k0 + e, klast) * (uint32_t)ID + (uint32_t)(16 * c);
+        lds_dma16(kc, off, lds_u32(&kbuf[gi % PNBUF][1024 * (2 * wv + h)]));
+      }
+      if (l < 16)
+        lds_dma4(ksc, (uint32_t)min(k0 + 16 * wv + l, klast) * 4u,
+                 lds_u32(&ksbuf[gi % PNBUF][16 * wv]));
     };
     // every wave is past the previous key block's reads of kbuf and sbuf
     __syncthreads();
     for (int gi = 0; gi < 3 && gi < ngroups; ++gi) issue_group(gi);
 
     for (int gi = 0; gi < ngroups; ++gi) {
-      // this wave's two loads of group gi are done once at most those of the (up
-      // to two) later groups in flight remain
+      // this wave's three loads of group gi are done once at most those of the
+      // (up to two) later groups in flight remain
       const int later = min(ngroups - 1 - gi, 2);
       if (later == 2)
-        asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
       else if (later == 1)
-        asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(3) lgkmcnt(0)\n\ts_barrier" ::: "memory");
       else
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
       if (gi + 3 < ngroups) issue_group(gi + 3);
       const uint8_t* kg = kbuf[gi % PNBUF];
-      const int k = kb0 + gi * PG;
-      i32x8 kf[4];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const uint8_t* row = kg + (16 * kt + n) * ID;
-        const i32x4 a = *reinterpret_cast<const i32x4*>(row + 16 * c0);
-        const i32x4 b = *reinterpret_cast<const i32x4*>(row + 16 * c1);
-        kf[kt] = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-      }
-      const float ksv = ksbuf[gi % PNBUF][l];
-#pragma unroll
-      for (int i = 0; i < PRW; ++i) {
-        if (k > tt[i]) continue;  // wave-uniform
-        // all 16 MFMAs of the row first (distinct accumulators keep the matrix pipe
-        // busy), then the ReLU / weighted head-sum epilogue
-        f32x4 acc[4][4];
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-            acc[kt][mt] = mfma_fp8_16x16x128(qa[i][mt], kf[kt], f32x4{0.f, 0.f, 0.f, 0.f});
-        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  // the 16 MFMAs first
-        float p[4];
+      // fragments of the 64-key half u (key tiles 4 u .. 4 u + 3)
+      auto read_half = [&](int u, i32x8 (&kf)[4]) {
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
-          float a = 0.f;
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) a = fmaf(wq[i][mt * 4 + v], relu_bits(acc[kt][mt][v]), a);
-          p[kt] = a;
+          const uint8_t* row = kg + (64 * u + 16 * kt + n) * ID;
+          const i32x4 a = *reinterpret_cast<const i32x4*>(row + 16 * c0);
+          const i32x4 b = *reinterpret_cast<const i32x4*>(row + 16 * c1);
+          kf[kt] = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
         }
-        sbuf[wv * PRW + i][gi * PG + l] = reduce_groups(p[0], p[1], p[2], p[3]) * ksv;
-      }
+      };
+      // One 64-key half: 8 units (row i, key tile kt), each 4 MFMAs (the 64 heads)
+      // and 32 VALU ops of epilogue (ReLU and the weighted head sum of 4 values
+      // per head tile).  The MFMAs of unit v + 1 are issued among the epilogue of
+      // unit v, so the matrix pipe and the VALU work at the same time (in this
+      // kernel the epilogue costs about as much as the MFMAs).  Both rows are
+      // computed even when a row ends before this half; such scores are never
+      // written out.
+      auto compute_half = [&](int u, const i32x8 (&kf)[4]) {
+        const int k = kb0 + gi * PG + 64 * u;
+        const float ksv = ksbuf[gi % PNBUF][64 * u + l];
+        constexpr int NU = PRW * 4;
+        f32x4 acc[2][4];
+        float p[PRW][4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          acc[0][mt] = mfma_fp8_16x16x128(qa[0][mt], kf[0], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int v = 0; v < NU; ++v) {
+          const int i = v >> 2, kt = v & 3;
+          if (v + 1 < NU) {
+            const int i1 = (v + 1) >> 2, kt1 = (v + 1) & 3;
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+              acc[(v + 1) & 1][mt] =
+                  mfma_fp8_16x16x128(qa[i1][mt], kf[kt1], f32x4{0.f, 0.f, 0.f, 0.f});
+          }
+          // four independent accumulation chains (one per head tile), so the
+          // FMAs do not wait on each other
+          float a[4];
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) {
+            a[mt] = wq[i][mt * 4] * relu_bits(acc[v & 1][mt][0]);
+#pragma unroll
+            for (int e = 1; e < 4; ++e)
+              a[mt] = fmaf(wq[i][mt * 4 + e], relu_bits(acc[v & 1][mt][e]), a[mt]);
+          }
+          p[i][kt] = (a[0] + a[1]) + (a[2] + a[3]);
+          if (v + 1 < NU) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA of unit v + 1
+              __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // then 8 epilogue ops
+            }
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < PRW; ++i)
+          if (k <= tt[i])  // wave-uniform
+            sbuf[wv * PRW + i][gi * PG + 64 * u + l] =
+                reduce_groups(p[i][0], p[i][1], p[i][2], p[i][3]) * ksv;
+      };
+      // the second half's fragments are read while the first half is multiplied
+      i32x8 kfa[4], kfb[4];
+      read_half(0, kfa);
+      read_half(1, kfb);
+      compute_half(0, kfa);
+      compute_half(1, kfb);
     }
     // The key block's scores leave LDS after its loop, so that no vector-memory
     // store sits between the direct loads whose completion the loop counts with
