@@ -184,8 +184,14 @@ def time_workload(dsa, di, cfg, reps):
     res = {"tokens_per_s": R / s, "ms": ms, "rows": R, "reps": reps,
            "fp8_tflop": fp8_tf, "bf16_tflop": bf16_tf,
            # time-weighted MFMA fraction: ideal time at both peaks over measured time
-           "mfma_frac": (fp8_tf / FP8_PEAK_TFLOPS + bf16_tf / BF16_PEAK_TFLOPS) / s,
-           "hbm_frac": hbm / s / HBM_PEAK_GBS}
+           "mfma_frac": (fp8_tf / FP8_PEAK_TFLOPS + bf16_tf / BF16_PEAK_TFLOPS) / s}
+    if cfg.q_len == 1:
+        # decode: every algorithmic byte is an HBM byte (each row's keys and entries once)
+        res["hbm_frac"] = hbm / s / HBM_PEAK_GBS
+    else:
+        # prefill: rows of one sequence share keys and entries, which L2 / MALL serve;
+        # the algorithmic bytes over time are an effective rate through the caches
+        res["bytes_through_cache_tbps"] = hbm / s / 1e3
     del inp, out, lse, ws
     torch.cuda.empty_cache()
     return res

@@ -23,6 +23,16 @@ namespace {
 constexpr int IH = kIdxHeads;  // 64
 constexpr int ID = kIdxDim;    // 128
 
+// Fragment of one 128-byte fp8 row for lane group g in the "split" layout: bytes
+// [16 g, 16 g + 16) and [64 + 16 g, 64 + 16 g + 16).  The MFMA contracts over the
+// 128 bytes in any order as long as both operands use the same one; with this
+// order each 16-byte load of the 16 rows of a tile covers whole 64-byte sectors.
+__device__ __forceinline__ i32x8 load_frag_split(const uint8_t* row, int g) {
+  const i32x4 a = *reinterpret_cast<const i32x4*>(row + 16 * g);
+  const i32x4 b = *reinterpret_cast<const i32x4*>(row + 64 + 16 * g);
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 __device__ __forceinline__ i32x8 load_frag32(const uint8_t* p) {
   const i32x4* v = reinterpret_cast<const i32x4*>(p);
   i32x4 a = v[0];
@@ -62,6 +72,8 @@ __device__ __forceinline__ float reduce_groups(float p0, float p1, float p2, flo
   return keep + xor16(send);
 }
 
+// SPLIT: the queries in the load_frag_split byte order (else contiguous 32 bytes)
+template <bool SPLIT = false>
 __device__ __forceinline__ void load_query(const uint8_t* __restrict__ q_idx,
                                            const float* __restrict__ q_scale,
                                            const float* __restrict__ w, int r, i32x8 (&qa)[4],
@@ -69,7 +81,9 @@ __device__ __forceinline__ void load_query(const uint8_t* __restrict__ q_idx,
   const int l = lane_id(), g = l >> 4, n = l & 15;
   const uint8_t* qr = q_idx + (size_t)r * IH * ID;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) qa[mt] = load_frag32(qr + (16 * mt + n) * ID + 32 * g);
+  for (int mt = 0; mt < 4; ++mt)
+    qa[mt] = SPLIT ? load_frag_split(qr + (16 * mt + n) * ID, g)
+                   : load_frag32(qr + (16 * mt + n) * ID + 32 * g);
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -81,11 +95,12 @@ __device__ __forceinline__ void load_query(const uint8_t* __restrict__ q_idx,
 
 // ---------------------------------------------------------------------------
 // Decode tiling: one query row per block row, keys streamed from HBM.  Each wave
-// walks 64-key groups (interleaved across the block's waves) with the next
-// group's fragments prefetched while the current one is multiplied.
+// walks 64-key groups (interleaved across the block's waves) with the loads of the
+// next DEPTH - 1 groups in flight while the current one is multiplied; fragments
+// use the sector-aligned split byte order.
 // Grid: num_rows * key_blocks blocks (row-major), WAVES waves each.
 // ---------------------------------------------------------------------------
-template <int WAVES, int KPB>
+template <int WAVES, int KPB, int DEPTH>
 __global__ __launch_bounds__(WAVES * 64) void indexer_fp8_decode_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale,
     const float* __restrict__ w, const uint8_t* __restrict__ k_idx,
@@ -99,12 +114,12 @@ __global__ __launch_bounds__(WAVES * 64) void indexer_fp8_decode_kernel(
   const int kend = min(kb0 + KPB, t + 1);
   const int l = lane_id(), wv = threadIdx.x >> 6, g = l >> 4, n = l & 15;
 
-  int k0 = kb0 + 64 * wv;
+  const int k0 = kb0 + 64 * wv;
   if (k0 >= kend) return;
 
   i32x8 qa[4];
   float wq[16];
-  load_query(q_idx, q_scale, w, r, qa, wq);
+  load_query<true>(q_idx, q_scale, w, r, qa, wq);
 
   const uint8_t* kc = k_idx + (size_t)b * N * ID;
   const float* ksc = k_scale + (size_t)b * N;
@@ -113,7 +128,7 @@ __global__ __launch_bounds__(WAVES * 64) void indexer_fp8_decode_kernel(
   auto load_group = [&](int k, i32x8(&kb)[4], float& ks) {
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
-      kb[kt] = load_frag32(kc + (size_t)min(k + 16 * kt + n, t) * ID + 32 * g);
+      kb[kt] = load_frag_split(kc + (size_t)min(k + 16 * kt + n, t) * ID, g);
     ks = ksc[min(k + l, t)];
   };
   auto compute = [&](int k, const i32x8(&kb)[4], float ks) {
@@ -124,22 +139,21 @@ __global__ __launch_bounds__(WAVES * 64) void indexer_fp8_decode_kernel(
     const float s = reduce_groups(p0, p1, p2, p3) * ks;
     if (k + l < kend) out[k + l] = s;
   };
-  // two register sets in ping-pong: the next group's loads are in flight while the
-  // current group is multiplied
   constexpr int STEP = 64 * WAVES;
-  i32x8 ka[4], kb[4];
-  float sa, sb;
-  load_group(k0, ka, sa);
-  for (;;) {
-    const int k1 = k0 + STEP;
-    if (k1 < kend) load_group(k1, kb, sb);
-    compute(k0, ka, sa);
-    if (k1 >= kend) break;
-    const int k2 = k1 + STEP;
-    if (k2 < kend) load_group(k2, ka, sa);
-    compute(k1, kb, sb);
-    if (k2 >= kend) break;
-    k0 = k2;
+  i32x8 kr[DEPTH][4];
+  float sr[DEPTH];
+#pragma unroll
+  for (int d = 0; d < DEPTH - 1; ++d)
+    if (k0 + d * STEP < kend) load_group(k0 + d * STEP, kr[d], sr[d]);
+  for (int it = 0;; it += DEPTH) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      const int k = k0 + (it + d) * STEP;
+      if (k >= kend) return;
+      const int kn = k + (DEPTH - 1) * STEP;
+      if (kn < kend) load_group(kn, kr[(d + DEPTH - 1) % DEPTH], sr[(d + DEPTH - 1) % DEPTH]);
+      compute(k, kr[d], sr[d]);
+    }
   }
 }
 
@@ -498,9 +512,9 @@ hipError_t launch_indexer_fp8(const dsa_rows& rows, const uint8_t* q_idx, const 
                        stream, q_idx, q_scale, w, k_idx, k_scale, rows.row_seq, rows.row_pos, R,
                        rows.num_seqs, rows.max_ctx, ksplit, scores, ld);
   } else {
-    constexpr int WAVES = 4, KPB = 2048;
+    constexpr int WAVES = 4, KPB = 1024, DEPTH = 3;
     const int nkb = (L + KPB - 1) / KPB;
-    hipLaunchKernelGGL((indexer_fp8_decode_kernel<WAVES, KPB>), dim3(R * nkb), dim3(WAVES * 64),
+    hipLaunchKernelGGL((indexer_fp8_decode_kernel<WAVES, KPB, DEPTH>), dim3(R * nkb), dim3(WAVES * 64),
                        0, stream, q_idx, q_scale, w, k_idx, k_scale, rows.row_seq, rows.row_pos,
                        rows.num_seqs, rows.max_ctx, nkb, scores, ld);
   }
