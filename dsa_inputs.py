@@ -33,7 +33,9 @@ Storage formats
   therefore exact; the only rounding is the fp8 cast.
 * bf16: round-to-nearest-even cast of the float32 draw.
 
-The workloads (shapes and distributions) are listed in ``CONFIGS``.
+The workloads (shapes and distributions) are listed in ``CONFIGS``; the
+projection workloads (hidden states and projection weights of new tokens) in
+``PROJ_CONFIGS``.
 """
 from __future__ import annotations
 
@@ -356,6 +358,84 @@ def make_inputs(cfg: Config, set_id: int = 0, device="cpu",
     return Inputs(c, set_id, q_idx, q_scale, w, k_idx, k_scale, q, latent,
                   torch.from_numpy(seq[r0:r1].copy()).to(device),
                   torch.from_numpy(pos[r0:r1].copy()).to(device))
+
+
+# ---------------------------------------------------------------------------
+# projection workloads: hidden states h of new tokens and the projection weights
+# ---------------------------------------------------------------------------
+
+T_H, T_WQ, T_WK, T_WC, T_WW = 6, 7, 8, 9, 10
+
+
+@dataclasses.dataclass(frozen=True)
+class ProjConfig:
+    name: str
+    cfg_id: int
+    num_tokens: int        # R new tokens
+    d_model: int           # width of h
+    num_seqs: int          # B (caches [B, N, ...])
+    max_ctx: int           # N
+    n_idx_heads: int = 64
+    idx_dim: int = 128
+    qk_dim: int = 576
+    description: str = ""
+
+    def row_seq_pos(self) -> Tuple[np.ndarray, np.ndarray]:
+        """Token r of a decode batch appends at the last position of sequence r; the
+        tokens of a one-sequence chunk append at positions 0..R-1."""
+        R = self.num_tokens
+        if self.num_seqs == R:
+            return (np.arange(R, dtype=np.int32),
+                    np.full(R, self.max_ctx - 1, dtype=np.int32))
+        return np.zeros(R, dtype=np.int32), np.arange(R, dtype=np.int32)
+
+
+PROJ_CONFIGS: Dict[str, ProjConfig] = {
+    c.name: c
+    for c in [
+        ProjConfig("proj_decode32", 6, 32, 7168, 32, 32768,
+                   description="projections of 32 decode tokens, d_model 7168, "
+                               "appended at position 32767 of their sequences"),
+        ProjConfig("proj_prefill8k", 7, 8192, 7168, 1, 8192,
+                   description="projections of an 8192-token prefill chunk, d_model 7168"),
+    ]
+}
+
+
+class ProjGenerator:
+    """h ~ N(0,1) and weights ~ N(0,1)/sqrt(d_model), both stored as bf16."""
+
+    def __init__(self, cfg_id: int, d_model: int, set_id: int = 0,
+                 n_idx_heads: int = 64, idx_dim: int = 128, qk_dim: int = 576):
+        self.cfg_id, self.d, self.set_id = cfg_id, d_model, set_id
+        self.shapes = {T_WQ: n_idx_heads * idx_dim, T_WK: idx_dim, T_WC: qk_dim,
+                       T_WW: n_idx_heads}
+
+    def _key(self, tensor_id: int) -> int:
+        return stream_key(self.cfg_id, self.set_id, tensor_id)
+
+    def h(self, r0: int, r1: int, device="cpu") -> torch.Tensor:
+        x = normal(self._key(T_H), _flat(r0 * self.d, (r1 - r0) * self.d, device))
+        return to_bf16(x.view(r1 - r0, self.d))
+
+    def weight(self, tensor_id: int, p0: int = 0, p1: Optional[int] = None,
+               device="cpu") -> torch.Tensor:
+        """Rows [p0, p1) of one projection matrix (T_WQ, T_WK, T_WC or T_WW)."""
+        p1 = self.shapes[tensor_id] if p1 is None else p1
+        x = normal(self._key(tensor_id), _flat(p0 * self.d, (p1 - p0) * self.d, device))
+        return to_bf16(x.view(p1 - p0, self.d) * (1.0 / math.sqrt(self.d)))
+
+    def weights(self, device="cpu") -> Tuple[torch.Tensor, ...]:
+        """(w_q, w_k, w_c, w_w), each materialised in row chunks."""
+        out = []
+        for tid in (T_WQ, T_WK, T_WC, T_WW):
+            P = self.shapes[tid]
+            t = torch.empty(P, self.d, dtype=torch.bfloat16, device=device)
+            step = _rows_per_chunk(self.d)
+            for a in range(0, P, step):
+                t[a:min(P, a + step)] = self.weight(tid, a, min(P, a + step), device)
+            out.append(t)
+        return tuple(out)
 
 
 def sample_rows(cfg: Config, count: int = 256, seed_offset: int = 99) -> np.ndarray:

@@ -31,6 +31,15 @@ prose around the lost equation.  "nsmao report" means the page
    bias, no sink.  The nsmao report ("DSA principle") gives the cache widths: 128 per
    token for the indexer key, 512 for the latent.
 
+4. Query and key projections with cache append (nsmao report, "DSA principle": the
+   workflow's first step projects the query and the keys before indexer scoring;
+   V3.2-Exp paper, §1: q[t,j] and w[t,j] are derived from the query token h_t and
+   k[s] from the token h_s).  Reading: plain linear maps of h without bias or
+   normalisation, stored in the formats the later steps read: the indexer query
+   per (token, head) and the indexer key per token as e4m3fn codes with a
+   power-of-two fp32 scale, the head weights as fp32, and the latent entry as
+   bf16 (round to nearest even).  RoPE is not applied.
+
 Inputs are the exact byte images the GPU receives: e4m3fn codes with fp32 scales
 (dequantised value = decode(code) * scale), bf16 bit patterns, or plain fp32.  The
 oracle decodes them with its own decoders and computes every step in float64.
@@ -44,6 +53,8 @@ import numpy as np
 __all__ = [
     "decode_e4m3fn", "decode_bf16", "indexer_scores", "select_topk",
     "sparse_attention", "indexer_row", "attention_row", "dsa_row",
+    "encode_e4m3fn", "encode_bf16", "pow2_scale", "quantize_e4m3fn", "project",
+    "project_tokens", "append_rows",
 ]
 
 
@@ -170,3 +181,114 @@ def dsa_row(q_idx, q_scale, w, k_idx, k_scale, q, latent, t: int, topk: int,
     S = select_topk(I, min(topk, t + 1))
     o, lse = attention_row(q, latent[S], scale, v_dim, quantised)
     return I, S, o, lse
+
+
+# ---------------------------------------------------------------------------
+# O5: projections of new tokens, storage encoders, cache append
+# ---------------------------------------------------------------------------
+
+E4M3FN_MAX = 448.0
+
+
+def _e4m3fn_magnitudes() -> np.ndarray:
+    """The 127 finite non-negative e4m3fn values, indexed by their code 0x00..0x7E."""
+    return decode_e4m3fn(np.arange(0x7F, dtype=np.uint8))
+
+
+def encode_e4m3fn(x: np.ndarray) -> np.ndarray:
+    """Nearest e4m3fn code of each value in [-448, 448] (float64 in, uint8 out).
+
+    The magnitude is matched against the table of representable values; a value
+    exactly halfway between two neighbours takes the code with the even mantissa
+    (round to nearest even).  The sign bit copies the sign of x, so -0.0 -> 0x80.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    if np.any(a > E4M3FN_MAX) or np.any(np.isnan(x)):
+        raise ValueError("encode_e4m3fn expects finite values within [-448, 448]")
+    table = _e4m3fn_magnitudes()
+    hi = np.clip(np.searchsorted(table, a, side="left"), 0, table.size - 1)
+    lo = np.maximum(hi - 1, 0)
+    d_hi = table[hi] - a
+    d_lo = a - table[lo]
+    take_lo = (d_lo < d_hi) | ((d_lo == d_hi) & (lo % 2 == 0) & (lo != hi))
+    code = np.where(take_lo, lo, hi).astype(np.uint8)
+    return code | (np.signbit(x).astype(np.uint8) << np.uint8(7))
+
+
+def encode_bf16(x: np.ndarray) -> np.ndarray:
+    """float64 -> bfloat16 bit patterns (uint16), rounded once to nearest even.
+
+    bf16 keeps 8 significant bits: x = m * 2^e with 0.5 <= |m| < 1 is rounded to a
+    multiple of 2^(e-8) (2^-133 below the normal range).  The rounding is done
+    directly from float64, with no intermediate float32 rounding.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)
+    quantum = np.ldexp(1.0, np.maximum(e - 8, -133))
+    r = np.rint(x / quantum) * quantum      # x / quantum is exact (a power of two)
+    bits = r.astype(np.float32).view(np.uint32) >> np.uint32(16)
+    return bits.astype(np.uint16)
+
+
+def pow2_scale(amax: np.ndarray) -> np.ndarray:
+    """Power-of-two quantisation scale: 2^e with e the smallest integer such that
+    amax <= 448 * 2^e; 1 where amax == 0.  The first guess from log2 is corrected
+    with exact comparisons (448 * 2^e is exact in float64)."""
+    amax = np.asarray(amax, dtype=np.float64)
+    safe = np.where(amax > 0, amax, E4M3FN_MAX)
+    e = np.ceil(np.log2(safe / E4M3FN_MAX)).astype(np.int64)
+    e = np.where(np.ldexp(E4M3FN_MAX, e) < safe, e + 1, e)
+    e = np.where(np.ldexp(E4M3FN_MAX, e - 1) >= safe, e - 1, e)
+    return np.where(amax > 0, np.ldexp(1.0, e), 1.0)
+
+
+def quantize_e4m3fn(y: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Quantise each vector along the last axis: (codes uint8, scale float64).
+    scale = pow2_scale(max |y|), code = encode_e4m3fn(y / scale), so that
+    decode(code) * scale approximates y."""
+    y = np.asarray(y, dtype=np.float64)
+    s = pow2_scale(np.abs(y).max(axis=-1))
+    v = np.clip(y / s[..., None], -E4M3FN_MAX, E4M3FN_MAX)
+    return encode_e4m3fn(v), s
+
+
+def project(h: np.ndarray, W: np.ndarray) -> np.ndarray:
+    """Linear projection of tokens: h [R, d], W [P, d] (one output per row of W)
+    -> y [R, P] with y[r, p] = sum_k W[p, k] h[r, k]."""
+    return np.asarray(h, dtype=np.float64) @ np.asarray(W, dtype=np.float64).T
+
+
+def project_tokens(h_bits: np.ndarray, wq_bits: np.ndarray, wk_bits: np.ndarray,
+                   wc_bits: np.ndarray, ww_bits: np.ndarray, n_idx_heads: int) -> dict:
+    """Projections of R new tokens and their stored forms.
+
+    h_bits [R, d] and the weights are bf16 bit patterns: wq [H_I*d_I, d] (head j =
+    rows j*d_I .. j*d_I+d_I-1), wk [d_I, d], wc [D_k, d], ww [H_I, d].
+    Returns the exact projections (y_q [R,H_I,d_I], y_k [R,d_I], y_c [R,D_k],
+    y_w [R,H_I]) and the stored forms: q_codes/q_scale (per token and head),
+    k_codes/k_scale (per token), latent_bits (bf16), w (float64).
+    """
+    h = decode_bf16(h_bits)
+    R = h.shape[0]
+    y_q = project(h, decode_bf16(wq_bits)).reshape(R, n_idx_heads, -1)
+    y_k = project(h, decode_bf16(wk_bits))
+    y_c = project(h, decode_bf16(wc_bits))
+    y_w = project(h, decode_bf16(ww_bits))
+    q_codes, q_scale = quantize_e4m3fn(y_q)
+    k_codes, k_scale = quantize_e4m3fn(y_k)
+    return dict(y_q=y_q, y_k=y_k, y_c=y_c, y_w=y_w, q_codes=q_codes, q_scale=q_scale,
+                k_codes=k_codes, k_scale=k_scale, latent_bits=encode_bf16(y_c), w=y_w)
+
+
+def append_rows(cache: np.ndarray, row_seq: np.ndarray, row_pos: np.ndarray,
+                values: np.ndarray) -> np.ndarray:
+    """Copy of a per-sequence cache [B, N, ...] with values[r] stored at
+    (row_seq[r], row_pos[r]); rows whose sequence or position is out of range are
+    skipped."""
+    out = np.array(cache, copy=True)
+    B, N = out.shape[0], out.shape[1]
+    for r, (b, t) in enumerate(zip(np.asarray(row_seq), np.asarray(row_pos))):
+        if 0 <= b < B and 0 <= t < N:
+            out[b, t] = values[r]
+    return out

@@ -15,6 +15,7 @@ import itertools
 import json
 import math
 import os
+from fractions import Fraction
 
 import numpy as np
 import torch
@@ -313,6 +314,205 @@ def pin_dsa_row_composition():
             ww = np.exp(zz - zz.max(1, keepdims=True))
             ww /= ww.sum(1, keepdims=True)
             np.testing.assert_allclose(o, ww @ lat[Sb, :Dv].astype(np.float64), rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- P6 projections
+# Storage encoders, the power-of-two quantiser, the projections and the cache
+# append of new tokens.
+
+def _exact_e4m3fn_code(v: Fraction) -> int:
+    """Brute force: nearest e4m3fn value to the exact rational v (|v| <= 448), ties
+    to the even code, by scanning every finite code."""
+    best = None
+    for c in range(0x7F):
+        e, m = c >> 3, c & 7
+        mag = Fraction(8 + m, 8) * Fraction(2) ** (e - 7) if e else Fraction(m, 8) * Fraction(2) ** -6
+        d = abs(abs(v) - mag)
+        if best is None or d < best[0] or (d == best[0] and c % 2 == 0):
+            best = (d, c)
+    return best[1] | (0x80 if v < 0 else 0)
+
+
+def _exact_bf16_bits(v: Fraction) -> int:
+    """Brute force: bf16 word nearest to the exact rational v (normal range), ties
+    to the even mantissa."""
+    if v == 0:
+        return 0
+    sign = 0x8000 if v < 0 else 0
+    a = abs(v)
+    e = 0
+    while a >= 2:
+        a /= 2
+        e += 1
+    while a < 1:
+        a *= 2
+        e -= 1
+    scaled = a * 128                      # 8 significant bits: integer part of a * 2^7
+    lo = scaled.numerator // scaled.denominator
+    rem = scaled - lo
+    m = lo + (1 if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo % 2 == 1) else 0)
+    if m == 256:
+        m, e = 128, e + 1
+    return sign | ((e + 127) << 7) | (m - 128)
+
+
+def pin_encode_e4m3fn_roundtrip_and_ties():
+    """Every finite code round-trips; a value halfway between two neighbours takes
+    the even code; values off the midpoint take the nearer code; signs mirror."""
+    codes = np.arange(256, dtype=np.uint8)
+    vals = O.decode_e4m3fn(codes)
+    fin = ~np.isnan(vals)
+    assert np.array_equal(O.encode_e4m3fn(vals[fin]), codes[fin])
+    pos = vals[:0x7F]
+    mid = (pos[:-1] + pos[1:]) / 2
+    even = np.where(np.arange(0x7E) % 2 == 0, np.arange(0x7E), np.arange(1, 0x7F))
+    assert np.array_equal(O.encode_e4m3fn(mid), even.astype(np.uint8))
+    assert np.array_equal(O.encode_e4m3fn(-mid), (even | 0x80).astype(np.uint8))
+    gap = pos[1:] - pos[:-1]
+    assert np.array_equal(O.encode_e4m3fn(mid - gap / 8), np.arange(0x7E, dtype=np.uint8))
+    assert np.array_equal(O.encode_e4m3fn(mid + gap / 8), np.arange(1, 0x7F, dtype=np.uint8))
+
+
+def pin_encode_e4m3fn_library():
+    """Random float32 values in [-448, 448], normal and subnormal range, against
+    torch's float8_e4m3fn cast (a library routine, round to nearest even)."""
+    r = _rng(21)
+    x = np.concatenate([r.uniform(-448, 448, 20000), r.uniform(-2 ** -5, 2 ** -5, 20000),
+                        r.standard_normal(20000) * 8]).astype(np.float32)
+    x = np.clip(x, -448, 448)
+    lib = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.encode_e4m3fn(x.astype(np.float64)), lib)
+
+
+def pin_encode_bf16():
+    """bf16 rounding: torch's bfloat16 cast of float32 values (library routine),
+    hand-worked midpoints, and one rounding straight from float64 (a value that a
+    float32 intermediate would turn into a tie)."""
+    r = _rng(22)
+    x = (r.standard_normal(50000) * np.exp2(r.integers(-60, 60, 50000))).astype(np.float32)
+    lib = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.encode_bf16(x.astype(np.float64)), lib)
+    cases = [(1.0 + 2.0 ** -8, 0x3F80),             # tie -> even mantissa 0
+             (1.0 + 3 * 2.0 ** -8, 0x3F82),         # tie -> even mantissa 2
+             (1.0 + 2.0 ** -8 + 2.0 ** -40, 0x3F81),  # just above the tie
+             (-(1.0 + 2.0 ** -8 - 2.0 ** -40), 0xBF80),
+             (3.0, 0x4040), (-0.0, 0x8000), (0.0, 0x0000)]
+    got = O.encode_bf16(np.array([c[0] for c in cases]))
+    assert [int(g) for g in got] == [c[1] for c in cases], [hex(int(g)) for g in got]
+
+
+def pin_pow2_scale():
+    """scale = 2^e with the smallest integer e such that amax <= 448 * 2^e, found by
+    an exhaustive search over e; amax = 0 gives 1."""
+    r = _rng(23)
+    amax = np.concatenate([np.exp2(r.uniform(-30, 30, 500)),
+                           448.0 * np.exp2(np.arange(-20, 21, dtype=np.float64)),
+                           np.nextafter(448.0 * np.exp2(np.arange(-20, 21, dtype=np.float64)), np.inf),
+                           np.nextafter(448.0 * np.exp2(np.arange(-20, 21, dtype=np.float64)), 0)])
+    got = O.pow2_scale(amax)
+    for a, g in zip(amax, got):
+        e = next(e for e in range(-80, 80) if a <= 448.0 * 2.0 ** e)
+        assert g == 2.0 ** e, (a, g, 2.0 ** e)
+    assert O.pow2_scale(np.array([0.0]))[0] == 1.0
+
+
+def pin_quantize_e4m3fn():
+    """Per-vector quantisation: codes equal torch's float8 cast of y / scale (exact
+    for float32 y and a power-of-two scale); the largest magnitude lands in
+    (224, 448]; reconstruction error within half a code spacing; a zero vector
+    gives scale 1 and zero codes; each vector gets its own scale."""
+    r = _rng(24)
+    y = (r.standard_normal((40, 128)) * np.exp2(r.integers(-8, 8, (40, 1)))).astype(np.float32)
+    y[3] = 0.0
+    codes, s = O.quantize_e4m3fn(y.astype(np.float64))
+    assert codes.shape == y.shape and s.shape == (40,)
+    assert s[3] == 1.0 and not codes[3].any()
+    ys = (y.astype(np.float64) / s[:, None]).astype(np.float32)
+    lib = torch.from_numpy(ys).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(codes, lib)
+    dec = O.decode_e4m3fn(codes) * s[:, None]
+    nz = np.arange(40) != 3
+    top = np.abs(O.decode_e4m3fn(codes[nz])).max(axis=1)
+    assert np.all((top > 224) & (top <= 448))
+    err = np.abs(dec - y)
+    bound = np.maximum(np.abs(y) * 2.0 ** -4, 2.0 ** -10 * s[:, None])
+    assert np.all(err <= bound + 1e-300)
+
+
+def pin_project_bruteforce():
+    """y[r, p] = sum_k W[p, k] h[r, k] against pure-Python loops on a tiny case."""
+    r = _rng(25)
+    h = r.standard_normal((3, 7))
+    W = r.standard_normal((5, 7))
+    got = O.project(h, W)
+    for i in range(3):
+        for p in range(5):
+            want = math.fsum(W[p, k] * h[i, k] for k in range(7))
+            assert abs(got[i, p] - want) <= 1e-12 * (1 + abs(want))
+
+
+def pin_project_tokens_exact():
+    """project_tokens on tiny bf16 inputs against exact rational arithmetic: each
+    projection summed as a Fraction, then rounded to bf16 or quantised with a
+    brute-force code scan; heads are consecutive row blocks of w_q."""
+    r = _rng(26)
+    H_I, d_I, Dk, d, R = 2, 4, 3, 6, 2
+
+    def bf(shape, scale):
+        x = (r.standard_normal(shape) * scale).astype(np.float32)
+        return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+    h, wq, wk, wc, ww = bf((R, d), 1), bf((H_I * d_I, d), 0.4), bf((d_I, d), 0.4), \
+        bf((Dk, d), 0.4), bf((H_I, d), 0.4)
+    out = O.project_tokens(h, wq, wk, wc, ww, H_I)
+
+    def frac(bits):
+        return [Fraction(float(v)) for v in
+                (np.asarray(bits, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)]
+
+    hF = [frac(h[i]) for i in range(R)]
+
+    def dot(i, wrow):
+        wF = frac(wrow)
+        return sum(a * b for a, b in zip(hF[i], wF))
+
+    def quant(vec):
+        amax = max(abs(v) for v in vec)
+        if amax == 0:
+            return [0] * len(vec), Fraction(1)
+        e = next(e for e in range(-60, 60) if amax <= 448 * Fraction(2) ** e)
+        s = Fraction(2) ** e
+        return [_exact_e4m3fn_code(v / s) for v in vec], s
+
+    for i in range(R):
+        for j in range(H_I):
+            vec = [dot(i, wq[j * d_I + c]) for c in range(d_I)]
+            codes, s = quant(vec)
+            assert list(out["q_codes"][i, j]) == codes and out["q_scale"][i, j] == s
+            for c in range(d_I):
+                assert abs(out["y_q"][i, j, c] - float(vec[c])) <= 1e-12
+        vec = [dot(i, wk[c]) for c in range(d_I)]
+        codes, s = quant(vec)
+        assert list(out["k_codes"][i]) == codes and out["k_scale"][i] == s
+        for c in range(Dk):
+            assert int(out["latent_bits"][i, c]) == _exact_bf16_bits(dot(i, wc[c]))
+        for j in range(H_I):
+            assert abs(out["w"][i, j] - float(dot(i, ww[j]))) <= 1e-12
+
+
+def pin_append_rows():
+    """Cache append: exactly the rows named by (seq, pos) change, each to its own
+    token's values; out-of-range rows are skipped."""
+    cache = np.arange(3 * 5 * 2, dtype=np.int64).reshape(3, 5, 2)
+    vals = -np.arange(1, 9, dtype=np.int64).reshape(4, 2)
+    seq = np.array([0, 2, 5, 1])
+    pos = np.array([4, 0, 1, -1])
+    out = O.append_rows(cache, seq, pos, vals)
+    want = cache.copy()
+    want[0, 4] = vals[0]
+    want[2, 0] = vals[1]
+    assert np.array_equal(out, want)
+    assert np.array_equal(cache, np.arange(30).reshape(3, 5, 2))  # input untouched
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -8,7 +8,8 @@ import oracle_pins
 
 _orig = {name: getattr(O, name) for name in
          ["indexer_scores", "select_topk", "sparse_attention", "decode_e4m3fn",
-          "decode_bf16", "indexer_row"]}
+          "decode_bf16", "indexer_row", "encode_e4m3fn", "encode_bf16", "pow2_scale",
+         "quantize_e4m3fn", "project", "project_tokens"]}
 
 
 def _no_relu(q, w, k):
@@ -90,6 +91,55 @@ def _scale_ignored(q_idx, q_scale, w, k_idx, k_scale, t, fp8):
     return _orig["indexer_row"](q_idx, None, w, k_idx, None, t, fp8)
 
 
+def _e4m3_ties_away(x):
+    # round half away from zero instead of to even
+    x = np.asarray(x, dtype=np.float64)
+    table = O.decode_e4m3fn(np.arange(0x7F, dtype=np.uint8))
+    a = np.abs(x)
+    hi = np.clip(np.searchsorted(table, a, side="left"), 0, 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    code = np.where(a - table[lo] < table[hi] - a, lo, hi).astype(np.uint8)
+    return code | (np.signbit(x).astype(np.uint8) << np.uint8(7))
+
+
+def _bf16_truncate(x):
+    b = np.asarray(x, dtype=np.float64).astype(np.float32).view(np.uint32) >> np.uint32(16)
+    return b.astype(np.uint16)
+
+
+def _bf16_via_f32(x):
+    # double rounding: float64 -> float32 -> bf16
+    return _orig["encode_bf16"](np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64))
+
+
+def _scale_amax_over_448(amax):
+    amax = np.asarray(amax, dtype=np.float64)
+    return np.where(amax > 0, amax / 448.0, 1.0)
+
+
+def _scale_one_too_big(amax):
+    return _orig["pow2_scale"](amax) * 2.0
+
+
+def _scale_per_tensor(y):
+    y = np.asarray(y, dtype=np.float64)
+    s = O.pow2_scale(np.abs(y).max())
+    return O.encode_e4m3fn(np.clip(y / s, -448, 448)), np.full(y.shape[:-1], s)
+
+
+def _project_drops_last(h, W):
+    return np.asarray(h, dtype=np.float64)[:, :-1] @ np.asarray(W, dtype=np.float64)[:, :-1].T
+
+
+def _heads_interleaved(h_bits, wq_bits, wk_bits, wc_bits, ww_bits, n_idx_heads):
+    out = _orig["project_tokens"](h_bits, wq_bits, wk_bits, wc_bits, ww_bits, n_idx_heads)
+    R = out["y_q"].shape[0]
+    y_q = out["y_q"].reshape(R, -1).reshape(R, -1, n_idx_heads).transpose(0, 2, 1)
+    out["q_codes"], out["q_scale"] = O.quantize_e4m3fn(y_q)
+    out["y_q"] = y_q
+    return out
+
+
 MUTANTS = [
     ("indexer_scores", _no_relu),
     ("indexer_scores", _relu_after_sum),
@@ -107,6 +157,14 @@ MUTANTS = [
     ("decode_bf16", _bf16_low_half),
     ("indexer_row", _exclusive_causal),
     ("indexer_row", _scale_ignored),
+    ("encode_e4m3fn", _e4m3_ties_away),
+    ("encode_bf16", _bf16_truncate),
+    ("encode_bf16", _bf16_via_f32),
+    ("pow2_scale", _scale_amax_over_448),
+    ("pow2_scale", _scale_one_too_big),
+    ("quantize_e4m3fn", _scale_per_tensor),
+    ("project", _project_drops_last),
+    ("project_tokens", _heads_interleaved),
 ]
 
 
