@@ -1,7 +1,8 @@
 /*
  * dsa.h - C ABI of the DeepSeek Sparse Attention (DSA) hot path on AMD MI355X (gfx950).
  *
- * The path has three steps, each a hand-written HIP kernel family:
+ * The path has three steps, each a hand-written HIP kernel family, and a step
+ * before them that produces the operands of a new token (step 0 below):
  *   1. lightning-indexer scores   I[t,s] = sum_j w[t,j] * ReLU(q[t,j] . k[s]),  s <= t
  *      (DeepSeek-V3.2-Exp paper as translated on the m.163.com page, section 1
  *      "Architecture", Eq. 1 and the prose around it: few indexer heads, ReLU,
@@ -165,6 +166,41 @@ dsa_status dsa_forward(const dsa_rows* rows, const dsa_dims* dims,
                        const void* q, const void* latent, float softmax_scale,
                        void* out, float* lse, int32_t* indices_out,
                        int32_t chunk_rows, void* workspace, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Step 0: projections of new tokens with fp8 quantisation and cache append.
+ * The first step of the DSA workflow, before indexer scoring ("DeepSeek-V3.2开源技术
+ * 报告", "DSA principle": query and key projection; DeepSeek-V3.2-Exp paper,
+ * section 1, text around Eq. 1: q[t,j] and w[t,j] are derived from the query token
+ * h_t, k[s] from the token h_s).  Production dims only (H_I = 64, d_I = 128,
+ * D_k = 576, idx_dtype fp8, attn_dtype bf16; the other dims fields are ignored).
+ *   h      [R, d_model] bf16: row r is the token at position row_pos[r] of sequence
+ *          row_seq[r]
+ *   w_q    [H_I*d_I, d_model] bf16, head j = rows j*d_I .. j*d_I + d_I - 1
+ *   w_k    [d_I, d_model] bf16;  w_c [D_k, d_model] bf16;  w_w [H_I, d_model] bf16
+ * With y = W h[r] (exact bf16 products, fp32 accumulation) the call writes
+ *   q_idx  [R, H_I, d_I] e4m3fn codes and q_scale [R, H_I] fp32
+ *   w      [R, H_I] fp32
+ *   k_idx  [B, N, d_I] codes and k_scale [B, N]: the row (row_seq[r], row_pos[r])
+ *   latent [B, N, D_k] bf16 (round to nearest even): the row (row_seq[r], row_pos[r])
+ * Each 128-wide vector (one per (token, head) for q, one per token for k) is
+ * quantised with scale = 2^e, e the smallest integer with max|y| <= 448 * 2^e
+ * (scale 1 when max|y| = 0), and code = e4m3fn round-to-nearest-even of y / scale,
+ * the format dsa_indexer_scores reads.  Rows whose row_seq or row_pos is out of
+ * range still get q_idx, q_scale and w but write no cache row; two rows naming the
+ * same cache row leave one of them (unspecified which).  Every other cache row is
+ * left untouched.  d_model must be a positive multiple of 64 (at most 65536).
+ * RoPE is not applied.  Few rows split the contraction over blocks; the workspace
+ * then holds the fp32 partial sums (dsa_project_append_workspace_size; 0 bytes
+ * when nothing is split).
+ * ------------------------------------------------------------------------- */
+size_t dsa_project_append_workspace_size(const dsa_rows* rows, int32_t d_model);
+
+dsa_status dsa_project_append(const dsa_rows* rows, const dsa_dims* dims, int32_t d_model,
+                              const void* h, const void* w_q, const void* w_k, const void* w_c,
+                              const void* w_w, void* q_idx, float* q_scale, float* w,
+                              void* k_idx, float* k_scale, void* latent, void* workspace,
+                              size_t ws_bytes, void* stream);
 
 /* Status text, and the detail of the last failure on the calling thread. */
 const char* dsa_status_string(dsa_status status);

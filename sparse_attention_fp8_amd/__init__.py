@@ -17,7 +17,8 @@ import torch
 __all__ = [
     "LIB_PATH", "lib", "Dims", "PRODUCTION_DIMS", "rows_struct", "dims_struct",
     "indexer_scores", "topk", "sparse_mla_attn", "forward", "forward_workspace_size",
-    "sparse_mla_attn_workspace_size", "DSAError", "EXPORTED_SYMBOLS",
+    "sparse_mla_attn_workspace_size", "project_append", "project_append_workspace_size",
+    "DSAError", "EXPORTED_SYMBOLS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
@@ -28,6 +29,7 @@ DSA_F32, DSA_BF16, DSA_FP8_E4M3FN = range(3)
 EXPORTED_SYMBOLS = [
     "dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_attn_workspace_size",
     "dsa_sparse_mla_attn", "dsa_forward_workspace_size", "dsa_forward",
+    "dsa_project_append_workspace_size", "dsa_project_append",
     "dsa_status_string", "dsa_last_error", "dsa_api_version",
 ]
 
@@ -67,7 +69,11 @@ def _load() -> ctypes.CDLL:
     L.dsa_forward_workspace_size.argtypes = [R, D, i32]
     L.dsa_forward_workspace_size.restype = sz
     L.dsa_forward.argtypes = [R, D, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, i32, vp, sz, vp]
-    for name in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_attn", "dsa_forward"):
+    L.dsa_project_append_workspace_size.argtypes = [R, i32]
+    L.dsa_project_append_workspace_size.restype = sz
+    L.dsa_project_append.argtypes = [R, D, i32] + [vp] * 12 + [sz, vp]
+    for name in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_attn", "dsa_forward",
+                 "dsa_project_append"):
         getattr(L, name).restype = ctypes.c_int
     L.dsa_status_string.argtypes = [ctypes.c_int]
     L.dsa_status_string.restype = ctypes.c_char_p
@@ -274,3 +280,50 @@ def forward(rows: _Rows, dims: Dims, q_idx, q_scale, w, k_idx, k_scale, q, laten
                            float(softmax_scale), _ptr(out), _ptr(lse), _ptr(indices_out),
                            int(chunk_rows), _ptr(workspace), workspace.numel(), _stream()))
     return out, lse, indices_out
+
+
+def project_append_workspace_size(rows: _Rows, d_model: int) -> int:
+    return int(lib.dsa_project_append_workspace_size(ctypes.byref(rows), int(d_model)))
+
+
+def project_append(rows: _Rows, h, w_q, w_k, w_c, w_w, k_idx, k_scale, latent,
+                   q_idx=None, q_scale=None, w=None, dims: Dims = PRODUCTION_DIMS,
+                   workspace: Optional[torch.Tensor] = None):
+    """dsa_project_append: projections of the R tokens in h, their indexer query
+    and head weights returned as (q_idx, q_scale, w); the indexer key and latent
+    rows are written into the caches k_idx/k_scale/latent in place."""
+    R, d_model = h.shape[0], h.shape[-1]
+    _dev(h, torch.bfloat16, "h")
+    for t, name in ((w_q, "w_q"), (w_k, "w_k"), (w_c, "w_c"), (w_w, "w_w")):
+        _dev(t, torch.bfloat16, name)
+    _shape(h, (rows.num_rows, None), "h")
+    _shape(w_q, (dims.n_idx_heads * dims.idx_dim, d_model), "w_q")
+    _shape(w_k, (dims.idx_dim, d_model), "w_k")
+    _shape(w_c, (dims.qk_dim, d_model), "w_c")
+    _shape(w_w, (dims.n_idx_heads, d_model), "w_w")
+    if q_idx is None:
+        q_idx = torch.empty(R, dims.n_idx_heads, dims.idx_dim, dtype=torch.uint8, device=h.device)
+    if q_scale is None:
+        q_scale = torch.empty(R, dims.n_idx_heads, dtype=torch.float32, device=h.device)
+    if w is None:
+        w = torch.empty(R, dims.n_idx_heads, dtype=torch.float32, device=h.device)
+    _dev(q_idx, torch.uint8, "q_idx")
+    _dev(q_scale, torch.float32, "q_scale")
+    _dev(w, torch.float32, "w")
+    _dev(k_idx, torch.uint8, "k_idx")
+    _dev(k_scale, torch.float32, "k_scale")
+    _dev(latent, torch.bfloat16, "latent")
+    _shape(q_idx, (R, dims.n_idx_heads, dims.idx_dim), "q_idx")
+    _shape(q_scale, (R, dims.n_idx_heads), "q_scale")
+    _shape(w, (R, dims.n_idx_heads), "w")
+    _caches(rows, dims, k_idx, k_scale, latent)
+    need = project_append_workspace_size(rows, d_model)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=h.device)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    ds = dims_struct(dims)
+    _check(lib.dsa_project_append(ctypes.byref(rows), ctypes.byref(ds), int(d_model), _ptr(h),
+                                  _ptr(w_q), _ptr(w_k), _ptr(w_c), _ptr(w_w), _ptr(q_idx),
+                                  _ptr(q_scale), _ptr(w), _ptr(k_idx), _ptr(k_scale),
+                                  _ptr(latent), _ptr(workspace), ws_bytes, _stream()))
+    return q_idx, q_scale, w

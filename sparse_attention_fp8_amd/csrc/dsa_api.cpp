@@ -242,4 +242,40 @@ dsa_status dsa_forward(const dsa_rows* rows, const dsa_dims* dims, const void* q
   return DSA_OK;
 }
 
+size_t dsa_project_append_workspace_size(const dsa_rows* rows, int32_t d_model) {
+  if (check_rows(rows) != DSA_OK || d_model < 64 || d_model % 64 != 0) return 0;
+  return dsa::project_workspace_bytes(rows->num_rows, d_model);
+}
+
+dsa_status dsa_project_append(const dsa_rows* rows, const dsa_dims* dims, int32_t d_model,
+                              const void* h, const void* w_q, const void* w_k, const void* w_c,
+                              const void* w_w, void* q_idx, float* q_scale, float* w,
+                              void* k_idx, float* k_scale, void* latent, void* workspace,
+                              size_t ws_bytes, void* stream) {
+  dsa_status st = check_rows(rows);
+  if (st != DSA_OK) return st;
+  if (dims == nullptr) return fail(DSA_E_INVALID, "dims is NULL");
+  if (dims->n_idx_heads != dsa::kIdxHeads || dims->idx_dim != dsa::kIdxDim ||
+      dims->qk_dim != dsa::kQkDim || dims->idx_dtype != DSA_FP8_E4M3FN ||
+      dims->attn_dtype != DSA_BF16)
+    return fail(DSA_E_UNSUPPORTED,
+                "projections support H_I=64, d_I=128, D_k=576, fp8 indexer, bf16 latent only");
+  if (d_model < 64 || d_model % 64 != 0 || d_model > 65536)
+    return fail(DSA_E_UNSUPPORTED, "d_model must be a positive multiple of 64, at most 65536");
+  if (rows->num_rows == 0) return DSA_OK;
+  if (!h || !w_q || !w_k || !w_c || !w_w || !q_idx || !q_scale || !w || !k_idx || !k_scale ||
+      !latent)
+    return fail(DSA_E_INVALID, "NULL tensor pointer");
+  const size_t need = dsa::project_workspace_bytes(rows->num_rows, d_model);
+  if (need > 0 && (workspace == nullptr || ws_bytes < need))
+    return fail(DSA_E_WORKSPACE, "projections need %zu workspace bytes, got %zu", need, ws_bytes);
+  const hipError_t err = dsa::launch_project(
+      *rows, d_model, static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w_q),
+      static_cast<const uint16_t*>(w_k), static_cast<const uint16_t*>(w_c),
+      static_cast<const uint16_t*>(w_w), static_cast<uint8_t*>(q_idx), q_scale, w,
+      static_cast<uint8_t*>(k_idx), k_scale, static_cast<uint16_t*>(latent), workspace,
+      as_stream(stream));
+  return err == hipSuccess ? DSA_OK : hip_fail(err, "projection launch");
+}
+
 }  // extern "C"

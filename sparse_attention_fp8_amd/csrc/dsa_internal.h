@@ -39,4 +39,11 @@ hipError_t launch_attn_f32(const dsa_rows& rows, const dsa_dims& dims, const flo
                            const float* latent, const int32_t* indices, float softmax_scale,
                            float* out, float* lse, hipStream_t stream);
 
+size_t project_workspace_bytes(int num_rows, int d_model);
+
+hipError_t launch_project(const dsa_rows& rows, int d_model, const uint16_t* h, const uint16_t* wq,
+                          const uint16_t* wk, const uint16_t* wc, const uint16_t* ww, uint8_t* q_idx,
+                          float* q_scale, float* w, uint8_t* k_idx, float* k_scale,
+                          uint16_t* latent, void* workspace, hipStream_t stream);
+
 }  // namespace dsa

@@ -16,10 +16,22 @@ hot path is held to:
   -1 padded; it equals the oracle's set outside the tie band
   A = {s : |I_ref[s] - tau| <= 1e-3 |tau|}, tau = the n-th largest oracle score.
 * C3 attention (bf16): max |o_gpu - o_ref| <= 2e-2 and mean <= 2e-3.
+* C4 projections: the kernel accumulates y = W h in fp32, so its y differs from
+  the exact one by rounding.  Each output gets the bound
+  err = 16 sqrt(d) 2^-24 ||(h_k W_pk)_k||_2: the rounding errors of any summation
+  order form a sum of at most d terms, each at most 2^-24 times a partial sum,
+  and the partial sums of these sign-random products stay within a few
+  ||x||_2 (a random-walk bound, ~4 sigma with margin).  A stored value is
+  correct when it is what the oracle's encoder gives for some y' within err of
+  the exact y: the fp8 scale is one of the power-of-two scales of amax +- err,
+  each code lies between the codes of (y - err) / scale and (y + err) / scale,
+  each bf16 word between the words of y - err and y + err, and fp32 w within
+  err.  Away from rounding boundaries this is exact equality.
 """
 from __future__ import annotations
 
 import dataclasses
+import math
 from typing import Dict, List, Optional, Sequence
 
 import numpy as np
@@ -155,3 +167,74 @@ def check_attention(gpu_o: np.ndarray, ref_o: np.ndarray):
 
 def to_f64(x: torch.Tensor) -> np.ndarray:
     return x.detach().float().cpu().numpy().astype(np.float64)
+
+
+# ---------------------------------------------------------------- C4 projections
+
+U32 = 2.0 ** -24
+
+
+def proj_error_bound(h: np.ndarray, W: np.ndarray) -> np.ndarray:
+    """C4 bound [R, P] on |fp32 projection - exact| for h [R, d], W [P, d]."""
+    d = h.shape[1]
+    return 16.0 * math.sqrt(d) * U32 * np.sqrt((h * h) @ (W * W).T)
+
+
+def check_quantised(codes_g: np.ndarray, scale_g: np.ndarray, y: np.ndarray,
+                    err: np.ndarray) -> float:
+    """C4 for e4m3fn vectors along the last axis; returns the fraction of codes
+    whose allowed range holds more than one code."""
+    codes_g = np.asarray(codes_g)
+    scale_g = np.asarray(scale_g, dtype=np.float64)
+    amax_lo = np.max(np.maximum(np.abs(y) - err, 0.0), axis=-1)
+    amax_hi = np.max(np.abs(y) + err, axis=-1)
+    s_lo, s_hi = oracle.pow2_scale(amax_lo), oracle.pow2_scale(amax_hi)
+    m, _ = np.frexp(scale_g)
+    ok_s = (m == 0.5) & (scale_g >= s_lo) & (scale_g <= s_hi)
+    assert ok_s.all(), (f"scale outside the allowed powers of two at {np.argwhere(~ok_s)[:4]}: "
+                        f"gpu {scale_g[~ok_s][:4]} allowed [{s_lo[~ok_s][:4]}, {s_hi[~ok_s][:4]}]")
+    s = scale_g[..., None]
+    lo = np.clip((y - err) / s, -448.0, 448.0)
+    hi = np.clip((y + err) / s, -448.0, 448.0)
+    v_lo = oracle.decode_e4m3fn(oracle.encode_e4m3fn(lo))
+    v_hi = oracle.decode_e4m3fn(oracle.encode_e4m3fn(hi))
+    v_g = oracle.decode_e4m3fn(codes_g)
+    ok = (v_g >= v_lo) & (v_g <= v_hi)
+    assert np.all(~np.isnan(v_g)), "NaN code"
+    assert ok.all(), (f"fp8 code outside its allowed range at {np.argwhere(~ok)[:4]}: gpu "
+                      f"{v_g[~ok][:4]} allowed [{v_lo[~ok][:4]}, {v_hi[~ok][:4]}]")
+    return float(np.mean(v_lo != v_hi))
+
+
+def check_bf16_words(bits_g: np.ndarray, y: np.ndarray, err: np.ndarray) -> float:
+    """C4 for bf16 outputs; returns the fraction with more than one allowed word."""
+    v_g = oracle.decode_bf16(bits_g)
+    v_lo = oracle.decode_bf16(oracle.encode_bf16(y - err))
+    v_hi = oracle.decode_bf16(oracle.encode_bf16(y + err))
+    ok = (v_g >= v_lo) & (v_g <= v_hi)
+    assert ok.all(), (f"bf16 word outside its allowed range at {np.argwhere(~ok)[:4]}: gpu "
+                      f"{v_g[~ok][:4]} allowed [{v_lo[~ok][:4]}, {v_hi[~ok][:4]}]")
+    return float(np.mean(v_lo != v_hi))
+
+
+def check_fp32_within(g: np.ndarray, y: np.ndarray, err: np.ndarray) -> float:
+    """C4 for fp32 outputs; returns the worst |g - y| / err."""
+    d = np.abs(np.asarray(g, dtype=np.float64) - y)
+    ok = d <= err
+    assert ok.all(), f"fp32 output off by more than the bound at {np.argwhere(~ok)[:4]}"
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(err > 0, d / err, 0.0)
+    return float(ratio.max()) if ratio.size else 0.0
+
+
+def proj_reference(h_bits: np.ndarray, weights_bits: Sequence[np.ndarray], n_idx_heads: int):
+    """Oracle projections of the tokens in h_bits and their C4 bounds."""
+    wq, wk, wc, ww = weights_bits
+    ref = oracle.project_tokens(h_bits, wq, wk, wc, ww, n_idx_heads)
+    h = oracle.decode_bf16(h_bits)
+    R = h.shape[0]
+    ref["err_q"] = proj_error_bound(h, oracle.decode_bf16(wq)).reshape(R, n_idx_heads, -1)
+    ref["err_k"] = proj_error_bound(h, oracle.decode_bf16(wk))
+    ref["err_c"] = proj_error_bound(h, oracle.decode_bf16(wc))
+    ref["err_w"] = proj_error_bound(h, oracle.decode_bf16(ww))
+    return ref

@@ -98,3 +98,35 @@ def test_workspace_sizes(m):
     f32 = m.dims_struct(m.Dims(4, 32, 16, 80, 64, 64, True))
     tiny = _rows(m, R=256, B=1, N=256, max_pos=255)
     assert L.dsa_sparse_mla_attn_workspace_size(ctypes.byref(tiny), ctypes.byref(f32)) == 0
+
+
+def test_project_append_host_checks(m):
+    L = m.lib
+    d = m.dims_struct(m.PRODUCTION_DIMS)
+    r = _rows(m, R=32, B=32, N=32768, max_pos=32767)
+    p = ctypes.c_void_p(16)
+    ptrs = [p] * 11
+    # d_model not a multiple of 64, too large, or zero
+    for dm in (0, 100, 65600):
+        assert L.dsa_project_append(ctypes.byref(r), ctypes.byref(d), dm, *ptrs, p, 1 << 30,
+                                    None) == m.DSA_E_UNSUPPORTED
+    # only the production indexer / latent dims have a kernel
+    f32 = m.dims_struct(m.Dims(4, 32, 16, 80, 64, 64, True))
+    assert L.dsa_project_append(ctypes.byref(r), ctypes.byref(f32), 7168, *ptrs, p, 1 << 30,
+                                None) == m.DSA_E_UNSUPPORTED
+    # a NULL output
+    bad = list(ptrs)
+    bad[9] = None
+    assert L.dsa_project_append(ctypes.byref(r), ctypes.byref(d), 7168, *bad, p, 1 << 30,
+                                None) == m.DSA_E_INVALID
+    # decode-sized calls split the contraction and need the partial-sum workspace
+    need = L.dsa_project_append_workspace_size(ctypes.byref(r), 7168)
+    assert need == 7 * 32 * 8960 * 4
+    assert L.dsa_project_append(ctypes.byref(r), ctypes.byref(d), 7168, *ptrs, p, need - 1,
+                                None) == m.DSA_E_WORKSPACE
+    # prefill-sized calls split nothing; zero rows do nothing
+    big = _rows(m, R=8192, B=1, N=8192, max_pos=8191)
+    assert L.dsa_project_append_workspace_size(ctypes.byref(big), 7168) == 0
+    empty = _rows(m, R=0, seq=None, pos=None)
+    assert L.dsa_project_append(ctypes.byref(empty), ctypes.byref(d), 7168, *([None] * 11), None,
+                                0, None) == m.DSA_OK
