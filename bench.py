@@ -36,6 +36,8 @@ TOPK_BYTES_PER_PAIR = 4           # one fp32 score read per (row, candidate)
 ATTN_BYTES_PER_ENTRY = 1152       # one gathered 576-wide bf16 latent row per (row, selected)
 ATTN_BYTES_PER_ROW = 128 * 576 * 2 + 128 * 512 * 2  # q in + out
 ATTN_FLOP_PER_ENTRY = 2 * 128 * (576 + 512)
+PROJ_COLS = 64 * 128 + 128 + 576 + 64   # projection outputs per token (q heads, k, latent, w)
+PROJ_OUT_BYTES = 64 * 128 + 64 * 4 + 64 * 4 + 128 + 4 + 576 * 2  # stored per token
 
 
 # Kernel sources whose digest ties a committed HBM-traffic measurement to the code
@@ -197,6 +199,57 @@ def time_workload(dsa, di, cfg, reps):
     return res
 
 
+def time_projection(dsa, di, pcfg, reps, sets=3):
+    """dsa_project_append on one projection workload: HIP events around each call on
+    the library's stream; weight sets rotate so the MALL cannot hold them."""
+    import torch
+
+    print(f"[bench] projections {pcfg.name}", file=sys.stderr, flush=True)
+    R, d = pcfg.num_tokens, pcfg.d_model
+    gens = [di.ProjGenerator(pcfg.cfg_id, d, s) for s in range(sets)]
+    W = [g.weights(device="cuda") for g in gens]
+    h = gens[0].h(0, R, device="cuda")
+    dev = torch.device("cuda")
+    k_idx = torch.zeros(pcfg.num_seqs, pcfg.max_ctx, 128, dtype=torch.uint8, device=dev)
+    k_scale = torch.zeros(pcfg.num_seqs, pcfg.max_ctx, dtype=torch.float32, device=dev)
+    latent = torch.zeros(pcfg.num_seqs, pcfg.max_ctx, 576, dtype=torch.bfloat16, device=dev)
+    seq, pos = pcfg.row_seq_pos()
+    rows = dsa.rows_struct(torch.from_numpy(seq).to(dev), torch.from_numpy(pos).to(dev),
+                           pcfg.num_seqs, pcfg.max_ctx, pcfg.max_ctx - 1)
+    q_idx = torch.empty(R, 64, 128, dtype=torch.uint8, device=dev)
+    q_scale = torch.empty(R, 64, dtype=torch.float32, device=dev)
+    w = torch.empty(R, 64, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(dsa.project_append_workspace_size(rows, d), 1), dtype=torch.uint8,
+                     device=dev)
+    run = lambda i: dsa.project_append(rows, h, *W[i % sets], k_idx, k_scale, latent, q_idx,
+                                       q_scale, w, workspace=ws)
+    for i in range(2 * sets):
+        run(i)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(reps):
+        run(i)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[reps]) / reps
+    s = ms * 1e-3
+    bytes_ = PROJ_COLS * d * 2 + R * d * 2 + R * PROJ_OUT_BYTES
+    flop = 2.0 * R * d * PROJ_COLS
+    res = {"ms": ms, "tokens": R, "d_model": d, "reps": reps, "weight_sets": sets,
+           "algorithmic_bytes": bytes_, "flop": flop, "gbs": bytes_ / s / 1e9,
+           "tflops": flop / s / 1e12}
+    if flop / bytes_ > BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3:
+        res["roofline"] = {"bound": "mfma", "achieved": res["tflops"], "peak": BF16_PEAK_TFLOPS,
+                           "unit": "TFLOP/s", "frac": res["tflops"] / BF16_PEAK_TFLOPS}
+    else:
+        res["roofline"] = {"bound": "hbm", "achieved": res["gbs"], "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": res["gbs"] / HBM_PEAK_GBS}
+    del W, h, k_idx, k_scale, latent, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(di, cfg, budget_s=20.0):
     """The float64 oracle on a bounded sample of the workload's rows, host cores."""
     import numpy as np
@@ -300,9 +353,12 @@ def main():
         "step_hbm_frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "kernels": kernels,
     }
+    del steps
+    torch.cuda.empty_cache()
+    # the step before the path: projections and cache append of the new tokens
+    line["projections"] = {name: time_projection(dsa, di, di.PROJ_CONFIGS[name], reps)
+                           for name, reps in (("proj_decode32", 30), ("proj_prefill8k", 10))}
     if args.extra:
-        del steps
-        torch.cuda.empty_cache()
         line["extra"] = {name: time_workload(dsa, di, di.CONFIGS[name], reps)
                          for name, reps in (("decode128k", 20), ("prefill8k", 5),
                                             ("prefill128k", 2))}

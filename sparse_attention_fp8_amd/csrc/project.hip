@@ -227,41 +227,45 @@ __global__ __launch_bounds__(NTH) void proj_gemm_kernel(ProjParams p) {
       ar[slot][i] = *reinterpret_cast<const i32x4*>(hrow[i] + (size_t)ch * KC);
   };
 
+  // The main loop body has no data-dependent branch, so the compiler's wait
+  // counts stay exact across iterations: a split of n chunks runs n / PD full
+  // groups, then up to PD - 1 chunks with guards.  Loads past the last chunk repeat
+  // it (cache hits; never consumed).
+  const int n = c1 - c0;  // >= 1 chunks in this split
+  const int groups = n / PD;
+  auto step = [&](int q, int j) {
+    const i32x4* ab = reinterpret_cast<const i32x4*>(abuf[j & 1]);
 #pragma unroll
-  for (int q = 0; q < PD; ++q)
-    if (c0 + q < c1) issue(q, c0 + q);
-  if (c0 < c1) {
+    for (int s = 0; s < 2; ++s)
 #pragma unroll
-    for (int i = 0; i < APT; ++i) reinterpret_cast<i32x4*>(abuf[0])[aslot[i]] = ar[0][i];
-  }
-  lds_barrier();
-
-  for (int c = c0; c < c1; c += PD) {
+      for (int mt = 0; mt < MT; ++mt) {
+        const int row = 16 * mt + ln;
+        const bf16x8 a = as_bf16x8(ab[row * 8 + ((4 * s + g) ^ (row & 7))]);
 #pragma unroll
-    for (int q = 0; q < PD; ++q) {
-      const int ch = c + q;
-      if (ch < c1) {
-        const i32x4* ab = reinterpret_cast<const i32x4*>(abuf[(ch - c0) & 1]);
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            const int row = 16 * mt + ln;
-            const bf16x8 a = as_bf16x8(ab[row * 8 + ((4 * s + g) ^ (row & 7))]);
-#pragma unroll
-            for (int ns = 0; ns < NS; ++ns)
-              acc[mt][ns] = mfma_bf16_16x16x32(a, as_bf16x8(wr[q][ns][s]), acc[mt][ns]);
-          }
-        if (ch + PD < c1) issue(q, ch + PD);
-        if (ch + 1 < c1) {
-          i32x4* nb = reinterpret_cast<i32x4*>(abuf[(ch + 1 - c0) & 1]);
-#pragma unroll
-          for (int i = 0; i < APT; ++i) nb[aslot[i]] = ar[(q + 1) % PD][i];
-          lds_barrier();
-        }
+        for (int ns = 0; ns < NS; ++ns)
+          acc[mt][ns] = mfma_bf16_16x16x32(a, as_bf16x8(wr[q][ns][s]), acc[mt][ns]);
       }
-    }
+    issue(q, c0 + min(j + PD, n - 1));
+    // keep the new loads ahead of the LDS stores below, so that waiting for the
+    // next h tile leaves them in flight
+    asm volatile("" ::: "memory");
+    i32x4* nb = reinterpret_cast<i32x4*>(abuf[(j + 1) & 1]);
+#pragma unroll
+    for (int i = 0; i < APT; ++i) nb[aslot[i]] = ar[(q + 1) % PD][i];
+    lds_barrier();
+  };
+#pragma unroll
+  for (int q = 0; q < PD; ++q) issue(q, c0 + min(q, n - 1));
+#pragma unroll
+  for (int i = 0; i < APT; ++i) reinterpret_cast<i32x4*>(abuf[0])[aslot[i]] = ar[0][i];
+  lds_barrier();
+  for (int gi = 0; gi < groups; ++gi) {
+#pragma unroll
+    for (int q = 0; q < PD; ++q) step(q, gi * PD + q);
   }
+#pragma unroll
+  for (int q = 0; q + 1 < PD; ++q)
+    if (groups * PD + q < n) step(q, groups * PD + q);
 
   // epilogue, one 16-token slab at a time through LDS
   const int erow = tid >> 4, eseg = tid & 15;
