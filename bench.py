@@ -137,17 +137,23 @@ class Step:
 
 
 def time_steps(steps, K, W):
+    """Times K steps twice: once bare (the throughput: nothing but the three calls
+    per step), then with HIP events around each call (per-call durations; the
+    markers add a little time of their own)."""
     import torch
 
     for i in range(W):
         steps[i % len(steps)].run()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        steps[i % len(steps)].run(evs[i])
+        steps[i % len(steps)].run()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    for i in range(K):
+        steps[i % len(steps)].run(evs[i])
+    torch.cuda.synchronize()
     k_ms = [[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in evs]
     avg = [sum(x[j] for x in k_ms) / K for j in range(3)]
     return wall / K * 1e3, avg
