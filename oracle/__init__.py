@@ -13,6 +13,8 @@ from .dsa_oracle import (  # noqa: F401
     encode_e4m3fn,
     indexer_row,
     indexer_scores,
+    paged_append,
+    paged_view,
     pow2_scale,
     project,
     project_tokens,

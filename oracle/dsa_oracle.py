@@ -40,6 +40,12 @@ prose around the lost equation.  "nsmao report" means the page
    power-of-two fp32 scale, the head weights as fp32, and the latent entry as
    bf16 (round to nearest even).  RoPE is not applied.
 
+5. Paged ("dynamic") caches (nsmao report, "DSA principle": the serving path uses
+   a dynamic KV cache).  Reading: the per-sequence caches are views of a shared
+   pool of fixed-size pages through a block table: entry s of sequence b is entry
+   s mod P of pool page block_table[b][s div P].  Every step computes exactly what
+   it computes on the contiguous cache those views describe.
+
 Inputs are the exact byte images the GPU receives: e4m3fn codes with fp32 scales
 (dequantised value = decode(code) * scale), bf16 bit patterns, or plain fp32.  The
 oracle decodes them with its own decoders and computes every step in float64.
@@ -54,7 +60,7 @@ __all__ = [
     "decode_e4m3fn", "decode_bf16", "indexer_scores", "select_topk",
     "sparse_attention", "indexer_row", "attention_row", "dsa_row",
     "encode_e4m3fn", "encode_bf16", "pow2_scale", "quantize_e4m3fn", "project",
-    "project_tokens", "append_rows",
+    "project_tokens", "append_rows", "paged_view", "paged_append",
 ]
 
 
@@ -291,4 +297,36 @@ def append_rows(cache: np.ndarray, row_seq: np.ndarray, row_pos: np.ndarray,
     for r, (b, t) in enumerate(zip(np.asarray(row_seq), np.asarray(row_pos))):
         if 0 <= b < B and 0 <= t < N:
             out[b, t] = values[r]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# O6: paged caches
+# ---------------------------------------------------------------------------
+
+def paged_view(pool: np.ndarray, block_table: np.ndarray, page_size: int) -> np.ndarray:
+    """The per-sequence caches a page pool describes.
+
+    pool [num_pages, P, ...]; block_table [B, pages_per_seq] (pool page of each
+    logical page).  Returns cache [B, pages_per_seq * P, ...] with
+    cache[b, s] = pool[block_table[b, s // P], s % P].
+    """
+    pool = np.asarray(pool)
+    table = np.asarray(block_table)
+    if pool.shape[1] != page_size:
+        raise ValueError("pool pages must hold page_size entries")
+    B, pps = table.shape
+    return pool[table].reshape((B, pps * page_size) + pool.shape[2:])
+
+
+def paged_append(pool: np.ndarray, block_table: np.ndarray, page_size: int,
+                 row_seq: np.ndarray, row_pos: np.ndarray, values: np.ndarray) -> np.ndarray:
+    """Copy of the pool with values[r] stored at logical entry (row_seq[r],
+    row_pos[r]); rows outside [0, B) x [0, pages_per_seq * P) are skipped."""
+    out = np.array(pool, copy=True)
+    table = np.asarray(block_table)
+    B, pps = table.shape
+    for r, (b, t) in enumerate(zip(np.asarray(row_seq), np.asarray(row_pos))):
+        if 0 <= b < B and 0 <= t < pps * page_size:
+            out[table[b, t // page_size], t % page_size] = values[r]
     return out

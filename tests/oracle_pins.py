@@ -515,4 +515,43 @@ def pin_append_rows():
     assert np.array_equal(cache, np.arange(30).reshape(3, 5, 2))  # input untouched
 
 
+# ---------------------------------------------------------------- P7 paged caches
+
+def pin_paged_view_bruteforce():
+    """paged_view against a loop over every (sequence, entry), for a shuffled block
+    table; the identity table is a plain reshape of the pool."""
+    r = _rng(31)
+    P, B, pps = 4, 3, 5
+    pool = r.integers(0, 1000, size=(B * pps + 2, P, 3))
+    table = r.permutation(B * pps + 2)[: B * pps].reshape(B, pps)
+    got = O.paged_view(pool, table, P)
+    assert got.shape == (B, pps * P, 3)
+    for b in range(B):
+        for s in range(pps * P):
+            assert np.array_equal(got[b, s], pool[table[b, s // P], s % P])
+    ident = np.arange(B * pps).reshape(B, pps)
+    assert np.array_equal(O.paged_view(pool[: B * pps], ident, P),
+                          pool[: B * pps].reshape(B, pps * P, 3))
+
+
+def pin_paged_invariants():
+    """Moving pages around the pool with the table updated to match leaves every
+    sequence's cache unchanged; the paged append writes exactly the entry its
+    logical cache would get (compared with append_rows on the view)."""
+    r = _rng(32)
+    P, B, pps, npg = 8, 2, 3, 9
+    pool = r.standard_normal((npg, P, 4))
+    table = r.choice(npg, size=(B, pps), replace=False)
+    view = O.paged_view(pool, table, P)
+    perm = r.permutation(npg)            # page i moves to slot perm[i]
+    pool2 = np.empty_like(pool)
+    pool2[perm] = pool
+    assert np.array_equal(O.paged_view(pool2, perm[table], P), view)
+    seq = np.array([0, 1, 1, 2, 0])
+    pos = np.array([3, 23, 9, 0, 24])     # (2, 0) and (0, 24) are out of range
+    vals = r.standard_normal((5, 4))
+    got = O.paged_view(O.paged_append(pool, table, P, seq, pos, vals), table, P)
+    assert np.array_equal(got, O.append_rows(view, seq, pos, vals))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -9,7 +9,7 @@ import oracle_pins
 _orig = {name: getattr(O, name) for name in
          ["indexer_scores", "select_topk", "sparse_attention", "decode_e4m3fn",
           "decode_bf16", "indexer_row", "encode_e4m3fn", "encode_bf16", "pow2_scale",
-         "quantize_e4m3fn", "project", "project_tokens"]}
+         "quantize_e4m3fn", "project", "project_tokens", "paged_view", "paged_append"]}
 
 
 def _no_relu(q, w, k):
@@ -140,6 +140,27 @@ def _heads_interleaved(h_bits, wq_bits, wk_bits, wc_bits, ww_bits, n_idx_heads):
     return out
 
 
+def _paged_table_transposed(pool, block_table, page_size):
+    # entries taken page-major across sequences (table read in the wrong order)
+    t = np.asarray(block_table)
+    return _orig["paged_view"](pool, t.T.reshape(t.shape), page_size)
+
+
+def _paged_offset_swapped(pool, block_table, page_size):
+    pool = np.asarray(pool)
+    v = pool[np.asarray(block_table)]             # [B, pps, P, ...]
+    return np.swapaxes(v, 1, 2).reshape((v.shape[0], -1) + pool.shape[2:])
+
+
+def _paged_append_logical_index(pool, block_table, page_size, row_seq, row_pos, values):
+    # writes pool page s // P directly, ignoring the table
+    out = np.array(pool, copy=True)
+    for r, (b, t) in enumerate(zip(row_seq, row_pos)):
+        if 0 <= b < np.asarray(block_table).shape[0] and 0 <= t < np.asarray(block_table).shape[1] * page_size:
+            out[t // page_size, t % page_size] = values[r]
+    return out
+
+
 MUTANTS = [
     ("indexer_scores", _no_relu),
     ("indexer_scores", _relu_after_sum),
@@ -165,6 +186,9 @@ MUTANTS = [
     ("quantize_e4m3fn", _scale_per_tensor),
     ("project", _project_drops_last),
     ("project_tokens", _heads_interleaved),
+    ("paged_view", _paged_table_transposed),
+    ("paged_view", _paged_offset_swapped),
+    ("paged_append", _paged_append_logical_index),
 ]
 
 
