@@ -123,6 +123,33 @@ class Step:
         self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
         self.dsa = dsa
 
+    def make_paged(self, P=64, seed=0):
+        """Page pools holding this set's caches, pages scattered in a seeded order."""
+        import numpy as np
+        import torch
+
+        c, i = self.cfg, self.inp
+        B, N = c.num_seqs, c.max_ctx
+        pps = N // P
+        npg = B * pps
+        perm = torch.from_numpy(np.random.default_rng(seed).permutation(npg)).cuda()
+        self.table = perm.view(B, pps).to(torch.int32).contiguous()
+        self.k_pool = torch.empty(npg, P, c.idx_dim, dtype=torch.uint8, device="cuda")
+        self.ks_pool = torch.empty(npg, P, dtype=torch.float32, device="cuda")
+        self.lat_pool = torch.empty(npg, P, c.qk_dim, dtype=torch.bfloat16, device="cuda")
+        self.k_pool[perm] = i.k_idx.view(npg, P, c.idx_dim)
+        self.ks_pool[perm] = i.k_scale.view(npg, P)
+        self.lat_pool[perm] = i.latent.view(npg, P, c.qk_dim)
+        self.pages = self.dsa.pages_struct(self.table, P, npg)
+
+    def run_paged(self):
+        d, i = self.dsa, self.inp
+        d.indexer_scores_paged(self.rows, self.dims, self.pages, i.q_idx, i.q_scale, i.w,
+                               self.k_pool, self.ks_pool, scores=self.scores)
+        d.topk(self.rows, self.cfg.topk, self.scores, indices=self.idx)
+        d.sparse_mla_attn_paged(self.rows, self.dims, self.pages, i.q, self.lat_pool, self.idx,
+                                self.cfg.scale, out=self.out, lse=self.lse, workspace=self.ws)
+
     def run(self, ev=None):
         d, i = self.dsa, self.inp
         if ev: ev[0].record()
@@ -359,6 +386,20 @@ def main():
         "step_hbm_frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "kernels": kernels,
     }
+    # the same step over paged caches (64-entry pages in shuffled order)
+    P = 64
+    for k, st in enumerate(steps):
+        st.make_paged(P, seed=k)
+    for i in range(args.warmup):
+        steps[i % len(steps)].run_paged()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        steps[i % len(steps)].run_paged()
+    torch.cuda.synchronize()
+    pms = (time.perf_counter() - t0) / args.steps * 1e3
+    line["paged"] = {"page_size": P, "ms_per_step": pms, "tokens_per_s": R / (pms * 1e-3),
+                     "vs_contiguous": ms / pms}
     del steps
     torch.cuda.empty_cache()
     # the step before the path: projections and cache append of the new tokens

@@ -202,6 +202,57 @@ dsa_status dsa_project_append(const dsa_rows* rows, const dsa_dims* dims, int32_
                               void* k_idx, float* k_scale, void* latent, void* workspace,
                               size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Paged ("dynamic") caches.  The serving path keeps its KV caches dynamic
+ * ("DeepSeek-V3.2开源技术报告", "DSA principle": optimised kernels with a dynamic KV
+ * cache); here that is a pool of fixed-size pages seen through a block table.
+ * Entry s of sequence b is entry s % P of pool page block_table[b * pages_per_seq
+ * + s / P], for the indexer-key pool, its scale pool and the latent pool alike
+ * (one table for all three).  The _paged calls compute exactly what their
+ * contiguous forms compute on the caches these views describe; workspace sizes
+ * are those of the contiguous forms.
+ *   - Production dims only; page_size a power of two in [64, 65536];
+ *     rows->max_ctx must equal pages_per_seq * page_size; each pool < 4 GiB.
+ *   - Pools: k_pool [num_pages, P, d_I] fp8 codes, k_scale_pool [num_pages, P] fp32,
+ *     latent_pool [num_pages, P, D_k] bf16.
+ *   - block_table entries outside [0, num_pages) are read as page 0 (the result is
+ *     unspecified; nothing outside the pools is accessed).
+ * ------------------------------------------------------------------------- */
+typedef struct dsa_pages {
+  int32_t page_size;          /* P: entries per page */
+  int32_t pages_per_seq;      /* columns of block_table */
+  int32_t num_pages;          /* pages in each pool */
+  const int32_t* block_table; /* device [B, pages_per_seq] */
+} dsa_pages;
+
+dsa_status dsa_indexer_scores_paged(const dsa_rows* rows, const dsa_dims* dims,
+                                    const dsa_pages* pages, const void* q_idx,
+                                    const float* q_scale, const float* w, const void* k_pool,
+                                    const float* k_scale_pool, float* scores, int64_t ld_scores,
+                                    void* stream);
+
+dsa_status dsa_sparse_mla_attn_paged(const dsa_rows* rows, const dsa_dims* dims,
+                                     const dsa_pages* pages, const void* q,
+                                     const void* latent_pool, const int32_t* indices,
+                                     float softmax_scale, void* out, float* lse, void* workspace,
+                                     size_t ws_bytes, void* stream);
+
+dsa_status dsa_forward_paged(const dsa_rows* rows, const dsa_dims* dims, const dsa_pages* pages,
+                             const void* q_idx, const float* q_scale, const float* w,
+                             const void* k_pool, const float* k_scale_pool, const void* q,
+                             const void* latent_pool, float softmax_scale, void* out, float* lse,
+                             int32_t* indices_out, int32_t chunk_rows, void* workspace,
+                             size_t ws_bytes, void* stream);
+
+/* Step 0 into paged caches: the appended indexer key, its scale and the latent
+ * entry of row r go to logical entry (row_seq[r], row_pos[r]) of the pools. */
+dsa_status dsa_project_append_paged(const dsa_rows* rows, const dsa_dims* dims,
+                                    const dsa_pages* pages, int32_t d_model, const void* h,
+                                    const void* w_q, const void* w_k, const void* w_c,
+                                    const void* w_w, void* q_idx, float* q_scale, float* w,
+                                    void* k_pool, float* k_scale_pool, void* latent_pool,
+                                    void* workspace, size_t ws_bytes, void* stream);
+
 /* Status text, and the detail of the last failure on the calling thread. */
 const char* dsa_status_string(dsa_status status);
 const char* dsa_last_error(void);

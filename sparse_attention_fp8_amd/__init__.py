@@ -18,7 +18,8 @@ __all__ = [
     "LIB_PATH", "lib", "Dims", "PRODUCTION_DIMS", "rows_struct", "dims_struct",
     "indexer_scores", "topk", "sparse_mla_attn", "forward", "forward_workspace_size",
     "sparse_mla_attn_workspace_size", "project_append", "project_append_workspace_size",
-    "DSAError", "EXPORTED_SYMBOLS",
+    "pages_struct", "indexer_scores_paged", "sparse_mla_attn_paged", "forward_paged",
+    "project_append_paged", "DSAError", "EXPORTED_SYMBOLS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
@@ -29,7 +30,8 @@ DSA_F32, DSA_BF16, DSA_FP8_E4M3FN = range(3)
 EXPORTED_SYMBOLS = [
     "dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_attn_workspace_size",
     "dsa_sparse_mla_attn", "dsa_forward_workspace_size", "dsa_forward",
-    "dsa_project_append_workspace_size", "dsa_project_append",
+    "dsa_project_append_workspace_size", "dsa_project_append", "dsa_indexer_scores_paged",
+    "dsa_sparse_mla_attn_paged", "dsa_forward_paged", "dsa_project_append_paged",
     "dsa_status_string", "dsa_last_error", "dsa_api_version",
 ]
 
@@ -53,6 +55,11 @@ class _Dims(ctypes.Structure):
                 ("idx_dtype", ctypes.c_int32), ("attn_dtype", ctypes.c_int32)]
 
 
+class _Pages(ctypes.Structure):
+    _fields_ = [("page_size", ctypes.c_int32), ("pages_per_seq", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32), ("block_table", ctypes.c_void_p)]
+
+
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
@@ -72,8 +79,15 @@ def _load() -> ctypes.CDLL:
     L.dsa_project_append_workspace_size.argtypes = [R, i32]
     L.dsa_project_append_workspace_size.restype = sz
     L.dsa_project_append.argtypes = [R, D, i32] + [vp] * 12 + [sz, vp]
+    PG = ctypes.POINTER(_Pages)
+    L.dsa_indexer_scores_paged.argtypes = [R, D, PG, vp, vp, vp, vp, vp, vp, i64, vp]
+    L.dsa_sparse_mla_attn_paged.argtypes = [R, D, PG, vp, vp, vp, f32, vp, vp, vp, sz, vp]
+    L.dsa_forward_paged.argtypes = [R, D, PG, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, i32,
+                                    vp, sz, vp]
+    L.dsa_project_append_paged.argtypes = [R, D, PG, i32] + [vp] * 12 + [sz, vp]
     for name in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_attn", "dsa_forward",
-                 "dsa_project_append"):
+                 "dsa_project_append", "dsa_indexer_scores_paged", "dsa_sparse_mla_attn_paged",
+                 "dsa_forward_paged", "dsa_project_append_paged"):
         getattr(L, name).restype = ctypes.c_int
     L.dsa_status_string.argtypes = [ctypes.c_int]
     L.dsa_status_string.restype = ctypes.c_char_p
@@ -326,4 +340,155 @@ def project_append(rows: _Rows, h, w_q, w_k, w_c, w_w, k_idx, k_scale, latent,
                                   _ptr(w_q), _ptr(w_k), _ptr(w_c), _ptr(w_w), _ptr(q_idx),
                                   _ptr(q_scale), _ptr(w), _ptr(k_idx), _ptr(k_scale),
                                   _ptr(latent), _ptr(workspace), ws_bytes, _stream()))
+    return q_idx, q_scale, w
+
+
+# ---------------------------------------------------------------- paged caches
+
+def pages_struct(block_table: torch.Tensor, page_size: int, num_pages: int) -> _Pages:
+    """dsa_pages for a device block table [B, pages_per_seq] int32 (kept alive by
+    the struct)."""
+    _dev(block_table, torch.int32, "block_table")
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [B, pages_per_seq]")
+    ps = _Pages(int(page_size), block_table.shape[1], int(num_pages), _ptr(block_table))
+    ps._keep = block_table
+    return ps
+
+
+def _pools(pages: _Pages, dims: Dims, k_pool=None, k_scale_pool=None, latent_pool=None):
+    P, n = pages.page_size, pages.num_pages
+    _shape(k_pool, (n, P, dims.idx_dim), "k_pool")
+    _shape(k_scale_pool, (n, P), "k_scale_pool")
+    _shape(latent_pool, (n, P, dims.qk_dim), "latent_pool")
+
+
+def indexer_scores_paged(rows: _Rows, dims: Dims, pages: _Pages, q_idx, q_scale, w, k_pool,
+                         k_scale_pool, scores: Optional[torch.Tensor] = None,
+                         ld: Optional[int] = None) -> torch.Tensor:
+    """dsa_indexer_scores_paged: scores [R, ld] from paged key / scale pools."""
+    for t, dt, name in ((q_idx, torch.uint8, "q_idx"), (k_pool, torch.uint8, "k_pool"),
+                        (w, torch.float32, "w"), (q_scale, torch.float32, "q_scale"),
+                        (k_scale_pool, torch.float32, "k_scale_pool")):
+        _dev(t, dt, name)
+    R = rows.num_rows
+    _shape(q_idx, (R, dims.n_idx_heads, dims.idx_dim), "q_idx")
+    _shape(q_scale, (R, dims.n_idx_heads), "q_scale")
+    _shape(w, (R, dims.n_idx_heads), "w")
+    _pools(pages, dims, k_pool, k_scale_pool)
+    if scores is None:
+        ld = ld or rows.max_pos + 1
+        scores = torch.empty(R, ld, dtype=torch.float32, device=q_idx.device)
+    _dev(scores, torch.float32, "scores")
+    _shape(scores, (R, None), "scores")
+    ds = dims_struct(dims)
+    _check(lib.dsa_indexer_scores_paged(ctypes.byref(rows), ctypes.byref(ds), ctypes.byref(pages),
+                                        _ptr(q_idx), _ptr(q_scale), _ptr(w), _ptr(k_pool),
+                                        _ptr(k_scale_pool), _ptr(scores), scores.shape[1],
+                                        _stream()))
+    return scores
+
+
+def sparse_mla_attn_paged(rows: _Rows, dims: Dims, pages: _Pages, q, latent_pool, indices,
+                          softmax_scale: float, out: Optional[torch.Tensor] = None,
+                          lse: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None):
+    """dsa_sparse_mla_attn_paged: (out, lse) from a paged latent pool."""
+    _dev(q, torch.bfloat16, "q")
+    _dev(latent_pool, torch.bfloat16, "latent_pool")
+    _dev(indices, torch.int32, "indices")
+    R = rows.num_rows
+    if out is None:
+        out = torch.empty(R, dims.n_heads, dims.v_dim, dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty(R, dims.n_heads, dtype=torch.float32, device=q.device)
+    _dev(out, torch.bfloat16, "out")
+    _dev(lse, torch.float32, "lse")
+    _shape(q, (R, dims.n_heads, dims.qk_dim), "q")
+    _shape(indices, (R, dims.topk), "indices")
+    _shape(out, (R, dims.n_heads, dims.v_dim), "out")
+    _pools(pages, dims, latent_pool=latent_pool)
+    need = sparse_mla_attn_workspace_size(rows, dims)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    ds = dims_struct(dims)
+    _check(lib.dsa_sparse_mla_attn_paged(ctypes.byref(rows), ctypes.byref(ds), ctypes.byref(pages),
+                                         _ptr(q), _ptr(latent_pool), _ptr(indices),
+                                         float(softmax_scale), _ptr(out), _ptr(lse),
+                                         _ptr(workspace), ws_bytes, _stream()))
+    return out, lse
+
+
+def forward_paged(rows: _Rows, dims: Dims, pages: _Pages, q_idx, q_scale, w, k_pool,
+                  k_scale_pool, q, latent_pool, softmax_scale: float, out=None, lse=None,
+                  indices_out=None, chunk_rows: int = 0,
+                  workspace: Optional[torch.Tensor] = None):
+    """dsa_forward_paged: the whole path over paged caches; (out, lse, indices_out)."""
+    for t, dt, name in ((q_idx, torch.uint8, "q_idx"), (k_pool, torch.uint8, "k_pool"),
+                        (w, torch.float32, "w"), (q_scale, torch.float32, "q_scale"),
+                        (k_scale_pool, torch.float32, "k_scale_pool"), (q, torch.bfloat16, "q"),
+                        (latent_pool, torch.bfloat16, "latent_pool")):
+        _dev(t, dt, name)
+    R = rows.num_rows
+    if out is None:
+        out = torch.empty(R, dims.n_heads, dims.v_dim, dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty(R, dims.n_heads, dtype=torch.float32, device=q.device)
+    _dev(out, torch.bfloat16, "out")
+    _dev(lse, torch.float32, "lse")
+    _dev(indices_out, torch.int32, "indices_out")
+    _shape(q_idx, (R, dims.n_idx_heads, dims.idx_dim), "q_idx")
+    _shape(q_scale, (R, dims.n_idx_heads), "q_scale")
+    _shape(w, (R, dims.n_idx_heads), "w")
+    _shape(q, (R, dims.n_heads, dims.qk_dim), "q")
+    _shape(out, (R, dims.n_heads, dims.v_dim), "out")
+    _shape(indices_out, (R, dims.topk), "indices_out")
+    _pools(pages, dims, k_pool, k_scale_pool, latent_pool)
+    need = forward_workspace_size(rows, dims, chunk_rows)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _dev(workspace, torch.uint8, "workspace")
+    ds = dims_struct(dims)
+    _check(lib.dsa_forward_paged(ctypes.byref(rows), ctypes.byref(ds), ctypes.byref(pages),
+                                 _ptr(q_idx), _ptr(q_scale), _ptr(w), _ptr(k_pool),
+                                 _ptr(k_scale_pool), _ptr(q), _ptr(latent_pool),
+                                 float(softmax_scale), _ptr(out), _ptr(lse), _ptr(indices_out),
+                                 int(chunk_rows), _ptr(workspace), workspace.numel(), _stream()))
+    return out, lse, indices_out
+
+
+def project_append_paged(rows: _Rows, pages: _Pages, h, w_q, w_k, w_c, w_w, k_pool,
+                         k_scale_pool, latent_pool, q_idx=None, q_scale=None, w=None,
+                         dims: Dims = PRODUCTION_DIMS, workspace: Optional[torch.Tensor] = None):
+    """dsa_project_append_paged: as project_append, appending into paged pools."""
+    R, d_model = h.shape[0], h.shape[-1]
+    _dev(h, torch.bfloat16, "h")
+    for t, name in ((w_q, "w_q"), (w_k, "w_k"), (w_c, "w_c"), (w_w, "w_w")):
+        _dev(t, torch.bfloat16, name)
+    _shape(h, (R, None), "h")
+    _shape(w_q, (dims.n_idx_heads * dims.idx_dim, d_model), "w_q")
+    _shape(w_k, (dims.idx_dim, d_model), "w_k")
+    _shape(w_c, (dims.qk_dim, d_model), "w_c")
+    _shape(w_w, (dims.n_idx_heads, d_model), "w_w")
+    if q_idx is None:
+        q_idx = torch.empty(R, dims.n_idx_heads, dims.idx_dim, dtype=torch.uint8, device=h.device)
+    if q_scale is None:
+        q_scale = torch.empty(R, dims.n_idx_heads, dtype=torch.float32, device=h.device)
+    if w is None:
+        w = torch.empty(R, dims.n_idx_heads, dtype=torch.float32, device=h.device)
+    _dev(k_pool, torch.uint8, "k_pool")
+    _dev(k_scale_pool, torch.float32, "k_scale_pool")
+    _dev(latent_pool, torch.bfloat16, "latent_pool")
+    _pools(pages, dims, k_pool, k_scale_pool, latent_pool)
+    need = project_append_workspace_size(rows, d_model)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=h.device)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    ds = dims_struct(dims)
+    _check(lib.dsa_project_append_paged(ctypes.byref(rows), ctypes.byref(ds), ctypes.byref(pages),
+                                        int(d_model), _ptr(h), _ptr(w_q), _ptr(w_k), _ptr(w_c),
+                                        _ptr(w_w), _ptr(q_idx), _ptr(q_scale), _ptr(w),
+                                        _ptr(k_pool), _ptr(k_scale_pool), _ptr(latent_pool),
+                                        _ptr(workspace), ws_bytes, _stream()))
     return q_idx, q_scale, w

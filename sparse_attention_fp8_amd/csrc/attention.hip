@@ -101,12 +101,13 @@ __device__ __forceinline__ i32x2 ds_read_tr16(const uint8_t* p) {
   return __builtin_bit_cast(i32x2, v);
 }
 
+template <bool PAGED>
 __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ latent,
     const int32_t* __restrict__ indices, const int32_t* __restrict__ row_seq,
     const int32_t* __restrict__ row_pos, int R, int B, int N, int topk, int splits,
     float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
-    uint16_t* __restrict__ o_part, float* __restrict__ lse_part) {
+    uint16_t* __restrict__ o_part, float* __restrict__ lse_part, PageMap pm) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
   __shared__ __attribute__((aligned(16))) float xbuf[NWAVE][16][64];  // S partials
   __shared__ int sidx[kTopk];
@@ -129,8 +130,15 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
   const int ES = topk / splits;  // positions of this split
   const int nblk = ES / BE;
   const int32_t* irow = indices + (size_t)r * topk + (size_t)sp * ES;
-  const uint16_t* lat = latent + (size_t)b * N * DK;
+  // paged: offsets from the pool base (pool rows from the block table); contiguous:
+  // from this sequence's cache
+  const uint16_t* lat = PAGED ? latent : latent + (size_t)b * N * DK;
   const uint8_t* lat_bytes = reinterpret_cast<const uint8_t*>(lat);
+  auto cache_row = [&](int p) -> int { return PAGED ? (int)paged_row(pm, b, p) : p; };
+  // Padding slots gather the sequence's own entry 0 (present, since t >= 0) and are
+  // then masked: a masked row still meets a zero softmax weight in the value
+  // product, so it must hold finite data, which an unused page need not.
+  const int row0 = cache_row(0);
 
   // Prologue, ordered so that three memory latencies do not add up: the first
   // block's gather positions are read straight from the index row, the rest of the
@@ -145,7 +153,8 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
     const int e = (P * 3641) >> 18;  // P / 72 for P < 2304
     const int c = kswz(e, P - e * KCH);
     const int p = nblk > 0 ? irow[e] : 0;
-    off_first[j] = __umul24((uint32_t)((p >= 0 && p < N) ? p : 0), (uint32_t)KROW) + (uint32_t)(16 * c);
+    off_first[j] = __umul24((uint32_t)((p >= 0 && p < N) ? cache_row(p) : row0), (uint32_t)KROW) +
+                   (uint32_t)(16 * c);
   }
   constexpr int IPT = kTopk / NT;  // selected positions per thread (at most)
   int pv[IPT];
@@ -185,7 +194,7 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
 #pragma unroll
   for (int k = 0; k < IPT; ++k) {
     const int i = tid + NT * k;
-    if (i < ES) sidx[i] = (pv[k] >= 0 && pv[k] < N) ? pv[k] : -1;
+    if (i < ES) sidx[i] = (pv[k] >= 0 && pv[k] < N) ? cache_row(pv[k]) : -1;
   }
 #pragma unroll
   for (int k = 0; k < QRC; ++k) {
@@ -216,9 +225,9 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
     const int e = (P * 3641) >> 18;  // P / 72 for P < 2304
     const int c = kswz(e, P - e * KCH);
     const int pos = sidx[blk * BE + e];
-    // 32-bit offset from the sequence base (a sequence's cache is < 4 GiB and
-    // positions are < 2^24)
-    return __umul24((uint32_t)(pos >= 0 ? pos : 0), (uint32_t)KROW) + (uint32_t)(16 * c);
+    // 32-bit offset from the sequence base or the pool base (a sequence's cache and
+    // a pool are < 4 GiB, so rows are < 2^24)
+    return __umul24((uint32_t)(pos >= 0 ? pos : row0), (uint32_t)KROW) + (uint32_t)(16 * c);
   };
   // The first MAXL - 1 offsets are computed before the barrier that frees the
   // buffer; the last load (waves 0..3 only) computes its own when it issues.
@@ -613,7 +622,7 @@ size_t attn_workspace_bytes(int num_rows, const dsa_dims& dims) {
 
 hipError_t launch_attn_bf16(const dsa_rows& rows, const void* q, const void* latent,
                             const int32_t* indices, float softmax_scale, void* out, float* lse,
-                            void* workspace, hipStream_t stream) {
+                            void* workspace, hipStream_t stream, const PageMap& pm) {
   const int R = rows.num_rows;
   const int S = attn_num_splits(R, kTopk);
   uint16_t* o_part = nullptr;
@@ -624,10 +633,11 @@ hipError_t launch_attn_bf16(const dsa_rows& rows, const void* q, const void* lat
   }
   const int row_groups = (R + 7) / 8;
   const float scale_log2 = softmax_scale * 1.44269504088896340736f;
-  hipLaunchKernelGGL(attn_bf16_kernel, dim3(row_groups * 8 * S), dim3(NT), 0, stream,
+  auto kern = pm.table != nullptr ? attn_bf16_kernel<true> : attn_bf16_kernel<false>;
+  hipLaunchKernelGGL(kern, dim3(row_groups * 8 * S), dim3(NT), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(latent), indices,
                      rows.row_seq, rows.row_pos, R, rows.num_seqs, rows.max_ctx, kTopk, S,
-                     scale_log2, static_cast<uint16_t*>(out), lse, o_part, lse_part);
+                     scale_log2, static_cast<uint16_t*>(out), lse, o_part, lse_part, pm);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || S == 1) return err;
   hipLaunchKernelGGL(attn_combine_kernel, dim3((R * H + CMB_RH - 1) / CMB_RH), dim3(CMB_T * CMB_RH),

@@ -64,15 +64,43 @@ dsa_status check_dims(const dsa_dims* dims) {
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
+// Paged caches: descriptor checks and the kernels' page map.  row_bytes is the
+// largest cache row a call addresses (32-bit offsets from a pool's base).
+dsa_status check_pages(const dsa_rows& rows, const dsa_dims& dims, const dsa_pages* pages,
+                       size_t row_bytes, dsa::PageMap* pm) {
+  if (pages == nullptr) return fail(DSA_E_INVALID, "pages is NULL");
+  if (!is_production(dims))
+    return fail(DSA_E_UNSUPPORTED, "paged caches need the production dims (fp8 indexer, bf16 latent)");
+  const int P = pages->page_size;
+  if (P < 64 || P > 65536 || (P & (P - 1)) != 0)
+    return fail(DSA_E_UNSUPPORTED, "page_size must be a power of two in [64, 65536]");
+  if (pages->pages_per_seq < 1 || pages->num_pages < 1 || pages->block_table == nullptr)
+    return fail(DSA_E_INVALID, "pages_per_seq and num_pages must be >= 1 and block_table set");
+  if ((int64_t)pages->pages_per_seq * P != rows.max_ctx)
+    return fail(DSA_E_INVALID, "max_ctx must equal pages_per_seq * page_size");
+  if ((uint64_t)pages->num_pages * (uint64_t)P * row_bytes > 0xFFFFFFFFull)
+    return fail(DSA_E_UNSUPPORTED, "a page pool must stay below 4 GiB");
+  pm->table = pages->block_table;
+  pm->pps = pages->pages_per_seq;
+  pm->shift = __builtin_ctz((unsigned)P);
+  pm->npages = pages->num_pages;
+  return DSA_OK;
+}
+
+constexpr size_t kKeyRow = dsa::kIdxDim;                  // fp8 indexer key
+constexpr size_t kLatentRow = dsa::kQkDim * sizeof(uint16_t);  // bf16 latent entry
+
 // --- step launchers shared by the public calls and dsa_forward -----------------
 
 dsa_status run_indexer(const dsa_rows& rows, const dsa_dims& dims, const void* q_idx,
                        const float* q_scale, const float* w, const void* k_idx,
-                       const float* k_scale, float* scores, int64_t ld, hipStream_t stream) {
+                       const float* k_scale, float* scores, int64_t ld, hipStream_t stream,
+                       const dsa::PageMap& pm) {
   hipError_t err;
   if (dims.idx_dtype == DSA_FP8_E4M3FN)
     err = dsa::launch_indexer_fp8(rows, static_cast<const uint8_t*>(q_idx), q_scale, w,
-                                  static_cast<const uint8_t*>(k_idx), k_scale, scores, ld, stream);
+                                  static_cast<const uint8_t*>(k_idx), k_scale, scores, ld, stream,
+                                  pm);
   else
     err = dsa::launch_indexer_f32(rows, dims, static_cast<const float*>(q_idx), w,
                                   static_cast<const float*>(k_idx), scores, ld, stream);
@@ -87,10 +115,10 @@ dsa_status run_topk(const dsa_rows& rows, int topk, const float* scores, int64_t
 
 dsa_status run_attn(const dsa_rows& rows, const dsa_dims& dims, const void* q,
                     const void* latent, const int32_t* indices, float scale, void* out,
-                    float* lse, void* ws, hipStream_t stream) {
+                    float* lse, void* ws, hipStream_t stream, const dsa::PageMap& pm) {
   hipError_t err;
   if (dims.attn_dtype == DSA_BF16)
-    err = dsa::launch_attn_bf16(rows, q, latent, indices, scale, out, lse, ws, stream);
+    err = dsa::launch_attn_bf16(rows, q, latent, indices, scale, out, lse, ws, stream, pm);
   else
     err = dsa::launch_attn_f32(rows, dims, static_cast<const float*>(q),
                                static_cast<const float*>(latent), indices, scale,
@@ -102,99 +130,17 @@ size_t elem_bytes(dsa_dtype t) { return t == DSA_FP8_E4M3FN ? 1 : (t == DSA_BF16
 
 int64_t scores_ld(const dsa_rows& rows) { return (int64_t)align_up((size_t)rows.max_pos + 1, 64); }
 
-}  // namespace
-
-extern "C" {
-
-int32_t dsa_api_version(void) { return DSA_API_VERSION; }
-
-const char* dsa_status_string(dsa_status status) {
-  switch (status) {
-    case DSA_OK: return "DSA_OK";
-    case DSA_E_INVALID: return "DSA_E_INVALID: invalid argument";
-    case DSA_E_UNSUPPORTED: return "DSA_E_UNSUPPORTED: unsupported dimensions or dtype";
-    case DSA_E_WORKSPACE: return "DSA_E_WORKSPACE: workspace missing or too small";
-    case DSA_E_HIP: return "DSA_E_HIP: HIP runtime error";
-  }
-  return "unknown dsa_status";
-}
-
-const char* dsa_last_error(void) { return g_last_error; }
-
-dsa_status dsa_indexer_scores(const dsa_rows* rows, const dsa_dims* dims, const void* q_idx,
-                              const float* q_scale, const float* w, const void* k_idx,
-                              const float* k_scale, float* scores, int64_t ld_scores,
-                              void* stream) {
+dsa_status forward_impl(const dsa_rows* rows, const dsa_dims* dims, const dsa_pages* pages,
+                        const void* q_idx, const float* q_scale, const float* w, const void* k_idx,
+                        const float* k_scale, const void* q, const void* latent,
+                        float softmax_scale, void* out, float* lse, int32_t* indices_out,
+                        int32_t chunk_rows, void* workspace, size_t ws_bytes, void* stream) {
   dsa_status st = check_rows(rows);
   if (st != DSA_OK) return st;
   if ((st = check_dims(dims)) != DSA_OK) return st;
-  if (rows->num_rows == 0) return DSA_OK;
-  if (!q_idx || !w || !k_idx || !scores) return fail(DSA_E_INVALID, "NULL tensor pointer");
-  if (dims->idx_dtype == DSA_FP8_E4M3FN && (!q_scale || !k_scale))
-    return fail(DSA_E_INVALID, "fp8 indexer needs q_scale and k_scale");
-  if (ld_scores < (int64_t)rows->max_pos + 1)
-    return fail(DSA_E_INVALID, "ld_scores < max_pos + 1");
-  return run_indexer(*rows, *dims, q_idx, q_scale, w, k_idx, k_scale, scores, ld_scores,
-                     as_stream(stream));
-}
-
-dsa_status dsa_topk(const dsa_rows* rows, int32_t topk, const float* scores, int64_t ld_scores,
-                    int32_t* indices, void* stream) {
-  dsa_status st = check_rows(rows);
-  if (st != DSA_OK) return st;
-  if (topk < 1 || topk > 4096) return fail(DSA_E_UNSUPPORTED, "topk must lie in [1, 4096]");
-  if (rows->num_rows == 0) return DSA_OK;
-  if (!scores || !indices) return fail(DSA_E_INVALID, "NULL tensor pointer");
-  if (ld_scores < (int64_t)rows->max_pos + 1)
-    return fail(DSA_E_INVALID, "ld_scores < max_pos + 1");
-  return run_topk(*rows, topk, scores, ld_scores, indices, as_stream(stream));
-}
-
-size_t dsa_sparse_mla_attn_workspace_size(const dsa_rows* rows, const dsa_dims* dims) {
-  if (check_rows(rows) != DSA_OK || check_dims(dims) != DSA_OK) return 0;
-  return dsa::attn_workspace_bytes(rows->num_rows, *dims);
-}
-
-dsa_status dsa_sparse_mla_attn(const dsa_rows* rows, const dsa_dims* dims, const void* q,
-                               const void* latent, const int32_t* indices, float softmax_scale,
-                               void* out, float* lse, void* workspace, size_t ws_bytes,
-                               void* stream) {
-  dsa_status st = check_rows(rows);
-  if (st != DSA_OK) return st;
-  if ((st = check_dims(dims)) != DSA_OK) return st;
-  if (rows->num_rows == 0) return DSA_OK;
-  if (!q || !latent || !indices || !out) return fail(DSA_E_INVALID, "NULL tensor pointer");
-  const size_t need = dsa::attn_workspace_bytes(rows->num_rows, *dims);
-  if (need > 0 && (workspace == nullptr || ws_bytes < need))
-    return fail(DSA_E_WORKSPACE, "attention needs %zu workspace bytes, got %zu", need, ws_bytes);
-  return run_attn(*rows, *dims, q, latent, indices, softmax_scale, out, lse, workspace,
-                  as_stream(stream));
-}
-
-size_t dsa_forward_workspace_size(const dsa_rows* rows, const dsa_dims* dims, int32_t chunk_rows) {
-  if (check_rows(rows) != DSA_OK || check_dims(dims) != DSA_OK || chunk_rows < 0) return 0;
-  const int R = rows->num_rows;
-  const int CH = (chunk_rows > 0 && chunk_rows < R) ? chunk_rows : R;
-  if (CH == 0) return 0;
-  const int64_t ld = scores_ld(*rows);
-  size_t bytes = align_up((size_t)CH * ld * sizeof(float), 256);
-  bytes += align_up((size_t)CH * dims->topk * sizeof(int32_t), 256);
-  // the last chunk may hold fewer rows and therefore use more attention splits
-  const int last = R - (R - 1) / CH * CH;
-  const size_t attn = dsa::attn_workspace_bytes(CH, *dims);
-  const size_t attn_last = dsa::attn_workspace_bytes(last, *dims);
-  bytes += align_up(attn > attn_last ? attn : attn_last, 256);
-  return bytes;
-}
-
-dsa_status dsa_forward(const dsa_rows* rows, const dsa_dims* dims, const void* q_idx,
-                       const float* q_scale, const float* w, const void* k_idx,
-                       const float* k_scale, const void* q, const void* latent,
-                       float softmax_scale, void* out, float* lse, int32_t* indices_out,
-                       int32_t chunk_rows, void* workspace, size_t ws_bytes, void* stream) {
-  dsa_status st = check_rows(rows);
-  if (st != DSA_OK) return st;
-  if ((st = check_dims(dims)) != DSA_OK) return st;
+  dsa::PageMap pm;
+  if (pages != nullptr && (st = check_pages(*rows, *dims, pages, kLatentRow, &pm)) != DSA_OK)
+    return st;
   if (chunk_rows < 0) return fail(DSA_E_INVALID, "chunk_rows < 0");
   const int R = rows->num_rows;
   if (R == 0) return DSA_OK;
@@ -230,28 +176,23 @@ dsa_status dsa_forward(const dsa_rows* rows, const dsa_dims* dims, const void* q
     int32_t* idx = indices_out ? indices_out + (size_t)r0 * dims->topk : idx_ws;
     st = run_indexer(sub, *dims, static_cast<const uint8_t*>(q_idx) + r0 * qi_row,
                      q_scale ? q_scale + r0 * hi : nullptr, w + r0 * hi, k_idx, k_scale, scores,
-                     ld, s);
+                     ld, s, pm);
     if (st != DSA_OK) return st;
     st = run_topk(sub, dims->topk, scores, ld, idx, s);
     if (st != DSA_OK) return st;
     st = run_attn(sub, *dims, static_cast<const uint8_t*>(q) + r0 * q_row, latent, idx,
                   softmax_scale, static_cast<uint8_t*>(out) + r0 * o_row,
-                  lse ? lse + (size_t)r0 * dims->n_heads : nullptr, attn_ws, s);
+                  lse ? lse + (size_t)r0 * dims->n_heads : nullptr, attn_ws, s, pm);
     if (st != DSA_OK) return st;
   }
   return DSA_OK;
 }
 
-size_t dsa_project_append_workspace_size(const dsa_rows* rows, int32_t d_model) {
-  if (check_rows(rows) != DSA_OK || d_model < 64 || d_model % 64 != 0) return 0;
-  return dsa::project_workspace_bytes(rows->num_rows, d_model);
-}
-
-dsa_status dsa_project_append(const dsa_rows* rows, const dsa_dims* dims, int32_t d_model,
-                              const void* h, const void* w_q, const void* w_k, const void* w_c,
-                              const void* w_w, void* q_idx, float* q_scale, float* w,
-                              void* k_idx, float* k_scale, void* latent, void* workspace,
-                              size_t ws_bytes, void* stream) {
+dsa_status project_impl(const dsa_rows* rows, const dsa_dims* dims, const dsa_pages* pages,
+                        int32_t d_model, const void* h, const void* w_q, const void* w_k,
+                        const void* w_c, const void* w_w, void* q_idx, float* q_scale, float* w,
+                        void* k_idx, float* k_scale, void* latent, void* workspace,
+                        size_t ws_bytes, void* stream) {
   dsa_status st = check_rows(rows);
   if (st != DSA_OK) return st;
   if (dims == nullptr) return fail(DSA_E_INVALID, "dims is NULL");
@@ -262,6 +203,14 @@ dsa_status dsa_project_append(const dsa_rows* rows, const dsa_dims* dims, int32_
                 "projections support H_I=64, d_I=128, D_k=576, fp8 indexer, bf16 latent only");
   if (d_model < 64 || d_model % 64 != 0 || d_model > 65536)
     return fail(DSA_E_UNSUPPORTED, "d_model must be a positive multiple of 64, at most 65536");
+  dsa::PageMap pm;
+  if (pages != nullptr) {
+    dsa_dims full = *dims;  // the paged check wants the whole production set
+    full.n_heads = dsa::kHeads;
+    full.v_dim = dsa::kVDim;
+    full.topk = dsa::kTopk;
+    if ((st = check_pages(*rows, full, pages, kLatentRow, &pm)) != DSA_OK) return st;
+  }
   if (rows->num_rows == 0) return DSA_OK;
   if (!h || !w_q || !w_k || !w_c || !w_w || !q_idx || !q_scale || !w || !k_idx || !k_scale ||
       !latent)
@@ -274,8 +223,178 @@ dsa_status dsa_project_append(const dsa_rows* rows, const dsa_dims* dims, int32_
       static_cast<const uint16_t*>(w_k), static_cast<const uint16_t*>(w_c),
       static_cast<const uint16_t*>(w_w), static_cast<uint8_t*>(q_idx), q_scale, w,
       static_cast<uint8_t*>(k_idx), k_scale, static_cast<uint16_t*>(latent), workspace,
-      as_stream(stream));
+      as_stream(stream), pm);
   return err == hipSuccess ? DSA_OK : hip_fail(err, "projection launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t dsa_api_version(void) { return DSA_API_VERSION; }
+
+const char* dsa_status_string(dsa_status status) {
+  switch (status) {
+    case DSA_OK: return "DSA_OK";
+    case DSA_E_INVALID: return "DSA_E_INVALID: invalid argument";
+    case DSA_E_UNSUPPORTED: return "DSA_E_UNSUPPORTED: unsupported dimensions or dtype";
+    case DSA_E_WORKSPACE: return "DSA_E_WORKSPACE: workspace missing or too small";
+    case DSA_E_HIP: return "DSA_E_HIP: HIP runtime error";
+  }
+  return "unknown dsa_status";
+}
+
+const char* dsa_last_error(void) { return g_last_error; }
+
+dsa_status dsa_indexer_scores(const dsa_rows* rows, const dsa_dims* dims, const void* q_idx,
+                              const float* q_scale, const float* w, const void* k_idx,
+                              const float* k_scale, float* scores, int64_t ld_scores,
+                              void* stream) {
+  dsa_status st = check_rows(rows);
+  if (st != DSA_OK) return st;
+  if ((st = check_dims(dims)) != DSA_OK) return st;
+  if (rows->num_rows == 0) return DSA_OK;
+  if (!q_idx || !w || !k_idx || !scores) return fail(DSA_E_INVALID, "NULL tensor pointer");
+  if (dims->idx_dtype == DSA_FP8_E4M3FN && (!q_scale || !k_scale))
+    return fail(DSA_E_INVALID, "fp8 indexer needs q_scale and k_scale");
+  if (ld_scores < (int64_t)rows->max_pos + 1)
+    return fail(DSA_E_INVALID, "ld_scores < max_pos + 1");
+  return run_indexer(*rows, *dims, q_idx, q_scale, w, k_idx, k_scale, scores, ld_scores,
+                     as_stream(stream), dsa::PageMap());
+}
+
+dsa_status dsa_topk(const dsa_rows* rows, int32_t topk, const float* scores, int64_t ld_scores,
+                    int32_t* indices, void* stream) {
+  dsa_status st = check_rows(rows);
+  if (st != DSA_OK) return st;
+  if (topk < 1 || topk > 4096) return fail(DSA_E_UNSUPPORTED, "topk must lie in [1, 4096]");
+  if (rows->num_rows == 0) return DSA_OK;
+  if (!scores || !indices) return fail(DSA_E_INVALID, "NULL tensor pointer");
+  if (ld_scores < (int64_t)rows->max_pos + 1)
+    return fail(DSA_E_INVALID, "ld_scores < max_pos + 1");
+  return run_topk(*rows, topk, scores, ld_scores, indices, as_stream(stream));
+}
+
+size_t dsa_sparse_mla_attn_workspace_size(const dsa_rows* rows, const dsa_dims* dims) {
+  if (check_rows(rows) != DSA_OK || check_dims(dims) != DSA_OK) return 0;
+  return dsa::attn_workspace_bytes(rows->num_rows, *dims);
+}
+
+dsa_status dsa_sparse_mla_attn(const dsa_rows* rows, const dsa_dims* dims, const void* q,
+                               const void* latent, const int32_t* indices, float softmax_scale,
+                               void* out, float* lse, void* workspace, size_t ws_bytes,
+                               void* stream) {
+  dsa_status st = check_rows(rows);
+  if (st != DSA_OK) return st;
+  if ((st = check_dims(dims)) != DSA_OK) return st;
+  if (rows->num_rows == 0) return DSA_OK;
+  if (!q || !latent || !indices || !out) return fail(DSA_E_INVALID, "NULL tensor pointer");
+  const size_t need = dsa::attn_workspace_bytes(rows->num_rows, *dims);
+  if (need > 0 && (workspace == nullptr || ws_bytes < need))
+    return fail(DSA_E_WORKSPACE, "attention needs %zu workspace bytes, got %zu", need, ws_bytes);
+  return run_attn(*rows, *dims, q, latent, indices, softmax_scale, out, lse, workspace,
+                  as_stream(stream), dsa::PageMap());
+}
+
+size_t dsa_forward_workspace_size(const dsa_rows* rows, const dsa_dims* dims, int32_t chunk_rows) {
+  if (check_rows(rows) != DSA_OK || check_dims(dims) != DSA_OK || chunk_rows < 0) return 0;
+  const int R = rows->num_rows;
+  const int CH = (chunk_rows > 0 && chunk_rows < R) ? chunk_rows : R;
+  if (CH == 0) return 0;
+  const int64_t ld = scores_ld(*rows);
+  size_t bytes = align_up((size_t)CH * ld * sizeof(float), 256);
+  bytes += align_up((size_t)CH * dims->topk * sizeof(int32_t), 256);
+  // the last chunk may hold fewer rows and therefore use more attention splits
+  const int last = R - (R - 1) / CH * CH;
+  const size_t attn = dsa::attn_workspace_bytes(CH, *dims);
+  const size_t attn_last = dsa::attn_workspace_bytes(last, *dims);
+  bytes += align_up(attn > attn_last ? attn : attn_last, 256);
+  return bytes;
+}
+
+dsa_status dsa_forward(const dsa_rows* rows, const dsa_dims* dims, const void* q_idx,
+                       const float* q_scale, const float* w, const void* k_idx,
+                       const float* k_scale, const void* q, const void* latent,
+                       float softmax_scale, void* out, float* lse, int32_t* indices_out,
+                       int32_t chunk_rows, void* workspace, size_t ws_bytes, void* stream) {
+  return forward_impl(rows, dims, nullptr, q_idx, q_scale, w, k_idx, k_scale, q, latent,
+                      softmax_scale, out, lse, indices_out, chunk_rows, workspace, ws_bytes,
+                      stream);
+}
+
+dsa_status dsa_forward_paged(const dsa_rows* rows, const dsa_dims* dims, const dsa_pages* pages,
+                             const void* q_idx, const float* q_scale, const float* w,
+                             const void* k_pool, const float* k_scale_pool, const void* q,
+                             const void* latent_pool, float softmax_scale, void* out, float* lse,
+                             int32_t* indices_out, int32_t chunk_rows, void* workspace,
+                             size_t ws_bytes, void* stream) {
+  if (pages == nullptr) return fail(DSA_E_INVALID, "pages is NULL");
+  return forward_impl(rows, dims, pages, q_idx, q_scale, w, k_pool, k_scale_pool, q,
+                      latent_pool, softmax_scale, out, lse, indices_out, chunk_rows, workspace,
+                      ws_bytes, stream);
+}
+
+dsa_status dsa_indexer_scores_paged(const dsa_rows* rows, const dsa_dims* dims,
+                                    const dsa_pages* pages, const void* q_idx,
+                                    const float* q_scale, const float* w, const void* k_pool,
+                                    const float* k_scale_pool, float* scores, int64_t ld_scores,
+                                    void* stream) {
+  dsa_status st = check_rows(rows);
+  if (st != DSA_OK) return st;
+  if ((st = check_dims(dims)) != DSA_OK) return st;
+  dsa::PageMap pm;
+  if ((st = check_pages(*rows, *dims, pages, kKeyRow, &pm)) != DSA_OK) return st;
+  if (rows->num_rows == 0) return DSA_OK;
+  if (!q_idx || !q_scale || !w || !k_pool || !k_scale_pool || !scores)
+    return fail(DSA_E_INVALID, "NULL tensor pointer");
+  if (ld_scores < (int64_t)rows->max_pos + 1)
+    return fail(DSA_E_INVALID, "ld_scores < max_pos + 1");
+  return run_indexer(*rows, *dims, q_idx, q_scale, w, k_pool, k_scale_pool, scores, ld_scores,
+                     as_stream(stream), pm);
+}
+
+dsa_status dsa_sparse_mla_attn_paged(const dsa_rows* rows, const dsa_dims* dims,
+                                     const dsa_pages* pages, const void* q,
+                                     const void* latent_pool, const int32_t* indices,
+                                     float softmax_scale, void* out, float* lse, void* workspace,
+                                     size_t ws_bytes, void* stream) {
+  dsa_status st = check_rows(rows);
+  if (st != DSA_OK) return st;
+  if ((st = check_dims(dims)) != DSA_OK) return st;
+  dsa::PageMap pm;
+  if ((st = check_pages(*rows, *dims, pages, kLatentRow, &pm)) != DSA_OK) return st;
+  if (rows->num_rows == 0) return DSA_OK;
+  if (!q || !latent_pool || !indices || !out) return fail(DSA_E_INVALID, "NULL tensor pointer");
+  const size_t need = dsa::attn_workspace_bytes(rows->num_rows, *dims);
+  if (need > 0 && (workspace == nullptr || ws_bytes < need))
+    return fail(DSA_E_WORKSPACE, "attention needs %zu workspace bytes, got %zu", need, ws_bytes);
+  return run_attn(*rows, *dims, q, latent_pool, indices, softmax_scale, out, lse, workspace,
+                  as_stream(stream), pm);
+}
+
+size_t dsa_project_append_workspace_size(const dsa_rows* rows, int32_t d_model) {
+  if (check_rows(rows) != DSA_OK || d_model < 64 || d_model % 64 != 0) return 0;
+  return dsa::project_workspace_bytes(rows->num_rows, d_model);
+}
+
+dsa_status dsa_project_append(const dsa_rows* rows, const dsa_dims* dims, int32_t d_model,
+                              const void* h, const void* w_q, const void* w_k, const void* w_c,
+                              const void* w_w, void* q_idx, float* q_scale, float* w,
+                              void* k_idx, float* k_scale, void* latent, void* workspace,
+                              size_t ws_bytes, void* stream) {
+  return project_impl(rows, dims, nullptr, d_model, h, w_q, w_k, w_c, w_w, q_idx, q_scale, w,
+                      k_idx, k_scale, latent, workspace, ws_bytes, stream);
+}
+
+dsa_status dsa_project_append_paged(const dsa_rows* rows, const dsa_dims* dims,
+                                    const dsa_pages* pages, int32_t d_model, const void* h,
+                                    const void* w_q, const void* w_k, const void* w_c,
+                                    const void* w_w, void* q_idx, float* q_scale, float* w,
+                                    void* k_pool, float* k_scale_pool, void* latent_pool,
+                                    void* workspace, size_t ws_bytes, void* stream) {
+  if (pages == nullptr) return fail(DSA_E_INVALID, "pages is NULL");
+  return project_impl(rows, dims, pages, d_model, h, w_q, w_k, w_c, w_w, q_idx, q_scale, w,
+                      k_pool, k_scale_pool, latent_pool, workspace, ws_bytes, stream);
 }
 
 }  // extern "C"

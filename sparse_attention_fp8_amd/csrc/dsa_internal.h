@@ -16,9 +16,29 @@ constexpr int kQkDim = 576;
 constexpr int kVDim = 512;
 constexpr int kTopk = 2048;
 
+// Location of cache entries.  table == nullptr: contiguous caches [B, N, ...], entry
+// (b, s) at row b * N + s.  Otherwise a page pool [npages, 1 << shift, ...] seen
+// through the block table [B, pps]: entry (b, s) at row
+// table[b * pps + (s >> shift)] * (1 << shift) + (s & ((1 << shift) - 1)); table
+// entries outside [0, npages) are read as page 0 (results unspecified, no fault).
+struct PageMap {
+  const int32_t* table = nullptr;
+  int pps = 0;
+  int shift = 0;
+  int npages = 0;
+};
+
+// pool row of entry s of sequence b (s < pps << shift)
+__host__ __device__ __forceinline__ uint32_t paged_row(const PageMap& pm, int b, int s) {
+  int pg = pm.table[(size_t)b * pm.pps + (s >> pm.shift)];
+  pg = (pg >= 0 && pg < pm.npages) ? pg : 0;
+  return ((uint32_t)pg << pm.shift) | (uint32_t)(s & ((1 << pm.shift) - 1));
+}
+
 hipError_t launch_indexer_fp8(const dsa_rows& rows, const uint8_t* q_idx, const float* q_scale,
                               const float* w, const uint8_t* k_idx, const float* k_scale,
-                              float* scores, int64_t ld, hipStream_t stream);
+                              float* scores, int64_t ld, hipStream_t stream,
+                              const PageMap& pm = PageMap());
 
 hipError_t launch_indexer_f32(const dsa_rows& rows, const dsa_dims& dims, const float* q_idx,
                               const float* w, const float* k_idx, float* scores, int64_t ld,
@@ -33,7 +53,7 @@ size_t attn_workspace_bytes(int num_rows, const dsa_dims& dims);
 
 hipError_t launch_attn_bf16(const dsa_rows& rows, const void* q, const void* latent,
                             const int32_t* indices, float softmax_scale, void* out, float* lse,
-                            void* workspace, hipStream_t stream);
+                            void* workspace, hipStream_t stream, const PageMap& pm = PageMap());
 
 hipError_t launch_attn_f32(const dsa_rows& rows, const dsa_dims& dims, const float* q,
                            const float* latent, const int32_t* indices, float softmax_scale,
@@ -44,6 +64,7 @@ size_t project_workspace_bytes(int num_rows, int d_model);
 hipError_t launch_project(const dsa_rows& rows, int d_model, const uint16_t* h, const uint16_t* wq,
                           const uint16_t* wk, const uint16_t* wc, const uint16_t* ww, uint8_t* q_idx,
                           float* q_scale, float* w, uint8_t* k_idx, float* k_scale,
-                          uint16_t* latent, void* workspace, hipStream_t stream);
+                          uint16_t* latent, void* workspace, hipStream_t stream,
+                          const PageMap& pm = PageMap());
 
 }  // namespace dsa

@@ -100,13 +100,13 @@ __device__ __forceinline__ void load_query(const uint8_t* __restrict__ q_idx,
 // use the sector-aligned split byte order.
 // Grid: num_rows * key_blocks blocks (row-major), WAVES waves each.
 // ---------------------------------------------------------------------------
-template <int WAVES, int KPB, int DEPTH>
+template <int WAVES, int KPB, int DEPTH, bool PAGED>
 __global__ __launch_bounds__(WAVES * 64) void indexer_fp8_decode_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale,
     const float* __restrict__ w, const uint8_t* __restrict__ k_idx,
     const float* __restrict__ k_scale, const int32_t* __restrict__ row_seq,
     const int32_t* __restrict__ row_pos, int B, int N, int nkb, float* __restrict__ scores,
-    int64_t ld) {
+    int64_t ld, PageMap pm) {
   const int r = blockIdx.x / nkb;
   const int kb0 = (blockIdx.x - r * nkb) * KPB;
   const int b = row_seq[r], t = row_pos[r];
@@ -121,15 +121,27 @@ __global__ __launch_bounds__(WAVES * 64) void indexer_fp8_decode_kernel(
   float wq[16];
   load_query<true>(q_idx, q_scale, w, r, qa, wq);
 
-  const uint8_t* kc = k_idx + (size_t)b * N * ID;
-  const float* ksc = k_scale + (size_t)b * N;
+  // paged: the pools; contiguous: this sequence's caches
+  const uint8_t* kc = PAGED ? k_idx : k_idx + (size_t)b * N * ID;
+  const float* ksc = PAGED ? k_scale : k_scale + (size_t)b * N;
   float* out = scores + (size_t)r * ld;
 
+  // k is a multiple of 64 and a page holds at least 64 entries, so a group's keys
+  // are consecutive rows of one page
   auto load_group = [&](int k, i32x8(&kb)[4], float& ks) {
+    if constexpr (PAGED) {
+      const uint32_t row0 = paged_row(pm, b, k);
+      const uint8_t* gb = kc + (size_t)row0 * ID;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-      kb[kt] = load_frag_split(kc + (size_t)min(k + 16 * kt + n, t) * ID, g);
-    ks = ksc[min(k + l, t)];
+      for (int kt = 0; kt < 4; ++kt)
+        kb[kt] = load_frag_split(gb + (size_t)(min(k + 16 * kt + n, t) - k) * ID, g);
+      ks = ksc[row0 + (min(k + l, t) - k)];
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+        kb[kt] = load_frag_split(kc + (size_t)min(k + 16 * kt + n, t) * ID, g);
+      ks = ksc[min(k + l, t)];
+    }
   };
   auto compute = [&](int k, const i32x8(&kb)[4], float ks) {
     const float p0 = head_partial(qa, wq, kb[0]);
@@ -164,25 +176,36 @@ __global__ __launch_bounds__(WAVES * 64) void indexer_fp8_decode_kernel(
 // L1/L2 serve.  Rows of a wave that belong to different sequences fall back to one
 // row at a time.  Grid: row_tiles * key_blocks blocks.
 // ---------------------------------------------------------------------------
-template <int NR>
+template <int NR, bool PAGED>
 __device__ __forceinline__ void prefill_rows(const uint8_t* __restrict__ q_idx,
                                              const float* __restrict__ q_scale,
                                              const float* __restrict__ w,
                                              const uint8_t* __restrict__ kc,
                                              const float* __restrict__ ksc, const int* rr,
                                              const int* tt, int kb0, int kend,
-                                             float* __restrict__ scores, int64_t ld) {
+                                             float* __restrict__ scores, int64_t ld,
+                                             const PageMap& pm, int b) {
   const int l = lane_id(), g = l >> 4, n = l & 15;
   i32x8 qa[NR][4];
   float wq[NR][16];
 #pragma unroll
   for (int i = 0; i < NR; ++i) load_query(q_idx, q_scale, w, rr[i], qa[i], wq[i]);
   const int klast = kend - 1;
+  // k is a multiple of 64: one page per group (see the decode kernel)
   auto load_group = [&](int k, i32x8(&kb)[4], float& ks) {
+    if constexpr (PAGED) {
+      const uint32_t row0 = paged_row(pm, b, k);
+      const uint8_t* gb = kc + (size_t)row0 * ID;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-      kb[kt] = load_frag32(kc + (size_t)min(k + 16 * kt + n, klast) * ID + 32 * g);
-    ks = ksc[min(k + l, klast)];
+      for (int kt = 0; kt < 4; ++kt)
+        kb[kt] = load_frag32(gb + (size_t)(min(k + 16 * kt + n, klast) - k) * ID + 32 * g);
+      ks = ksc[row0 + (min(k + l, klast) - k)];
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+        kb[kt] = load_frag32(kc + (size_t)min(k + 16 * kt + n, klast) * ID + 32 * g);
+      ks = ksc[min(k + l, klast)];
+    }
   };
   auto compute = [&](int k, const i32x8(&kb)[4], float ks) {
 #pragma unroll
@@ -254,13 +277,14 @@ constexpr int PGB = PG * ID;  // 16 KB per group
 static_assert(PGB == PW * 2048, "two 1 KB direct loads per wave and group");
 static_assert(PG == PW * 16, "16 key scales per wave and group");
 
+template <bool PAGED>
 __global__ __launch_bounds__(PW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void indexer_fp8_prefill_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale,
     const float* __restrict__ w, const uint8_t* __restrict__ k_idx,
     const float* __restrict__ k_scale, const int32_t* __restrict__ row_seq,
     const int32_t* __restrict__ row_pos, int R, int B, int N, int ksplit,
-    float* __restrict__ scores, int64_t ld) {
+    float* __restrict__ scores, int64_t ld, PageMap pm) {
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[PNBUF][PGB];
   __shared__ float ksbuf[PNBUF][PG];
   __shared__ __attribute__((aligned(16))) float sbuf[PROWS][PKPB];  // one key block's scores
@@ -314,15 +338,16 @@ void indexer_fp8_prefill_kernel(
       for (int i = 0; i < PRW; ++i) {
         if (tt[i] < kb0) continue;
         const int kend = min(kb0 + PKPB, tt[i] + 1);
-        prefill_rows<1>(q_idx, q_scale, w, k_idx + (size_t)bs[i] * N * ID,
-                        k_scale + (size_t)bs[i] * N, &rr[i], &tt[i], kb0, kend, scores, ld);
+        prefill_rows<1, PAGED>(q_idx, q_scale, w, PAGED ? k_idx : k_idx + (size_t)bs[i] * N * ID,
+                               PAGED ? k_scale : k_scale + (size_t)bs[i] * N, &rr[i], &tt[i],
+                               kb0, kend, scores, ld, pm, bs[i]);
       }
     }
     return;
   }
 
-  const uint8_t* kc = k_idx + (size_t)Bmin * N * ID;
-  const uint8_t* ksc = reinterpret_cast<const uint8_t*>(k_scale + (size_t)Bmin * N);
+  const uint8_t* kc = PAGED ? k_idx : k_idx + (size_t)Bmin * N * ID;
+  const uint8_t* ksc = reinterpret_cast<const uint8_t*>(PAGED ? k_scale : k_scale + (size_t)Bmin * N);
 
   i32x8 qa[PRW][4];
   float wq[PRW][16];
@@ -342,16 +367,29 @@ void indexer_fp8_prefill_kernel(
     // [128 wv, 128 wv + 128) of the keys and the scales of keys [16 wv, 16 wv + 16)
     auto issue_group = [&](int gi) {
       const int k0 = kb0 + gi * PG;
+      // paged: a group's keys lie in page k0 >> shift and (pages of 64) the next one
+      int p0 = 0;
+      uint32_t pg0 = 0, pg1 = 0;
+      if constexpr (PAGED) {
+        p0 = k0 >> pm.shift;
+        pg0 = paged_row(pm, Bmin, p0 << pm.shift) >> pm.shift;
+        pg1 = paged_row(pm, Bmin, min(p0 + 1, pm.pps - 1) << pm.shift) >> pm.shift;
+      }
+      auto row = [&](int key) -> uint32_t {
+        if constexpr (!PAGED) return (uint32_t)key;
+        const uint32_t pg = (key >> pm.shift) == p0 ? pg0 : pg1;
+        return (pg << pm.shift) | (uint32_t)(key & ((1 << pm.shift) - 1));
+      };
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int P = 64 * (2 * wv + h) + l;
         const int e = P >> 3;
         const int c = (P & 7) ^ (e & 7);
-        const uint32_t off = (uint32_t)min(k0 + e, klast) * (uint32_t)ID + (uint32_t)(16 * c);
+        const uint32_t off = row(min(k0 + e, klast)) * (uint32_t)ID + (uint32_t)(16 * c);
         lds_dma16(kc, off, lds_u32(&kbuf[gi % PNBUF][1024 * (2 * wv + h)]));
       }
       if (l < 16)
-        lds_dma4(ksc, (uint32_t)min(k0 + 16 * wv + l, klast) * 4u,
+        lds_dma4(ksc, row(min(k0 + 16 * wv + l, klast)) * 4u,
                  lds_u32(&ksbuf[gi % PNBUF][16 * wv]));
     };
     // every wave is past the previous key block's reads of kbuf and sbuf
@@ -498,7 +536,8 @@ __global__ __launch_bounds__(256) void indexer_f32_kernel(
 
 hipError_t launch_indexer_fp8(const dsa_rows& rows, const uint8_t* q_idx, const float* q_scale,
                               const float* w, const uint8_t* k_idx, const float* k_scale,
-                              float* scores, int64_t ld, hipStream_t stream) {
+                              float* scores, int64_t ld, hipStream_t stream, const PageMap& pm) {
+  const bool paged = pm.table != nullptr;
   const int R = rows.num_rows;
   const int L = rows.max_pos + 1;
   if (R >= 8 && R >= 4 * rows.num_seqs) {
@@ -508,15 +547,18 @@ hipError_t launch_indexer_fp8(const dsa_rows& rows, const uint8_t* q_idx, const 
     const int tiles = (R + PROWS - 1) / PROWS;
     int ksplit = 1;
     while (ksplit < nkb && (int64_t)tiles * ksplit < 2048) ksplit <<= 1;
-    hipLaunchKernelGGL(indexer_fp8_prefill_kernel, dim3(tiles * ksplit), dim3(PW * 64), 0,
-                       stream, q_idx, q_scale, w, k_idx, k_scale, rows.row_seq, rows.row_pos, R,
-                       rows.num_seqs, rows.max_ctx, ksplit, scores, ld);
+    auto kern = paged ? indexer_fp8_prefill_kernel<true> : indexer_fp8_prefill_kernel<false>;
+    hipLaunchKernelGGL(kern, dim3(tiles * ksplit), dim3(PW * 64), 0, stream, q_idx, q_scale, w,
+                       k_idx, k_scale, rows.row_seq, rows.row_pos, R, rows.num_seqs,
+                       rows.max_ctx, ksplit, scores, ld, pm);
   } else {
     constexpr int WAVES = 4, KPB = 1024, DEPTH = 3;
     const int nkb = (L + KPB - 1) / KPB;
-    hipLaunchKernelGGL((indexer_fp8_decode_kernel<WAVES, KPB, DEPTH>), dim3(R * nkb), dim3(WAVES * 64),
-                       0, stream, q_idx, q_scale, w, k_idx, k_scale, rows.row_seq, rows.row_pos,
-                       rows.num_seqs, rows.max_ctx, nkb, scores, ld);
+    auto kern = paged ? indexer_fp8_decode_kernel<WAVES, KPB, DEPTH, true>
+                      : indexer_fp8_decode_kernel<WAVES, KPB, DEPTH, false>;
+    hipLaunchKernelGGL(kern, dim3(R * nkb), dim3(WAVES * 64), 0, stream, q_idx, q_scale, w,
+                       k_idx, k_scale, rows.row_seq, rows.row_pos, rows.num_seqs, rows.max_ctx,
+                       nkb, scores, ld, pm);
   }
   return hipGetLastError();
 }

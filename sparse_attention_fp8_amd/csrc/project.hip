@@ -55,7 +55,15 @@ struct ProjParams {
   uint16_t* latent;
   float* part;  // [ksplit][R][kCols] partial sums (split contraction only)
   int ksplit;
+  PageMap pm;   // cache rows: contiguous (table == nullptr) or a page pool
 };
+
+// cache row of token r, or -1 when its (sequence, position) is out of range
+__device__ __forceinline__ int64_t cache_row(const ProjParams& p, int r) {
+  const int b = p.row_seq[r], t = p.row_pos[r];
+  if (b < 0 || b >= p.B || t < 0 || t >= p.N) return -1;
+  return p.pm.table != nullptr ? (int64_t)paged_row(p.pm, b, t) : (int64_t)b * p.N + t;
+}
 
 __device__ __forceinline__ const uint16_t* weight_row(const ProjParams& p, int col) {
   const uint16_t* base;
@@ -139,10 +147,9 @@ __device__ __forceinline__ void finish(const ProjParams& p, const float (&v)[V],
       dst = p.q_idx + (size_t)r * kColK + col;
       sdst = p.q_scale + (size_t)r * kIdxHeads + col / kIdxDim;
     } else {
-      const int b = p.row_seq[r], t = p.row_pos[r];
-      if (b < 0 || b >= p.B || t < 0 || t >= p.N) return;
-      const size_t row = (size_t)b * p.N + t;
-      dst = p.k_idx + row * kIdxDim + (col - kColK);
+      const int64_t row = cache_row(p, r);
+      if (row < 0) return;
+      dst = p.k_idx + (size_t)row * kIdxDim + (col - kColK);
       sdst = p.k_scale + row;
     }
     if constexpr (V == 16) {
@@ -152,9 +159,9 @@ __device__ __forceinline__ void finish(const ProjParams& p, const float (&v)[V],
     }
     if ((col & (kIdxDim - 1)) == 0) *sdst = scale;
   } else if (col < kColW) {  // latent entry: bf16 into the cache row
-    const int b = p.row_seq[r], t = p.row_pos[r];
-    if (b < 0 || b >= p.B || t < 0 || t >= p.N) return;
-    uint16_t* dst = p.latent + ((size_t)b * p.N + t) * kQkDim + (col - kColC);
+    const int64_t row = cache_row(p, r);
+    if (row < 0) return;
+    uint16_t* dst = p.latent + (size_t)row * kQkDim + (col - kColC);
 #pragma unroll
     for (int i = 0; i < V / 8; ++i)
       reinterpret_cast<uint4*>(dst)[i] =
@@ -358,13 +365,14 @@ size_t project_workspace_bytes(int num_rows, int d_model) {
 hipError_t launch_project(const dsa_rows& rows, int d_model, const uint16_t* h, const uint16_t* wq,
                           const uint16_t* wk, const uint16_t* wc, const uint16_t* ww, uint8_t* q_idx,
                           float* q_scale, float* w, uint8_t* k_idx, float* k_scale,
-                          uint16_t* latent, void* workspace, hipStream_t stream) {
+                          uint16_t* latent, void* workspace, hipStream_t stream,
+                          const PageMap& pm) {
   const int R = rows.num_rows;
   if (R == 0) return hipSuccess;
   const ProjShape s = proj_shape(R, d_model);
   ProjParams p{h, wq, wk, wc, ww, rows.row_seq, rows.row_pos, R, d_model, rows.num_seqs,
                rows.max_ctx, q_idx, q_scale, w, k_idx, k_scale, latent,
-               static_cast<float*>(workspace), s.ksplit};
+               static_cast<float*>(workspace), s.ksplit, pm};
   if (s.big) {
     proj_gemm_kernel<8, 4, 2><<<dim3(kCols / 256, (R + 127) / 128, 1), NTH, 0, stream>>>(p);
   } else {

@@ -130,3 +130,37 @@ def test_project_append_host_checks(m):
     empty = _rows(m, R=0, seq=None, pos=None)
     assert L.dsa_project_append(ctypes.byref(empty), ctypes.byref(d), 7168, *([None] * 11), None,
                                 0, None) == m.DSA_OK
+
+
+def test_paged_host_checks(m):
+    L = m.lib
+    d = m.dims_struct(m.PRODUCTION_DIMS)
+    r = _rows(m, R=32, B=32, N=32768, max_pos=32767)
+    p = ctypes.c_void_p(16)
+
+    def pages(P=64, pps=512, n=32 * 512, table=16):
+        return m._Pages(P, pps, n, table)
+
+    def idx(pg, rows=r, dims=d):
+        return L.dsa_indexer_scores_paged(ctypes.byref(rows), ctypes.byref(dims),
+                                          None if pg is None else ctypes.byref(pg),
+                                          p, p, p, p, p, p, 32768, None)
+    assert idx(None) == m.DSA_E_INVALID
+    for P in (32, 96, 1 << 17):
+        assert idx(pages(P=P, pps=max(1, 32768 // P))) == m.DSA_E_UNSUPPORTED
+    assert idx(pages(pps=256)) == m.DSA_E_INVALID                 # max_ctx != pps * P
+    assert idx(pages(table=None)) == m.DSA_E_INVALID
+    assert idx(pages(n=0)) == m.DSA_E_INVALID
+    f32 = m.dims_struct(m.Dims(4, 32, 16, 80, 64, 64, True))
+    assert idx(pages(), dims=f32) == m.DSA_E_UNSUPPORTED
+    # a latent pool past 4 GiB cannot be addressed with 32-bit offsets
+    big = pages(n=(1 << 32) // (64 * 1152) + 1)
+    assert L.dsa_sparse_mla_attn_paged(ctypes.byref(r), ctypes.byref(d), ctypes.byref(big), p, p,
+                                       p, 0.1, p, p, p, 1 << 30, None) == m.DSA_E_UNSUPPORTED
+    # the same pool size is fine for the 128-byte key rows
+    empty = _rows(m, R=0, B=32, N=32768, max_pos=32767, seq=None, pos=None)
+    assert idx(big, rows=empty) == m.DSA_OK
+    assert L.dsa_forward_paged(ctypes.byref(r), ctypes.byref(d), ctypes.byref(pages()), p, p, p, p,
+                               p, p, p, 0.1, p, p, None, 0, p, 16, None) == m.DSA_E_WORKSPACE
+    assert L.dsa_project_append_paged(ctypes.byref(r), ctypes.byref(d), ctypes.byref(pages()), 100,
+                                      *([p] * 11), p, 1 << 30, None) == m.DSA_E_UNSUPPORTED
