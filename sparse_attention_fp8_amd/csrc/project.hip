@@ -55,6 +55,7 @@ struct ProjParams {
   uint16_t* latent;
   float* part;  // [ksplit][R][kCols] partial sums (split contraction only)
   int ksplit;
+  int mtiles, ntiles;  // tile grid of the GEMM launch
   PageMap pm;   // cache rows: contiguous (table == nullptr) or a page pool
 };
 
@@ -175,6 +176,22 @@ __device__ __forceinline__ void finish(const ProjParams& p, const float (&v)[V],
   }
 }
 
+// Tile of a block in a 1-D grid of mtiles * ntiles blocks.  Blocks are dealt to the
+// 8 XCDs round-robin, so the block ids are first regrouped to give each XCD a
+// contiguous run of tiles; the run is walked in groups of 8 token tiles, output
+// tile by output tile, so the ~32 blocks an XCD runs at once share 4 weight tiles
+// and 8 h tiles through its L2 instead of each fetching its own.
+__device__ __forceinline__ void tile_of_block(const ProjParams& p, int L, int G, int& m, int& n) {
+  constexpr int GM = 8;
+  const int id = (G % 8 == 0) ? (L % 8) * (G / 8) + L / 8 : L;
+  const int per_group = GM * p.ntiles;
+  const int first_m = (id / per_group) * GM;
+  const int gm = min(p.mtiles - first_m, GM);
+  const int in = id % per_group;
+  m = first_m + in % gm;
+  n = in / gm;
+}
+
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
@@ -197,7 +214,9 @@ __global__ __launch_bounds__(NTH) void proj_gemm_kernel(ProjParams p) {
 
   const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63;
   const int g = l >> 4, ln = l & 15;
-  const int n0 = blockIdx.x * COLS, m0 = blockIdx.y * ROWS, ks = blockIdx.z;
+  int mt_i, nt_i;
+  tile_of_block(p, blockIdx.x, gridDim.x, mt_i, nt_i);
+  const int n0 = nt_i * COLS, m0 = mt_i * ROWS, ks = blockIdx.z;
   const int nch = p.d / KC;
   const int c0 = (int)((int64_t)nch * ks / p.ksplit);
   const int c1 = (int)((int64_t)nch * (ks + 1) / p.ksplit);
@@ -372,11 +391,15 @@ hipError_t launch_project(const dsa_rows& rows, int d_model, const uint16_t* h, 
   const ProjShape s = proj_shape(R, d_model);
   ProjParams p{h, wq, wk, wc, ww, rows.row_seq, rows.row_pos, R, d_model, rows.num_seqs,
                rows.max_ctx, q_idx, q_scale, w, k_idx, k_scale, latent,
-               static_cast<float*>(workspace), s.ksplit, pm};
+               static_cast<float*>(workspace), s.ksplit, 0, 0, pm};
   if (s.big) {
-    proj_gemm_kernel<8, 4, 2><<<dim3(kCols / 256, (R + 127) / 128, 1), NTH, 0, stream>>>(p);
+    p.mtiles = (R + 127) / 128;
+    p.ntiles = kCols / 256;
+    proj_gemm_kernel<8, 4, 2><<<dim3(p.mtiles * p.ntiles, 1, 1), NTH, 0, stream>>>(p);
   } else {
-    proj_gemm_kernel<2, 2, 4><<<dim3(kCols / 128, (R + 31) / 32, s.ksplit), NTH, 0, stream>>>(p);
+    p.mtiles = (R + 31) / 32;
+    p.ntiles = kCols / 128;
+    proj_gemm_kernel<2, 2, 4><<<dim3(p.mtiles * p.ntiles, 1, s.ksplit), NTH, 0, stream>>>(p);
     if (s.ksplit > 1) {
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
