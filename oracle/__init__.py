@@ -6,11 +6,14 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 from .dsa_oracle import (  # noqa: F401
     append_rows,
     attention_row,
+    attention_target,
     decode_bf16,
     decode_e4m3fn,
     dsa_row,
     encode_bf16,
     encode_e4m3fn,
+    indexer_backward,
+    indexer_kl,
     indexer_row,
     indexer_scores,
     paged_append,

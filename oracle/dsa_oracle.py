@@ -46,6 +46,15 @@ prose around the lost equation.  "nsmao report" means the page
    s mod P of pool page block_table[b][s div P].  Every step computes exactly what
    it computes on the contiguous cache those views describe.
 
+6. Indexer training loss (V3.2-Exp paper, §2.1, dense warm-up and sparse training
+   stages): the main attention scores of query token t are summed over all heads
+   and L1-normalised along the sequence into the target p[t,:]; the indexer is
+   trained with KL(p[t,:] || Softmax(I[t,:])), in the sparse stage over the
+   selected set S_t only; the indexer's inputs are detached, so the loss trains the
+   indexer alone.  Reading: the "attention scores" are each head's softmax weights
+   over the attended positions; gradients flow into I (p is a constant target) and
+   from I into the indexer queries, weights and keys.
+
 Inputs are the exact byte images the GPU receives: e4m3fn codes with fp32 scales
 (dequantised value = decode(code) * scale), bf16 bit patterns, or plain fp32.  The
 oracle decodes them with its own decoders and computes every step in float64.
@@ -60,7 +69,8 @@ __all__ = [
     "decode_e4m3fn", "decode_bf16", "indexer_scores", "select_topk",
     "sparse_attention", "indexer_row", "attention_row", "dsa_row",
     "encode_e4m3fn", "encode_bf16", "pow2_scale", "quantize_e4m3fn", "project",
-    "project_tokens", "append_rows", "paged_view", "paged_append",
+    "project_tokens", "append_rows", "paged_view", "paged_append", "attention_target",
+    "indexer_kl", "indexer_backward",
 ]
 
 
@@ -330,3 +340,47 @@ def paged_append(pool: np.ndarray, block_table: np.ndarray, page_size: int,
         if 0 <= b < B and 0 <= t < pps * page_size:
             out[table[b, t // page_size], t % page_size] = values[r]
     return out
+
+
+# ---------------------------------------------------------------------------
+# O7: indexer training loss and its gradients
+# ---------------------------------------------------------------------------
+
+def attention_target(q: np.ndarray, entries: np.ndarray, scale: float) -> np.ndarray:
+    """Target distribution over the attended entries of one query token: each
+    head's softmax weights over the entries, summed over the heads, then divided by
+    their total (L1 normalisation along the sequence).  q [H, D_k], entries [n, D_k]."""
+    z = scale * (np.asarray(q, dtype=np.float64) @ np.asarray(entries, dtype=np.float64).T)
+    a = np.exp(z - z.max(axis=1, keepdims=True))
+    a /= a.sum(axis=1, keepdims=True)          # per-head attention weights
+    agg = a.sum(axis=0)                        # summed over heads
+    return agg / agg.sum()
+
+
+def indexer_kl(p: np.ndarray, scores: np.ndarray) -> Tuple[float, np.ndarray]:
+    """KL(p || softmax(scores)) over one row's entries and its gradient with respect
+    to the scores (p is a constant target).  Terms with p = 0 contribute 0."""
+    p = np.asarray(p, dtype=np.float64)
+    I = np.asarray(scores, dtype=np.float64)
+    m = I.max()
+    lse = m + np.log(np.exp(I - m).sum())
+    logq = I - lse
+    pos = p > 0
+    loss = float(np.sum(p[pos] * (np.log(p[pos]) - logq[pos])))
+    grad = np.exp(logq) * p.sum() - p
+    return loss, grad
+
+
+def indexer_backward(q: np.ndarray, w: np.ndarray, k: np.ndarray,
+                     g: np.ndarray) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Gradients of sum_s g[s] * I[s] with I[s] = sum_j w[j] ReLU(q[j] . k[s]):
+    (dq [H_I, d_I], dw [H_I], dk [n, d_I]).  The ReLU's derivative is taken as 0 at
+    0 (the kink)."""
+    q = np.asarray(q, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    dots = q @ k.T                             # [H_I, n]
+    dw = np.maximum(dots, 0.0) @ g
+    coef = (w[:, None] * (dots > 0)) * g[None, :]
+    return coef @ k, dw, coef.T @ q

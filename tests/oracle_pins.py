@@ -554,4 +554,82 @@ def pin_paged_invariants():
     assert np.array_equal(got, O.append_rows(view, seq, pos, vals))
 
 
+# ---------------------------------------------------------------- P8 indexer training loss
+
+def pin_attention_target():
+    """Target distribution: a pure-Python loop over heads and entries (per-head
+    softmax, sum over heads, L1 normalisation); one head gives that head's softmax;
+    identical entries give the uniform distribution."""
+    r = _rng(41)
+    H, n, D = 3, 5, 4
+    q = r.standard_normal((H, D)) * np.array([[0.5], [2.0], [4.0]])
+    e = r.standard_normal((n, D))
+    got = O.attention_target(q, e, 0.7)
+    agg = [0.0] * n
+    for h in range(H):
+        z = [0.7 * math.fsum(q[h, d] * e[s, d] for d in range(D)) for s in range(n)]
+        m = max(z)
+        ex = [math.exp(v - m) for v in z]
+        tot = math.fsum(ex)
+        for s in range(n):
+            agg[s] += ex[s] / tot
+    want = np.array(agg) / math.fsum(agg)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-15)
+    z0 = 0.7 * (q[1] @ e.T)
+    np.testing.assert_allclose(O.attention_target(q[1:2], e, 0.7), np.exp(z0) / np.exp(z0).sum(),
+                               rtol=1e-12)
+    np.testing.assert_allclose(O.attention_target(q, np.tile(e[:1], (n, 1)), 0.7),
+                               np.full(n, 1.0 / n), rtol=1e-12)
+
+
+def pin_indexer_kl():
+    """KL(p || softmax(I)): the hand-worked case p = (1, 0), I = (0, 0) gives log 2
+    and gradient (-1/2, 1/2); p = softmax(I) gives 0; adding a constant to I changes
+    nothing; the loss is non-negative; the gradient equals central differences."""
+    loss, g = O.indexer_kl(np.array([1.0, 0.0]), np.array([0.0, 0.0]))
+    assert abs(loss - math.log(2.0)) < 1e-15 and np.allclose(g, [-0.5, 0.5], atol=1e-15)
+    r = _rng(42)
+    I = r.standard_normal(7) * 3
+    sm = np.exp(I - I.max())
+    sm /= sm.sum()
+    l0, g0 = O.indexer_kl(sm, I)
+    assert abs(l0) < 1e-14 and np.abs(g0).max() < 1e-14
+    p = r.random(7)
+    p[2] = 0.0
+    p /= p.sum()
+    loss, g = O.indexer_kl(p, I)
+    loss2, g2 = O.indexer_kl(p, I + 5.0)
+    assert loss > 0 and abs(loss - loss2) < 1e-12 and np.allclose(g, g2, atol=1e-12)
+    h = 1e-6
+    for s in range(7):
+        e = np.zeros(7)
+        e[s] = h
+        fd = (O.indexer_kl(p, I + e)[0] - O.indexer_kl(p, I - e)[0]) / (2 * h)
+        assert abs(fd - g[s]) < 1e-7, (s, fd, g[s])
+
+
+def pin_indexer_backward():
+    """Gradients of sum_s g[s] I[s] against central differences of the oracle's own
+    forward indexer_scores, away from the ReLU kinks."""
+    r = _rng(43)
+    H_I, d_I, n = 3, 5, 6
+    q = r.standard_normal((H_I, d_I))
+    w = r.standard_normal(H_I)
+    k = r.standard_normal((n, d_I))
+    assert np.abs(q @ k.T).min() > 1e-3
+    g = r.standard_normal(n)
+    dq, dw, dk = O.indexer_backward(q, w, k, g)
+    F = lambda q_, w_, k_: float(g @ O.indexer_scores(q_, w_, k_))
+    h = 1e-6
+    for (arr, grad, name) in ((q, dq, "q"), (w, dw, "w"), (k, dk, "k")):
+        for idx in np.ndindex(arr.shape):
+            a1, a2 = arr.copy(), arr.copy()
+            a1[idx] += h
+            a2[idx] -= h
+            args1 = {"q": (a1, w, k), "w": (q, a1, k), "k": (q, w, a1)}[name]
+            args2 = {"q": (a2, w, k), "w": (q, a2, k), "k": (q, w, a2)}[name]
+            fd = (F(*args1) - F(*args2)) / (2 * h)
+            assert abs(fd - grad[idx]) < 1e-6 * (1 + abs(fd)), (name, idx, fd, grad[idx])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -9,7 +9,8 @@ import oracle_pins
 _orig = {name: getattr(O, name) for name in
          ["indexer_scores", "select_topk", "sparse_attention", "decode_e4m3fn",
           "decode_bf16", "indexer_row", "encode_e4m3fn", "encode_bf16", "pow2_scale",
-         "quantize_e4m3fn", "project", "project_tokens", "paged_view", "paged_append"]}
+         "quantize_e4m3fn", "project", "project_tokens", "paged_view", "paged_append",
+         "attention_target", "indexer_kl", "indexer_backward"]}
 
 
 def _no_relu(q, w, k):
@@ -161,6 +162,39 @@ def _paged_append_logical_index(pool, block_table, page_size, row_seq, row_pos, 
     return out
 
 
+def _target_unnormalised_heads(q, entries, scale):
+    # exp of the scores summed over heads without the per-head softmax
+    z = scale * (np.asarray(q, dtype=np.float64) @ np.asarray(entries, dtype=np.float64).T)
+    a = np.exp(z - z.max()).sum(axis=0)
+    return a / a.sum()
+
+
+def _kl_reversed(p, scores):
+    # KL(softmax(I) || p) instead of KL(p || softmax(I))
+    I = np.asarray(scores, dtype=np.float64)
+    qd = np.exp(I - I.max())
+    qd /= qd.sum()
+    p = np.asarray(p, dtype=np.float64)
+    with np.errstate(divide="ignore"):
+        loss = float(np.sum(qd * (np.log(qd) - np.log(np.maximum(p, 1e-300)))))
+    return loss, _orig["indexer_kl"](p, scores)[1]
+
+
+def _kl_grad_sign(p, scores):
+    loss, g = _orig["indexer_kl"](p, scores)
+    return loss, -g
+
+
+def _bwd_no_relu_in_dw(q, w, k, g):
+    dq, dw, dk = _orig["indexer_backward"](q, w, k, g)
+    return dq, (np.asarray(q) @ np.asarray(k).T) @ np.asarray(g), dk
+
+
+def _bwd_dq_without_w(q, w, k, g):
+    return _orig["indexer_backward"](q, np.ones_like(np.asarray(w)), k, g)[0], \
+        _orig["indexer_backward"](q, w, k, g)[1], _orig["indexer_backward"](q, w, k, g)[2]
+
+
 MUTANTS = [
     ("indexer_scores", _no_relu),
     ("indexer_scores", _relu_after_sum),
@@ -189,6 +223,11 @@ MUTANTS = [
     ("paged_view", _paged_table_transposed),
     ("paged_view", _paged_offset_swapped),
     ("paged_append", _paged_append_logical_index),
+    ("attention_target", _target_unnormalised_heads),
+    ("indexer_kl", _kl_reversed),
+    ("indexer_kl", _kl_grad_sign),
+    ("indexer_backward", _bwd_no_relu_in_dw),
+    ("indexer_backward", _bwd_dq_without_w),
 ]
 
 
