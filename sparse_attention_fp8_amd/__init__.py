@@ -19,7 +19,8 @@ __all__ = [
     "indexer_scores", "topk", "sparse_mla_attn", "forward", "forward_workspace_size",
     "sparse_mla_attn_workspace_size", "project_append", "project_append_workspace_size",
     "pages_struct", "indexer_scores_paged", "sparse_mla_attn_paged", "forward_paged",
-    "project_append_paged", "DSAError", "EXPORTED_SYMBOLS",
+    "project_append_paged", "indexer_loss", "indexer_loss_workspace_size", "indexer_backward",
+    "DSAError", "EXPORTED_SYMBOLS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
@@ -32,6 +33,7 @@ EXPORTED_SYMBOLS = [
     "dsa_sparse_mla_attn", "dsa_forward_workspace_size", "dsa_forward",
     "dsa_project_append_workspace_size", "dsa_project_append", "dsa_indexer_scores_paged",
     "dsa_sparse_mla_attn_paged", "dsa_forward_paged", "dsa_project_append_paged",
+    "dsa_indexer_loss_workspace_size", "dsa_indexer_loss", "dsa_indexer_backward",
     "dsa_status_string", "dsa_last_error", "dsa_api_version",
 ]
 
@@ -63,7 +65,7 @@ class _Pages(ctypes.Structure):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it first (python -m sparse_attention_fp8_amd.build)")
+            f"{LIB_PATH} is missing: build it first (python sparse_attention_fp8_amd/build.py)")
     L = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
                              ctypes.c_size_t)
@@ -85,9 +87,14 @@ def _load() -> ctypes.CDLL:
     L.dsa_forward_paged.argtypes = [R, D, PG, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, i32,
                                     vp, sz, vp]
     L.dsa_project_append_paged.argtypes = [R, D, PG, i32] + [vp] * 12 + [sz, vp]
+    L.dsa_indexer_loss_workspace_size.argtypes = [R, D]
+    L.dsa_indexer_loss_workspace_size.restype = sz
+    L.dsa_indexer_loss.argtypes = [R, D, vp, vp, vp, vp, f32, vp, i64, vp, vp, vp, sz, vp]
+    L.dsa_indexer_backward.argtypes = [R, D] + [vp] * 10 + [vp]
     for name in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_attn", "dsa_forward",
                  "dsa_project_append", "dsa_indexer_scores_paged", "dsa_sparse_mla_attn_paged",
-                 "dsa_forward_paged", "dsa_project_append_paged"):
+                 "dsa_forward_paged", "dsa_project_append_paged", "dsa_indexer_loss",
+                 "dsa_indexer_backward"):
         getattr(L, name).restype = ctypes.c_int
     L.dsa_status_string.argtypes = [ctypes.c_int]
     L.dsa_status_string.restype = ctypes.c_char_p
@@ -492,3 +499,68 @@ def project_append_paged(rows: _Rows, pages: _Pages, h, w_q, w_k, w_c, w_w, k_po
                                         _ptr(k_pool), _ptr(k_scale_pool), _ptr(latent_pool),
                                         _ptr(workspace), ws_bytes, _stream()))
     return q_idx, q_scale, w
+
+
+# ---------------------------------------------------------------- indexer training loss
+
+def indexer_loss_workspace_size(rows: _Rows, dims: Dims = PRODUCTION_DIMS) -> int:
+    ds = dims_struct(dims)
+    return int(lib.dsa_indexer_loss_workspace_size(ctypes.byref(rows), ctypes.byref(ds)))
+
+
+def indexer_loss(rows: _Rows, q, latent, indices, lse, softmax_scale: float, scores,
+                 dims: Dims = PRODUCTION_DIMS, loss=None, dscores=None,
+                 workspace: Optional[torch.Tensor] = None):
+    """dsa_indexer_loss: (loss [R], dscores [R, k]) of the sparse-stage KL."""
+    R = rows.num_rows
+    _dev(q, torch.bfloat16, "q")
+    _dev(latent, torch.bfloat16, "latent")
+    _dev(indices, torch.int32, "indices")
+    _dev(lse, torch.float32, "lse")
+    _dev(scores, torch.float32, "scores")
+    _shape(q, (R, dims.n_heads, dims.qk_dim), "q")
+    _shape(indices, (R, dims.topk), "indices")
+    _shape(lse, (R, dims.n_heads), "lse")
+    _shape(scores, (R, None), "scores")
+    _caches(rows, dims, None, None, latent)
+    if loss is None:
+        loss = torch.empty(R, dtype=torch.float32, device=q.device)
+    if dscores is None:
+        dscores = torch.empty(R, dims.topk, dtype=torch.float32, device=q.device)
+    _dev(loss, torch.float32, "loss")
+    _dev(dscores, torch.float32, "dscores")
+    need = indexer_loss_workspace_size(rows, dims)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ds = dims_struct(dims)
+    _check(lib.dsa_indexer_loss(ctypes.byref(rows), ctypes.byref(ds), _ptr(q), _ptr(latent),
+                                _ptr(indices), _ptr(lse), float(softmax_scale), _ptr(scores),
+                                scores.shape[1], _ptr(loss), _ptr(dscores), _ptr(workspace),
+                                workspace.numel(), _stream()))
+    return loss, dscores
+
+
+def indexer_backward(rows: _Rows, q_idx, q_scale, w, k_idx, k_scale, indices, dscores, dq, dw,
+                     dk, dims: Dims = PRODUCTION_DIMS):
+    """dsa_indexer_backward: adds the gradients into dq [R,H_I,d_I], dw [R,H_I] and
+    dk [B,N,d_I] (fp32, zeroed by the caller)."""
+    R = rows.num_rows
+    for t, dt, name in ((q_idx, torch.uint8, "q_idx"), (q_scale, torch.float32, "q_scale"),
+                        (w, torch.float32, "w"), (k_idx, torch.uint8, "k_idx"),
+                        (k_scale, torch.float32, "k_scale"), (indices, torch.int32, "indices"),
+                        (dscores, torch.float32, "dscores"), (dq, torch.float32, "dq"),
+                        (dw, torch.float32, "dw"), (dk, torch.float32, "dk")):
+        _dev(t, dt, name)
+    _shape(q_idx, (R, dims.n_idx_heads, dims.idx_dim), "q_idx")
+    _shape(dq, (R, dims.n_idx_heads, dims.idx_dim), "dq")
+    _shape(dw, (R, dims.n_idx_heads), "dw")
+    _shape(indices, (R, dims.topk), "indices")
+    _shape(dscores, (R, dims.topk), "dscores")
+    _caches(rows, dims, k_idx, k_scale)
+    _shape(dk, (rows.num_seqs, rows.max_ctx, dims.idx_dim), "dk")
+    ds = dims_struct(dims)
+    _check(lib.dsa_indexer_backward(ctypes.byref(rows), ctypes.byref(ds), _ptr(q_idx),
+                                    _ptr(q_scale), _ptr(w), _ptr(k_idx), _ptr(k_scale),
+                                    _ptr(indices), _ptr(dscores), _ptr(dq), _ptr(dw), _ptr(dk),
+                                    _stream()))
+    return dq, dw, dk

@@ -1,6 +1,8 @@
 """Build libdsa.so (the HIP kernels and the C ABI) in-tree for gfx950.
 
-    python -m sparse_attention_fp8_amd.build      # or sparse_attention_fp8_amd.build.build()
+    python sparse_attention_fp8_amd/build.py      # or __graft_entry__.build()
+
+(Run it as a script: importing the package loads the library it builds.)
 """
 from __future__ import annotations
 
@@ -18,11 +20,12 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdsa.so")
 ARCH = "gfx950"
 
-SOURCES = ["indexer.hip", "topk.hip", "attention.hip", "project.hip", "dsa_api.cpp"]
+SOURCES = ["indexer.hip", "topk.hip", "attention.hip", "project.hip", "train.hip", "dsa_api.cpp"]
 # per-source code generation options
 EXTRA = {
     # keep MFMA results in VGPRs: the indexer epilogue reads every result with VALU
     "indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "train.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 
