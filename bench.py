@@ -283,6 +283,52 @@ def time_projection(dsa, di, pcfg, reps, sets=3):
     return res
 
 
+def time_training(dsa, st, K):
+    """The sparse-stage indexer loss (target, KL, dI) and its backward on one input
+    set of the headline workload, each timed with HIP events over K calls."""
+    import torch
+
+    c = st.cfg
+    R = c.num_rows
+    st.run()  # scores, selection, attention lse of this set
+    loss = torch.empty(R, dtype=torch.float32, device="cuda")
+    dsc = torch.empty(R, c.topk, dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(dsa.indexer_loss_workspace_size(st.rows), 1), dtype=torch.uint8,
+                     device="cuda")
+    dq = torch.zeros(R, c.n_idx_heads, c.idx_dim, dtype=torch.float32, device="cuda")
+    dw = torch.zeros(R, c.n_idx_heads, dtype=torch.float32, device="cuda")
+    dk = torch.zeros(c.num_seqs, c.max_ctx, c.idx_dim, dtype=torch.float32, device="cuda")
+    i = st.inp
+    fwd = lambda: dsa.indexer_loss(st.rows, i.q, i.latent, st.idx, st.lse, c.scale, st.scores,
+                                   loss=loss, dscores=dsc, workspace=ws)
+    bwd = lambda: dsa.indexer_backward(st.rows, i.q_idx, i.q_scale, i.w, i.k_idx, i.k_scale,
+                                       st.idx, dsc, dq, dw, dk)
+    out = {}
+    for name, fn in (("loss", fwd), ("backward", bwd)):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(K):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = {"ms": e0.elapsed_time(e1) / K}
+    sel = R * c.topk
+    # loss: the selected latent rows are gathered again and q.c recomputed (bf16 MFMA)
+    lb = sel * ATTN_BYTES_PER_ENTRY
+    out["loss"].update({"bytes": lb, "gbs": lb / out["loss"]["ms"] / 1e6,
+                        "bf16_tflops": sel * 2 * 128 * 576 / out["loss"]["ms"] / 1e9})
+    # backward: two 64 x 128 fp32 products per selected key, 2 flops per FMA (VALU)
+    fl = sel * 2 * 64 * 128 * 2
+    out["backward"].update({"fp32_tflops": fl / out["backward"]["ms"] / 1e9,
+                            "frac_of_fp32_vector_peak": fl / out["backward"]["ms"] / 1e9 / 157.3})
+    del dk, dq, dw, ws, dsc, loss
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(di, cfg, budget_s=20.0):
     """The float64 oracle on a bounded sample of the workload's rows, host cores."""
     import numpy as np
@@ -400,6 +446,7 @@ def main():
     pms = (time.perf_counter() - t0) / args.steps * 1e3
     line["paged"] = {"page_size": P, "ms_per_step": pms, "tokens_per_s": R / (pms * 1e-3),
                      "vs_contiguous": ms / pms}
+    line["indexer_training"] = time_training(dsa, steps[0], args.steps)
     del steps
     torch.cuda.empty_cache()
     # the step before the path: projections and cache append of the new tokens

@@ -253,6 +253,46 @@ dsa_status dsa_project_append_paged(const dsa_rows* rows, const dsa_dims* dims,
                                     void* k_pool, float* k_scale_pool, void* latent_pool,
                                     void* workspace, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Indexer training loss of the sparse stage (DeepSeek-V3.2-Exp paper, section 2.1,
+ * "sparse training stage": the indexer output is aligned with the main attention
+ * distribution over the selected set S_t only, by a KL divergence; the indexer's
+ * inputs are detached from the main model).  Production dims only.
+ *
+ * dsa_indexer_loss, for each row r with S = {indices[r, i] in [0, t]}:
+ *   u_i   = sum_h exp(softmax_scale q[r,h,:] . latent[b,s_i,:] - lse[r,h])   (target)
+ *   p_i   = u_i / sum_i u_i       (the heads' attention weights summed, L1-normalised)
+ *   loss[r]        = sum_i p_i (log p_i - log softmax_S(scores[r, s_i]))
+ *   dscores[r, i]  = softmax_S(scores[r, s_i]) - p_i   (0 at padding entries)
+ * lse is the attention call's lse output for the same indices; scores the indexer
+ * scores [R, ld_scores].  fp32 throughout; the target recomputes the q.c products on
+ * the bf16 MFMA.  The workspace holds u (dsa_indexer_loss_workspace_size bytes).
+ *
+ * dsa_indexer_backward, with d = (q_scale q_idx[r,j,:]) . (k_scale k_idx[b,s,:]) and
+ * m = [d > 0], for every selected entry s_i of row r and every head j:
+ *   dw[r,j]      += dscores[r,i] * max(d, 0)
+ *   dq[r,j,:]    += dscores[r,i] * w[r,j] * m * (k_scale k_idx[b,s_i,:])
+ *   dk[b,s_i,:]  += dscores[r,i] * w[r,j] * m * (q_scale q_idx[r,j,:])
+ * i.e. the gradients of sum_i dscores[r,i] I[r,s_i] with respect to w and the
+ * dequantised indexer queries and keys.  dq [R, H_I, d_I], dw [R, H_I] and
+ * dk [B, N, d_I] are fp32 and ACCUMULATED (the caller zeroes them); the additions
+ * are atomic, so their order, and the last bits, vary from run to run.  The dots
+ * are the forward's (exact fp8 products, fp32 sums); the products run in fp32.
+ * ------------------------------------------------------------------------- */
+size_t dsa_indexer_loss_workspace_size(const dsa_rows* rows, const dsa_dims* dims);
+
+dsa_status dsa_indexer_loss(const dsa_rows* rows, const dsa_dims* dims, const void* q,
+                            const void* latent, const int32_t* indices, const float* lse,
+                            float softmax_scale, const float* scores, int64_t ld_scores,
+                            float* loss, float* dscores, void* workspace, size_t ws_bytes,
+                            void* stream);
+
+dsa_status dsa_indexer_backward(const dsa_rows* rows, const dsa_dims* dims, const void* q_idx,
+                                const float* q_scale, const float* w, const void* k_idx,
+                                const float* k_scale, const int32_t* indices,
+                                const float* dscores, float* dq, float* dw, float* dk,
+                                void* stream);
+
 /* Status text, and the detail of the last failure on the calling thread. */
 const char* dsa_status_string(dsa_status status);
 const char* dsa_last_error(void);

@@ -397,4 +397,53 @@ dsa_status dsa_project_append_paged(const dsa_rows* rows, const dsa_dims* dims,
                       k_pool, k_scale_pool, latent_pool, workspace, ws_bytes, stream);
 }
 
+size_t dsa_indexer_loss_workspace_size(const dsa_rows* rows, const dsa_dims* dims) {
+  if (check_rows(rows) != DSA_OK || dims == nullptr || !is_production(*dims)) return 0;
+  return dsa::indexer_loss_workspace_bytes(rows->num_rows, dims->topk);
+}
+
+dsa_status dsa_indexer_loss(const dsa_rows* rows, const dsa_dims* dims, const void* q,
+                            const void* latent, const int32_t* indices, const float* lse,
+                            float softmax_scale, const float* scores, int64_t ld_scores,
+                            float* loss, float* dscores, void* workspace, size_t ws_bytes,
+                            void* stream) {
+  dsa_status st = check_rows(rows);
+  if (st != DSA_OK) return st;
+  if (dims == nullptr) return fail(DSA_E_INVALID, "dims is NULL");
+  if (!is_production(*dims))
+    return fail(DSA_E_UNSUPPORTED, "the indexer loss supports the production dims only");
+  if (rows->num_rows == 0) return DSA_OK;
+  if (!q || !latent || !indices || !lse || !scores || !loss || !dscores)
+    return fail(DSA_E_INVALID, "NULL tensor pointer");
+  if (ld_scores < (int64_t)rows->max_pos + 1)
+    return fail(DSA_E_INVALID, "ld_scores < max_pos + 1");
+  const size_t need = dsa::indexer_loss_workspace_bytes(rows->num_rows, dims->topk);
+  if (workspace == nullptr || ws_bytes < need)
+    return fail(DSA_E_WORKSPACE, "the indexer loss needs %zu workspace bytes, got %zu", need,
+                ws_bytes);
+  const hipError_t err = dsa::launch_indexer_loss(*rows, q, latent, indices, lse, softmax_scale,
+                                                  scores, ld_scores, loss, dscores, workspace,
+                                                  as_stream(stream));
+  return err == hipSuccess ? DSA_OK : hip_fail(err, "indexer loss launch");
+}
+
+dsa_status dsa_indexer_backward(const dsa_rows* rows, const dsa_dims* dims, const void* q_idx,
+                                const float* q_scale, const float* w, const void* k_idx,
+                                const float* k_scale, const int32_t* indices,
+                                const float* dscores, float* dq, float* dw, float* dk,
+                                void* stream) {
+  dsa_status st = check_rows(rows);
+  if (st != DSA_OK) return st;
+  if (dims == nullptr) return fail(DSA_E_INVALID, "dims is NULL");
+  if (!is_production(*dims))
+    return fail(DSA_E_UNSUPPORTED, "the indexer backward supports the production dims only");
+  if (rows->num_rows == 0) return DSA_OK;
+  if (!q_idx || !q_scale || !w || !k_idx || !k_scale || !indices || !dscores || !dq || !dw || !dk)
+    return fail(DSA_E_INVALID, "NULL tensor pointer");
+  const hipError_t err = dsa::launch_indexer_backward(
+      *rows, static_cast<const uint8_t*>(q_idx), q_scale, w, static_cast<const uint8_t*>(k_idx),
+      k_scale, indices, dscores, dq, dw, dk, as_stream(stream));
+  return err == hipSuccess ? DSA_OK : hip_fail(err, "indexer backward launch");
+}
+
 }  // extern "C"

@@ -123,6 +123,11 @@ __device__ __forceinline__ float wave_min(float v) {
     return __float_as_uint(fminf(__uint_as_float(a), __uint_as_float(b)));
   }));
 }
+__device__ __forceinline__ float wave_sum_f(float v) {
+  return __uint_as_float(wave_reduce_bits(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+  }));
+}
 __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
   return wave_reduce_bits(v, [](uint32_t a, uint32_t b) { return a + b; });
 }

@@ -67,4 +67,17 @@ hipError_t launch_project(const dsa_rows& rows, int d_model, const uint16_t* h, 
                           uint16_t* latent, void* workspace, hipStream_t stream,
                           const PageMap& pm = PageMap());
 
+size_t indexer_loss_workspace_bytes(int num_rows, int topk);
+
+hipError_t launch_indexer_loss(const dsa_rows& rows, const void* q, const void* latent,
+                               const int32_t* indices, const float* lse, float softmax_scale,
+                               const float* scores, int64_t ld, float* loss, float* dscores,
+                               void* workspace, hipStream_t stream, const PageMap& pm = PageMap());
+
+hipError_t launch_indexer_backward(const dsa_rows& rows, const uint8_t* q_idx,
+                                   const float* q_scale, const float* w, const uint8_t* k_idx,
+                                   const float* k_scale, const int32_t* indices,
+                                   const float* dscores, float* dq, float* dw, float* dk,
+                                   hipStream_t stream, const PageMap& pm = PageMap());
+
 }  // namespace dsa

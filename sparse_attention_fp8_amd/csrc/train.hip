@@ -1,0 +1,406 @@
+// Indexer training loss of the sparse stage and its gradients.
+//
+// DeepSeek-V3.2-Exp paper, section 2.1 (dense warm-up and sparse training stages):
+// for query token t the main attention scores are summed over all heads and
+// L1-normalised along the sequence into a target p[t,:], and the indexer is trained
+// with KL(p[t,:] || Softmax(I[t,:])), in the sparse stage over the selected set S_t;
+// the indexer's inputs are detached, so this loss trains the indexer alone.
+//
+//   target:   a[h,i] = exp(scale q[h] . c[s_i] - lse[h])   (each head's softmax
+//             weights over S_t; lse is the attention call's output)
+//             u[i] = sum_h a[h,i]                       (attn_target_kernel)
+//   loss:     p = u / sum_i u;  L = sum_i p_i (log p_i - log softmax(I[S_t])_i)
+//             dI_i = softmax(I[S_t])_i - p_i            (indexer_kl_kernel)
+//   backward: with d = q_j . k_s (dequantised) and m = [d > 0]
+//             dw_j += dI_s relu(d),  dq_j += dI_s w_j m k_s,  dk_s += dI_s w_j m q_j
+//                                                       (indexer_bwd_kernel)
+#include "dsa_device.h"
+#include "dsa_internal.h"
+
+namespace dsa {
+namespace {
+
+constexpr int H = kHeads;      // 128
+constexpr int DK = kQkDim;     // 576
+constexpr int IH = kIdxHeads;  // 64
+constexpr int ID = kIdxDim;    // 128
+
+// ---------------------------------------------------------------------------
+// Target u[r, i] for the entries of one slice of row r's selection.  Eight waves,
+// wave w owns heads [16 w, 16 w + 16) with their queries in registers; entries are
+// staged 32 at a time in LDS (16-byte pieces XOR-swizzled by entry) and multiplied
+// on the bf16 MFMA as S^T tiles (16 entries x 16 heads), so each lane ends with 4
+// entries of one head.  The head sum is a DPP row reduction plus an LDS sum over
+// the waves.
+// ---------------------------------------------------------------------------
+constexpr int TT = 512;            // threads per target block
+constexpr int TBE = 32;            // entries per stage
+constexpr int TCH = DK * 2 / 16;   // 72 pieces of 16 bytes per entry
+constexpr int TKS = DK / 32;       // 18 contraction steps
+
+__global__ __launch_bounds__(TT) void attn_target_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ latent,
+    const int32_t* __restrict__ indices, const float* __restrict__ lse,
+    const int32_t* __restrict__ row_seq, const int32_t* __restrict__ row_pos, int R, int B,
+    int N, int topk, int splits, float scale_log2, float* __restrict__ u, PageMap pm) {
+  __shared__ __attribute__((aligned(16))) i32x4 tile[TBE * TCH];
+  __shared__ float part[TT / 64][TBE];
+  const int r = blockIdx.x / splits, sp = blockIdx.x - r * splits;
+  if (r >= R) return;
+  const int b = row_seq[r], t = row_pos[r];
+  const int ES = topk / splits;
+  const int32_t* irow = indices + (size_t)r * topk + (size_t)sp * ES;
+  float* urow = u + (size_t)r * topk + (size_t)sp * ES;
+  if (b < 0 || b >= B || t < 0 || t >= N) {
+    for (int i = threadIdx.x; i < ES; i += TT) urow[i] = 0.f;
+    return;
+  }
+  const int tid = threadIdx.x, l = lane_id(), g = l >> 4, n = l & 15;
+  const int wv = tid >> 6;
+  const bool paged = pm.table != nullptr;
+  const uint8_t* base = reinterpret_cast<const uint8_t*>(paged ? latent : latent + (size_t)b * N * DK);
+  auto row_of = [&](int p) -> uint32_t { return paged ? paged_row(pm, b, p) : (uint32_t)p; };
+  const uint32_t row0 = row_of(0);
+
+  // queries of heads 16 wv + n, contraction step s: dims [32 s + 8 g, +8)
+  i32x4 qr[TKS];
+  const uint16_t* qrow = q + ((size_t)r * H + 16 * wv + n) * DK + 8 * g;
+#pragma unroll
+  for (int s = 0; s < TKS; ++s) qr[s] = *reinterpret_cast<const i32x4*>(qrow + 32 * s);
+  // log2-domain lse of this lane's head
+  const float lse2 = lse[(size_t)r * H + 16 * wv + n] * 1.44269504088896340736f;
+
+  for (int e0 = 0; e0 < ES; e0 += TBE) {
+    __syncthreads();  // previous stage's tile reads are done
+    for (int c = tid; c < TBE * TCH; c += TT) {
+      const int e = c / TCH, pc = c - e * TCH;
+      const int p = irow[e0 + e];
+      const uint32_t row = (p >= 0 && p < N) ? row_of(p) : row0;
+      tile[e * TCH + (pc ^ (e & 7))] =
+          *reinterpret_cast<const i32x4*>(base + (size_t)row * (DK * 2) + 16 * pc);
+    }
+    __syncthreads();
+    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int s = 0; s < TKS; ++s)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const int e = 16 * mt + n;
+        const bf16x8 a = as_bf16x8(tile[e * TCH + ((4 * s + g) ^ (e & 7))]);
+        acc[mt] = mfma_bf16_16x16x32(a, as_bf16x8(qr[s]), acc[mt]);
+      }
+    // lane: entries 16 mt + 4 g + v of head 16 wv + n
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        float x = exp2f(acc[mt][v] * scale_log2 - lse2);
+        uint32_t xb = __float_as_uint(x);
+        xb = __float_as_uint(__uint_as_float(xb) + __uint_as_float(dpp<kDppXor1>(xb)));
+        xb = __float_as_uint(__uint_as_float(xb) + __uint_as_float(dpp<kDppXor2>(xb)));
+        xb = __float_as_uint(__uint_as_float(xb) + __uint_as_float(dpp<kDppHalfMirror>(xb)));
+        xb = __float_as_uint(__uint_as_float(xb) + __uint_as_float(dpp<kDppMirror>(xb)));
+        if (n == 0) part[wv][16 * mt + 4 * g + v] = __uint_as_float(xb);
+      }
+    __syncthreads();
+    if (tid < TBE) {
+      float sum = 0.f;
+#pragma unroll
+      for (int w8 = 0; w8 < TT / 64; ++w8) sum += part[w8][tid];
+      const int p = irow[e0 + tid];
+      urow[e0 + tid] = (p >= 0 && p < N) ? sum : 0.f;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// KL(p || softmax(I over the selection)) and its gradient for one row per block.
+// ---------------------------------------------------------------------------
+constexpr int KT = 256;
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum_f(v);
+  __syncthreads();
+  if (lane_id() == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < KT / 64; ++i) s += red[i];
+  return s;
+}
+__device__ __forceinline__ float block_max(float v, float* red) {
+  v = wave_max(v);
+  __syncthreads();
+  if (lane_id() == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float s = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < KT / 64; ++i) s = fmaxf(s, red[i]);
+  return s;
+}
+
+__global__ __launch_bounds__(KT) void indexer_kl_kernel(
+    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ indices,
+    const float* __restrict__ u, const int32_t* __restrict__ row_seq,
+    const int32_t* __restrict__ row_pos, int B, int N, int topk, float* __restrict__ loss,
+    float* __restrict__ dscores) {
+  __shared__ float red[KT / 64];
+  const int r = blockIdx.x;
+  const int b = row_seq[r], t = row_pos[r];
+  const int32_t* irow = indices + (size_t)r * topk;
+  const float* urow = u + (size_t)r * topk;
+  float* grow = dscores + (size_t)r * topk;
+  const bool ok = b >= 0 && b < B && t >= 0 && t < N && (int64_t)t < ld;
+  const float* srow = scores + (size_t)r * ld;
+  auto valid = [&](int p) { return ok && p >= 0 && p <= t; };
+  float m = -INFINITY, us = 0.f;
+  for (int i = threadIdx.x; i < topk; i += KT) {
+    const int p = irow[i];
+    if (valid(p)) {
+      m = fmaxf(m, srow[p]);
+      us += urow[i];
+    }
+  }
+  m = block_max(m, red);
+  us = block_sum(us, red);
+  float z = 0.f;
+  for (int i = threadIdx.x; i < topk; i += KT) {
+    const int p = irow[i];
+    if (valid(p)) z += expf(srow[p] - m);
+  }
+  z = block_sum(z, red);
+  const float lz = m + logf(z);
+  const float inv_u = us > 0.f ? 1.f / us : 0.f;
+  float kl = 0.f;
+  for (int i = threadIdx.x; i < topk; i += KT) {
+    const int p = irow[i];
+    float gi = 0.f;
+    if (valid(p)) {
+      const float pi = urow[i] * inv_u;
+      const float lq = srow[p] - lz;
+      if (pi > 0.f) kl += pi * (logf(pi) - lq);
+      gi = expf(lq) - pi;
+    }
+    grow[i] = gi;
+  }
+  kl = block_sum(kl, red);
+  if (threadIdx.x == 0) loss[r] = (ok && z > 0.f) ? kl : 0.f;
+}
+
+// ---------------------------------------------------------------------------
+// Backward into the indexer for 4 groups of 64 selected entries of one row per
+// block.  The
+// 64-head x 64-key dots come from the fp8 MFMA exactly as in the forward (exact
+// fp8 products, fp32 sums); each wave owns one 16-key tile, each lane 16 heads of
+// one key.  The coefficient matrices for dq and dk go through LDS; the two
+// 64 x 64 x 128 products run in fp32 on the VALU (each thread 4 heads or 4 keys
+// x 8 dims), and the results are added with atomics (dq over the row's blocks,
+// dk over the rows that select a key, dw over the row's blocks).
+// ---------------------------------------------------------------------------
+constexpr int BT = 256;
+constexpr int BG = 64;   // entries per group
+constexpr int BGPB = 4;  // groups per block (dq and dw stay in registers across them)
+
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  const uint32_t s = (c & 0x80u) << 24, e = (c >> 3) & 15u, m = c & 7u;
+  const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+  return __uint_as_float(__float_as_uint(mag) | s);
+}
+
+__global__ __launch_bounds__(BT) void indexer_bwd_kernel(
+    const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale,
+    const float* __restrict__ w, const uint8_t* __restrict__ k_idx,
+    const float* __restrict__ k_scale, const int32_t* __restrict__ indices,
+    const float* __restrict__ dscores, const int32_t* __restrict__ row_seq,
+    const int32_t* __restrict__ row_pos, int B, int N, int topk, float* __restrict__ dq,
+    float* __restrict__ dw, float* __restrict__ dk, PageMap pm) {
+  __shared__ __attribute__((aligned(16))) float kf[BG][ID + 4];   // dequantised keys
+  __shared__ __attribute__((aligned(16))) float qf[IH][ID + 4];   // dequantised queries
+  __shared__ __attribute__((aligned(16))) float cq[IH][BG + 4];   // dI w m, head-major
+  __shared__ __attribute__((aligned(16))) float ck[BG][IH + 4];   // the same, key-major
+  __shared__ float dwp[BT / 64][IH];
+  __shared__ int rows_s[BG];
+  __shared__ float g_s[BG], ks_s[BG];
+  const int nblk = topk / (BG * BGPB);
+  const int r = blockIdx.x / nblk, ebase = (blockIdx.x - r * nblk) * BG * BGPB;
+  const int b = row_seq[r], t = row_pos[r];
+  if (b < 0 || b >= B || t < 0 || t >= N) return;
+  const int tid = threadIdx.x, l = lane_id(), g = l >> 4, n = l & 15, wv = tid >> 6;
+  const bool paged = pm.table != nullptr;
+  const uint8_t* kbase = paged ? k_idx : k_idx + (size_t)b * N * ID;
+  const float* sbase = paged ? k_scale : k_scale + (size_t)b * N;
+  const uint8_t* qr = q_idx + (size_t)r * IH * ID;
+
+  // dequantised queries, once per block
+  for (int c = tid; c < IH * ID / 4; c += BT) {
+    const int j = c / (ID / 4), d4 = c - j * (ID / 4);
+    const uint32_t word = *reinterpret_cast<const uint32_t*>(qr + (size_t)j * ID + 4 * d4);
+    const float sc = q_scale[(size_t)r * IH + j];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qf[j][4 * d4 + i] = e4m3_value((word >> (8 * i)) & 0xffu) * sc;
+  }
+  // this lane's fp8 queries for the dots (A operand of head tile mt)
+  i32x8 qa[4];
+  float qsj[16], wjj[16];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const i32x4* qp = reinterpret_cast<const i32x4*>(qr + (size_t)(16 * mt + n) * ID + 32 * g);
+    const i32x4 b0 = qp[0], b1 = qp[1];
+    qa[mt] = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int j = 16 * mt + 4 * g + v;
+      qsj[4 * mt + v] = q_scale[(size_t)r * IH + j];
+      wjj[4 * mt + v] = w[(size_t)r * IH + j];
+    }
+  }
+  float dwacc = 0.f;                       // head tid (tid < 64), over the block's groups
+  const int j0 = 4 * (tid >> 4), d0 = 8 * (tid & 15);
+  float accq[4][8] = {};                   // dq of heads j0.., dims d0.., over the groups
+
+  for (int gi = 0; gi < BGPB; ++gi) {
+    const int e0 = ebase + gi * BG;
+    __syncthreads();  // the previous group's LDS reads are done
+    if (tid < BG) {
+      const int p = indices[(size_t)r * topk + e0 + tid];
+      const bool v = p >= 0 && p <= t;
+      const int row = v ? (paged ? (int)paged_row(pm, b, p) : p) : -1;
+      rows_s[tid] = row;
+      g_s[tid] = v ? dscores[(size_t)r * topk + e0 + tid] : 0.f;
+      ks_s[tid] = v ? sbase[row] : 0.f;
+    }
+    __syncthreads();
+    for (int c = tid; c < BG * ID / 4; c += BT) {
+      const int e = c / (ID / 4), d4 = c - e * (ID / 4);
+      const int row = rows_s[e];
+      const uint32_t word =
+          row >= 0 ? *reinterpret_cast<const uint32_t*>(kbase + (size_t)row * ID + 4 * d4) : 0u;
+      const float sc = ks_s[e];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kf[e][4 * d4 + i] = e4m3_value((word >> (8 * i)) & 0xffu) * sc;
+    }
+    // fp8 dots of the 64 heads with this wave's 16 keys (the forward's arithmetic)
+    {
+      const int e = 16 * wv + n;  // this lane's key
+      const int row = rows_s[e];
+      i32x8 kb = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (row >= 0) {
+        const i32x4* kp = reinterpret_cast<const i32x4*>(kbase + (size_t)row * ID + 32 * g);
+        const i32x4 a0 = kp[0], a1 = kp[1];
+        kb = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+      const float ge = g_s[e], kse = ks_s[e];
+      float dwl[16];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const f32x4 d8 = mfma_fp8_16x16x128(qa[mt], kb, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int j = 16 * mt + 4 * g + v;
+          const bool pos = d8[v] > 0.f;
+          // kf and qf hold dequantised values, so the coefficient carries no scale
+          const float c = pos ? ge * wjj[4 * mt + v] : 0.f;
+          dwl[4 * mt + v] = pos ? ge * d8[v] * qsj[4 * mt + v] * kse : 0.f;
+          cq[j][e] = c;
+          ck[e][j] = c;
+        }
+      }
+      // dw: sum over the wave's 16 keys (the 16 lanes of a row), then over waves
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        uint32_t x = __float_as_uint(dwl[i]);
+        x = __float_as_uint(__uint_as_float(x) + __uint_as_float(dpp<kDppXor1>(x)));
+        x = __float_as_uint(__uint_as_float(x) + __uint_as_float(dpp<kDppXor2>(x)));
+        x = __float_as_uint(__uint_as_float(x) + __uint_as_float(dpp<kDppHalfMirror>(x)));
+        x = __float_as_uint(__uint_as_float(x) + __uint_as_float(dpp<kDppMirror>(x)));
+        if (n == 0) dwp[wv][16 * (i >> 2) + 4 * g + (i & 3)] = __uint_as_float(x);
+      }
+    }
+    __syncthreads();
+    if (tid < IH) dwacc += dwp[0][tid] + dwp[1][tid] + dwp[2][tid] + dwp[3][tid];
+    // dq[j][d] += sum_e cq[j][e] kf[e][d]: thread = 4 heads x 8 dims, kept in registers
+    for (int e = 0; e < BG; ++e) {
+      const float4 k0 = *reinterpret_cast<const float4*>(&kf[e][d0]);
+      const float4 k1 = *reinterpret_cast<const float4*>(&kf[e][d0 + 4]);
+      const float kv[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const float c = cq[j0 + a][e];
+#pragma unroll
+        for (int d = 0; d < 8; ++d) accq[a][d] = fmaf(c, kv[d], accq[a][d]);
+      }
+    }
+    // dk[e][d] += sum_j ck[e][j] qf[j][d]: thread = 4 keys x 8 dims, added per group
+    {
+      float acc[4][8] = {};
+      for (int j = 0; j < IH; ++j) {
+        const float4 q0 = *reinterpret_cast<const float4*>(&qf[j][d0]);
+        const float4 q1 = *reinterpret_cast<const float4*>(&qf[j][d0 + 4]);
+        const float qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const float c = ck[j0 + a][j];
+#pragma unroll
+          for (int d = 0; d < 8; ++d) acc[a][d] = fmaf(c, qv[d], acc[a][d]);
+        }
+      }
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int row = rows_s[j0 + a];
+        if (row < 0) continue;
+        float* dkr = dk + (paged ? (size_t)row : (size_t)b * N + row) * ID;
+#pragma unroll
+        for (int d = 0; d < 8; ++d)
+          if (acc[a][d] != 0.f) atomicAdd(&dkr[d0 + d], acc[a][d]);
+      }
+    }
+  }
+  if (tid < IH && dwacc != 0.f) atomicAdd(&dw[(size_t)r * IH + tid], dwacc);
+  float* dqr = dq + (size_t)r * IH * ID;
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int d = 0; d < 8; ++d)
+      if (accq[a][d] != 0.f) atomicAdd(&dqr[(size_t)(j0 + a) * ID + d0 + d], accq[a][d]);
+}
+
+}  // namespace
+
+size_t indexer_loss_workspace_bytes(int num_rows, int topk) {
+  return (size_t)num_rows * topk * sizeof(float);
+}
+
+hipError_t launch_indexer_loss(const dsa_rows& rows, const void* q, const void* latent,
+                               const int32_t* indices, const float* lse, float softmax_scale,
+                               const float* scores, int64_t ld, float* loss, float* dscores,
+                               void* workspace, hipStream_t stream, const PageMap& pm) {
+  const int R = rows.num_rows;
+  if (R == 0) return hipSuccess;
+  int splits = 1;
+  while (splits < kTopk / TBE && (int64_t)R * splits < 256) splits <<= 1;
+  float* u = static_cast<float*>(workspace);
+  hipLaunchKernelGGL(attn_target_kernel, dim3(R * splits), dim3(TT), 0, stream,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(latent), indices,
+                     lse, rows.row_seq, rows.row_pos, R, rows.num_seqs, rows.max_ctx, kTopk, splits,
+                     softmax_scale * 1.44269504088896340736f, u, pm);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(indexer_kl_kernel, dim3(R), dim3(KT), 0, stream, scores, ld, indices, u,
+                     rows.row_seq, rows.row_pos, rows.num_seqs, rows.max_ctx, kTopk, loss, dscores);
+  return hipGetLastError();
+}
+
+hipError_t launch_indexer_backward(const dsa_rows& rows, const uint8_t* q_idx,
+                                   const float* q_scale, const float* w, const uint8_t* k_idx,
+                                   const float* k_scale, const int32_t* indices,
+                                   const float* dscores, float* dq, float* dw, float* dk,
+                                   hipStream_t stream, const PageMap& pm) {
+  const int R = rows.num_rows;
+  if (R == 0) return hipSuccess;
+  hipLaunchKernelGGL(indexer_bwd_kernel, dim3(R * (kTopk / (BG * BGPB))), dim3(BT), 0, stream, q_idx,
+                     q_scale, w, k_idx, k_scale, indices, dscores, rows.row_seq, rows.row_pos,
+                     rows.num_seqs, rows.max_ctx, kTopk, dq, dw, dk, pm);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

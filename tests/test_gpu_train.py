@@ -1,0 +1,202 @@
+"""Parity of the indexer training loss and its backward (through the C ABI) with
+the float64 oracle.
+
+Each kernel is checked on oracle inputs, so that only its own arithmetic is
+measured.  The loss is fed the oracle's scores (rounded to fp32) and the oracle's
+selection; it uses the attention lse that the library computes for that
+selection.  The backward is fed a seeded gradient.  The bars follow the
+arithmetic:
+* target and softmax run in fp32 over 576-term bf16 dots and 2048-entry sums, so
+  p and softmax carry relative errors near 1e-5: |d dI_i| <= 1e-3 (p_i +
+  softmax_i) + 1e-7 and |d loss| <= 1e-3 |loss| + 1e-6;
+* the backward's dots are the forward's fp8 MFMA sums, whose error reaches
+  2.6e-4 of the largest product, so a ReLU mask may flip where a dot lies within
+  2e-3 of sum_d |q_d k_d| of zero.  Such a pair may add its whole term, and it is
+  allowed for.  The fp32 sums add 1e-5 of the absolute sum of the terms.
+A composed run (the GPU's own scores and selection) is held to C2 plus a bar on
+the loss that accounts for the indexer's own C1 error.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import dsa_inputs as di
+import oracle
+from dsa_check import HostInputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import sparse_attention_fp8_amd as m
+    return m
+
+
+_DEV = {}
+
+
+def dev_inputs(name: str) -> di.Inputs:
+    if name not in _DEV:
+        _DEV.clear()
+        torch.cuda.empty_cache()
+        print(f"[gen] {name}", flush=True)
+        _DEV[name] = di.make_inputs(di.CONFIGS[name], 0, device="cuda")
+    return _DEV[name]
+
+
+def _oracle_setup(cfg, host, rows):
+    """Per sampled row: oracle scores, oracle selection (padded to k), dequantised
+    q, keys and latent entries of the selection."""
+    out = []
+    for r in rows:
+        row = host.row(int(r))
+        I = host.scores(row)
+        n = min(cfg.topk, row.t + 1)
+        S = oracle.select_topk(I, n)
+        out.append((row, I, S))
+    return out
+
+
+@pytest.mark.parametrize("name,rows", [("decode32k", [0, 9, 17, 31]),
+                                       ("prefill8k", [5, 2047, 2048, 4100, 8191])])
+def test_indexer_loss_parity(dsa, name, rows):
+    cfg = di.CONFIGS[name]
+    inp = dev_inputs(name)
+    host = HostInputs(cfg)
+    print(f"[loss] {name} rows {rows}", flush=True)
+    setup = _oracle_setup(cfg, host, rows)
+    R = len(rows)
+    ridx = torch.tensor(rows, device="cuda")
+    seq, pos = inp.row_seq[ridx].contiguous(), inp.row_pos[ridx].contiguous()
+    rs = dsa.rows_struct(seq, pos, cfg.num_seqs, cfg.max_ctx, cfg.kv_len - 1)
+    dims = dsa.Dims.from_config(cfg)
+    ld = (cfg.kv_len + 63) // 64 * 64
+    sc = np.zeros((R, ld), dtype=np.float32)
+    idx = np.full((R, cfg.topk), -1, dtype=np.int32)
+    for i, (row, I, S) in enumerate(setup):
+        sc[i, : row.t + 1] = I.astype(np.float32)
+        idx[i, : S.size] = S
+    sc_d, idx_d = torch.from_numpy(sc).cuda(), torch.from_numpy(idx).cuda()
+    q = inp.q[ridx].contiguous()
+    _, lse = dsa.sparse_mla_attn(rs, dims, q, inp.latent, idx_d, cfg.scale)
+    loss, dsc = dsa.indexer_loss(rs, q, inp.latent, idx_d, lse, cfg.scale, sc_d)
+    torch.cuda.synchronize()
+    loss, dsc = loss.cpu().numpy(), dsc.cpu().numpy()
+    for i, (row, I, S) in enumerate(setup):
+        ent = host.latent_rows(row.b, S)
+        p = oracle.attention_target(oracle.decode_bf16(row.q), oracle.decode_bf16(ent), cfg.scale)
+        Is = sc[i, S].astype(np.float64)      # the fp32 scores the kernel read
+        l_ref, g_ref = oracle.indexer_kl(p, Is)
+        sm = np.exp(Is - Is.max())
+        sm /= sm.sum()
+        assert abs(loss[i] - l_ref) <= 1e-3 * abs(l_ref) + 1e-6, (loss[i], l_ref)
+        err = np.abs(dsc[i, : S.size] - g_ref)
+        assert np.all(err <= 1e-3 * (p + sm) + 1e-7), float(err.max())
+        assert np.all(dsc[i, S.size:] == 0.0)
+        print(f"[loss] row {int(rows[i])}: loss {loss[i]:.6f} ref {l_ref:.6f}, "
+              f"max |d dI| {err.max():.2e}", flush=True)
+
+
+def test_indexer_loss_composed(dsa):
+    """The whole forward on the GPU (scores, top-k, attention, loss): the loss is
+    finite and non-negative, dscores sum to ~0 per row, and the loss agrees with the
+    oracle's on its own selection within the indexer's score error."""
+    cfg = di.CONFIGS["decode32k"]
+    inp = dev_inputs("decode32k")
+    host = HostInputs(cfg)
+    R = cfg.num_rows
+    rs = dsa.rows_struct(inp.row_seq, inp.row_pos, cfg.num_seqs, cfg.max_ctx, cfg.kv_len - 1)
+    dims = dsa.Dims.from_config(cfg)
+    sc = dsa.indexer_scores(rs, dims, inp.q_idx, inp.q_scale, inp.w, inp.k_idx, inp.k_scale)
+    idx = dsa.topk(rs, cfg.topk, sc)
+    _, lse = dsa.sparse_mla_attn(rs, dims, inp.q, inp.latent, idx, cfg.scale)
+    loss, dsc = dsa.indexer_loss(rs, inp.q, inp.latent, idx, lse, cfg.scale, sc)
+    torch.cuda.synchronize()
+    loss, dsc = loss.cpu().numpy(), dsc.cpu().numpy()
+    assert np.all(np.isfinite(loss)) and np.all(loss >= -1e-6)
+    assert np.all(np.abs(dsc.sum(axis=1)) < 1e-3)
+    for r in (0, 31):
+        row = host.row(r)
+        I = host.scores(row)
+        S = oracle.select_topk(I, cfg.topk)
+        ent = host.latent_rows(row.b, S)
+        p = oracle.attention_target(oracle.decode_bf16(row.q), oracle.decode_bf16(ent), cfg.scale)
+        l_ref, _ = oracle.indexer_kl(p, I[S])
+        # C1 allows score errors up to 2e-2 of the row's largest score in principle;
+        # measured errors are ~1e-4 of it, which moves a KL of this size by < 5 %
+        assert abs(loss[r] - l_ref) <= 0.05 * l_ref + 1e-4, (r, loss[r], l_ref)
+
+
+@pytest.mark.parametrize("name,rows", [("decode32k", [0, 13, 31]),
+                                       ("prefill8k", list(range(4000, 4016)))])
+def test_indexer_backward_parity(dsa, name, rows):
+    """Seeded dscores on the oracle's selections; for the prefill rows the key
+    gradients of rows that select the same key add up."""
+    cfg = di.CONFIGS[name]
+    inp = dev_inputs(name)
+    host = HostInputs(cfg)
+    print(f"[backward] {name} rows {rows[0]}..{rows[-1]}", flush=True)
+    setup = _oracle_setup(cfg, host, rows)
+    R = len(rows)
+    ridx = torch.tensor(rows, device="cuda")
+    seq, pos = inp.row_seq[ridx].contiguous(), inp.row_pos[ridx].contiguous()
+    rs = dsa.rows_struct(seq, pos, cfg.num_seqs, cfg.max_ctx, cfg.kv_len - 1)
+    rng = np.random.default_rng(77)
+    idx = np.full((R, cfg.topk), -1, dtype=np.int32)
+    g = np.zeros((R, cfg.topk), dtype=np.float32)
+    for i, (row, I, S) in enumerate(setup):
+        idx[i, : S.size] = S
+        g[i, : S.size] = (rng.standard_normal(S.size) * 1e-3).astype(np.float32)
+    dq = torch.zeros(R, 64, 128, dtype=torch.float32, device="cuda")
+    dw = torch.zeros(R, 64, dtype=torch.float32, device="cuda")
+    dk = torch.zeros(cfg.num_seqs, cfg.max_ctx, 128, dtype=torch.float32, device="cuda")
+    dsa.indexer_backward(rs, inp.q_idx[ridx].contiguous(), inp.q_scale[ridx].contiguous(),
+                         inp.w[ridx].contiguous(), inp.k_idx, inp.k_scale,
+                         torch.from_numpy(idx).cuda(), torch.from_numpy(g).cuda(), dq, dw, dk)
+    torch.cuda.synchronize()
+    dq, dw = dq.cpu().numpy(), dw.cpu().numpy()
+    dk_ref, dk_tol, keys_of = {}, {}, {}
+    for i, (row, I, S) in enumerate(setup):
+        qf = oracle.decode_e4m3fn(row.q_idx) * row.q_scale[:, None]
+        codes, ksc = host.keys(row.b, row.t + 1)
+        kf = oracle.decode_e4m3fn(codes[S]) * ksc[S][:, None]
+        gi = g[i, : S.size].astype(np.float64)
+        q_ref, w_ref, k_ref = oracle.indexer_backward(qf, row.w, kf, gi)
+        dots = qf @ kf.T
+        amb = np.abs(dots) <= 2e-3 * (np.abs(qf) @ np.abs(kf).T)     # mask may flip
+        coef_abs = np.abs(row.w)[:, None] * np.abs(gi)[None, :]       # |w_j g_s|
+        terms_q = (coef_abs * (dots > 0)) @ np.abs(kf)
+        tol_q = 1e-5 * terms_q + (coef_abs * amb) @ np.abs(kf) + 1e-12
+        assert np.all(np.abs(dq[i] - q_ref) <= tol_q), float(np.max(np.abs(dq[i] - q_ref) - tol_q))
+        # every dot may be off by the MFMA's error bound (2e-3 of sum |q_d k_d|)
+        tol_w = 1e-5 * (np.maximum(dots, 0) @ np.abs(gi)) + \
+            (2e-3 * (np.abs(qf) @ np.abs(kf).T)) @ np.abs(gi) + 1e-12
+        assert np.all(np.abs(dw[i] - w_ref) <= tol_w)
+        tol_k = 1e-5 * ((coef_abs * (dots > 0)).T @ np.abs(qf)) + (coef_abs * amb).T @ np.abs(qf) + 1e-12
+        for a, s in enumerate(S):
+            key = (row.b, int(s))
+            dk_ref[key] = dk_ref.get(key, 0.0) + k_ref[a]
+            dk_tol[key] = dk_tol.get(key, 0.0) + tol_k[a]
+    keys = list(dk_ref)
+    bt = torch.tensor([k[0] for k in keys], device="cuda")
+    st = torch.tensor([k[1] for k in keys], device="cuda")
+    got = dk[bt, st].cpu().numpy()
+    ref = np.stack([dk_ref[k] for k in keys])
+    tol = np.stack([dk_tol[k] for k in keys])
+    assert np.all(np.abs(got - ref) <= tol + 1e-12), float(np.max(np.abs(got - ref) - tol))
+    count = {}
+    for row, I, S in setup:
+        for s_ in S.tolist():
+            count[(row.b, s_)] = count.get((row.b, s_), 0) + 1
+    shared = sum(1 for k in keys if count[k] > 1)
+    print(f"[backward] {name}: dq, dw, dk within bars; {len(keys)} keys, {shared} selected by "
+          f"several rows", flush=True)
+    # nothing outside the selected keys is written
+    mask = torch.zeros(cfg.num_seqs, cfg.max_ctx, dtype=torch.bool, device="cuda")
+    mask[bt, st] = True
+    assert bool((dk[~mask] == 0).all())
