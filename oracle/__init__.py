@@ -16,6 +16,8 @@ from .dsa_oracle import (  # noqa: F401
     indexer_kl,
     indexer_row,
     indexer_scores,
+    mha_attention,
+    mha_decompress,
     paged_append,
     paged_view,
     pow2_scale,

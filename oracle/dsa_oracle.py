@@ -55,6 +55,15 @@ prose around the lost equation.  "nsmao report" means the page
    over the attended positions; gradients flow into I (p is a constant target) and
    from I into the indexer queries, weights and keys.
 
+7. Masked MHA mode (V3.2-Exp paper, §3 "inference cost": short-sequence prefill
+   runs a masked MHA mode that simulates DSA; Appendix A, Fig. 4: MLA's MHA mode,
+   used for training and prefill, and its MQA mode, used for decoding).  Reading:
+   each head decompresses its own key k[h,s] = [W_UK[h] c[s,:512]; c[s,512:]] and
+   value v[h,s] = W_UV[h] c[s,:512] from the shared latent entry, and attends over
+   the positions the indexer selected (a mask on the causal positions).  With the
+   absorbed query [W_UK[h]^T q_nope[h]; q_rope[h]] the MQA mode gives the same
+   weights, and W_UV[h] times its latent-space output is the MHA output.
+
 Inputs are the exact byte images the GPU receives: e4m3fn codes with fp32 scales
 (dequantised value = decode(code) * scale), bf16 bit patterns, or plain fp32.  The
 oracle decodes them with its own decoders and computes every step in float64.
@@ -70,7 +79,7 @@ __all__ = [
     "sparse_attention", "indexer_row", "attention_row", "dsa_row",
     "encode_e4m3fn", "encode_bf16", "pow2_scale", "quantize_e4m3fn", "project",
     "project_tokens", "append_rows", "paged_view", "paged_append", "attention_target",
-    "indexer_kl", "indexer_backward",
+    "indexer_kl", "indexer_backward", "mha_decompress", "mha_attention",
 ]
 
 
@@ -384,3 +393,36 @@ def indexer_backward(q: np.ndarray, w: np.ndarray, k: np.ndarray,
     dw = np.maximum(dots, 0.0) @ g
     coef = (w[:, None] * (dots > 0)) * g[None, :]
     return coef @ k, dw, coef.T @ q
+
+
+# ---------------------------------------------------------------------------
+# O8: masked MHA mode
+# ---------------------------------------------------------------------------
+
+def mha_decompress(entries: np.ndarray, w_uk: np.ndarray, w_uv: np.ndarray,
+                   v_dim: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Per-head keys and values of latent entries [n, D_k] (first v_dim columns
+    latent, the rest rope): k [H, n, dh + D_k - v_dim] = [W_UK[h] c; c_rope] and
+    v [H, n, dv] = W_UV[h] c, with w_uk [H, dh, v_dim], w_uv [H, dv, v_dim]."""
+    c = np.asarray(entries, dtype=np.float64)
+    lat, rope = c[:, :v_dim], c[:, v_dim:]
+    k_nope = np.einsum("hdc,nc->hnd", np.asarray(w_uk, dtype=np.float64), lat)
+    v = np.einsum("hdc,nc->hnd", np.asarray(w_uv, dtype=np.float64), lat)
+    H = k_nope.shape[0]
+    k = np.concatenate([k_nope, np.broadcast_to(rope, (H,) + rope.shape)], axis=2)
+    return k, v
+
+
+def mha_attention(q: np.ndarray, entries: np.ndarray, w_uk: np.ndarray, w_uv: np.ndarray,
+                  scale: float, v_dim: int) -> Tuple[np.ndarray, np.ndarray]:
+    """MHA-mode attention of one query token over its selected latent entries:
+    q [H, dh + rope] (per-head nope and rope parts); returns (o [H, dv], lse [H])
+    with z[h,s] = scale q[h] . k[h,s] and o[h] = sum_s softmax_s(z[h]) v[h,s]."""
+    k, v = mha_decompress(entries, w_uk, w_uv, v_dim)
+    q = np.asarray(q, dtype=np.float64)
+    z = scale * np.einsum("hd,hnd->hn", q, k)
+    m = z.max(axis=1, keepdims=True)
+    e = np.exp(z - m)
+    Z = e.sum(axis=1, keepdims=True)
+    o = np.einsum("hn,hnd->hd", e / Z, v)
+    return o, m[:, 0] + np.log(Z[:, 0])

@@ -632,4 +632,41 @@ def pin_indexer_backward():
             assert abs(fd - grad[idx]) < 1e-6 * (1 + abs(fd)), (name, idx, fd, grad[idx])
 
 
+# ---------------------------------------------------------------- P9 masked MHA mode
+
+def pin_mha_matches_mqa_absorbed():
+    """MHA mode equals MQA mode with the absorbed query: sparse_attention with
+    q_mqa[h] = [W_UK[h]^T q_nope[h]; q_rope[h]] gives the same lse, and W_UV[h] times
+    its latent-space output is the MHA output (App. A, Fig. 4)."""
+    r = _rng(51)
+    H, dh, dv, lat, rope, n = 3, 4, 5, 6, 2, 7
+    w_uk = r.standard_normal((H, dh, lat))
+    w_uv = r.standard_normal((H, dv, lat))
+    ent = r.standard_normal((n, lat + rope))
+    q = r.standard_normal((H, dh + rope))
+    o, lse = O.mha_attention(q, ent, w_uk, w_uv, 0.4, lat)
+    q_mqa = np.concatenate([np.einsum("hdc,hd->hc", w_uk, q[:, :dh]), q[:, dh:]], axis=1)
+    o_lat, lse_mqa = O.sparse_attention(q_mqa, ent, 0.4, lat)
+    np.testing.assert_allclose(lse, lse_mqa, rtol=1e-12)
+    np.testing.assert_allclose(o, np.einsum("hdc,hc->hd", w_uv, o_lat), rtol=1e-11, atol=1e-12)
+
+
+def pin_mha_decompress_bruteforce():
+    """Decompressed keys and values against loops over heads, entries and dims."""
+    r = _rng(52)
+    H, dh, dv, lat, rope, n = 2, 3, 2, 4, 2, 3
+    w_uk = r.standard_normal((H, dh, lat))
+    w_uv = r.standard_normal((H, dv, lat))
+    ent = r.standard_normal((n, lat + rope))
+    k, v = O.mha_decompress(ent, w_uk, w_uv, lat)
+    for h in range(H):
+        for s in range(n):
+            for d in range(dh):
+                assert abs(k[h, s, d] - math.fsum(w_uk[h, d, c] * ent[s, c] for c in range(lat))) < 1e-12
+            for d in range(rope):
+                assert k[h, s, dh + d] == ent[s, lat + d]
+            for d in range(dv):
+                assert abs(v[h, s, d] - math.fsum(w_uv[h, d, c] * ent[s, c] for c in range(lat))) < 1e-12
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -10,7 +10,7 @@ _orig = {name: getattr(O, name) for name in
          ["indexer_scores", "select_topk", "sparse_attention", "decode_e4m3fn",
           "decode_bf16", "indexer_row", "encode_e4m3fn", "encode_bf16", "pow2_scale",
          "quantize_e4m3fn", "project", "project_tokens", "paged_view", "paged_append",
-         "attention_target", "indexer_kl", "indexer_backward"]}
+         "attention_target", "indexer_kl", "indexer_backward", "mha_decompress"]}
 
 
 def _no_relu(q, w, k):
@@ -195,6 +195,19 @@ def _bwd_dq_without_w(q, w, k, g):
         _orig["indexer_backward"](q, w, k, g)[1], _orig["indexer_backward"](q, w, k, g)[2]
 
 
+def _mha_rope_dropped(entries, w_uk, w_uv, v_dim):
+    k, v = _orig["mha_decompress"](entries, w_uk, w_uv, v_dim)
+    k = k.copy()
+    k[:, :, w_uk.shape[1]:] = 0.0
+    return k, v
+
+
+def _mha_value_uses_uk(entries, w_uk, w_uv, v_dim):
+    k, _ = _orig["mha_decompress"](entries, w_uk, w_uv, v_dim)
+    _, v = _orig["mha_decompress"](entries, w_uv, w_uk, v_dim)
+    return k, v
+
+
 MUTANTS = [
     ("indexer_scores", _no_relu),
     ("indexer_scores", _relu_after_sum),
@@ -228,6 +241,8 @@ MUTANTS = [
     ("indexer_kl", _kl_grad_sign),
     ("indexer_backward", _bwd_no_relu_in_dw),
     ("indexer_backward", _bwd_dq_without_w),
+    ("mha_decompress", _mha_rope_dropped),
+    ("mha_decompress", _mha_value_uses_uk),
 ]
 
 
