@@ -438,6 +438,49 @@ class ProjGenerator:
         return tuple(out)
 
 
+# ---------------------------------------------------------------------------
+# masked MHA mode: per-head queries and the key / value up-projections
+# ---------------------------------------------------------------------------
+
+T_QMHA, T_WUK, T_WUV = 11, 12, 13
+
+
+class MhaGenerator:
+    """q ~ N(0,1) [R, 128, 192] and w_uk, w_uv ~ N(0,1)/sqrt(512) [128, 128, 512],
+    all bf16, for a workload's rows."""
+
+    def __init__(self, cfg_id: int, set_id: int = 0, heads: int = 128, head_dim: int = 128,
+                 rope: int = 64, latent: int = 512):
+        self.cfg_id, self.set_id = cfg_id, set_id
+        self.H, self.dh, self.dr, self.dl = heads, head_dim, rope, latent
+
+    def _key(self, tensor_id: int) -> int:
+        return stream_key(self.cfg_id, self.set_id, tensor_id)
+
+    def q(self, r0: int, r1: int, device="cpu") -> torch.Tensor:
+        per = self.H * (self.dh + self.dr)
+        x = normal(self._key(T_QMHA), _flat(r0 * per, (r1 - r0) * per, device))
+        return to_bf16(x.view(r1 - r0, self.H, self.dh + self.dr))
+
+    def weights(self, device="cpu") -> Tuple[torch.Tensor, torch.Tensor]:
+        n = self.H * self.dh * self.dl
+        out = []
+        for tid in (T_WUK, T_WUV):
+            x = normal(self._key(tid), _flat(0, n, device)) * (1.0 / math.sqrt(self.dl))
+            out.append(to_bf16(x.view(self.H, self.dh, self.dl)))
+        return tuple(out)
+
+
+def random_selection(t: int, k: int, rng: np.random.Generator) -> np.ndarray:
+    """A valid selection for a row at position t: all of 0..t when t + 1 <= k, else
+    k distinct positions drawn uniformly; ascending, padded with -1 to k."""
+    n = min(k, t + 1)
+    s = np.arange(t + 1) if t + 1 <= k else np.sort(rng.choice(t + 1, size=k, replace=False))
+    out = np.full(k, -1, dtype=np.int32)
+    out[:n] = s
+    return out
+
+
 def sample_rows(cfg: Config, count: int = 256, seed_offset: int = 99) -> np.ndarray:
     """Seeded sample of global row indices, always holding the first row, the rows
     at positions k-1 and k (the dense/sparse boundary) and the last row."""

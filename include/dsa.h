@@ -293,6 +293,32 @@ dsa_status dsa_indexer_backward(const dsa_rows* rows, const dsa_dims* dims, cons
                                 const float* dscores, float* dq, float* dw, float* dk,
                                 void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Masked MHA mode for short prefill (DeepSeek-V3.2-Exp paper, section 3: short-
+ * sequence prefill runs a masked MHA mode that simulates DSA; Appendix A, Fig. 4:
+ * MLA's MHA mode).  Each head decompresses its own key and value from the latent:
+ *   k[h,s] = [w_uk[h] latent[b,s,0:512] ; latent[b,s,512:576]],  v[h,s] = w_uv[h] latent[b,s,0:512]
+ * and row r attends per head over its selected positions S (indices[r,:] in [0, t]):
+ *   out[r,h,:] = sum_{s in S} softmax_s(softmax_scale q[r,h,:] . k[h,s]) v[h,s],
+ *   lse[r,h] = log sum_{s in S} e^(softmax_scale q[r,h,:] . k[h,s])
+ * This equals w_uv[h] times the MQA-mode output (dsa_sparse_mla_attn) for the
+ * absorbed query [w_uk[h]^T q[r,h,0:128] ; q[r,h,128:192]].
+ *   q     [R, H, 192] bf16 (128 nope + 64 rope dims per head)
+ *   w_uk  [H, 128, 512] bf16, w_uv [H, 128, 512] bf16
+ *   out   [R, H, 128] bf16; lse [R, H] fp32 or NULL
+ * Production dims; one sequence per call (rows of a sequence other than
+ * row_seq[0]'s are not processed); max_pos + 1 <= 16384.  The workspace holds the
+ * decompressed keys and values of positions [0, max_pos] and the selection mask
+ * (dsa_mha_prefill_workspace_size).  bf16 MFMA with fp32 accumulation and softmax;
+ * decompressed keys and values and the softmax weights are rounded to bf16.
+ * ------------------------------------------------------------------------- */
+size_t dsa_mha_prefill_workspace_size(const dsa_rows* rows, const dsa_dims* dims);
+
+dsa_status dsa_mha_prefill(const dsa_rows* rows, const dsa_dims* dims, const void* q,
+                           const void* latent, const void* w_uk, const void* w_uv,
+                           const int32_t* indices, float softmax_scale, void* out, float* lse,
+                           void* workspace, size_t ws_bytes, void* stream);
+
 /* Status text, and the detail of the last failure on the calling thread. */
 const char* dsa_status_string(dsa_status status);
 const char* dsa_last_error(void);

@@ -20,6 +20,7 @@ __all__ = [
     "sparse_mla_attn_workspace_size", "project_append", "project_append_workspace_size",
     "pages_struct", "indexer_scores_paged", "sparse_mla_attn_paged", "forward_paged",
     "project_append_paged", "indexer_loss", "indexer_loss_workspace_size", "indexer_backward",
+    "mha_prefill", "mha_prefill_workspace_size",
     "DSAError", "EXPORTED_SYMBOLS",
 ]
 
@@ -34,6 +35,7 @@ EXPORTED_SYMBOLS = [
     "dsa_project_append_workspace_size", "dsa_project_append", "dsa_indexer_scores_paged",
     "dsa_sparse_mla_attn_paged", "dsa_forward_paged", "dsa_project_append_paged",
     "dsa_indexer_loss_workspace_size", "dsa_indexer_loss", "dsa_indexer_backward",
+    "dsa_mha_prefill_workspace_size", "dsa_mha_prefill",
     "dsa_status_string", "dsa_last_error", "dsa_api_version",
 ]
 
@@ -91,10 +93,13 @@ def _load() -> ctypes.CDLL:
     L.dsa_indexer_loss_workspace_size.restype = sz
     L.dsa_indexer_loss.argtypes = [R, D, vp, vp, vp, vp, f32, vp, i64, vp, vp, vp, sz, vp]
     L.dsa_indexer_backward.argtypes = [R, D] + [vp] * 10 + [vp]
+    L.dsa_mha_prefill_workspace_size.argtypes = [R, D]
+    L.dsa_mha_prefill_workspace_size.restype = sz
+    L.dsa_mha_prefill.argtypes = [R, D, vp, vp, vp, vp, vp, f32, vp, vp, vp, sz, vp]
     for name in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_attn", "dsa_forward",
                  "dsa_project_append", "dsa_indexer_scores_paged", "dsa_sparse_mla_attn_paged",
                  "dsa_forward_paged", "dsa_project_append_paged", "dsa_indexer_loss",
-                 "dsa_indexer_backward"):
+                 "dsa_indexer_backward", "dsa_mha_prefill"):
         getattr(L, name).restype = ctypes.c_int
     L.dsa_status_string.argtypes = [ctypes.c_int]
     L.dsa_status_string.restype = ctypes.c_char_p
@@ -564,3 +569,40 @@ def indexer_backward(rows: _Rows, q_idx, q_scale, w, k_idx, k_scale, indices, ds
                                     _ptr(indices), _ptr(dscores), _ptr(dq), _ptr(dw), _ptr(dk),
                                     _stream()))
     return dq, dw, dk
+
+
+# ---------------------------------------------------------------- masked MHA mode
+
+def mha_prefill_workspace_size(rows: _Rows, dims: Dims = PRODUCTION_DIMS) -> int:
+    ds = dims_struct(dims)
+    return int(lib.dsa_mha_prefill_workspace_size(ctypes.byref(rows), ctypes.byref(ds)))
+
+
+def mha_prefill(rows: _Rows, q, latent, w_uk, w_uv, indices, softmax_scale: float,
+                dims: Dims = PRODUCTION_DIMS, out=None, lse=None,
+                workspace: Optional[torch.Tensor] = None):
+    """dsa_mha_prefill: (out [R, H, 128] bf16, lse [R, H]) of the masked MHA mode."""
+    R = rows.num_rows
+    for t, name in ((q, "q"), (latent, "latent"), (w_uk, "w_uk"), (w_uv, "w_uv")):
+        _dev(t, torch.bfloat16, name)
+    _dev(indices, torch.int32, "indices")
+    _shape(q, (R, dims.n_heads, 192), "q")
+    _shape(w_uk, (dims.n_heads, 128, dims.v_dim), "w_uk")
+    _shape(w_uv, (dims.n_heads, 128, dims.v_dim), "w_uv")
+    _shape(indices, (R, dims.topk), "indices")
+    _caches(rows, dims, None, None, latent)
+    if out is None:
+        out = torch.empty(R, dims.n_heads, 128, dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty(R, dims.n_heads, dtype=torch.float32, device=q.device)
+    _dev(out, torch.bfloat16, "out")
+    _dev(lse, torch.float32, "lse")
+    need = mha_prefill_workspace_size(rows, dims)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ds = dims_struct(dims)
+    _check(lib.dsa_mha_prefill(ctypes.byref(rows), ctypes.byref(ds), _ptr(q), _ptr(latent),
+                               _ptr(w_uk), _ptr(w_uv), _ptr(indices), float(softmax_scale),
+                               _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+                               _stream()))
+    return out, lse

@@ -446,4 +446,31 @@ dsa_status dsa_indexer_backward(const dsa_rows* rows, const dsa_dims* dims, cons
   return err == hipSuccess ? DSA_OK : hip_fail(err, "indexer backward launch");
 }
 
+size_t dsa_mha_prefill_workspace_size(const dsa_rows* rows, const dsa_dims* dims) {
+  if (check_rows(rows) != DSA_OK || dims == nullptr || !is_production(*dims)) return 0;
+  return dsa::mha_workspace_bytes(rows->num_rows, rows->num_seqs, rows->max_pos);
+}
+
+dsa_status dsa_mha_prefill(const dsa_rows* rows, const dsa_dims* dims, const void* q,
+                           const void* latent, const void* w_uk, const void* w_uv,
+                           const int32_t* indices, float softmax_scale, void* out, float* lse,
+                           void* workspace, size_t ws_bytes, void* stream) {
+  dsa_status st = check_rows(rows);
+  if (st != DSA_OK) return st;
+  if (dims == nullptr) return fail(DSA_E_INVALID, "dims is NULL");
+  if (!is_production(*dims))
+    return fail(DSA_E_UNSUPPORTED, "the MHA mode supports the production dims only");
+  if (rows->max_pos + 1 > 16384)
+    return fail(DSA_E_UNSUPPORTED, "the MHA mode is for short prefill: max_pos + 1 <= 16384");
+  if (rows->num_rows == 0) return DSA_OK;
+  if (!q || !latent || !w_uk || !w_uv || !indices || !out)
+    return fail(DSA_E_INVALID, "NULL tensor pointer");
+  const size_t need = dsa::mha_workspace_bytes(rows->num_rows, rows->num_seqs, rows->max_pos);
+  if (workspace == nullptr || ws_bytes < need)
+    return fail(DSA_E_WORKSPACE, "the MHA mode needs %zu workspace bytes, got %zu", need, ws_bytes);
+  const hipError_t err = dsa::launch_mha(*rows, q, latent, w_uk, w_uv, indices, softmax_scale, out,
+                                         lse, workspace, as_stream(stream));
+  return err == hipSuccess ? DSA_OK : hip_fail(err, "MHA-mode launch");
+}
+
 }  // extern "C"

@@ -15,6 +15,7 @@ constexpr int kHeads = 128;
 constexpr int kQkDim = 576;
 constexpr int kVDim = 512;
 constexpr int kTopk = 2048;
+constexpr int kMhaHeadDim = 128;  // MHA mode: per-head nope-key and value width
 
 // Location of cache entries.  table == nullptr: contiguous caches [B, N, ...], entry
 // (b, s) at row b * N + s.  Otherwise a page pool [npages, 1 << shift, ...] seen
@@ -79,5 +80,11 @@ hipError_t launch_indexer_backward(const dsa_rows& rows, const uint8_t* q_idx,
                                    const float* k_scale, const int32_t* indices,
                                    const float* dscores, float* dq, float* dw, float* dk,
                                    hipStream_t stream, const PageMap& pm = PageMap());
+
+size_t mha_workspace_bytes(int num_rows, int num_seqs, int max_pos);
+
+hipError_t launch_mha(const dsa_rows& rows, const void* q, const void* latent, const void* w_uk,
+                      const void* w_uv, const int32_t* indices, float softmax_scale, void* out,
+                      float* lse, void* workspace, hipStream_t stream);
 
 }  // namespace dsa

@@ -1,0 +1,304 @@
+// Masked MHA mode of the sparse attention, for short prefill.
+//
+// DeepSeek-V3.2-Exp paper, section 3 ("inference cost"): for short-sequence
+// prefill a masked MHA mode simulates DSA; Appendix A, Fig. 4: MLA's MHA mode
+// (training and prefill) and MQA mode (decoding).  In MHA mode every head has its
+// own key and value, decompressed from the shared latent entry c_s:
+//   k[h,s] = [W_UK[h] c_s[:512] ; c_s[512:576]]     (128 + 64 dims)
+//   v[h,s] = W_UV[h] c_s[:512]                       (128 dims)
+// and query row r attends, per head, over the positions the indexer selected:
+//   o[r,h] = sum_{s in S_r} softmax_s(scale q[r,h] . k[h,s]) v[h,s]
+// which equals W_UV[h] times the MQA-mode output with the absorbed query.
+//
+// Three kernels: mha_decompress_kernel (bf16 MFMA GEMM of the latent rows with the
+// stacked W_UK / W_UV; keys stored [s][h][128], values transposed [h][128][s]),
+// mha_mask_kernel (the selection as one bit per causal position), and
+// mha_attn_kernel (flash attention per head over 32-key stages with the mask).
+#include "dsa_device.h"
+#include "dsa_internal.h"
+
+namespace dsa {
+namespace {
+
+constexpr int H = kHeads;    // 128
+constexpr int DL = kVDim;    // 512 latent dims
+constexpr int DR = kQkDim - kVDim;  // 64 rope dims
+constexpr int DH = kMhaHeadDim;     // 128 nope / value dims per head
+constexpr int DQ = DH + DR;         // 192 query dims per head
+constexpr int KCOLS = H * DH;       // 16384 key columns, then as many value columns
+
+// ---------------------------------------------------------------------------
+// Decompression: y[s, :] = W c_s with W = [W_UK; W_UV] (32768 x 512).  Block =
+// 4 waves, 64 positions x 256 columns; wave w owns columns [64 w, 64 w + 64) for
+// all 64 positions (4 x 4 MFMA tiles); operands go straight from global memory
+// into registers one contraction step ahead.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void mha_decompress_kernel(
+    const uint16_t* __restrict__ latent, const uint16_t* __restrict__ w_uk,
+    const uint16_t* __restrict__ w_uv, int N, int Lc, int L, uint16_t* __restrict__ kout,
+    uint16_t* __restrict__ vtout) {
+  // positions [0, Lc) hold entries; the rest of the padded length L repeats the last
+  // one, so every position of the outputs is finite
+  const int b = blockIdx.z;
+  const int s0 = blockIdx.y * 64;
+  const int c0 = blockIdx.x * 256;
+  const int l = lane_id(), wv = threadIdx.x >> 6, g = l >> 4, n = l & 15;
+  const uint16_t* lat = latent + (size_t)b * N * kQkDim;
+  // A rows (positions, clamped to the last valid one) and B rows (weight rows)
+  const uint16_t* arow[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+    arow[mt] = lat + (size_t)min(s0 + 16 * mt + n, Lc - 1) * kQkDim + 8 * g;
+  const uint16_t* brow[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int col = c0 + 64 * wv + 16 * nt + n;
+    brow[nt] = (col < KCOLS ? w_uk + (size_t)col * DL : w_uv + (size_t)(col - KCOLS) * DL) + 8 * g;
+  }
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  i32x4 a[2][4], bb[2][4];
+  auto load = [&](int slot, int ks) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[slot][i] = *reinterpret_cast<const i32x4*>(arow[i] + 32 * ks);
+      bb[slot][i] = *reinterpret_cast<const i32x4*>(brow[i] + 32 * ks);
+    }
+  };
+  load(0, 0);
+#pragma unroll
+  for (int ks = 0; ks < DL / 32; ++ks) {
+    if (ks + 1 < DL / 32) load((ks + 1) & 1, ks + 1);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        acc[mt][nt] = mfma_bf16_16x16x32(as_bf16x8(a[ks & 1][mt]), as_bf16x8(bb[ks & 1][nt]),
+                                         acc[mt][nt]);
+  }
+  // lane holds positions s0 + 16 mt + 4 g + v of column c0 + 64 wv + 16 nt + n
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int col = c0 + 64 * wv + 16 * nt + n;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const int sp = s0 + 16 * mt + 4 * g;  // L is a multiple of 64: all four exist
+      if (col < KCOLS) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          kout[((size_t)b * L + sp + v) * KCOLS + col] = bf16_bits(acc[mt][nt][v]);
+      } else {  // four consecutive positions of one value row
+        uint16_t* dst = vtout + ((size_t)b * KCOLS + (col - KCOLS)) * L + sp;
+        *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(acc[mt][nt][0], acc[mt][nt][1]),
+                                                    pack_bf16x2(acc[mt][nt][2], acc[mt][nt][3]));
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Selection mask: bit s of row r (words [R, L / 32]) is set when s is one of the
+// row's selected positions (0 <= s <= t).  One block per row, built in LDS.
+// ---------------------------------------------------------------------------
+constexpr int kMaxMhaLen = 16384;
+
+__global__ __launch_bounds__(256) void mha_mask_kernel(const int32_t* __restrict__ indices,
+                                                       const int32_t* __restrict__ row_pos,
+                                                       int topk, int L, uint32_t* __restrict__ mask) {
+  __shared__ uint32_t words[kMaxMhaLen / 32];
+  const int r = blockIdx.x, W = L / 32;
+  const int t = row_pos[r];
+  for (int i = threadIdx.x; i < W; i += 256) words[i] = 0u;
+  __syncthreads();
+  for (int i = threadIdx.x; i < topk; i += 256) {
+    const int p = indices[(size_t)r * topk + i];
+    if (p >= 0 && p <= t && p < L) atomicOr(&words[p >> 5], 1u << (p & 31));
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < W; i += 256) mask[(size_t)r * W + i] = words[i];
+}
+
+// ---------------------------------------------------------------------------
+// Attention: block = (head h, 128 query rows), 8 waves of 16 rows.  Per stage of
+// 32 keys the block stages the keys (32 x 192: decompressed nope part + the
+// entries' rope part) and the transposed values (128 x 32) in LDS.  Each wave
+// forms S^T tiles (keys x rows), so a lane holds 8 keys of one row: exactly the
+// B operand (P^T) of the O^T = V^T P^T product, whose A operand (V^T) is read from
+// the transposed value tile in the same key order.  Online softmax in the exp2
+// domain; masked keys get -inf.
+// ---------------------------------------------------------------------------
+constexpr int AW = 8;            // waves
+constexpr int AR = 16 * AW;      // rows per block
+constexpr int AKS = 32;          // keys per stage
+constexpr int KST = DQ + 8;      // key tile row stride (bf16), padded
+constexpr int VST = AKS + 8;     // value tile row stride (bf16), padded
+
+__global__ __launch_bounds__(AW * 64) void mha_attn_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ latent,
+    const uint16_t* __restrict__ kdec, const uint16_t* __restrict__ vtdec,
+    const uint32_t* __restrict__ mask, const int32_t* __restrict__ row_seq,
+    const int32_t* __restrict__ row_pos, int R, int B, int N, int Lc, int L, float scale_log2,
+    uint16_t* __restrict__ out, float* __restrict__ lse) {
+  __shared__ __attribute__((aligned(16))) uint16_t kt[AKS][KST];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[DH][VST];
+  __shared__ int tmax_s[AW];
+  const int h = blockIdx.x;
+  const int r0 = blockIdx.y * AR;
+  const int tid = threadIdx.x, l = lane_id(), wv = tid >> 6, g = l >> 4, n = l & 15;
+  const int W = L / 32;
+
+  // this lane's row (B operand column n of the S^T tiles) and its sequence
+  const int r = r0 + 16 * wv + n;
+  const bool rv = r < R;
+  const int b = rv ? row_seq[r] : -1, t = rv ? row_pos[r] : -1;
+  // the block's sequence: that of its first row (one sequence per call)
+  int bseq = row_seq[min(r0, R - 1)];
+  bseq = (bseq >= 0 && bseq < B) ? bseq : 0;
+  const bool ok = rv && b == bseq && t >= 0 && t < Lc;
+  int tw = ok ? t : -1;
+  tw = max(tw, __shfl_xor(tw, 16));
+  tw = max(tw, __shfl_xor(tw, 32));
+  tw = max(tw, __shfl_xor(tw, 1));
+  tw = max(tw, __shfl_xor(tw, 2));
+  tw = max(tw, __shfl_xor(tw, 4));
+  tw = max(tw, __shfl_xor(tw, 8));
+  if (l == 0) tmax_s[wv] = tw;
+  // queries of this lane's row, contraction step s: dims [32 s + 8 g, +8)
+  i32x4 qr[DQ / 32];
+  {
+    const uint16_t* qp = q + ((size_t)(rv ? r : 0) * H + h) * DQ + 8 * g;
+#pragma unroll
+    for (int s = 0; s < DQ / 32; ++s) qr[s] = *reinterpret_cast<const i32x4*>(qp + 32 * s);
+  }
+  __syncthreads();
+  int tmax = -1;
+#pragma unroll
+  for (int i = 0; i < AW; ++i) tmax = max(tmax, tmax_s[i]);
+  const uint16_t* kseq = kdec + (size_t)bseq * L * KCOLS + (size_t)h * DH;
+  const uint16_t* vseq = vtdec + ((size_t)bseq * KCOLS + (size_t)h * DH) * L;
+  const uint16_t* lseq = latent + (size_t)bseq * N * kQkDim;
+  const uint32_t* mrow = mask + (size_t)(rv ? r : 0) * W;
+
+  f32x4 acc[DH / 16];
+#pragma unroll
+  for (int i = 0; i < DH / 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  for (int k0 = 0; k0 <= tmax; k0 += AKS) {
+    __syncthreads();  // previous stage's tile reads are done
+    // stage keys: 32 keys x (128 nope + 64 rope) and values: 128 dims x 32 keys
+    for (int c = tid; c < AKS * (DQ / 8); c += AW * 64) {
+      const int e = c / (DQ / 8), d8 = c - e * (DQ / 8);
+      const int s = min(k0 + e, L - 1);
+      const uint16_t* src = d8 < DH / 8 ? kseq + (size_t)s * KCOLS + 8 * d8
+                                        : lseq + (size_t)min(s, Lc - 1) * kQkDim + DL + 8 * (d8 - DH / 8);
+      *reinterpret_cast<i32x4*>(&kt[e][8 * d8]) = *reinterpret_cast<const i32x4*>(src);
+    }
+    for (int c = tid; c < DH * (AKS / 8); c += AW * 64) {
+      const int d = c / (AKS / 8), k8 = c - d * (AKS / 8);
+      const int s = k0 + 8 * k8;
+      i32x4 v4 = {0, 0, 0, 0};
+      if (s + 8 <= L) v4 = *reinterpret_cast<const i32x4*>(vseq + (size_t)d * L + s);
+      *reinterpret_cast<i32x4*>(&vt[d][8 * k8]) = v4;
+    }
+    __syncthreads();
+    // S^T = K Q^T: keys 16 mt + 4 g + v (mt = 0, 1) of this lane's row
+    f32x4 st[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int s = 0; s < DQ / 32; ++s)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const bf16x8 ka = as_bf16x8(*reinterpret_cast<const i32x4*>(&kt[16 * mt + n][32 * s + 8 * g]));
+        st[mt] = mfma_bf16_16x16x32(ka, as_bf16x8(qr[s]), st[mt]);
+      }
+    const uint32_t mw = ok ? mrow[k0 >> 5] : 0u;
+    float x[8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int e = 16 * mt + 4 * g + v;
+        const float z = ((mw >> e) & 1u) ? st[mt][v] * scale_log2 : -INFINITY;
+        x[4 * mt + v] = z;
+        mx = fmaxf(mx, z);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
+    float psum = 0.f;
+    float pv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      pv[i] = x[i] == -INFINITY ? 0.f : exp2f(x[i] - m_new);
+      psum += pv[i];
+    }
+    psum += __shfl_xor(psum, 16);
+    psum += __shfl_xor(psum, 32);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    // P^T operand: keys {4g..4g+3, 16+4g..16+4g+3} of this lane's row, as bf16
+    const i32x4 pb = {(int)pack_bf16x2(pv[0], pv[1]), (int)pack_bf16x2(pv[2], pv[3]),
+                      (int)pack_bf16x2(pv[4], pv[5]), (int)pack_bf16x2(pv[6], pv[7])};
+#pragma unroll
+    for (int dt = 0; dt < DH / 16; ++dt) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[dt][v] *= alpha;
+      const uint16_t* vr = &vt[16 * dt + n][0];
+      const uint2 lo = *reinterpret_cast<const uint2*>(vr + 4 * g);
+      const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16 + 4 * g);
+      const i32x4 va = {(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
+      acc[dt] = mfma_bf16_16x16x32(as_bf16x8(va), as_bf16x8(pb), acc[dt]);
+    }
+  }
+  // lane holds dims 16 dt + 4 g + v of its row
+  if (ok) {
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    uint16_t* orow = out + ((size_t)r * H + h) * DH;
+#pragma unroll
+    for (int dt = 0; dt < DH / 16; ++dt)
+      *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * g) =
+          make_uint2(pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv),
+                     pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv));
+    if (lse != nullptr && g == 0)
+      lse[(size_t)r * H + h] = l_run > 0.f ? (m_run + log2f(l_run)) * 0.69314718055994530942f : -INFINITY;
+  }
+}
+
+}  // namespace
+
+size_t mha_workspace_bytes(int num_rows, int num_seqs, int max_pos) {
+  const size_t L = (size_t)(max_pos + 1 + 63) / 64 * 64;
+  return (size_t)num_seqs * L * KCOLS * 2 * sizeof(uint16_t) + (size_t)num_rows * (L / 32) * 4;
+}
+
+hipError_t launch_mha(const dsa_rows& rows, const void* q, const void* latent, const void* w_uk,
+                      const void* w_uv, const int32_t* indices, float softmax_scale, void* out,
+                      float* lse, void* workspace, hipStream_t stream) {
+  const int R = rows.num_rows, B = rows.num_seqs;
+  if (R == 0) return hipSuccess;
+  const int L = (rows.max_pos + 1 + 63) / 64 * 64;
+  uint16_t* kdec = static_cast<uint16_t*>(workspace);
+  uint16_t* vtdec = kdec + (size_t)B * L * KCOLS;
+  uint32_t* mask = reinterpret_cast<uint32_t*>(vtdec + (size_t)B * L * KCOLS);
+  const int Lc = rows.max_pos + 1 <= rows.max_ctx ? rows.max_pos + 1 : rows.max_ctx;
+  hipLaunchKernelGGL(mha_decompress_kernel, dim3(2 * KCOLS / 256, L / 64, B), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(latent), static_cast<const uint16_t*>(w_uk),
+                     static_cast<const uint16_t*>(w_uv), rows.max_ctx, Lc, L, kdec, vtdec);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(mha_mask_kernel, dim3(R), dim3(256), 0, stream, indices, rows.row_pos, kTopk,
+                     L, mask);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(mha_attn_kernel, dim3(H, (R + AR - 1) / AR), dim3(AW * 64), 0, stream,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(latent), kdec,
+                     vtdec, mask, rows.row_seq, rows.row_pos, R, B, rows.max_ctx, Lc, L,
+                     softmax_scale * 1.44269504088896340736f, static_cast<uint16_t*>(out), lse);
+  return hipGetLastError();
+}
+
+}  // namespace dsa
