@@ -130,13 +130,30 @@ __global__ __launch_bounds__(256) void mha_mask_kernel(const int32_t* __restrict
 // the transposed value tile in the same key order.  Online softmax in the exp2
 // domain; masked keys get -inf.
 // ---------------------------------------------------------------------------
+// Reductions over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one row's four key
+// groups): v_permlane16_swap and v_permlane32_swap pair each lane with its partner
+// in VALU, without the LDS round trip of a shuffle.
+__device__ __forceinline__ float max4g(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum4g(float v) {
+  // both lanes of a pair add the same two values in the same order
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 constexpr int AW = 8;            // waves
 constexpr int AR = 16 * AW;      // rows per block
 constexpr int AKS = 32;          // keys per stage
 constexpr int KST = DQ + 8;      // key tile row stride (bf16), padded
 constexpr int VST = AKS + 8;     // value tile row stride (bf16), padded
 
-__global__ __launch_bounds__(AW * 64) void mha_attn_kernel(
+__global__ __launch_bounds__(AW * 64, 4) void mha_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ latent,
     const uint16_t* __restrict__ kdec, const uint16_t* __restrict__ vtdec,
     const uint32_t* __restrict__ mask, const int32_t* __restrict__ row_seq,
@@ -145,8 +162,13 @@ __global__ __launch_bounds__(AW * 64) void mha_attn_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t kt[AKS][KST];
   __shared__ __attribute__((aligned(16))) uint16_t vt[DH][VST];
   __shared__ int tmax_s[AW];
-  const int h = blockIdx.x;
-  const int r0 = blockIdx.y * AR;
+  // Block order: XCD x (block id mod 8) runs heads x, x + 8, ... one after the
+  // other, each head's row blocks longest first, so the row blocks that stream one
+  // head's keys and values run together on one L2.
+  const int nrb = (R + AR - 1) / AR;
+  const int xcd = blockIdx.x & 7, within = blockIdx.x >> 3;
+  const int h = 8 * (within / nrb) + xcd;
+  const int r0 = (nrb - 1 - within % nrb) * AR;
   const int tid = threadIdx.x, l = lane_id(), wv = tid >> 6, g = l >> 4, n = l & 15;
   const int W = L / 32;
 
@@ -187,24 +209,46 @@ __global__ __launch_bounds__(AW * 64) void mha_attn_kernel(
   for (int i = 0; i < DH / 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
+  // Stage k0's tiles are fetched into registers one stage ahead (the loads are in
+  // flight while the previous stage computes): key chunks tid and tid + 512 (the
+  // latter for tid < 256) of 32 keys x 24 chunks, value chunk tid of 128 dims x 4,
+  // and this lane's mask word.
+  static_assert(AKS * (DQ / 8) == AW * 64 + AW * 32 && DH * (AKS / 8) == AW * 64, "chunk counts");
+  i32x4 pf_k0, pf_k1 = {0, 0, 0, 0}, pf_v;
+  uint32_t pf_m;
+  auto key_src = [&](int k0, int c) {
+    const int e = c / (DQ / 8), d8 = c - e * (DQ / 8);
+    const int s = min(k0 + e, L - 1);
+    return d8 < DH / 8 ? kseq + (size_t)s * KCOLS + 8 * d8
+                       : lseq + (size_t)min(s, Lc - 1) * kQkDim + DL + 8 * (d8 - DH / 8);
+  };
+  auto fetch = [&](int k0) {
+    pf_k0 = *reinterpret_cast<const i32x4*>(key_src(k0, tid));
+    if (tid < AW * 32) pf_k1 = *reinterpret_cast<const i32x4*>(key_src(k0, tid + AW * 64));
+    const int d = tid / (AKS / 8), k8 = tid - d * (AKS / 8);
+    const int s = k0 + 8 * k8;
+    pf_v = s + 8 <= L ? *reinterpret_cast<const i32x4*>(vseq + (size_t)d * L + s) : i32x4{0, 0, 0, 0};
+    pf_m = ok ? mrow[k0 >> 5] : 0u;
+  };
+  auto stash = [&]() {
+    {
+      const int e = tid / (DQ / 8), d8 = tid - e * (DQ / 8);
+      *reinterpret_cast<i32x4*>(&kt[e][8 * d8]) = pf_k0;
+    }
+    if (tid < AW * 32) {
+      const int c = tid + AW * 64, e = c / (DQ / 8), d8 = c - e * (DQ / 8);
+      *reinterpret_cast<i32x4*>(&kt[e][8 * d8]) = pf_k1;
+    }
+    const int d = tid / (AKS / 8), k8 = tid - d * (AKS / 8);
+    *reinterpret_cast<i32x4*>(&vt[d][8 * k8]) = pf_v;
+  };
+  if (tmax >= 0) fetch(0);
   for (int k0 = 0; k0 <= tmax; k0 += AKS) {
     __syncthreads();  // previous stage's tile reads are done
-    // stage keys: 32 keys x (128 nope + 64 rope) and values: 128 dims x 32 keys
-    for (int c = tid; c < AKS * (DQ / 8); c += AW * 64) {
-      const int e = c / (DQ / 8), d8 = c - e * (DQ / 8);
-      const int s = min(k0 + e, L - 1);
-      const uint16_t* src = d8 < DH / 8 ? kseq + (size_t)s * KCOLS + 8 * d8
-                                        : lseq + (size_t)min(s, Lc - 1) * kQkDim + DL + 8 * (d8 - DH / 8);
-      *reinterpret_cast<i32x4*>(&kt[e][8 * d8]) = *reinterpret_cast<const i32x4*>(src);
-    }
-    for (int c = tid; c < DH * (AKS / 8); c += AW * 64) {
-      const int d = c / (AKS / 8), k8 = c - d * (AKS / 8);
-      const int s = k0 + 8 * k8;
-      i32x4 v4 = {0, 0, 0, 0};
-      if (s + 8 <= L) v4 = *reinterpret_cast<const i32x4*>(vseq + (size_t)d * L + s);
-      *reinterpret_cast<i32x4*>(&vt[d][8 * k8]) = v4;
-    }
+    stash();
+    const uint32_t mw = pf_m;
     __syncthreads();
+    if (k0 + AKS <= tmax) fetch(k0 + AKS);
     // S^T = K Q^T: keys 16 mt + 4 g + v (mt = 0, 1) of this lane's row
     f32x4 st[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
@@ -214,7 +258,6 @@ __global__ __launch_bounds__(AW * 64) void mha_attn_kernel(
         const bf16x8 ka = as_bf16x8(*reinterpret_cast<const i32x4*>(&kt[16 * mt + n][32 * s + 8 * g]));
         st[mt] = mfma_bf16_16x16x32(ka, as_bf16x8(qr[s]), st[mt]);
       }
-    const uint32_t mw = ok ? mrow[k0 >> 5] : 0u;
     float x[8];
     float mx = -INFINITY;
 #pragma unroll
@@ -226,8 +269,7 @@ __global__ __launch_bounds__(AW * 64) void mha_attn_kernel(
         x[4 * mt + v] = z;
         mx = fmaxf(mx, z);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max4g(mx);
     const float m_new = fmaxf(m_run, mx);
     const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
     float psum = 0.f;
@@ -237,8 +279,7 @@ __global__ __launch_bounds__(AW * 64) void mha_attn_kernel(
       pv[i] = x[i] == -INFINITY ? 0.f : exp2f(x[i] - m_new);
       psum += pv[i];
     }
-    psum += __shfl_xor(psum, 16);
-    psum += __shfl_xor(psum, 32);
+    psum = sum4g(psum);
     l_run = l_run * alpha + psum;
     m_run = m_new;
     // P^T operand: keys {4g..4g+3, 16+4g..16+4g+3} of this lane's row, as bf16
@@ -294,7 +335,8 @@ hipError_t launch_mha(const dsa_rows& rows, const void* q, const void* latent, c
   hipLaunchKernelGGL(mha_mask_kernel, dim3(R), dim3(256), 0, stream, indices, rows.row_pos, kTopk,
                      L, mask);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL(mha_attn_kernel, dim3(H, (R + AR - 1) / AR), dim3(AW * 64), 0, stream,
+  static_assert(H % 8 == 0, "heads spread evenly over the XCDs");
+  hipLaunchKernelGGL(mha_attn_kernel, dim3(H * ((R + AR - 1) / AR)), dim3(AW * 64), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(latent), kdec,
                      vtdec, mask, rows.row_seq, rows.row_pos, R, B, rows.max_ctx, Lc, L,
                      softmax_scale * 1.44269504088896340736f, static_cast<uint16_t*>(out), lse);
