@@ -85,6 +85,9 @@ def parse():
     p.add_argument("--workload", default="decode32k")
     p.add_argument("--sets", type=int, default=4)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--headline-only", action="store_true",
+                   help="time only the headline step, so that a profiler run sees its kernels "
+                        "alone (no paged, training, projection or MHA sections)")
     p.add_argument("--extra", action="store_true",
                    help="also time decode128k, prefill8k and prefill128k")
     p.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
@@ -484,27 +487,28 @@ def main():
         "step_hbm_frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "kernels": kernels,
     }
-    # the same step over paged caches (64-entry pages in shuffled order)
-    P = 64
-    for k, st in enumerate(steps):
-        st.make_paged(P, seed=k)
-    for i in range(args.warmup):
-        steps[i % len(steps)].run_paged()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        steps[i % len(steps)].run_paged()
-    torch.cuda.synchronize()
-    pms = (time.perf_counter() - t0) / args.steps * 1e3
-    line["paged"] = {"page_size": P, "ms_per_step": pms, "tokens_per_s": R / (pms * 1e-3),
-                     "vs_contiguous": ms / pms}
-    line["indexer_training"] = time_training(dsa, steps[0], args.steps)
-    del steps
-    torch.cuda.empty_cache()
-    # the step before the path: projections and cache append of the new tokens
-    line["projections"] = {name: time_projection(dsa, di, di.PROJ_CONFIGS[name], reps)
-                           for name, reps in (("proj_decode32", 30), ("proj_prefill8k", 10))}
-    line["mha_prefill8k"] = time_mha(dsa, di, max(2, args.steps // 4))
+    if not args.headline_only:
+        # the same step over paged caches (64-entry pages in shuffled order)
+        P = 64
+        for k, st in enumerate(steps):
+            st.make_paged(P, seed=k)
+        for i in range(args.warmup):
+            steps[i % len(steps)].run_paged()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            steps[i % len(steps)].run_paged()
+        torch.cuda.synchronize()
+        pms = (time.perf_counter() - t0) / args.steps * 1e3
+        line["paged"] = {"page_size": P, "ms_per_step": pms, "tokens_per_s": R / (pms * 1e-3),
+                         "vs_contiguous": ms / pms}
+        line["indexer_training"] = time_training(dsa, steps[0], args.steps)
+        del steps
+        torch.cuda.empty_cache()
+        # the step before the path: projections and cache append of the new tokens
+        line["projections"] = {name: time_projection(dsa, di, di.PROJ_CONFIGS[name], reps)
+                               for name, reps in (("proj_decode32", 30), ("proj_prefill8k", 10))}
+        line["mha_prefill8k"] = time_mha(dsa, di, max(2, args.steps // 4))
     if args.extra:
         line["extra"] = {name: time_workload(dsa, di, di.CONFIGS[name], reps)
                          for name, reps in (("decode128k", 20), ("prefill8k", 5),
