@@ -306,8 +306,10 @@ dsa_status dsa_indexer_backward(const dsa_rows* rows, const dsa_dims* dims, cons
  *   q     [R, H, 192] bf16 (128 nope + 64 rope dims per head)
  *   w_uk  [H, 128, 512] bf16, w_uv [H, 128, 512] bf16
  *   out   [R, H, 128] bf16; lse [R, H] fp32 or NULL
- * Production dims; one sequence per call (rows of a sequence other than
- * row_seq[0]'s are not processed); max_pos + 1 <= 16384.  The workspace holds the
+ * Production dims; max_pos + 1 <= 16384.  Rows may belong to any sequences in any
+ * order: a tile of 128 consecutive rows makes one pass over the keys per distinct
+ * sequence among its rows, so rows grouped by sequence cost least.  Rows whose
+ * sequence or position is out of range are not written.  The workspace holds the
  * decompressed keys and values of positions [0, max_pos] and the selection mask
  * (dsa_mha_prefill_workspace_size).  bf16 MFMA with fp32 accumulation and softmax;
  * decompressed keys and values and the softmax weights are rounded to bf16.

@@ -162,6 +162,7 @@ __global__ __launch_bounds__(AW * 64, 4) void mha_attn_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t kt[AKS][KST];
   __shared__ __attribute__((aligned(16))) uint16_t vt[DH][VST];
   __shared__ int tmax_s[AW];
+  __shared__ int seq_s[AW];
   // Block order: XCD x (block id mod 8) runs heads x, x + 8, ... one after the
   // other, each head's row blocks longest first, so the row blocks that stream one
   // head's keys and values run together on one L2.
@@ -176,137 +177,149 @@ __global__ __launch_bounds__(AW * 64, 4) void mha_attn_kernel(
   const int r = r0 + 16 * wv + n;
   const bool rv = r < R;
   const int b = rv ? row_seq[r] : -1, t = rv ? row_pos[r] : -1;
-  // the block's sequence: that of its first row (one sequence per call)
-  int bseq = row_seq[min(r0, R - 1)];
-  bseq = (bseq >= 0 && bseq < B) ? bseq : 0;
-  const bool ok = rv && b == bseq && t >= 0 && t < Lc;
-  int tw = ok ? t : -1;
-  tw = max(tw, __shfl_xor(tw, 16));
-  tw = max(tw, __shfl_xor(tw, 32));
-  tw = max(tw, __shfl_xor(tw, 1));
-  tw = max(tw, __shfl_xor(tw, 2));
-  tw = max(tw, __shfl_xor(tw, 4));
-  tw = max(tw, __shfl_xor(tw, 8));
-  if (l == 0) tmax_s[wv] = tw;
-  // queries of this lane's row, contraction step s: dims [32 s + 8 g, +8)
-  i32x4 qr[DQ / 32];
-  {
-    const uint16_t* qp = q + ((size_t)(rv ? r : 0) * H + h) * DQ + 8 * g;
-#pragma unroll
-    for (int s = 0; s < DQ / 32; ++s) qr[s] = *reinterpret_cast<const i32x4*>(qp + 32 * s);
-  }
-  __syncthreads();
-  int tmax = -1;
-#pragma unroll
-  for (int i = 0; i < AW; ++i) tmax = max(tmax, tmax_s[i]);
-  const uint16_t* kseq = kdec + (size_t)bseq * L * KCOLS + (size_t)h * DH;
-  const uint16_t* vseq = vtdec + ((size_t)bseq * KCOLS + (size_t)h * DH) * L;
-  const uint16_t* lseq = latent + (size_t)bseq * N * kQkDim;
+  const bool valid = rv && b >= 0 && b < B && t >= 0 && t < Lc;
   const uint32_t* mrow = mask + (size_t)(rv ? r : 0) * W;
 
-  f32x4 acc[DH / 16];
+  // One pass over the keys per distinct sequence among the block's rows, in
+  // ascending sequence order: a single pass when the rows are grouped by sequence.
+  int bdone = -1;
+  for (;;) {
+    // the next sequence: the smallest above bdone among the block's valid rows
+    int bn = valid && b > bdone ? b : INT_MAX;
 #pragma unroll
-  for (int i = 0; i < DH / 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
-
-  // Stage k0's tiles are fetched into registers one stage ahead (the loads are in
-  // flight while the previous stage computes): key chunks tid and tid + 512 (the
-  // latter for tid < 256) of 32 keys x 24 chunks, value chunk tid of 128 dims x 4,
-  // and this lane's mask word.
-  static_assert(AKS * (DQ / 8) == AW * 64 + AW * 32 && DH * (AKS / 8) == AW * 64, "chunk counts");
-  i32x4 pf_k0, pf_k1 = {0, 0, 0, 0}, pf_v;
-  uint32_t pf_m;
-  auto key_src = [&](int k0, int c) {
-    const int e = c / (DQ / 8), d8 = c - e * (DQ / 8);
-    const int s = min(k0 + e, L - 1);
-    return d8 < DH / 8 ? kseq + (size_t)s * KCOLS + 8 * d8
-                       : lseq + (size_t)min(s, Lc - 1) * kQkDim + DL + 8 * (d8 - DH / 8);
-  };
-  auto fetch = [&](int k0) {
-    pf_k0 = *reinterpret_cast<const i32x4*>(key_src(k0, tid));
-    if (tid < AW * 32) pf_k1 = *reinterpret_cast<const i32x4*>(key_src(k0, tid + AW * 64));
-    const int d = tid / (AKS / 8), k8 = tid - d * (AKS / 8);
-    const int s = k0 + 8 * k8;
-    pf_v = s + 8 <= L ? *reinterpret_cast<const i32x4*>(vseq + (size_t)d * L + s) : i32x4{0, 0, 0, 0};
-    pf_m = ok ? mrow[k0 >> 5] : 0u;
-  };
-  auto stash = [&]() {
-    {
-      const int e = tid / (DQ / 8), d8 = tid - e * (DQ / 8);
-      *reinterpret_cast<i32x4*>(&kt[e][8 * d8]) = pf_k0;
-    }
-    if (tid < AW * 32) {
-      const int c = tid + AW * 64, e = c / (DQ / 8), d8 = c - e * (DQ / 8);
-      *reinterpret_cast<i32x4*>(&kt[e][8 * d8]) = pf_k1;
-    }
-    const int d = tid / (AKS / 8), k8 = tid - d * (AKS / 8);
-    *reinterpret_cast<i32x4*>(&vt[d][8 * k8]) = pf_v;
-  };
-  if (tmax >= 0) fetch(0);
-  for (int k0 = 0; k0 <= tmax; k0 += AKS) {
-    __syncthreads();  // previous stage's tile reads are done
-    stash();
-    const uint32_t mw = pf_m;
+    for (int o = 1; o < 64; o <<= 1) bn = min(bn, __shfl_xor(bn, o));
+    if (l == 0) seq_s[wv] = bn;
     __syncthreads();
-    if (k0 + AKS <= tmax) fetch(k0 + AKS);
-    // S^T = K Q^T: keys 16 mt + 4 g + v (mt = 0, 1) of this lane's row
-    f32x4 st[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    int bseq = INT_MAX;
 #pragma unroll
-    for (int s = 0; s < DQ / 32; ++s)
+    for (int i = 0; i < AW; ++i) bseq = min(bseq, seq_s[i]);
+    if (bseq == INT_MAX) break;  // the same for every thread of the block
+    bdone = bseq;
+    const bool ok = valid && b == bseq;
+    int tw = ok ? t : -1;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const bf16x8 ka = as_bf16x8(*reinterpret_cast<const i32x4*>(&kt[16 * mt + n][32 * s + 8 * g]));
-        st[mt] = mfma_bf16_16x16x32(ka, as_bf16x8(qr[s]), st[mt]);
-      }
-    float x[8];
-    float mx = -INFINITY;
+    for (int o = 1; o < 64; o <<= 1) tw = max(tw, __shfl_xor(tw, o));
+    if (l == 0) tmax_s[wv] = tw;
+    __syncthreads();
+    int tmax = -1;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int i = 0; i < AW; ++i) tmax = max(tmax, tmax_s[i]);
+    const uint16_t* kseq = kdec + (size_t)bseq * L * KCOLS + (size_t)h * DH;
+    const uint16_t* vseq = vtdec + ((size_t)bseq * KCOLS + (size_t)h * DH) * L;
+    const uint16_t* lseq = latent + (size_t)bseq * N * kQkDim;
+    // queries of this lane's row, contraction step s: dims [32 s + 8 g, +8)
+    i32x4 qr[DQ / 32];
+    {
+      const uint16_t* qp = q + ((size_t)(rv ? r : 0) * H + h) * DQ + 8 * g;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int e = 16 * mt + 4 * g + v;
-        const float z = ((mw >> e) & 1u) ? st[mt][v] * scale_log2 : -INFINITY;
-        x[4 * mt + v] = z;
-        mx = fmaxf(mx, z);
-      }
-    mx = max4g(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
-    float psum = 0.f;
-    float pv[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      pv[i] = x[i] == -INFINITY ? 0.f : exp2f(x[i] - m_new);
-      psum += pv[i];
+      for (int s = 0; s < DQ / 32; ++s) qr[s] = *reinterpret_cast<const i32x4*>(qp + 32 * s);
     }
-    psum = sum4g(psum);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    // P^T operand: keys {4g..4g+3, 16+4g..16+4g+3} of this lane's row, as bf16
-    const i32x4 pb = {(int)pack_bf16x2(pv[0], pv[1]), (int)pack_bf16x2(pv[2], pv[3]),
-                      (int)pack_bf16x2(pv[4], pv[5]), (int)pack_bf16x2(pv[6], pv[7])};
+
+    f32x4 acc[DH / 16];
 #pragma unroll
-    for (int dt = 0; dt < DH / 16; ++dt) {
+    for (int i = 0; i < DH / 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    // Stage k0's tiles are fetched into registers one stage ahead (the loads are in
+    // flight while the previous stage computes): key chunks tid and tid + 512 (the
+    // latter for tid < 256) of 32 keys x 24 chunks, value chunk tid of 128 dims x 4,
+    // and this lane's mask word.
+    static_assert(AKS * (DQ / 8) == AW * 64 + AW * 32 && DH * (AKS / 8) == AW * 64, "chunk counts");
+    i32x4 pf_k0, pf_k1 = {0, 0, 0, 0}, pf_v;
+    uint32_t pf_m;
+    auto key_src = [&](int k0, int c) {
+      const int e = c / (DQ / 8), d8 = c - e * (DQ / 8);
+      const int s = min(k0 + e, L - 1);
+      return d8 < DH / 8 ? kseq + (size_t)s * KCOLS + 8 * d8
+                         : lseq + (size_t)min(s, Lc - 1) * kQkDim + DL + 8 * (d8 - DH / 8);
+    };
+    auto fetch = [&](int k0) {
+      pf_k0 = *reinterpret_cast<const i32x4*>(key_src(k0, tid));
+      if (tid < AW * 32) pf_k1 = *reinterpret_cast<const i32x4*>(key_src(k0, tid + AW * 64));
+      const int d = tid / (AKS / 8), k8 = tid - d * (AKS / 8);
+      const int s = k0 + 8 * k8;
+      pf_v = s + 8 <= L ? *reinterpret_cast<const i32x4*>(vseq + (size_t)d * L + s) : i32x4{0, 0, 0, 0};
+      pf_m = ok ? mrow[k0 >> 5] : 0u;
+    };
+    auto stash = [&]() {
+      {
+        const int e = tid / (DQ / 8), d8 = tid - e * (DQ / 8);
+        *reinterpret_cast<i32x4*>(&kt[e][8 * d8]) = pf_k0;
+      }
+      if (tid < AW * 32) {
+        const int c = tid + AW * 64, e = c / (DQ / 8), d8 = c - e * (DQ / 8);
+        *reinterpret_cast<i32x4*>(&kt[e][8 * d8]) = pf_k1;
+      }
+      const int d = tid / (AKS / 8), k8 = tid - d * (AKS / 8);
+      *reinterpret_cast<i32x4*>(&vt[d][8 * k8]) = pf_v;
+    };
+    if (tmax >= 0) fetch(0);
+    for (int k0 = 0; k0 <= tmax; k0 += AKS) {
+      __syncthreads();  // previous stage's tile reads are done
+      stash();
+      const uint32_t mw = pf_m;
+      __syncthreads();
+      if (k0 + AKS <= tmax) fetch(k0 + AKS);
+      // S^T = K Q^T: keys 16 mt + 4 g + v (mt = 0, 1) of this lane's row
+      f32x4 st[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-      for (int v = 0; v < 4; ++v) acc[dt][v] *= alpha;
-      const uint16_t* vr = &vt[16 * dt + n][0];
-      const uint2 lo = *reinterpret_cast<const uint2*>(vr + 4 * g);
-      const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16 + 4 * g);
-      const i32x4 va = {(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
-      acc[dt] = mfma_bf16_16x16x32(as_bf16x8(va), as_bf16x8(pb), acc[dt]);
+      for (int s = 0; s < DQ / 32; ++s)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const bf16x8 ka = as_bf16x8(*reinterpret_cast<const i32x4*>(&kt[16 * mt + n][32 * s + 8 * g]));
+          st[mt] = mfma_bf16_16x16x32(ka, as_bf16x8(qr[s]), st[mt]);
+        }
+      float x[8];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int e = 16 * mt + 4 * g + v;
+          const float z = ((mw >> e) & 1u) ? st[mt][v] * scale_log2 : -INFINITY;
+          x[4 * mt + v] = z;
+          mx = fmaxf(mx, z);
+        }
+      mx = max4g(mx);
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
+      float psum = 0.f;
+      float pv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pv[i] = x[i] == -INFINITY ? 0.f : exp2f(x[i] - m_new);
+        psum += pv[i];
+      }
+      psum = sum4g(psum);
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+      // P^T operand: keys {4g..4g+3, 16+4g..16+4g+3} of this lane's row, as bf16
+      const i32x4 pb = {(int)pack_bf16x2(pv[0], pv[1]), (int)pack_bf16x2(pv[2], pv[3]),
+                        (int)pack_bf16x2(pv[4], pv[5]), (int)pack_bf16x2(pv[6], pv[7])};
+#pragma unroll
+      for (int dt = 0; dt < DH / 16; ++dt) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[dt][v] *= alpha;
+        const uint16_t* vr = &vt[16 * dt + n][0];
+        const uint2 lo = *reinterpret_cast<const uint2*>(vr + 4 * g);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16 + 4 * g);
+        const i32x4 va = {(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
+        acc[dt] = mfma_bf16_16x16x32(as_bf16x8(va), as_bf16x8(pb), acc[dt]);
+      }
     }
-  }
-  // lane holds dims 16 dt + 4 g + v of its row
-  if (ok) {
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    uint16_t* orow = out + ((size_t)r * H + h) * DH;
+    // lane holds dims 16 dt + 4 g + v of its row
+    if (ok) {
+      const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+      uint16_t* orow = out + ((size_t)r * H + h) * DH;
 #pragma unroll
-    for (int dt = 0; dt < DH / 16; ++dt)
-      *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * g) =
-          make_uint2(pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv),
-                     pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv));
-    if (lse != nullptr && g == 0)
-      lse[(size_t)r * H + h] = l_run > 0.f ? (m_run + log2f(l_run)) * 0.69314718055994530942f : -INFINITY;
+      for (int dt = 0; dt < DH / 16; ++dt)
+        *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * g) =
+            make_uint2(pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv),
+                       pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv));
+      if (lse != nullptr && g == 0)
+        lse[(size_t)r * H + h] = l_run > 0.f ? (m_run + log2f(l_run)) * 0.69314718055994530942f : -INFINITY;
+    }
+    __syncthreads();  // the pass's LDS reads are done before the next pass writes
   }
 }
 

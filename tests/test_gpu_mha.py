@@ -99,3 +99,52 @@ def test_mha_prefill8k_masked(dsa):
         o_ref = np.einsum("hdc,hc->hd", wuv, o_lat)
         _check(out[t].float().cpu().numpy().astype(np.float64), o_ref,
                lse[t].cpu().numpy().astype(np.float64), lse_ref, f"8K row {t}")
+
+
+def test_mha_interleaved_sequences(dsa):
+    """Three sequences of 100, 250 and 180 tokens whose rows are interleaved (row
+    order by position, then sequence), so every 128-row tile holds rows of all three;
+    each row selects a seeded random 60 % of 0..t (the rest masked)."""
+    cfg = di.CONFIGS["prefill8k"]
+    lens = (100, 250, 180)
+    N, B = 256, len(lens)
+    g = di.Generator(cfg, 0)
+    mg = di.MhaGenerator(cfg.cfg_id, 1)
+    dev = torch.device("cuda")
+    latent = torch.stack([g.latent(b, 0, N, device=dev) for b in range(B)]).contiguous()
+    rows = [(b, t) for t in range(max(lens)) for b in range(B) if t < lens[b]]
+    R = len(rows)
+    rng = np.random.default_rng(9)
+    idx = np.full((R, cfg.topk), -1, dtype=np.int32)
+    for i, (b, t) in enumerate(rows):
+        m = max(1, int(0.6 * (t + 1)))
+        idx[i, :m] = np.sort(rng.choice(t + 1, size=m, replace=False))
+    seq = torch.tensor([b for b, _ in rows], dtype=torch.int32, device=dev)
+    pos = torch.tensor([t for _, t in rows], dtype=torch.int32, device=dev)
+    rs = dsa.rows_struct(seq, pos, B, N, max(lens) - 1)
+    q = mg.q(0, R, device=dev)
+    w_uk, w_uv = mg.weights(device=dev)
+    dims = dsa.Dims.from_config(cfg)
+    out, lse = dsa.mha_prefill(rs, q, latent, w_uk, w_uv, torch.from_numpy(idx).to(dev), cfg.scale,
+                               dims=dims)
+    torch.cuda.synchronize()
+    out_h = out.float().cpu().numpy().astype(np.float64)
+    lse_h = lse.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(out_h)) and np.all(np.isfinite(lse_h))
+    wuk, wuv = (oracle.decode_bf16(di.bf16_bits(x)) for x in mg.weights())
+    qh_all = oracle.decode_bf16(di.bf16_bits(mg.q(0, R)))
+    kv = {}
+    for b in range(B):
+        ent = oracle.decode_bf16(di.bf16_bits(g.latent(b, 0, lens[b])))
+        kv[b] = oracle.mha_decompress(ent, wuk, wuv, cfg.v_dim)
+    picks = [0, 1, 2, 150, 299, 300, 301, R - 1] + list(rng.choice(R, size=4, replace=False))
+    for i in picks:
+        b, t = rows[int(i)]
+        S = idx[i][idx[i] >= 0]
+        k, v = kv[b]
+        z = cfg.scale * np.einsum("hd,hnd->hn", qh_all[i], k[:, S])
+        m = z.max(axis=1, keepdims=True)
+        e = np.exp(z - m)
+        o_ref = np.einsum("hn,hnd->hd", e / e.sum(axis=1, keepdims=True), v[:, S])
+        lse_ref = m[:, 0] + np.log(e.sum(axis=1))
+        _check(out_h[i], o_ref, lse_h[i], lse_ref, f"seq {b} row t={t} ({S.size} selected)")
