@@ -306,8 +306,13 @@ def time_training(dsa, st, K):
                                    loss=loss, dscores=dsc, workspace=ws)
     bwd = lambda: dsa.indexer_backward(st.rows, i.q_idx, i.q_scale, i.w, i.k_idx, i.k_scale,
                                        st.idx, dsc, dq, dw, dk)
+    dsc_d = torch.empty_like(st.scores)
+    ws_d = torch.empty(max(dsa.indexer_loss_dense_workspace_size(st.rows), 1), dtype=torch.uint8,
+                       device="cuda")
+    dense = lambda: dsa.indexer_loss_dense(st.rows, i.q, i.latent, c.scale, st.scores, loss=loss,
+                                           dscores=dsc_d, workspace=ws_d)
     out = {}
-    for name, fn in (("loss", fwd), ("backward", bwd)):
+    for name, fn in (("loss", fwd), ("backward", bwd), ("loss_dense", dense)):
         for _ in range(3):
             fn()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -327,7 +332,13 @@ def time_training(dsa, st, K):
     fl = sel * 2 * 64 * 128 * 2
     out["backward"].update({"fp32_tflops": fl / out["backward"]["ms"] / 1e9,
                             "frac_of_fp32_vector_peak": fl / out["backward"]["ms"] / 1e9 / 157.3})
-    del dk, dq, dw, ws, dsc, loss
+    # dense warm-up loss: two passes of q.c over every causal position (bf16 MFMA)
+    cand, _ = _pairs(c)
+    fl_d = cand * 2 * 2 * 128 * 576
+    out["loss_dense"].update({"positions": cand, "bf16_tflops": fl_d / out["loss_dense"]["ms"] / 1e9,
+                              "frac_of_bf16_peak": fl_d / out["loss_dense"]["ms"] / 1e9
+                              / BF16_PEAK_TFLOPS})
+    del dk, dq, dw, ws, dsc, loss, dsc_d, ws_d
     torch.cuda.empty_cache()
     return out
 

@@ -287,6 +287,27 @@ dsa_status dsa_indexer_loss(const dsa_rows* rows, const dsa_dims* dims, const vo
                             float* loss, float* dscores, void* workspace, size_t ws_bytes,
                             void* stream);
 
+/* Dense warm-up loss of the indexer (DeepSeek-V3.2-Exp paper, section 2.1, "dense
+ * warm-up stage": with the main attention dense, the indexer is trained with the
+ * KL divergence to the heads' attention weights summed and L1-normalised over all
+ * preceding positions).  Production dims only.  For each row r at position t:
+ *   lse[h]  = log sum_{s<=t} exp(softmax_scale q[r,h,:] . latent[b,s,:])
+ *   u_s     = sum_h exp(softmax_scale q[r,h,:] . latent[b,s,:] - lse[h]),  p = u / sum_s u_s
+ *   loss[r]         = sum_{s<=t} p_s (log p_s - log softmax_{s<=t}(scores[r,s]))
+ *   dscores[r, s]   = softmax_{s<=t}(scores[r,s]) - p_s for s <= t, 0 for t < s < ld_scores
+ * scores and dscores are [R, ld_scores] fp32; every causal position is read, so the
+ * cost is that of dense attention (two passes of q.c on the bf16 MFMA, in chunks of
+ * 1024 positions; fp32 softmax sums).  The workspace holds the target and the
+ * per-chunk partial sums (dsa_indexer_loss_dense_workspace_size bytes).  Rows whose
+ * sequence or position is out of range get loss 0 and a zero dscores row.
+ */
+size_t dsa_indexer_loss_dense_workspace_size(const dsa_rows* rows, const dsa_dims* dims);
+
+dsa_status dsa_indexer_loss_dense(const dsa_rows* rows, const dsa_dims* dims, const void* q,
+                                  const void* latent, float softmax_scale, const float* scores,
+                                  int64_t ld_scores, float* loss, float* dscores, void* workspace,
+                                  size_t ws_bytes, void* stream);
+
 dsa_status dsa_indexer_backward(const dsa_rows* rows, const dsa_dims* dims, const void* q_idx,
                                 const float* q_scale, const float* w, const void* k_idx,
                                 const float* k_scale, const int32_t* indices,

@@ -35,6 +35,7 @@ EXPORTED_SYMBOLS = [
     "dsa_project_append_workspace_size", "dsa_project_append", "dsa_indexer_scores_paged",
     "dsa_sparse_mla_attn_paged", "dsa_forward_paged", "dsa_project_append_paged",
     "dsa_indexer_loss_workspace_size", "dsa_indexer_loss", "dsa_indexer_backward",
+    "dsa_indexer_loss_dense_workspace_size", "dsa_indexer_loss_dense",
     "dsa_mha_prefill_workspace_size", "dsa_mha_prefill",
     "dsa_status_string", "dsa_last_error", "dsa_api_version",
 ]
@@ -93,13 +94,16 @@ def _load() -> ctypes.CDLL:
     L.dsa_indexer_loss_workspace_size.restype = sz
     L.dsa_indexer_loss.argtypes = [R, D, vp, vp, vp, vp, f32, vp, i64, vp, vp, vp, sz, vp]
     L.dsa_indexer_backward.argtypes = [R, D] + [vp] * 10 + [vp]
+    L.dsa_indexer_loss_dense_workspace_size.argtypes = [R, D]
+    L.dsa_indexer_loss_dense_workspace_size.restype = sz
+    L.dsa_indexer_loss_dense.argtypes = [R, D, vp, vp, f32, vp, i64, vp, vp, vp, sz, vp]
     L.dsa_mha_prefill_workspace_size.argtypes = [R, D]
     L.dsa_mha_prefill_workspace_size.restype = sz
     L.dsa_mha_prefill.argtypes = [R, D, vp, vp, vp, vp, vp, f32, vp, vp, vp, sz, vp]
     for name in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_attn", "dsa_forward",
                  "dsa_project_append", "dsa_indexer_scores_paged", "dsa_sparse_mla_attn_paged",
                  "dsa_forward_paged", "dsa_project_append_paged", "dsa_indexer_loss",
-                 "dsa_indexer_backward", "dsa_mha_prefill"):
+                 "dsa_indexer_backward", "dsa_mha_prefill", "dsa_indexer_loss_dense"):
         getattr(L, name).restype = ctypes.c_int
     L.dsa_status_string.argtypes = [ctypes.c_int]
     L.dsa_status_string.restype = ctypes.c_char_p
@@ -542,6 +546,40 @@ def indexer_loss(rows: _Rows, q, latent, indices, lse, softmax_scale: float, sco
                                 _ptr(indices), _ptr(lse), float(softmax_scale), _ptr(scores),
                                 scores.shape[1], _ptr(loss), _ptr(dscores), _ptr(workspace),
                                 workspace.numel(), _stream()))
+    return loss, dscores
+
+
+def indexer_loss_dense_workspace_size(rows: _Rows, dims: Dims = PRODUCTION_DIMS) -> int:
+    ds = dims_struct(dims)
+    return int(lib.dsa_indexer_loss_dense_workspace_size(ctypes.byref(rows), ctypes.byref(ds)))
+
+
+def indexer_loss_dense(rows: _Rows, q, latent, softmax_scale: float, scores,
+                       dims: Dims = PRODUCTION_DIMS, loss=None, dscores=None,
+                       workspace: Optional[torch.Tensor] = None):
+    """dsa_indexer_loss_dense: (loss [R], dscores [R, ld]) of the dense warm-up KL."""
+    R = rows.num_rows
+    _dev(q, torch.bfloat16, "q")
+    _dev(latent, torch.bfloat16, "latent")
+    _dev(scores, torch.float32, "scores")
+    _shape(q, (R, dims.n_heads, dims.qk_dim), "q")
+    _shape(scores, (R, None), "scores")
+    _caches(rows, dims, None, None, latent)
+    if loss is None:
+        loss = torch.empty(R, dtype=torch.float32, device=q.device)
+    if dscores is None:
+        dscores = torch.empty_like(scores)
+    _dev(loss, torch.float32, "loss")
+    _dev(dscores, torch.float32, "dscores")
+    _shape(dscores, tuple(scores.shape), "dscores")
+    need = indexer_loss_dense_workspace_size(rows, dims)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ds = dims_struct(dims)
+    _check(lib.dsa_indexer_loss_dense(ctypes.byref(rows), ctypes.byref(ds), _ptr(q), _ptr(latent),
+                                      float(softmax_scale), _ptr(scores), scores.shape[1],
+                                      _ptr(loss), _ptr(dscores), _ptr(workspace),
+                                      workspace.numel(), _stream()))
     return loss, dscores
 
 

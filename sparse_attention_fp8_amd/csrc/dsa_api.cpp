@@ -427,6 +427,34 @@ dsa_status dsa_indexer_loss(const dsa_rows* rows, const dsa_dims* dims, const vo
   return err == hipSuccess ? DSA_OK : hip_fail(err, "indexer loss launch");
 }
 
+size_t dsa_indexer_loss_dense_workspace_size(const dsa_rows* rows, const dsa_dims* dims) {
+  if (check_rows(rows) != DSA_OK || dims == nullptr || !is_production(*dims)) return 0;
+  return dsa::indexer_loss_dense_workspace_bytes(rows->num_rows, rows->max_pos);
+}
+
+dsa_status dsa_indexer_loss_dense(const dsa_rows* rows, const dsa_dims* dims, const void* q,
+                                  const void* latent, float softmax_scale, const float* scores,
+                                  int64_t ld_scores, float* loss, float* dscores, void* workspace,
+                                  size_t ws_bytes, void* stream) {
+  dsa_status st = check_rows(rows);
+  if (st != DSA_OK) return st;
+  if (dims == nullptr) return fail(DSA_E_INVALID, "dims is NULL");
+  if (!is_production(*dims))
+    return fail(DSA_E_UNSUPPORTED, "the dense indexer loss supports the production dims only");
+  if (rows->num_rows == 0) return DSA_OK;
+  if (!q || !latent || !scores || !loss || !dscores) return fail(DSA_E_INVALID, "NULL tensor pointer");
+  if (ld_scores < (int64_t)rows->max_pos + 1)
+    return fail(DSA_E_INVALID, "ld_scores < max_pos + 1");
+  const size_t need = dsa::indexer_loss_dense_workspace_bytes(rows->num_rows, rows->max_pos);
+  if (workspace == nullptr || ws_bytes < need)
+    return fail(DSA_E_WORKSPACE, "the dense indexer loss needs %zu workspace bytes, got %zu", need,
+                ws_bytes);
+  const hipError_t err = dsa::launch_indexer_loss_dense(*rows, q, latent, softmax_scale, scores,
+                                                        ld_scores, loss, dscores, workspace,
+                                                        as_stream(stream));
+  return err == hipSuccess ? DSA_OK : hip_fail(err, "dense indexer loss launch");
+}
+
 dsa_status dsa_indexer_backward(const dsa_rows* rows, const dsa_dims* dims, const void* q_idx,
                                 const float* q_scale, const float* w, const void* k_idx,
                                 const float* k_scale, const int32_t* indices,

@@ -69,6 +69,11 @@ hipError_t launch_project(const dsa_rows& rows, int d_model, const uint16_t* h, 
                           const PageMap& pm = PageMap());
 
 size_t indexer_loss_workspace_bytes(int num_rows, int topk);
+size_t indexer_loss_dense_workspace_bytes(int num_rows, int max_pos);
+hipError_t launch_indexer_loss_dense(const dsa_rows& rows, const void* q, const void* latent,
+                                     float softmax_scale, const float* scores, int64_t ld,
+                                     float* loss, float* dscores, void* workspace,
+                                     hipStream_t stream);
 
 hipError_t launch_indexer_loss(const dsa_rows& rows, const void* q, const void* latent,
                                const int32_t* indices, const float* lse, float softmax_scale,

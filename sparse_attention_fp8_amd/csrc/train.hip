@@ -114,6 +114,133 @@ __global__ __launch_bounds__(TT) void attn_target_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Dense warm-up target over every causal position s <= t, in chunks of DCP
+// contiguous positions per block (same wave layout and MFMA tiles as above).
+// LSE_PASS: each block leaves the per-head (max, sum) of exp2(scale_log2 q.c) over
+// its chunk in part[r, chunk, h] (log2 domain).  Target pass: each block merges its
+// row's chunk partials into the head's lse and writes u[r, s] for its chunk.
+// ---------------------------------------------------------------------------
+constexpr int DCP = 1024;  // positions per dense chunk
+
+template <bool LSE_PASS>
+__global__ __launch_bounds__(TT) void dense_target_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ latent,
+    const int32_t* __restrict__ row_seq, const int32_t* __restrict__ row_pos, int R, int B, int N,
+    int C, float scale_log2, float2* __restrict__ part, float* __restrict__ u, int64_t ldu) {
+  __shared__ __attribute__((aligned(16))) i32x4 tile[TBE * TCH];
+  __shared__ float hsum[TT / 64][TBE];
+  const int r = blockIdx.x / C, c = blockIdx.x - (blockIdx.x / C) * C;
+  if (r >= R) return;
+  const int b = row_seq[r], t = row_pos[r];
+  const bool ok = b >= 0 && b < B && t >= 0 && t < N;
+  const int p0 = c * DCP;
+  const int pend = ok ? min(t + 1, p0 + DCP) : p0;  // this chunk's positions: [p0, pend)
+  const int tid = threadIdx.x, l = lane_id(), g = l >> 4, n = l & 15;
+  const int wv = tid >> 6;
+  const int head = 16 * wv + n;
+  float2* prow = part + (size_t)r * C * H;
+  if (pend <= p0) {  // no position of this row in the chunk
+    if (LSE_PASS && g == 0) prow[(size_t)c * H + head] = make_float2(-INFINITY, 0.f);
+    return;
+  }
+  const uint8_t* base = reinterpret_cast<const uint8_t*>(latent + (size_t)b * N * DK);
+
+  // queries of heads 16 wv + n, contraction step s: dims [32 s + 8 g, +8)
+  i32x4 qr[TKS];
+  const uint16_t* qrow = q + ((size_t)r * H + head) * DK + 8 * g;
+#pragma unroll
+  for (int s = 0; s < TKS; ++s) qr[s] = *reinterpret_cast<const i32x4*>(qrow + 32 * s);
+  float lse2 = 0.f;
+  if (!LSE_PASS) {  // merge the row's chunk partials of this lane's head
+    const int nc = (t + DCP) / DCP;
+    float M = -INFINITY;
+    for (int k = 0; k < nc; ++k) M = fmaxf(M, prow[(size_t)k * H + head].x);
+    float S = 0.f;
+    for (int k = 0; k < nc; ++k) {
+      const float2 pm = prow[(size_t)k * H + head];
+      if (pm.x != -INFINITY) S += pm.y * exp2f(pm.x - M);
+    }
+    lse2 = M + log2f(S);
+  }
+  float m_run = -INFINITY, l_run = 0.f;
+
+  for (int e0 = p0; e0 < pend; e0 += TBE) {
+    __syncthreads();  // previous stage's tile reads are done
+    for (int cc = tid; cc < TBE * TCH; cc += TT) {
+      const int e = cc / TCH, pc = cc - e * TCH;
+      const int pos = min(e0 + e, pend - 1);  // past the end: a valid entry, masked below
+      tile[e * TCH + (pc ^ (e & 7))] =
+          *reinterpret_cast<const i32x4*>(base + (size_t)pos * (DK * 2) + 16 * pc);
+    }
+    __syncthreads();
+    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int s = 0; s < TKS; ++s)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const int e = 16 * mt + n;
+        const bf16x8 a = as_bf16x8(tile[e * TCH + ((4 * s + g) ^ (e & 7))]);
+        acc[mt] = mfma_bf16_16x16x32(a, as_bf16x8(qr[s]), acc[mt]);
+      }
+    // lane: entries 16 mt + 4 g + v of head 16 wv + n
+    if (LSE_PASS) {
+      float z[8];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const bool in = e0 + 16 * mt + 4 * g + v < pend;
+          z[4 * mt + v] = in ? acc[mt][v] * scale_log2 : -INFINITY;
+          mx = fmaxf(mx, z[4 * mt + v]);
+        }
+      const float m_new = fmaxf(m_run, mx);
+      if (m_new != -INFINITY) {
+        float add = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) add += z[i] == -INFINITY ? 0.f : exp2f(z[i] - m_new);
+        l_run = (m_run == -INFINITY ? 0.f : l_run * exp2f(m_run - m_new)) + add;
+        m_run = m_new;
+      }
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          float x = exp2f(acc[mt][v] * scale_log2 - lse2);
+          uint32_t xb = __float_as_uint(x);
+          xb = __float_as_uint(__uint_as_float(xb) + __uint_as_float(dpp<kDppXor1>(xb)));
+          xb = __float_as_uint(__uint_as_float(xb) + __uint_as_float(dpp<kDppXor2>(xb)));
+          xb = __float_as_uint(__uint_as_float(xb) + __uint_as_float(dpp<kDppHalfMirror>(xb)));
+          xb = __float_as_uint(__uint_as_float(xb) + __uint_as_float(dpp<kDppMirror>(xb)));
+          if (n == 0) hsum[wv][16 * mt + 4 * g + v] = __uint_as_float(xb);
+        }
+      __syncthreads();
+      if (tid < TBE && e0 + tid < pend) {
+        float sum = 0.f;
+#pragma unroll
+        for (int w8 = 0; w8 < TT / 64; ++w8) sum += hsum[w8][tid];
+        u[(size_t)r * ldu + e0 + tid] = sum;
+      }
+    }
+  }
+  if (LSE_PASS) {
+    // merge the four lanes (g) that hold this head's entries
+#pragma unroll
+    for (int o = 16; o <= 32; o <<= 1) {
+      const float mo = __shfl_xor(m_run, o), lo = __shfl_xor(l_run, o);
+      const float mn = fmaxf(m_run, mo);
+      if (mn != -INFINITY) {
+        l_run = (m_run == -INFINITY ? 0.f : l_run * exp2f(m_run - mn)) +
+                (mo == -INFINITY ? 0.f : lo * exp2f(mo - mn));
+        m_run = mn;
+      }
+    }
+    if (g == 0) prow[(size_t)c * H + head] = make_float2(m_run, l_run);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // KL(p || softmax(I over the selection)) and its gradient for one row per block.
 // ---------------------------------------------------------------------------
 constexpr int KT = 256;
@@ -182,6 +309,47 @@ __global__ __launch_bounds__(KT) void indexer_kl_kernel(
       gi = expf(lq) - pi;
     }
     grow[i] = gi;
+  }
+  kl = block_sum(kl, red);
+  if (threadIdx.x == 0) loss[r] = (ok && z > 0.f) ? kl : 0.f;
+}
+
+// KL(p || softmax(I over all s <= t)) and its gradient, one row per block: the
+// dense warm-up loss, from the dense target u[r, s].
+__global__ __launch_bounds__(KT) void indexer_kl_dense_kernel(
+    const float* __restrict__ scores, int64_t ld, const float* __restrict__ u, int64_t ldu,
+    const int32_t* __restrict__ row_seq, const int32_t* __restrict__ row_pos, int B, int N,
+    float* __restrict__ loss, float* __restrict__ dscores) {
+  __shared__ float red[KT / 64];
+  const int r = blockIdx.x;
+  const int b = row_seq[r], t = row_pos[r];
+  const bool ok = b >= 0 && b < B && t >= 0 && t < N && (int64_t)t < ld;
+  const int np = ok ? t + 1 : 0;
+  const float* srow = scores + (size_t)r * ld;
+  const float* urow = u + (size_t)r * ldu;
+  float* grow = dscores + (size_t)r * ld;
+  float m = -INFINITY, us = 0.f;
+  for (int p = threadIdx.x; p < np; p += KT) {
+    m = fmaxf(m, srow[p]);
+    us += urow[p];
+  }
+  m = block_max(m, red);
+  us = block_sum(us, red);
+  float z = 0.f;
+  for (int p = threadIdx.x; p < np; p += KT) z += expf(srow[p] - m);
+  z = block_sum(z, red);
+  const float lz = m + logf(z);
+  const float inv_u = us > 0.f ? 1.f / us : 0.f;
+  float kl = 0.f;
+  for (int64_t p = threadIdx.x; p < ld; p += KT) {
+    float gi = 0.f;
+    if (p < np) {
+      const float pi = urow[p] * inv_u;
+      const float lq = srow[p] - lz;
+      if (pi > 0.f) kl += pi * (logf(pi) - lq);
+      gi = expf(lq) - pi;
+    }
+    grow[p] = gi;
   }
   kl = block_sum(kl, red);
   if (threadIdx.x == 0) loss[r] = (ok && z > 0.f) ? kl : 0.f;
@@ -387,6 +555,37 @@ hipError_t launch_indexer_loss(const dsa_rows& rows, const void* q, const void* 
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(indexer_kl_kernel, dim3(R), dim3(KT), 0, stream, scores, ld, indices, u,
                      rows.row_seq, rows.row_pos, rows.num_seqs, rows.max_ctx, kTopk, loss, dscores);
+  return hipGetLastError();
+}
+
+size_t indexer_loss_dense_workspace_bytes(int num_rows, int max_pos) {
+  const size_t C = (size_t)(max_pos + DCP) / DCP;
+  return (size_t)num_rows * C * (DCP * sizeof(float) + H * sizeof(float2));
+}
+
+hipError_t launch_indexer_loss_dense(const dsa_rows& rows, const void* q, const void* latent,
+                                     float softmax_scale, const float* scores, int64_t ld,
+                                     float* loss, float* dscores, void* workspace,
+                                     hipStream_t stream) {
+  const int R = rows.num_rows;
+  if (R == 0) return hipSuccess;
+  const int C = (rows.max_pos + DCP) / DCP;
+  const int64_t ldu = (int64_t)C * DCP;
+  float* u = static_cast<float*>(workspace);
+  float2* part = reinterpret_cast<float2*>(u + (size_t)R * ldu);
+  const float sl2 = softmax_scale * 1.44269504088896340736f;
+  const dim3 grid((unsigned)((int64_t)R * C));
+  hipLaunchKernelGGL(dense_target_kernel<true>, grid, dim3(TT), 0, stream,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(latent),
+                     rows.row_seq, rows.row_pos, R, rows.num_seqs, rows.max_ctx, C, sl2, part, u, ldu);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(dense_target_kernel<false>, grid, dim3(TT), 0, stream,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(latent),
+                     rows.row_seq, rows.row_pos, R, rows.num_seqs, rows.max_ctx, C, sl2, part, u, ldu);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(indexer_kl_dense_kernel, dim3(R), dim3(KT), 0, stream, scores, ld, u, ldu,
+                     rows.row_seq, rows.row_pos, rows.num_seqs, rows.max_ctx, loss, dscores);
   return hipGetLastError();
 }
 

@@ -102,6 +102,45 @@ def test_indexer_loss_parity(dsa, name, rows):
               f"max |d dI| {err.max():.2e}", flush=True)
 
 
+@pytest.mark.parametrize("name,rows", [("decode32k", [0, 31]),
+                                       ("prefill8k", [0, 5, 2047, 2048, 5000, 8191])])
+def test_indexer_loss_dense_parity(dsa, name, rows):
+    """The dense warm-up loss over every s <= t, fed the oracle's scores (as fp32):
+    against the oracle's target over all t + 1 entries and its KL, under the same
+    bars as the sparse loss (the sums now run over up to 32768 terms)."""
+    cfg = di.CONFIGS[name]
+    inp = dev_inputs(name)
+    host = HostInputs(cfg)
+    print(f"[dense loss] {name} rows {rows}", flush=True)
+    R = len(rows)
+    ridx = torch.tensor(rows, device="cuda")
+    seq, pos = inp.row_seq[ridx].contiguous(), inp.row_pos[ridx].contiguous()
+    rs = dsa.rows_struct(seq, pos, cfg.num_seqs, cfg.max_ctx, cfg.kv_len - 1)
+    ld = (cfg.kv_len + 63) // 64 * 64
+    sc = np.full((R, ld), np.nan, dtype=np.float32)  # past t: never read
+    hrows = [host.row(int(r)) for r in rows]
+    for i, row in enumerate(hrows):
+        sc[i, : row.t + 1] = host.scores(row).astype(np.float32)
+    q = inp.q[ridx].contiguous()
+    loss, dsc = dsa.indexer_loss_dense(rs, q, inp.latent, cfg.scale, torch.from_numpy(sc).cuda())
+    torch.cuda.synchronize()
+    loss, dsc = loss.cpu().numpy(), dsc.cpu().numpy()
+    for i, row in enumerate(hrows):
+        n = row.t + 1
+        ent = host.latent_rows(row.b, np.arange(n))
+        p = oracle.attention_target(oracle.decode_bf16(row.q), oracle.decode_bf16(ent), cfg.scale)
+        Is = sc[i, :n].astype(np.float64)
+        l_ref, g_ref = oracle.indexer_kl(p, Is)
+        sm = np.exp(Is - Is.max())
+        sm /= sm.sum()
+        assert abs(loss[i] - l_ref) <= 1e-3 * abs(l_ref) + 1e-6, (rows[i], loss[i], l_ref)
+        err = np.abs(dsc[i, :n] - g_ref)
+        assert np.all(err <= 1e-3 * (p + sm) + 1e-7), (rows[i], float(err.max()))
+        assert np.all(dsc[i, n:] == 0.0)
+        print(f"[dense loss] row {int(rows[i])} (t = {row.t}): loss {loss[i]:.6f} ref {l_ref:.6f}, "
+              f"max |d dI| {err.max():.2e}", flush=True)
+
+
 def test_indexer_loss_composed(dsa):
     """The whole forward on the GPU (scores, top-k, attention, loss): the loss is
     finite and non-negative, dscores sum to ~0 per row, and the loss agrees with the
