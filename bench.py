@@ -312,7 +312,10 @@ def time_training(dsa, st, K):
     dense = lambda: dsa.indexer_loss_dense(st.rows, i.q, i.latent, c.scale, st.scores, loss=loss,
                                            dscores=dsc_d, workspace=ws_d)
     out = {}
-    for name, fn in (("loss", fwd), ("backward", bwd), ("loss_dense", dense)):
+    bwd_d = lambda: dsa.indexer_backward_dense(st.rows, i.q_idx, i.q_scale, i.w, i.k_idx,
+                                               i.k_scale, dsc_d, dq, dw, dk)
+    for name, fn in (("loss", fwd), ("backward", bwd), ("loss_dense", dense),
+                     ("backward_dense", bwd_d)):
         for _ in range(3):
             fn()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -338,6 +341,10 @@ def time_training(dsa, st, K):
     out["loss_dense"].update({"positions": cand, "bf16_tflops": fl_d / out["loss_dense"]["ms"] / 1e9,
                               "frac_of_bf16_peak": fl_d / out["loss_dense"]["ms"] / 1e9
                               / BF16_PEAK_TFLOPS})
+    fl_bd = cand * 2 * 64 * 128 * 2
+    out["backward_dense"].update({"fp32_tflops": fl_bd / out["backward_dense"]["ms"] / 1e9,
+                                  "frac_of_fp32_vector_peak": fl_bd / out["backward_dense"]["ms"]
+                                  / 1e9 / 157.3})
     del dk, dq, dw, ws, dsc, loss, dsc_d, ws_d
     torch.cuda.empty_cache()
     return out

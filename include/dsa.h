@@ -308,6 +308,19 @@ dsa_status dsa_indexer_loss_dense(const dsa_rows* rows, const dsa_dims* dims, co
                                   int64_t ld_scores, float* loss, float* dscores, void* workspace,
                                   size_t ws_bytes, void* stream);
 
+/* Backward of the dense warm-up loss into the indexer: dsa_indexer_backward's
+ * products with every causal position s <= t as an entry and dscores [R, ld_dscores]
+ * indexed by position (the dscores of dsa_indexer_loss_dense):
+ *   dw[r,j] += dscores[r,s] max(d, 0),  dq[r,j,:] += dscores[r,s] w[r,j] m k_s,
+ *   dk[b,s,:] += dscores[r,s] w[r,j] m q_j          for all s <= t(r)
+ * Same formats, accumulation (atomic, caller-zeroed) and arithmetic as
+ * dsa_indexer_backward.  Contiguous caches; production dims. */
+dsa_status dsa_indexer_backward_dense(const dsa_rows* rows, const dsa_dims* dims, const void* q_idx,
+                                      const float* q_scale, const float* w, const void* k_idx,
+                                      const float* k_scale, const float* dscores,
+                                      int64_t ld_dscores, float* dq, float* dw, float* dk,
+                                      void* stream);
+
 dsa_status dsa_indexer_backward(const dsa_rows* rows, const dsa_dims* dims, const void* q_idx,
                                 const float* q_scale, const float* w, const void* k_idx,
                                 const float* k_scale, const int32_t* indices,

@@ -35,7 +35,7 @@ EXPORTED_SYMBOLS = [
     "dsa_project_append_workspace_size", "dsa_project_append", "dsa_indexer_scores_paged",
     "dsa_sparse_mla_attn_paged", "dsa_forward_paged", "dsa_project_append_paged",
     "dsa_indexer_loss_workspace_size", "dsa_indexer_loss", "dsa_indexer_backward",
-    "dsa_indexer_loss_dense_workspace_size", "dsa_indexer_loss_dense",
+    "dsa_indexer_loss_dense_workspace_size", "dsa_indexer_loss_dense", "dsa_indexer_backward_dense",
     "dsa_mha_prefill_workspace_size", "dsa_mha_prefill",
     "dsa_status_string", "dsa_last_error", "dsa_api_version",
 ]
@@ -97,13 +97,15 @@ def _load() -> ctypes.CDLL:
     L.dsa_indexer_loss_dense_workspace_size.argtypes = [R, D]
     L.dsa_indexer_loss_dense_workspace_size.restype = sz
     L.dsa_indexer_loss_dense.argtypes = [R, D, vp, vp, f32, vp, i64, vp, vp, vp, sz, vp]
+    L.dsa_indexer_backward_dense.argtypes = [R, D, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp]
     L.dsa_mha_prefill_workspace_size.argtypes = [R, D]
     L.dsa_mha_prefill_workspace_size.restype = sz
     L.dsa_mha_prefill.argtypes = [R, D, vp, vp, vp, vp, vp, f32, vp, vp, vp, sz, vp]
     for name in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_attn", "dsa_forward",
                  "dsa_project_append", "dsa_indexer_scores_paged", "dsa_sparse_mla_attn_paged",
                  "dsa_forward_paged", "dsa_project_append_paged", "dsa_indexer_loss",
-                 "dsa_indexer_backward", "dsa_mha_prefill", "dsa_indexer_loss_dense"):
+                 "dsa_indexer_backward", "dsa_mha_prefill", "dsa_indexer_loss_dense",
+                 "dsa_indexer_backward_dense"):
         getattr(L, name).restype = ctypes.c_int
     L.dsa_status_string.argtypes = [ctypes.c_int]
     L.dsa_status_string.restype = ctypes.c_char_p
@@ -606,6 +608,31 @@ def indexer_backward(rows: _Rows, q_idx, q_scale, w, k_idx, k_scale, indices, ds
                                     _ptr(q_scale), _ptr(w), _ptr(k_idx), _ptr(k_scale),
                                     _ptr(indices), _ptr(dscores), _ptr(dq), _ptr(dw), _ptr(dk),
                                     _stream()))
+    return dq, dw, dk
+
+
+def indexer_backward_dense(rows: _Rows, q_idx, q_scale, w, k_idx, k_scale, dscores, dq, dw, dk,
+                           dims: Dims = PRODUCTION_DIMS):
+    """dsa_indexer_backward_dense: the dense warm-up loss's dscores [R, ld] (by position)
+    into dq, dw and dk (fp32, accumulated; zeroed by the caller)."""
+    R = rows.num_rows
+    for t, dt, name in ((q_idx, torch.uint8, "q_idx"), (q_scale, torch.float32, "q_scale"),
+                        (w, torch.float32, "w"), (k_idx, torch.uint8, "k_idx"),
+                        (k_scale, torch.float32, "k_scale"), (dscores, torch.float32, "dscores"),
+                        (dq, torch.float32, "dq"), (dw, torch.float32, "dw"),
+                        (dk, torch.float32, "dk")):
+        _dev(t, dt, name)
+    _shape(q_idx, (R, dims.n_idx_heads, dims.idx_dim), "q_idx")
+    _shape(dq, (R, dims.n_idx_heads, dims.idx_dim), "dq")
+    _shape(dw, (R, dims.n_idx_heads), "dw")
+    _shape(dscores, (R, None), "dscores")
+    _caches(rows, dims, k_idx, k_scale)
+    _shape(dk, (rows.num_seqs, rows.max_ctx, dims.idx_dim), "dk")
+    ds = dims_struct(dims)
+    _check(lib.dsa_indexer_backward_dense(ctypes.byref(rows), ctypes.byref(ds), _ptr(q_idx),
+                                          _ptr(q_scale), _ptr(w), _ptr(k_idx), _ptr(k_scale),
+                                          _ptr(dscores), dscores.shape[1], _ptr(dq), _ptr(dw),
+                                          _ptr(dk), _stream()))
     return dq, dw, dk
 
 

@@ -455,6 +455,27 @@ dsa_status dsa_indexer_loss_dense(const dsa_rows* rows, const dsa_dims* dims, co
   return err == hipSuccess ? DSA_OK : hip_fail(err, "dense indexer loss launch");
 }
 
+dsa_status dsa_indexer_backward_dense(const dsa_rows* rows, const dsa_dims* dims, const void* q_idx,
+                                      const float* q_scale, const float* w, const void* k_idx,
+                                      const float* k_scale, const float* dscores,
+                                      int64_t ld_dscores, float* dq, float* dw, float* dk,
+                                      void* stream) {
+  dsa_status st = check_rows(rows);
+  if (st != DSA_OK) return st;
+  if (dims == nullptr) return fail(DSA_E_INVALID, "dims is NULL");
+  if (!is_production(*dims))
+    return fail(DSA_E_UNSUPPORTED, "the indexer backward supports the production dims only");
+  if (rows->num_rows == 0) return DSA_OK;
+  if (!q_idx || !q_scale || !w || !k_idx || !k_scale || !dscores || !dq || !dw || !dk)
+    return fail(DSA_E_INVALID, "NULL tensor pointer");
+  if (ld_dscores < (int64_t)rows->max_pos + 1)
+    return fail(DSA_E_INVALID, "ld_dscores < max_pos + 1");
+  const hipError_t err = dsa::launch_indexer_backward_dense(
+      *rows, static_cast<const uint8_t*>(q_idx), q_scale, w, static_cast<const uint8_t*>(k_idx),
+      k_scale, dscores, ld_dscores, dq, dw, dk, as_stream(stream));
+  return err == hipSuccess ? DSA_OK : hip_fail(err, "dense indexer backward launch");
+}
+
 dsa_status dsa_indexer_backward(const dsa_rows* rows, const dsa_dims* dims, const void* q_idx,
                                 const float* q_scale, const float* w, const void* k_idx,
                                 const float* k_scale, const int32_t* indices,

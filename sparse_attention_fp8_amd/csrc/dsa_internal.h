@@ -70,6 +70,10 @@ hipError_t launch_project(const dsa_rows& rows, int d_model, const uint16_t* h, 
 
 size_t indexer_loss_workspace_bytes(int num_rows, int topk);
 size_t indexer_loss_dense_workspace_bytes(int num_rows, int max_pos);
+hipError_t launch_indexer_backward_dense(const dsa_rows& rows, const uint8_t* q_idx,
+                                         const float* q_scale, const float* w, const uint8_t* k_idx,
+                                         const float* k_scale, const float* dscores, int64_t ld,
+                                         float* dq, float* dw, float* dk, hipStream_t stream);
 hipError_t launch_indexer_loss_dense(const dsa_rows& rows, const void* q, const void* latent,
                                      float softmax_scale, const float* scores, int64_t ld,
                                      float* loss, float* dscores, void* workspace,

@@ -375,13 +375,17 @@ __device__ __forceinline__ float e4m3_value(uint32_t c) {
   return __uint_as_float(__float_as_uint(mag) | s);
 }
 
+// DENSE: the entries are every causal position 0..t (no index list), with dscores
+// [R, ld] indexed by position (the dense warm-up loss's gradient); nblk_dense
+// blocks per row cover positions up to max_pos.
+template <bool DENSE>
 __global__ __launch_bounds__(BT) void indexer_bwd_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale,
     const float* __restrict__ w, const uint8_t* __restrict__ k_idx,
     const float* __restrict__ k_scale, const int32_t* __restrict__ indices,
     const float* __restrict__ dscores, const int32_t* __restrict__ row_seq,
     const int32_t* __restrict__ row_pos, int B, int N, int topk, float* __restrict__ dq,
-    float* __restrict__ dw, float* __restrict__ dk, PageMap pm) {
+    float* __restrict__ dw, float* __restrict__ dk, PageMap pm, int64_t ld, int nblk_dense) {
   __shared__ __attribute__((aligned(16))) float kf[BG][ID + 4];   // dequantised keys
   __shared__ __attribute__((aligned(16))) float qf[IH][ID + 4];   // dequantised queries
   __shared__ __attribute__((aligned(16))) float cq[IH][BG + 4];   // dI w m, head-major
@@ -389,10 +393,11 @@ __global__ __launch_bounds__(BT) void indexer_bwd_kernel(
   __shared__ float dwp[BT / 64][IH];
   __shared__ int rows_s[BG];
   __shared__ float g_s[BG], ks_s[BG];
-  const int nblk = topk / (BG * BGPB);
+  const int nblk = DENSE ? nblk_dense : topk / (BG * BGPB);
   const int r = blockIdx.x / nblk, ebase = (blockIdx.x - r * nblk) * BG * BGPB;
   const int b = row_seq[r], t = row_pos[r];
   if (b < 0 || b >= B || t < 0 || t >= N) return;
+  if (DENSE && ebase > t) return;  // every position of this block is past the row
   const int tid = threadIdx.x, l = lane_id(), g = l >> 4, n = l & 15, wv = tid >> 6;
   const bool paged = pm.table != nullptr;
   const uint8_t* kbase = paged ? k_idx : k_idx + (size_t)b * N * ID;
@@ -430,11 +435,11 @@ __global__ __launch_bounds__(BT) void indexer_bwd_kernel(
     const int e0 = ebase + gi * BG;
     __syncthreads();  // the previous group's LDS reads are done
     if (tid < BG) {
-      const int p = indices[(size_t)r * topk + e0 + tid];
+      const int p = DENSE ? e0 + tid : indices[(size_t)r * topk + e0 + tid];
       const bool v = p >= 0 && p <= t;
       const int row = v ? (paged ? (int)paged_row(pm, b, p) : p) : -1;
       rows_s[tid] = row;
-      g_s[tid] = v ? dscores[(size_t)r * topk + e0 + tid] : 0.f;
+      g_s[tid] = v ? (DENSE ? dscores[(size_t)r * ld + p] : dscores[(size_t)r * topk + e0 + tid]) : 0.f;
       ks_s[tid] = v ? sbase[row] : 0.f;
     }
     __syncthreads();
@@ -596,9 +601,23 @@ hipError_t launch_indexer_backward(const dsa_rows& rows, const uint8_t* q_idx,
                                    hipStream_t stream, const PageMap& pm) {
   const int R = rows.num_rows;
   if (R == 0) return hipSuccess;
-  hipLaunchKernelGGL(indexer_bwd_kernel, dim3(R * (kTopk / (BG * BGPB))), dim3(BT), 0, stream, q_idx,
-                     q_scale, w, k_idx, k_scale, indices, dscores, rows.row_seq, rows.row_pos,
-                     rows.num_seqs, rows.max_ctx, kTopk, dq, dw, dk, pm);
+  hipLaunchKernelGGL(indexer_bwd_kernel<false>, dim3(R * (kTopk / (BG * BGPB))), dim3(BT), 0, stream,
+                     q_idx, q_scale, w, k_idx, k_scale, indices, dscores, rows.row_seq, rows.row_pos,
+                     rows.num_seqs, rows.max_ctx, kTopk, dq, dw, dk, pm, (int64_t)0, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_indexer_backward_dense(const dsa_rows& rows, const uint8_t* q_idx,
+                                         const float* q_scale, const float* w, const uint8_t* k_idx,
+                                         const float* k_scale, const float* dscores, int64_t ld,
+                                         float* dq, float* dw, float* dk, hipStream_t stream) {
+  const int R = rows.num_rows;
+  if (R == 0) return hipSuccess;
+  const int nblk = (rows.max_pos + BG * BGPB) / (BG * BGPB);
+  hipLaunchKernelGGL(indexer_bwd_kernel<true>, dim3((unsigned)((int64_t)R * nblk)), dim3(BT), 0,
+                     stream, q_idx, q_scale, w, k_idx, k_scale, nullptr, dscores, rows.row_seq,
+                     rows.row_pos, rows.num_seqs, rows.max_ctx, kTopk, dq, dw, dk, PageMap{}, ld,
+                     nblk);
   return hipGetLastError();
 }
 

@@ -239,3 +239,66 @@ def test_indexer_backward_parity(dsa, name, rows):
     mask = torch.zeros(cfg.num_seqs, cfg.max_ctx, dtype=torch.bool, device="cuda")
     mask[bt, st] = True
     assert bool((dk[~mask] == 0).all())
+
+
+@pytest.mark.parametrize("name,rows", [("decode32k", [0, 13]),
+                                       ("prefill8k", list(range(3000, 3008)))])
+def test_indexer_backward_dense_parity(dsa, name, rows):
+    """The dense backward: a seeded gradient over every position s <= t, against the
+    oracle's backward over all t + 1 keys, under the sparse backward's bars; the
+    prefill rows share almost all of their keys, so dk sums over rows."""
+    cfg = di.CONFIGS[name]
+    inp = dev_inputs(name)
+    host = HostInputs(cfg)
+    print(f"[backward dense] {name} rows {rows[0]}..{rows[-1]}", flush=True)
+    R = len(rows)
+    ridx = torch.tensor(rows, device="cuda")
+    seq, pos = inp.row_seq[ridx].contiguous(), inp.row_pos[ridx].contiguous()
+    rs = dsa.rows_struct(seq, pos, cfg.num_seqs, cfg.max_ctx, cfg.kv_len - 1)
+    ld = (cfg.kv_len + 63) // 64 * 64
+    rng = np.random.default_rng(78)
+    g = np.zeros((R, ld), dtype=np.float32)
+    hrows = [host.row(int(r)) for r in rows]
+    for i, row in enumerate(hrows):
+        g[i, : row.t + 1] = (rng.standard_normal(row.t + 1) * 1e-4).astype(np.float32)
+        g[i, row.t + 1:] = np.nan  # past t: never read
+    dq = torch.zeros(R, 64, 128, dtype=torch.float32, device="cuda")
+    dw = torch.zeros(R, 64, dtype=torch.float32, device="cuda")
+    dk = torch.zeros(cfg.num_seqs, cfg.max_ctx, 128, dtype=torch.float32, device="cuda")
+    dsa.indexer_backward_dense(rs, inp.q_idx[ridx].contiguous(), inp.q_scale[ridx].contiguous(),
+                               inp.w[ridx].contiguous(), inp.k_idx, inp.k_scale,
+                               torch.from_numpy(g).cuda(), dq, dw, dk)
+    torch.cuda.synchronize()
+    dq, dw = dq.cpu().numpy(), dw.cpu().numpy()
+    dk_ref, dk_tol = {}, {}
+    for i, row in enumerate(hrows):
+        n = row.t + 1
+        qf = oracle.decode_e4m3fn(row.q_idx) * row.q_scale[:, None]
+        codes, ksc = host.keys(row.b, n)
+        kf = oracle.decode_e4m3fn(codes) * ksc[:, None]
+        gi = g[i, :n].astype(np.float64)
+        q_ref, w_ref, k_ref = oracle.indexer_backward(qf, row.w, kf, gi)
+        dots = qf @ kf.T
+        absd = np.abs(qf) @ np.abs(kf).T
+        amb = np.abs(dots) <= 2e-3 * absd
+        coef_abs = np.abs(row.w)[:, None] * np.abs(gi)[None, :]
+        tol_q = 1e-5 * ((coef_abs * (dots > 0)) @ np.abs(kf)) + (coef_abs * amb) @ np.abs(kf) + 1e-12
+        assert np.all(np.abs(dq[i] - q_ref) <= tol_q), float(np.max(np.abs(dq[i] - q_ref) - tol_q))
+        tol_w = 1e-5 * (np.maximum(dots, 0) @ np.abs(gi)) + (2e-3 * absd) @ np.abs(gi) + 1e-12
+        assert np.all(np.abs(dw[i] - w_ref) <= tol_w)
+        tol_k = 1e-5 * ((coef_abs * (dots > 0)).T @ np.abs(qf)) + (coef_abs * amb).T @ np.abs(qf) + 1e-12
+        for s_ in range(n):
+            key = (row.b, s_)
+            dk_ref[key] = dk_ref.get(key, 0.0) + k_ref[s_]
+            dk_tol[key] = dk_tol.get(key, 0.0) + tol_k[s_]
+    keys = list(dk_ref)
+    bt = torch.tensor([k[0] for k in keys], device="cuda")
+    st = torch.tensor([k[1] for k in keys], device="cuda")
+    got = dk[bt, st].cpu().numpy()
+    ref = np.stack([dk_ref[k] for k in keys])
+    tol = np.stack([dk_tol[k] for k in keys])
+    assert np.all(np.abs(got - ref) <= tol + 1e-12), float(np.max(np.abs(got - ref) - tol))
+    mask = torch.zeros(cfg.num_seqs, cfg.max_ctx, dtype=torch.bool, device="cuda")
+    mask[bt, st] = True
+    assert bool((dk[~mask] == 0).all())
+    print(f"[backward dense] {name}: dq, dw, dk within bars over {len(keys)} keys", flush=True)
