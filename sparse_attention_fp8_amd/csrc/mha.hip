@@ -30,54 +30,83 @@ constexpr int KCOLS = H * DH;       // 16384 key columns, then as many value col
 // ---------------------------------------------------------------------------
 // Decompression: y[s, :] = W c_s with W = [W_UK; W_UV] (32768 x 512).  Block =
 // 4 waves, 64 positions x 256 columns; wave w owns columns [64 w, 64 w + 64) for
-// all 64 positions (4 x 4 MFMA tiles); operands go straight from global memory
-// into registers one contraction step ahead.
+// all 64 positions (4 x 4 MFMA tiles).  Per contraction step of 32 the block
+// stages the A tile (64 positions x 32) and the B tile (256 weight rows x 32) in
+// LDS (rows padded to 80 bytes, so a tile column's 16 rows hit distinct banks),
+// double-buffered: the next step's tiles are loaded into registers while this
+// step's MFMAs run, then stored to the other buffer, one barrier per step.
 // ---------------------------------------------------------------------------
+constexpr int DKS = 32;          // contraction step
+constexpr int DPAD = DKS + 8;    // padded tile row (bf16)
+constexpr int DPOS = 64;         // positions per block
+constexpr int DCOL = 256;        // columns per block
+constexpr int DCH = (DPOS + DCOL) * (DKS / 8);  // 16-byte chunks per step (1280)
+static_assert(DCH % 256 == 0, "whole chunks per thread");
+
 __global__ __launch_bounds__(256) void mha_decompress_kernel(
     const uint16_t* __restrict__ latent, const uint16_t* __restrict__ w_uk,
     const uint16_t* __restrict__ w_uv, int N, int Lc, int L, uint16_t* __restrict__ kout,
     uint16_t* __restrict__ vtout) {
   // positions [0, Lc) hold entries; the rest of the padded length L repeats the last
   // one, so every position of the outputs is finite
+  __shared__ __attribute__((aligned(16))) uint16_t at[2][DPOS][DPAD];
+  __shared__ __attribute__((aligned(16))) uint16_t bt[2][DCOL][DPAD];
   const int b = blockIdx.z;
-  const int s0 = blockIdx.y * 64;
-  const int c0 = blockIdx.x * 256;
-  const int l = lane_id(), wv = threadIdx.x >> 6, g = l >> 4, n = l & 15;
+  const int s0 = blockIdx.y * DPOS;
+  const int c0 = blockIdx.x * DCOL;
+  const int tid = threadIdx.x, l = lane_id(), wv = tid >> 6, g = l >> 4, n = l & 15;
   const uint16_t* lat = latent + (size_t)b * N * kQkDim;
-  // A rows (positions, clamped to the last valid one) and B rows (weight rows)
-  const uint16_t* arow[4];
+  // this thread's chunks of a step: chunk c = tid + 256 j is row c / 4 (A rows
+  // first, then B rows), dims 8 (c % 4) .. +8 of the step
+  constexpr int CPT = DCH / 256;  // 5
+  const uint16_t* src[CPT];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-    arow[mt] = lat + (size_t)min(s0 + 16 * mt + n, Lc - 1) * kQkDim + 8 * g;
-  const uint16_t* brow[4];
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int col = c0 + 64 * wv + 16 * nt + n;
-    brow[nt] = (col < KCOLS ? w_uk + (size_t)col * DL : w_uv + (size_t)(col - KCOLS) * DL) + 8 * g;
+  for (int j = 0; j < CPT; ++j) {
+    const int c = tid + 256 * j, row = c >> 2, d8 = c & 3;
+    if (row < DPOS) {
+      src[j] = lat + (size_t)min(s0 + row, Lc - 1) * kQkDim + 8 * d8;
+    } else {
+      const int col = c0 + row - DPOS;
+      src[j] = (col < KCOLS ? w_uk + (size_t)col * DL : w_uv + (size_t)(col - KCOLS) * DL) + 8 * d8;
+    }
   }
+  i32x4 pf[CPT];
+  auto fetch = [&](int ks) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) pf[j] = *reinterpret_cast<const i32x4*>(src[j] + DKS * ks);
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int c = tid + 256 * j, row = c >> 2, d8 = c & 3;
+      uint16_t* dst = row < DPOS ? &at[buf][row][8 * d8] : &bt[buf][row - DPOS][8 * d8];
+      *reinterpret_cast<i32x4*>(dst) = pf[j];
+    }
+  };
   f32x4 acc[4][4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  i32x4 a[2][4], bb[2][4];
-  auto load = [&](int slot, int ks) {
+  fetch(0);
+  stash(0);
+  constexpr int NKS = DL / DKS;  // 16
+  for (int ks = 0; ks < NKS; ++ks) {
+    const int cur = ks & 1;
+    __syncthreads();  // buffer cur is complete; every wave is done with buffer cur ^ 1
+    if (ks + 1 < NKS) fetch(ks + 1);
+    bf16x8 a[4], bb[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      a[slot][i] = *reinterpret_cast<const i32x4*>(arow[i] + 32 * ks);
-      bb[slot][i] = *reinterpret_cast<const i32x4*>(brow[i] + 32 * ks);
-    }
-  };
-  load(0, 0);
+    for (int mt = 0; mt < 4; ++mt)
+      a[mt] = as_bf16x8(*reinterpret_cast<const i32x4*>(&at[cur][16 * mt + n][8 * g]));
 #pragma unroll
-  for (int ks = 0; ks < DL / 32; ++ks) {
-    if (ks + 1 < DL / 32) load((ks + 1) & 1, ks + 1);
+    for (int nt = 0; nt < 4; ++nt)
+      bb[nt] = as_bf16x8(*reinterpret_cast<const i32x4*>(&bt[cur][64 * wv + 16 * nt + n][8 * g]));
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-        acc[mt][nt] = mfma_bf16_16x16x32(as_bf16x8(a[ks & 1][mt]), as_bf16x8(bb[ks & 1][nt]),
-                                         acc[mt][nt]);
+      for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma_bf16_16x16x32(a[mt], bb[nt], acc[mt][nt]);
+    if (ks + 1 < NKS) stash(cur ^ 1);
   }
   // lane holds positions s0 + 16 mt + 4 g + v of column c0 + 64 wv + 16 nt + n
 #pragma unroll
