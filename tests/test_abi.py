@@ -164,3 +164,43 @@ def test_paged_host_checks(m):
                                p, p, p, 0.1, p, p, None, 0, p, 16, None) == m.DSA_E_WORKSPACE
     assert L.dsa_project_append_paged(ctypes.byref(r), ctypes.byref(d), ctypes.byref(pages()), 100,
                                       *([p] * 11), p, 1 << 30, None) == m.DSA_E_UNSUPPORTED
+
+
+def test_training_and_mha_host_checks(m):
+    """The loss, backward and masked-MHA entry points reject invalid arguments on
+    the host, and their workspace sizes follow the documented layouts."""
+    L = m.lib
+    d = m.dims_struct(m.PRODUCTION_DIMS)
+    f32 = m.dims_struct(m.Dims(4, 32, 16, 80, 64, 64, True))
+    p = ctypes.c_void_p(16)
+    dec = _rows(m, R=32, B=32, N=32768, max_pos=32767)
+    # dense warm-up loss: workspace = target [R, C * 1024] + per-chunk (max, sum) [R, C, 128]
+    need = L.dsa_indexer_loss_dense_workspace_size(ctypes.byref(dec), ctypes.byref(d))
+    assert need == 32 * 32 * (1024 * 4 + 128 * 8)
+    assert L.dsa_indexer_loss_dense_workspace_size(ctypes.byref(dec), ctypes.byref(f32)) == 0
+    dense = lambda rows, dims, ld, ws, n: L.dsa_indexer_loss_dense(
+        ctypes.byref(rows), dims, p, p, 0.1, p, ld, p, p, ws, n, None)
+    assert dense(dec, ctypes.byref(f32), 32768, p, need) == m.DSA_E_UNSUPPORTED
+    assert dense(dec, None, 32768, p, need) == m.DSA_E_INVALID
+    assert dense(dec, ctypes.byref(d), 32767, p, need) == m.DSA_E_INVALID      # ld < max_pos + 1
+    assert dense(dec, ctypes.byref(d), 32768, p, need - 1) == m.DSA_E_WORKSPACE
+    assert dense(dec, ctypes.byref(d), 32768, None, need) == m.DSA_E_WORKSPACE
+    assert L.dsa_indexer_loss_dense(ctypes.byref(dec), ctypes.byref(d), None, p, 0.1, p, 32768, p,
+                                    p, p, need, None) == m.DSA_E_INVALID
+    # dense backward
+    bwd = lambda ld, dq: L.dsa_indexer_backward_dense(ctypes.byref(dec), ctypes.byref(d), p, p, p, p,
+                                                      p, p, ld, dq, p, p, None)
+    assert bwd(32767, p) == m.DSA_E_INVALID
+    assert bwd(32768, None) == m.DSA_E_INVALID
+    # masked MHA mode: short prefill only, production dims, workspace
+    pre = _rows(m, R=8192, B=1, N=8192, max_pos=8191)
+    need = L.dsa_mha_prefill_workspace_size(ctypes.byref(pre), ctypes.byref(d))
+    assert need == 8192 * 16384 * 2 * 2 + 8192 * (8192 // 32) * 4
+    mha = lambda rows, dims, ws, n: L.dsa_mha_prefill(ctypes.byref(rows), dims, p, p, p, p, p, 0.1,
+                                                     p, p, ws, n, None)
+    assert mha(pre, ctypes.byref(f32), p, need) == m.DSA_E_UNSUPPORTED
+    assert mha(pre, ctypes.byref(d), p, need - 1) == m.DSA_E_WORKSPACE
+    long_rows = _rows(m, R=8, B=1, N=32768, max_pos=16384)                    # 16385 positions
+    assert mha(long_rows, ctypes.byref(d), p, 1 << 40) == m.DSA_E_UNSUPPORTED
+    assert L.dsa_mha_prefill(ctypes.byref(pre), ctypes.byref(d), None, p, p, p, p, 0.1, p, p, p,
+                             need, None) == m.DSA_E_INVALID
