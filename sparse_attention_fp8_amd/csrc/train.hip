@@ -164,15 +164,38 @@ __global__ __launch_bounds__(TT) void dense_target_kernel(
   }
   float m_run = -INFINITY, l_run = 0.f;
 
+  // The next stage's pieces are fetched into registers while this stage computes:
+  // piece tid + TT j (j < 5; the last only for tid < 256) of the 32 x 72 tile.
+  constexpr int PPT = (TBE * TCH + TT - 1) / TT;  // 5
+  static_assert(TBE * TCH - (PPT - 1) * TT == TT / 2, "the last piece: half the threads");
+  i32x4 pf[PPT];
+  auto fetch = [&](int e0) {
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+      const int cc = tid + TT * j;
+      if (j < PPT - 1 || tid < TT / 2) {
+        const int e = cc / TCH, pc = cc - e * TCH;
+        const int pos = min(e0 + e, pend - 1);  // past the end: a valid entry, masked below
+        pf[j] = *reinterpret_cast<const i32x4*>(base + (size_t)pos * (DK * 2) + 16 * pc);
+      }
+    }
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+      const int cc = tid + TT * j;
+      if (j < PPT - 1 || tid < TT / 2) {
+        const int e = cc / TCH, pc = cc - e * TCH;
+        tile[e * TCH + (pc ^ (e & 7))] = pf[j];
+      }
+    }
+  };
+  fetch(p0);
   for (int e0 = p0; e0 < pend; e0 += TBE) {
     __syncthreads();  // previous stage's tile reads are done
-    for (int cc = tid; cc < TBE * TCH; cc += TT) {
-      const int e = cc / TCH, pc = cc - e * TCH;
-      const int pos = min(e0 + e, pend - 1);  // past the end: a valid entry, masked below
-      tile[e * TCH + (pc ^ (e & 7))] =
-          *reinterpret_cast<const i32x4*>(base + (size_t)pos * (DK * 2) + 16 * pc);
-    }
+    stash();
     __syncthreads();
+    if (e0 + TBE < pend) fetch(e0 + TBE);
     f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int s = 0; s < TKS; ++s)
