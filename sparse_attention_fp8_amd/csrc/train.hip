@@ -70,16 +70,38 @@ __global__ __launch_bounds__(TT) void attn_target_kernel(
   // log2-domain lse of this lane's head
   const float lse2 = lse[(size_t)r * H + 16 * wv + n] * 1.44269504088896340736f;
 
+  // The next stage's pieces are fetched into registers while this stage computes:
+  // piece tid + TT j (j < 5; the last only for tid < 256) of the 32 x 72 tile.
+  constexpr int SPT = (TBE * TCH + TT - 1) / TT;  // 5
+  i32x4 spf[SPT];
+  auto sfetch = [&](int e0) {
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) {
+      const int c = tid + TT * j;
+      if (j < SPT - 1 || tid < TT / 2) {
+        const int e = c / TCH, pc = c - e * TCH;
+        const int p = irow[e0 + e];
+        const uint32_t row = (p >= 0 && p < N) ? row_of(p) : row0;
+        spf[j] = *reinterpret_cast<const i32x4*>(base + (size_t)row * (DK * 2) + 16 * pc);
+      }
+    }
+  };
+  auto sstash = [&]() {
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) {
+      const int c = tid + TT * j;
+      if (j < SPT - 1 || tid < TT / 2) {
+        const int e = c / TCH, pc = c - e * TCH;
+        tile[e * TCH + (pc ^ (e & 7))] = spf[j];
+      }
+    }
+  };
+  if (ES > 0) sfetch(0);
   for (int e0 = 0; e0 < ES; e0 += TBE) {
     __syncthreads();  // previous stage's tile reads are done
-    for (int c = tid; c < TBE * TCH; c += TT) {
-      const int e = c / TCH, pc = c - e * TCH;
-      const int p = irow[e0 + e];
-      const uint32_t row = (p >= 0 && p < N) ? row_of(p) : row0;
-      tile[e * TCH + (pc ^ (e & 7))] =
-          *reinterpret_cast<const i32x4*>(base + (size_t)row * (DK * 2) + 16 * pc);
-    }
+    sstash();
     __syncthreads();
+    if (e0 + TBE < ES) sfetch(e0 + TBE);
     f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int s = 0; s < TKS; ++s)
