@@ -302,3 +302,39 @@ def test_indexer_backward_dense_parity(dsa, name, rows):
     mask[bt, st] = True
     assert bool((dk[~mask] == 0).all())
     print(f"[backward dense] {name}: dq, dw, dk within bars over {len(keys)} keys", flush=True)
+
+
+def test_dense_and_sparse_loss_agree_below_k(dsa):
+    """Rows with t + 1 <= k select every causal position, so the sparse-stage loss
+    (selection = 0..t, lse from the attention call) and the dense warm-up loss (its
+    own lse over 0..t) must agree: two entry points with separate kernels."""
+    cfg = di.CONFIGS["prefill8k"]
+    inp = dev_inputs("prefill8k")
+    rows = [0, 1, 7, 100, 1000, 2047]
+    R = len(rows)
+    ridx = torch.tensor(rows, device="cuda")
+    seq, pos = inp.row_seq[ridx].contiguous(), inp.row_pos[ridx].contiguous()
+    rs = dsa.rows_struct(seq, pos, cfg.num_seqs, cfg.max_ctx, cfg.kv_len - 1)
+    dims = dsa.Dims.from_config(cfg)
+    ld = (cfg.kv_len + 63) // 64 * 64
+    rng = np.random.default_rng(11)
+    sc = rng.standard_normal((R, ld)).astype(np.float32)
+    idx = np.full((R, cfg.topk), -1, dtype=np.int32)
+    for i, r in enumerate(rows):
+        t = int(inp.row_pos[r])
+        idx[i, : t + 1] = np.arange(t + 1)
+    sc_d, idx_d = torch.from_numpy(sc).cuda(), torch.from_numpy(idx).cuda()
+    q = inp.q[ridx].contiguous()
+    _, lse = dsa.sparse_mla_attn(rs, dims, q, inp.latent, idx_d, cfg.scale)
+    l_s, g_s = dsa.indexer_loss(rs, q, inp.latent, idx_d, lse, cfg.scale, sc_d)
+    l_d, g_d = dsa.indexer_loss_dense(rs, q, inp.latent, cfg.scale, sc_d)
+    torch.cuda.synchronize()
+    l_s, g_s, l_d, g_d = (x.cpu().numpy() for x in (l_s, g_s, l_d, g_d))
+    for i, r in enumerate(rows):
+        t = int(inp.row_pos[r])
+        assert abs(l_s[i] - l_d[i]) <= 2e-3 * abs(l_d[i]) + 2e-6, (r, l_s[i], l_d[i])
+        # dI: sparse by selection slot, dense by position (slot i holds position i here)
+        sm = np.exp(sc[i, : t + 1] - sc[i, : t + 1].max())
+        sm /= sm.sum()
+        assert np.all(np.abs(g_s[i, : t + 1] - g_d[i, : t + 1]) <= 2e-3 * (sm + np.abs(g_d[i, : t + 1])) + 2e-7)
+        print(f"[loss agree] row {r} (t = {t}): sparse {l_s[i]:.6f} dense {l_d[i]:.6f}", flush=True)
