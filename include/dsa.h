@@ -28,7 +28,8 @@
  *     reports a failed launch (earlier launches of the same call may have run).
  *     Device-side faults surface at the caller's next synchronisation.
  *   - Thread-safe and re-entrant: no global mutable state except the per-thread
- *     text behind dsa_last_error().
+ *     text behind dsa_last_error() and the per-device index-domain flag (a
+ *     debugging aid, see dsa_check_index_domain).
  *   - No C++ exception crosses this interface.
  *
  * Row model: a call processes R query rows.  Row r belongs to sequence
@@ -120,8 +121,9 @@ dsa_status dsa_indexer_scores(const dsa_rows* rows, const dsa_dims* dims,
  * Row r selects exactly n = min(topk, t+1) positions: those with the largest
  * scores, equal scores taken from the lowest position first (-0.0 equals +0.0).
  * indices[r, 0..n) hold them in ascending order, indices[r, n..topk) hold -1.
- * Supports topk in [1, 4096] and any t.  Scores must not be NaN (a NaN row gives
- * an unspecified but in-range selection).
+ * Supports topk in [1, 4096] and rows of up to 131072 candidates: max_pos + 1 >
+ * 131072 returns DSA_E_UNSUPPORTED before anything is enqueued.  Scores must not be
+ * NaN (a NaN row gives an unspecified but in-range selection).
  * ------------------------------------------------------------------------- */
 dsa_status dsa_topk(const dsa_rows* rows, int32_t topk, const float* scores,
                     int64_t ld_scores, int32_t* indices, void* stream);
@@ -130,7 +132,10 @@ dsa_status dsa_topk(const dsa_rows* rows, int32_t topk, const float* scores,
  * Step 3: sparse MLA attention (MQA mode).
  *   q       [R, H, D_k]  bf16 or fp32 per attn_dtype
  *   latent  [B, N, D_k]  bf16 or fp32
- *   indices [R, topk] int32: positions to attend; entries < 0 or >= N are padding
+ *   indices [R, topk] int32: positions to attend; entries outside [0, t] are
+ *           padding (causal rule of the selection: S_t holds preceding positions).
+ *           An entry past t also sets the device's index-domain flag, which
+ *           dsa_check_index_domain reports; -1 and other negatives are plain padding.
  *   out     [R, H, D_v]  bf16 or fp32 output
  *   lse     [R, H] fp32 output (natural log of the softmax denominator), or NULL
  * For each row r and head h over the listed positions S:
@@ -143,6 +148,8 @@ dsa_status dsa_topk(const dsa_rows* rows, int32_t topk, const float* scores,
  * split into S slices; the workspace then holds each slice's normalised output
  * (bf16) and its lse (fp32), merged as out = sum_i e^(lse_i - LSE) out_i in fp32
  * (see dsa_sparse_mla_attn_workspace_size; 0 bytes when no row is split).
+ * A contiguous bf16 latent cache is addressed with 32-bit byte offsets per
+ * sequence: max_ctx * D_k * 2 must stay below 4 GiB (else DSA_E_UNSUPPORTED).
  * ------------------------------------------------------------------------- */
 size_t dsa_sparse_mla_attn_workspace_size(const dsa_rows* rows, const dsa_dims* dims);
 
@@ -152,11 +159,17 @@ dsa_status dsa_sparse_mla_attn(const dsa_rows* rows, const dsa_dims* dims,
                                void* workspace, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
- * Whole path: step 1 -> step 2 -> step 3 for all R rows, processed in chunks of
+ * Whole path: the scoring, selection and sparse-attention steps of the DSA
+ * workflow ("DeepSeek-V3.2开源技术报告", "DSA principle": after the query and key
+ * projection, the indexer scores the preceding tokens, the top-k are selected,
+ * and sparse attention runs over them), i.e. step 1 -> step 2 -> step 3 for all
+ * R rows, processed in chunks of
  * chunk_rows rows (0 = all rows at once) so the score workspace stays bounded.
  * Inputs are those of the three steps; outputs out/lse as in step 3, plus the
  * selected positions in indices_out [R, topk] when it is not NULL.  The workspace
  * must be at least dsa_forward_workspace_size(rows, dims, chunk_rows) bytes.
+ * The limits of steps 2 and 3 apply (max_pos + 1 <= 131072; contiguous latent
+ * below 4 GiB per sequence); they are checked before anything is enqueued.
  * ------------------------------------------------------------------------- */
 size_t dsa_forward_workspace_size(const dsa_rows* rows, const dsa_dims* dims, int32_t chunk_rows);
 
@@ -299,7 +312,8 @@ dsa_status dsa_indexer_loss(const dsa_rows* rows, const dsa_dims* dims, const vo
  * cost is that of dense attention (two passes of q.c on the bf16 MFMA, in chunks of
  * 1024 positions; fp32 softmax sums).  The workspace holds the target and the
  * per-chunk partial sums (dsa_indexer_loss_dense_workspace_size bytes).  Rows whose
- * sequence or position is out of range get loss 0 and a zero dscores row.
+ * sequence or position is out of range (including t > max_pos) get loss 0 and a
+ * zero dscores row, and read nothing past the workspace.
  */
 size_t dsa_indexer_loss_dense_workspace_size(const dsa_rows* rows, const dsa_dims* dims);
 
@@ -354,6 +368,13 @@ dsa_status dsa_mha_prefill(const dsa_rows* rows, const dsa_dims* dims, const voi
                            const void* latent, const void* w_uk, const void* w_uv,
                            const int32_t* indices, float softmax_scale, void* out, float* lse,
                            void* workspace, size_t ws_bytes, void* stream);
+
+/* Index-domain check (a debugging aid for callers that build index lists
+ * themselves).  Sets *seen to 1 if an attention kernel on the calling thread's
+ * current device met an index entry past its row's position t since the last
+ * check (such entries are padding in the result), else 0, and clears the flag.
+ * Synchronises the device first.  Returns DSA_E_HIP if a runtime call fails. */
+dsa_status dsa_check_index_domain(int32_t* seen);
 
 /* Status text, and the detail of the last failure on the calling thread. */
 const char* dsa_status_string(dsa_status status);

@@ -16,7 +16,8 @@ import torch
 
 __all__ = [
     "LIB_PATH", "lib", "Dims", "PRODUCTION_DIMS", "rows_struct", "dims_struct",
-    "indexer_scores", "topk", "sparse_mla_attn", "forward", "forward_workspace_size",
+    "indexer_scores", "topk", "sparse_mla_attn", "forward",
+    "forward_workspace_size", "check_index_domain",
     "sparse_mla_attn_workspace_size", "project_append", "project_append_workspace_size",
     "pages_struct", "indexer_scores_paged", "sparse_mla_attn_paged", "forward_paged",
     "project_append_paged", "indexer_loss", "indexer_loss_workspace_size", "indexer_backward",
@@ -37,7 +38,7 @@ EXPORTED_SYMBOLS = [
     "dsa_indexer_loss_workspace_size", "dsa_indexer_loss", "dsa_indexer_backward",
     "dsa_indexer_loss_dense_workspace_size", "dsa_indexer_loss_dense", "dsa_indexer_backward_dense",
     "dsa_mha_prefill_workspace_size", "dsa_mha_prefill",
-    "dsa_status_string", "dsa_last_error", "dsa_api_version",
+    "dsa_check_index_domain", "dsa_status_string", "dsa_last_error", "dsa_api_version",
 ]
 
 
@@ -105,8 +106,9 @@ def _load() -> ctypes.CDLL:
                  "dsa_project_append", "dsa_indexer_scores_paged", "dsa_sparse_mla_attn_paged",
                  "dsa_forward_paged", "dsa_project_append_paged", "dsa_indexer_loss",
                  "dsa_indexer_backward", "dsa_mha_prefill", "dsa_indexer_loss_dense",
-                 "dsa_indexer_backward_dense"):
+                 "dsa_indexer_backward_dense", "dsa_check_index_domain"):
         getattr(L, name).restype = ctypes.c_int
+    L.dsa_check_index_domain.argtypes = [ctypes.POINTER(ctypes.c_int32)]
     L.dsa_status_string.argtypes = [ctypes.c_int]
     L.dsa_status_string.restype = ctypes.c_char_p
     L.dsa_last_error.restype = ctypes.c_char_p
@@ -187,6 +189,14 @@ def _stream():
 def _check(status: int):
     if status != DSA_OK:
         raise DSAError(status, lib.dsa_last_error().decode() or lib.dsa_status_string(status).decode())
+
+
+def check_index_domain() -> bool:
+    """True if an attention call on the current device met an index entry past its
+    row's position since the last check (dsa_check_index_domain); clears the flag."""
+    seen = ctypes.c_int32(0)
+    _check(lib.dsa_check_index_domain(ctypes.byref(seen)))
+    return bool(seen.value)
 
 
 def _idx_dtype(d: Dims):
@@ -277,10 +287,10 @@ def forward_workspace_size(rows: _Rows, dims: Dims, chunk_rows: int = 0) -> int:
     return int(lib.dsa_forward_workspace_size(ctypes.byref(rows), ctypes.byref(ds), chunk_rows))
 
 
-def forward(rows: _Rows, dims: Dims, q_idx, q_scale, w, k_idx, k_scale, q, latent,
-            softmax_scale: float, out=None, lse=None, indices_out=None, chunk_rows: int = 0,
-            workspace: Optional[torch.Tensor] = None):
-    """dsa_forward: indexer -> top-k -> attention.  Returns (out, lse, indices_out)."""
+def _forward_outputs(rows: _Rows, dims: Dims, q_idx, q_scale, w, k_idx, k_scale, q, latent,
+                     out, lse, indices_out):
+    """Shape / dtype checks of the dsa_forward arguments; allocates out and lse when
+    not given."""
     adt = _attn_dtype(dims)
     for t, dt, name in ((q_idx, _idx_dtype(dims), "q_idx"), (k_idx, _idx_dtype(dims), "k_idx"),
                         (w, torch.float32, "w"), (q_scale, torch.float32, "q_scale"),
@@ -302,6 +312,15 @@ def forward(rows: _Rows, dims: Dims, q_idx, q_scale, w, k_idx, k_scale, q, laten
     _shape(lse, (R, dims.n_heads), "lse")
     _shape(indices_out, (R, dims.topk), "indices_out")
     _caches(rows, dims, k_idx, k_scale, latent)
+    return out, lse
+
+
+def forward(rows: _Rows, dims: Dims, q_idx, q_scale, w, k_idx, k_scale, q, latent,
+            softmax_scale: float, out=None, lse=None, indices_out=None, chunk_rows: int = 0,
+            workspace: Optional[torch.Tensor] = None):
+    """dsa_forward: indexer -> top-k -> attention.  Returns (out, lse, indices_out)."""
+    out, lse = _forward_outputs(rows, dims, q_idx, q_scale, w, k_idx, k_scale, q, latent, out,
+                                lse, indices_out)
     need = forward_workspace_size(rows, dims, chunk_rows)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)

@@ -36,14 +36,11 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libdsa.so)")
 
 
-def _flags(extra_debug: bool = False):
-    f = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
-         # packed fp32 VALU ops are kept out of every kernel
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-I", INCLUDE, "-I", CSRC, "-Wno-unused-command-line-argument"]
-    if extra_debug:
-        f.append("-DDSA_DEBUG=1")
-    return f
+def _flags():
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+            # packed fp32 VALU ops are kept out of every kernel
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-I", INCLUDE, "-I", CSRC, "-Wno-unused-command-line-argument"]
 
 
 def _compile(src: str, hipcc: str) -> str:

@@ -39,6 +39,16 @@
 namespace dsa {
 namespace {
 
+// Index-domain flag of this device: an attention kernel that meets an index entry
+// past its row's position t (a future position, which no causal selection holds)
+// stores 1 here with a plain vector store; the entry is treated as padding either
+// way.  The host reads and clears it through dsa_check_index_domain.
+__device__ uint32_t g_index_domain_flag = 0u;
+
+__device__ __forceinline__ void flag_index_domain() {
+  *static_cast<volatile uint32_t*>(&g_index_domain_flag) = 1u;
+}
+
 constexpr int H = kHeads;           // 128
 constexpr int DK = kQkDim;          // 576
 constexpr int DV = kVDim;           // 512
@@ -153,7 +163,7 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
     const int e = (P * 3641) >> 18;  // P / 72 for P < 2304
     const int c = kswz(e, P - e * KCH);
     const int p = nblk > 0 ? irow[e] : 0;
-    off_first[j] = __umul24((uint32_t)((p >= 0 && p < N) ? cache_row(p) : row0), (uint32_t)KROW) +
+    off_first[j] = __umul24((uint32_t)((p >= 0 && p <= t) ? cache_row(p) : row0), (uint32_t)KROW) +
                    (uint32_t)(16 * c);
   }
   constexpr int IPT = kTopk / NT;  // selected positions per thread (at most)
@@ -191,11 +201,18 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
       if (i < LOADS) gather16(lat_bytes, off_first[j], lds_addr(smem + i * 1024));
     }
   }
+  // Causal rule: entries outside [0, t] are padding.  An entry past t (a future
+  // position the selection cannot contain) also raises the index-domain flag.
+  bool future = false;
 #pragma unroll
   for (int k = 0; k < IPT; ++k) {
     const int i = tid + NT * k;
-    if (i < ES) sidx[i] = (pv[k] >= 0 && pv[k] < N) ? cache_row(pv[k]) : -1;
+    if (i < ES) {
+      sidx[i] = (pv[k] >= 0 && pv[k] <= t) ? cache_row(pv[k]) : -1;
+      future |= pv[k] > t;
+    }
   }
+  if (future) flag_index_domain();
 #pragma unroll
   for (int k = 0; k < QRC; ++k) {
     const int c = tid + NT * k, h = c >> 3, j = c & 7;
@@ -552,7 +569,8 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(
   float mx = -INFINITY;
   for (int i = tid; i < topk; i += 256) {
     const int p = indices[(size_t)r * topk + i];
-    const bool ok = p >= 0 && p < N;
+    const bool ok = p >= 0 && p <= t;  // entries outside [0, t] are padding
+    if (p > t) flag_index_domain();
     float s = -INFINITY;
     if (ok) {
       float dot = 0.f;
@@ -643,6 +661,19 @@ hipError_t launch_attn_bf16(const dsa_rows& rows, const void* q, const void* lat
   hipLaunchKernelGGL(attn_combine_kernel, dim3((R * H + CMB_RH - 1) / CMB_RH), dim3(CMB_T * CMB_RH),
                      0, stream, o_part, lse_part, R, S, static_cast<uint16_t*>(out), lse);
   return hipGetLastError();
+}
+
+hipError_t read_index_domain_flag(uint32_t* seen) {
+  hipError_t err = hipDeviceSynchronize();
+  if (err != hipSuccess) return err;
+  uint32_t v = 0u;
+  err = hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_index_domain_flag), sizeof(v), 0, hipMemcpyDeviceToHost);
+  if (err != hipSuccess) return err;
+  const uint32_t zero = 0u;
+  err = hipMemcpyToSymbol(HIP_SYMBOL(g_index_domain_flag), &zero, sizeof(zero), 0, hipMemcpyHostToDevice);
+  if (err != hipSuccess) return err;
+  *seen = v;
+  return hipDeviceSynchronize();
 }
 
 hipError_t launch_attn_f32(const dsa_rows& rows, const dsa_dims& dims, const float* q,

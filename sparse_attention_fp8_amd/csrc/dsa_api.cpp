@@ -39,6 +39,23 @@ dsa_status check_rows(const dsa_rows* rows) {
   return DSA_OK;
 }
 
+// The top-k kernels take rows of at most kTopkMaxPositions candidates.
+dsa_status check_topk_rows(const dsa_rows& rows) {
+  if ((int64_t)rows.max_pos + 1 > dsa::kTopkMaxPositions)
+    return fail(DSA_E_UNSUPPORTED, "top-k supports max_pos + 1 <= %d", dsa::kTopkMaxPositions);
+  return DSA_OK;
+}
+
+// Contiguous bf16 latent caches are addressed with 32-bit byte offsets within a
+// sequence: max_ctx * row bytes must fit.
+dsa_status check_latent_span(const dsa_rows& rows, const dsa_dims& dims) {
+  if (dims.attn_dtype == DSA_BF16 &&
+      (uint64_t)rows.max_ctx * (uint64_t)dims.qk_dim * 2u > dsa::kMaxLatentSeqBytes)
+    return fail(DSA_E_UNSUPPORTED, "a contiguous latent cache must stay below 4 GiB per sequence "
+                "(max_ctx * %d bytes)", dims.qk_dim * 2);
+  return DSA_OK;
+}
+
 bool is_production(const dsa_dims& d) {
   return d.n_idx_heads == dsa::kIdxHeads && d.idx_dim == dsa::kIdxDim &&
          d.n_heads == dsa::kHeads && d.qk_dim == dsa::kQkDim && d.v_dim == dsa::kVDim &&
@@ -141,6 +158,8 @@ dsa_status forward_impl(const dsa_rows* rows, const dsa_dims* dims, const dsa_pa
   dsa::PageMap pm;
   if (pages != nullptr && (st = check_pages(*rows, *dims, pages, kLatentRow, &pm)) != DSA_OK)
     return st;
+  if (pages == nullptr && (st = check_latent_span(*rows, *dims)) != DSA_OK) return st;
+  if ((st = check_topk_rows(*rows)) != DSA_OK) return st;
   if (chunk_rows < 0) return fail(DSA_E_INVALID, "chunk_rows < 0");
   const int R = rows->num_rows;
   if (R == 0) return DSA_OK;
@@ -246,6 +265,15 @@ const char* dsa_status_string(dsa_status status) {
 
 const char* dsa_last_error(void) { return g_last_error; }
 
+dsa_status dsa_check_index_domain(int32_t* seen) {
+  if (seen == nullptr) return fail(DSA_E_INVALID, "seen is NULL");
+  uint32_t v = 0u;
+  const hipError_t err = dsa::read_index_domain_flag(&v);
+  if (err != hipSuccess) return hip_fail(err, "index-domain flag read");
+  *seen = v != 0u ? 1 : 0;
+  return DSA_OK;
+}
+
 dsa_status dsa_indexer_scores(const dsa_rows* rows, const dsa_dims* dims, const void* q_idx,
                               const float* q_scale, const float* w, const void* k_idx,
                               const float* k_scale, float* scores, int64_t ld_scores,
@@ -268,6 +296,7 @@ dsa_status dsa_topk(const dsa_rows* rows, int32_t topk, const float* scores, int
   dsa_status st = check_rows(rows);
   if (st != DSA_OK) return st;
   if (topk < 1 || topk > 4096) return fail(DSA_E_UNSUPPORTED, "topk must lie in [1, 4096]");
+  if ((st = check_topk_rows(*rows)) != DSA_OK) return st;
   if (rows->num_rows == 0) return DSA_OK;
   if (!scores || !indices) return fail(DSA_E_INVALID, "NULL tensor pointer");
   if (ld_scores < (int64_t)rows->max_pos + 1)
@@ -287,6 +316,7 @@ dsa_status dsa_sparse_mla_attn(const dsa_rows* rows, const dsa_dims* dims, const
   dsa_status st = check_rows(rows);
   if (st != DSA_OK) return st;
   if ((st = check_dims(dims)) != DSA_OK) return st;
+  if ((st = check_latent_span(*rows, *dims)) != DSA_OK) return st;
   if (rows->num_rows == 0) return DSA_OK;
   if (!q || !latent || !indices || !out) return fail(DSA_E_INVALID, "NULL tensor pointer");
   const size_t need = dsa::attn_workspace_bytes(rows->num_rows, *dims);

@@ -16,6 +16,9 @@ constexpr int kQkDim = 576;
 constexpr int kVDim = 512;
 constexpr int kTopk = 2048;
 constexpr int kMhaHeadDim = 128;  // MHA mode: per-head nope-key and value width
+constexpr int kTopkMaxPositions = 131072;  // longest row (t + 1) the top-k kernels take
+// contiguous bf16 latent caches are addressed with 32-bit byte offsets per sequence
+constexpr uint64_t kMaxLatentSeqBytes = 0xFFFFFFFFull;
 
 // Location of cache entries.  table == nullptr: contiguous caches [B, N, ...], entry
 // (b, s) at row b * N + s.  Otherwise a page pool [npages, 1 << shift, ...] seen
@@ -55,6 +58,10 @@ size_t attn_workspace_bytes(int num_rows, const dsa_dims& dims);
 hipError_t launch_attn_bf16(const dsa_rows& rows, const void* q, const void* latent,
                             const int32_t* indices, float softmax_scale, void* out, float* lse,
                             void* workspace, hipStream_t stream, const PageMap& pm = PageMap());
+
+// Reads the calling device's index-domain flag (1 once an attention kernel met an
+// index entry past its row's position), then clears it.  Synchronises the device.
+hipError_t read_index_domain_flag(uint32_t* seen);
 
 hipError_t launch_attn_f32(const dsa_rows& rows, const dsa_dims& dims, const float* q,
                            const float* latent, const int32_t* indices, float softmax_scale,

@@ -35,7 +35,7 @@ constexpr int TK_T = 1024;
 constexpr int TK_W = TK_T / 64;
 constexpr int NBIN = 2048;
 constexpr int CMAX = 256;              // threshold-bin members ranked directly
-constexpr int BITMAP_POS = 131072;     // positions covered by the streaming bitmap
+constexpr int BITMAP_POS = kTopkMaxPositions;  // positions covered by the streaming bitmap
 
 struct TopkShared {
   uint32_t hist[NBIN];

@@ -81,7 +81,7 @@ __global__ __launch_bounds__(TT) void attn_target_kernel(
       if (j < SPT - 1 || tid < TT / 2) {
         const int e = c / TCH, pc = c - e * TCH;
         const int p = irow[e0 + e];
-        const uint32_t row = (p >= 0 && p < N) ? row_of(p) : row0;
+        const uint32_t row = (p >= 0 && p <= t) ? row_of(p) : row0;
         spf[j] = *reinterpret_cast<const i32x4*>(base + (size_t)row * (DK * 2) + 16 * pc);
       }
     }
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(TT) void attn_target_kernel(
 #pragma unroll
       for (int w8 = 0; w8 < TT / 64; ++w8) sum += part[w8][tid];
       const int p = irow[e0 + tid];
-      urow[e0 + tid] = (p >= 0 && p < N) ? sum : 0.f;
+      urow[e0 + tid] = (p >= 0 && p <= t) ? sum : 0.f;  // entries outside [0, t]: padding
     }
   }
 }
@@ -148,13 +148,15 @@ template <bool LSE_PASS>
 __global__ __launch_bounds__(TT) void dense_target_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ latent,
     const int32_t* __restrict__ row_seq, const int32_t* __restrict__ row_pos, int R, int B, int N,
-    int C, float scale_log2, float2* __restrict__ part, float* __restrict__ u, int64_t ldu) {
+    int max_pos, int C, float scale_log2, float2* __restrict__ part, float* __restrict__ u,
+    int64_t ldu) {
   __shared__ __attribute__((aligned(16))) i32x4 tile[TBE * TCH];
   __shared__ float hsum[TT / 64][TBE];
   const int r = blockIdx.x / C, c = blockIdx.x - (blockIdx.x / C) * C;
   if (r >= R) return;
   const int b = row_seq[r], t = row_pos[r];
-  const bool ok = b >= 0 && b < B && t >= 0 && t < N;
+  // a row past max_pos has no chunk partials or target space: it is not processed
+  const bool ok = b >= 0 && b < B && t >= 0 && t < N && t <= max_pos;
   const int p0 = c * DCP;
   const int pend = ok ? min(t + 1, p0 + DCP) : p0;  // this chunk's positions: [p0, pend)
   const int tid = threadIdx.x, l = lane_id(), g = l >> 4, n = l & 15;
@@ -364,11 +366,12 @@ __global__ __launch_bounds__(KT) void indexer_kl_kernel(
 __global__ __launch_bounds__(KT) void indexer_kl_dense_kernel(
     const float* __restrict__ scores, int64_t ld, const float* __restrict__ u, int64_t ldu,
     const int32_t* __restrict__ row_seq, const int32_t* __restrict__ row_pos, int B, int N,
-    float* __restrict__ loss, float* __restrict__ dscores) {
+    int max_pos, float* __restrict__ loss, float* __restrict__ dscores) {
   __shared__ float red[KT / 64];
   const int r = blockIdx.x;
   const int b = row_seq[r], t = row_pos[r];
-  const bool ok = b >= 0 && b < B && t >= 0 && t < N && (int64_t)t < ld;
+  // t <= max_pos keeps every read of the target row u inside its ldu entries
+  const bool ok = b >= 0 && b < B && t >= 0 && t < N && t <= max_pos && (int64_t)t < ld;
   const int np = ok ? t + 1 : 0;
   const float* srow = scores + (size_t)r * ld;
   const float* urow = u + (size_t)r * ldu;
@@ -429,8 +432,9 @@ __global__ __launch_bounds__(BT) void indexer_bwd_kernel(
     const float* __restrict__ w, const uint8_t* __restrict__ k_idx,
     const float* __restrict__ k_scale, const int32_t* __restrict__ indices,
     const float* __restrict__ dscores, const int32_t* __restrict__ row_seq,
-    const int32_t* __restrict__ row_pos, int B, int N, int topk, float* __restrict__ dq,
-    float* __restrict__ dw, float* __restrict__ dk, PageMap pm, int64_t ld, int nblk_dense) {
+    const int32_t* __restrict__ row_pos, int B, int N, int max_pos, int topk,
+    float* __restrict__ dq, float* __restrict__ dw, float* __restrict__ dk, PageMap pm, int64_t ld,
+    int nblk_dense) {
   __shared__ __attribute__((aligned(16))) float kf[BG][ID + 4];   // dequantised keys
   __shared__ __attribute__((aligned(16))) float qf[IH][ID + 4];   // dequantised queries
   __shared__ __attribute__((aligned(16))) float cq[IH][BG + 4];   // dI w m, head-major
@@ -441,7 +445,9 @@ __global__ __launch_bounds__(BT) void indexer_bwd_kernel(
   const int nblk = DENSE ? nblk_dense : topk / (BG * BGPB);
   const int r = blockIdx.x / nblk, ebase = (blockIdx.x - r * nblk) * BG * BGPB;
   const int b = row_seq[r], t = row_pos[r];
-  if (b < 0 || b >= B || t < 0 || t >= N) return;
+  // a row past max_pos is not processed (the dense blocks and dscores columns only
+  // reach max_pos)
+  if (b < 0 || b >= B || t < 0 || t >= N || t > max_pos) return;
   if (DENSE && ebase > t) return;  // every position of this block is past the row
   const int tid = threadIdx.x, l = lane_id(), g = l >> 4, n = l & 15, wv = tid >> 6;
   const bool paged = pm.table != nullptr;
@@ -627,15 +633,18 @@ hipError_t launch_indexer_loss_dense(const dsa_rows& rows, const void* q, const 
   const dim3 grid((unsigned)((int64_t)R * C));
   hipLaunchKernelGGL(dense_target_kernel<true>, grid, dim3(TT), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(latent),
-                     rows.row_seq, rows.row_pos, R, rows.num_seqs, rows.max_ctx, C, sl2, part, u, ldu);
+                     rows.row_seq, rows.row_pos, R, rows.num_seqs, rows.max_ctx, rows.max_pos, C, sl2,
+                     part, u, ldu);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(dense_target_kernel<false>, grid, dim3(TT), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(latent),
-                     rows.row_seq, rows.row_pos, R, rows.num_seqs, rows.max_ctx, C, sl2, part, u, ldu);
+                     rows.row_seq, rows.row_pos, R, rows.num_seqs, rows.max_ctx, rows.max_pos, C, sl2,
+                     part, u, ldu);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL(indexer_kl_dense_kernel, dim3(R), dim3(KT), 0, stream, scores, ld, u, ldu,
-                     rows.row_seq, rows.row_pos, rows.num_seqs, rows.max_ctx, loss, dscores);
+                     rows.row_seq, rows.row_pos, rows.num_seqs, rows.max_ctx, rows.max_pos, loss,
+                     dscores);
   return hipGetLastError();
 }
 
@@ -648,7 +657,7 @@ hipError_t launch_indexer_backward(const dsa_rows& rows, const uint8_t* q_idx,
   if (R == 0) return hipSuccess;
   hipLaunchKernelGGL(indexer_bwd_kernel<false>, dim3(R * (kTopk / (BG * BGPB))), dim3(BT), 0, stream,
                      q_idx, q_scale, w, k_idx, k_scale, indices, dscores, rows.row_seq, rows.row_pos,
-                     rows.num_seqs, rows.max_ctx, kTopk, dq, dw, dk, pm, (int64_t)0, 0);
+                     rows.num_seqs, rows.max_ctx, rows.max_pos, kTopk, dq, dw, dk, pm, (int64_t)0, 0);
   return hipGetLastError();
 }
 
@@ -661,8 +670,8 @@ hipError_t launch_indexer_backward_dense(const dsa_rows& rows, const uint8_t* q_
   const int nblk = (rows.max_pos + BG * BGPB) / (BG * BGPB);
   hipLaunchKernelGGL(indexer_bwd_kernel<true>, dim3((unsigned)((int64_t)R * nblk)), dim3(BT), 0,
                      stream, q_idx, q_scale, w, k_idx, k_scale, nullptr, dscores, rows.row_seq,
-                     rows.row_pos, rows.num_seqs, rows.max_ctx, kTopk, dq, dw, dk, PageMap{}, ld,
-                     nblk);
+                     rows.row_pos, rows.num_seqs, rows.max_ctx, rows.max_pos, kTopk, dq, dw, dk,
+                     PageMap{}, ld, nblk);
   return hipGetLastError();
 }
 

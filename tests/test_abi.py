@@ -204,3 +204,33 @@ def test_training_and_mha_host_checks(m):
     assert mha(long_rows, ctypes.byref(d), p, 1 << 40) == m.DSA_E_UNSUPPORTED
     assert L.dsa_mha_prefill(ctypes.byref(pre), ctypes.byref(d), None, p, p, p, p, 0.1, p, p, p,
                              need, None) == m.DSA_E_INVALID
+
+
+def test_size_limits_rejected_before_enqueue(m):
+    """Rows longer than the top-k kernels take (t + 1 > 131072), and contiguous
+    latent caches whose per-sequence byte span does not fit the attention kernel's
+    32-bit offsets, are refused on the host with DSA_E_UNSUPPORTED (the dummy
+    pointers would fault if anything were launched)."""
+    L = m.lib
+    d = m.dims_struct(m.PRODUCTION_DIMS)
+    p = ctypes.c_void_p(16)
+    long_rows = _rows(m, R=1, B=1, N=262144, max_pos=131072)           # 131073 candidates
+    assert L.dsa_topk(ctypes.byref(long_rows), 2048, p, 131136, p, None) == m.DSA_E_UNSUPPORTED
+    assert "131072" in L.dsa_last_error().decode()
+    ok_rows = _rows(m, R=0, B=1, N=262144, max_pos=131071, seq=None, pos=None)
+    assert L.dsa_topk(ctypes.byref(ok_rows), 2048, None, 131072, None, None) == m.DSA_OK
+    big = 1 << 30
+    assert L.dsa_forward(ctypes.byref(long_rows), ctypes.byref(d), p, p, p, p, p, p, p, 0.1, p, p,
+                         None, 0, p, big, None) == m.DSA_E_UNSUPPORTED
+    # 3728271 entries of 1152 bytes pass 2^32 bytes; one fewer fits
+    huge = _rows(m, R=1, B=1, N=3728271, max_pos=1000)
+    assert L.dsa_sparse_mla_attn(ctypes.byref(huge), ctypes.byref(d), p, p, p, 0.1, p, p, p, big,
+                                 None) == m.DSA_E_UNSUPPORTED
+    assert "4 GiB" in L.dsa_last_error().decode()
+    assert L.dsa_forward(ctypes.byref(huge), ctypes.byref(d), p, p, p, p, p, p, p, 0.1, p, p, None,
+                         0, p, big, None) == m.DSA_E_UNSUPPORTED
+    fits = _rows(m, R=0, B=1, N=3728270, max_pos=1000, seq=None, pos=None)
+    assert L.dsa_sparse_mla_attn(ctypes.byref(fits), ctypes.byref(d), None, None, None, 0.1, None,
+                                 None, None, 0, None) == m.DSA_OK
+    # the index-domain check rejects a NULL output before touching the device
+    assert L.dsa_check_index_domain(None) == m.DSA_E_INVALID

@@ -107,7 +107,7 @@ def test_indexer_parity(dsa, name):
         for i, r in enumerate(want):
             row = host.row(int(r))
             ref = host.scores(row)
-            worst = max(worst, check_scores(got[i, : row.t + 1], ref))
+            worst = max(worst, check_scores(got[i, : row.t + 1], ref, host.score_extra(row)))
             rel_row = max(rel_row, float(np.max(np.abs(got[i, : row.t + 1] - ref))
                                          / max(np.max(np.abs(ref)), 1e-30)))
     print(f"[indexer] {name}: worst error / allowed = {worst:.3e}, "
@@ -254,6 +254,61 @@ def test_attention_edge_rows(dsa):
         row = host.row(r)
         o_ref, _ = host.attention(row, s)
         check_attention(to_f64(out[r]), o_ref)
+
+
+def test_attention_future_positions_are_padding(dsa):
+    """The causal rule of the selection (S_t holds positions s <= t): an index entry
+    past its row's position is padding, exactly as -1 is, in the bf16 and fp32
+    attention and in the sparse-stage loss; it also raises the device's
+    index-domain flag, which a clean call leaves clear."""
+    assert dsa.check_index_domain() in (False, True)   # clear whatever earlier tests left
+    for name, rows in (("prefill8k", [0, 100, 5000, 8190]), ("tiny", [0, 3, 64, 200])):
+        cfg = di.CONFIGS[name]
+        inp = dev_inputs(name)
+        host = HostInputs(cfg)
+        dims = dsa.Dims.from_config(cfg)
+        rng = np.random.default_rng(21)
+        R = len(rows)
+        ridx = torch.tensor(rows, device="cuda")
+        seq, pos = inp.row_seq[ridx].contiguous(), inp.row_pos[ridx].contiguous()
+        rs = dsa.rows_struct(seq, pos, cfg.num_seqs, cfg.max_ctx, cfg.kv_len - 1)
+        clean = np.full((R, cfg.topk), -1, dtype=np.int32)
+        dirty = clean.copy()
+        for i, r in enumerate(rows):
+            t = int(host.row(r).t)
+            n = min(cfg.topk // 2, t + 1)
+            s = np.sort(rng.choice(t + 1, n, replace=False)).astype(np.int32)
+            clean[i, :n] = s
+            dirty[i, :n] = s
+            fut = np.arange(t + 1, cfg.max_ctx)
+            if fut.size:  # future positions in the free slots, some beyond the last row
+                f = rng.choice(fut, min(fut.size, cfg.topk - n), replace=False)
+                dirty[i, n:n + f.size] = f
+        q = inp.q[ridx].contiguous()
+        o_c, l_c = dsa.sparse_mla_attn(rs, dims, q, inp.latent, torch.from_numpy(clean).cuda(), cfg.scale)
+        torch.cuda.synchronize()
+        assert dsa.check_index_domain() is False, name
+        o_d, l_d = dsa.sparse_mla_attn(rs, dims, q, inp.latent, torch.from_numpy(dirty).cuda(), cfg.scale)
+        torch.cuda.synchronize()
+        assert dsa.check_index_domain() is True, name
+        assert dsa.check_index_domain() is False, name   # read-and-clear
+        for i, r in enumerate(rows):
+            o_ref, _ = host.attention(host.row(r), clean[i][clean[i] >= 0])
+            check_attention(to_f64(o_d[i]), o_ref)
+        if not cfg.fp32:
+            # the padding of both lists lands in the same slots, but a split's slice
+            # can hold different numbers of valid entries, so compare under C3 too
+            check_attention(to_f64(o_d), to_f64(o_c))
+            # the sparse-stage loss ignores the future entries as it ignores -1
+            ld = (cfg.kv_len + 63) // 64 * 64
+            sc = torch.randn(R, ld, device="cuda")
+            l1, g1 = dsa.indexer_loss(rs, q, inp.latent, torch.from_numpy(clean).cuda(), l_c,
+                                      cfg.scale, sc)
+            l2, g2 = dsa.indexer_loss(rs, q, inp.latent, torch.from_numpy(dirty).cuda(), l_c,
+                                      cfg.scale, sc)
+            torch.cuda.synchronize()
+            assert torch.equal(l1, l2) and torch.equal(g1, g2)
+        print(f"[future] {name}: future entries treated as padding, flag raised", flush=True)
 
 
 # ---------------------------------------------------------------- whole path

@@ -9,10 +9,12 @@ arithmetic:
 * target and softmax run in fp32 over 576-term bf16 dots and 2048-entry sums, so
   p and softmax carry relative errors near 1e-5: |d dI_i| <= 1e-3 (p_i +
   softmax_i) + 1e-7 and |d loss| <= 1e-3 |loss| + 1e-6;
-* the backward's dots are the forward's fp8 MFMA sums, whose error reaches
-  2.6e-4 of the largest product, so a ReLU mask may flip where a dot lies within
-  2e-3 of sum_d |q_d k_d| of zero.  Such a pair may add its whole term, and it is
-  allowed for.  The fp32 sums add 1e-5 of the absolute sum of the terms.
+* the backward's dots are the forward's fp8 MFMA sums, whose error is at most
+  EPS_MAX_PRODUCT of the largest product (tests/test_gpu_fp8_accumulation.py)
+  plus the rounding of the result, so a ReLU mask may flip where a dot lies within
+  (EPS_MAX_PRODUCT + 2^-24) sum_d |q_d k_d| of zero.  Such a pair may add its
+  whole term, and it is allowed for.  The fp32 sums add 1e-5 of the absolute sum
+  of the terms.
 A composed run (the GPU's own scores and selection) is held to C2 plus a bar on
 the loss that accounts for the indexer's own C1 error.
 """
@@ -24,9 +26,12 @@ import torch
 
 import dsa_inputs as di
 import oracle
-from dsa_check import HostInputs
+from dsa_check import EPS_MAX_PRODUCT, U32, HostInputs
 
 pytestmark = pytest.mark.gpu
+
+# bound on |MFMA dot - exact dot| per unit of sum_d |q_d k_d| (>= the largest product)
+DOT_EPS = EPS_MAX_PRODUCT + U32
 
 
 @pytest.fixture(scope="module")
@@ -207,14 +212,14 @@ def test_indexer_backward_parity(dsa, name, rows):
         gi = g[i, : S.size].astype(np.float64)
         q_ref, w_ref, k_ref = oracle.indexer_backward(qf, row.w, kf, gi)
         dots = qf @ kf.T
-        amb = np.abs(dots) <= 2e-3 * (np.abs(qf) @ np.abs(kf).T)     # mask may flip
+        amb = np.abs(dots) <= DOT_EPS * (np.abs(qf) @ np.abs(kf).T)  # mask may flip
         coef_abs = np.abs(row.w)[:, None] * np.abs(gi)[None, :]       # |w_j g_s|
         terms_q = (coef_abs * (dots > 0)) @ np.abs(kf)
         tol_q = 1e-5 * terms_q + (coef_abs * amb) @ np.abs(kf) + 1e-12
         assert np.all(np.abs(dq[i] - q_ref) <= tol_q), float(np.max(np.abs(dq[i] - q_ref) - tol_q))
-        # every dot may be off by the MFMA's error bound (2e-3 of sum |q_d k_d|)
+        # every dot may be off by the MFMA's error bound
         tol_w = 1e-5 * (np.maximum(dots, 0) @ np.abs(gi)) + \
-            (2e-3 * (np.abs(qf) @ np.abs(kf).T)) @ np.abs(gi) + 1e-12
+            (DOT_EPS * (np.abs(qf) @ np.abs(kf).T)) @ np.abs(gi) + 1e-12
         assert np.all(np.abs(dw[i] - w_ref) <= tol_w)
         tol_k = 1e-5 * ((coef_abs * (dots > 0)).T @ np.abs(qf)) + (coef_abs * amb).T @ np.abs(qf) + 1e-12
         for a, s in enumerate(S):
@@ -280,11 +285,11 @@ def test_indexer_backward_dense_parity(dsa, name, rows):
         q_ref, w_ref, k_ref = oracle.indexer_backward(qf, row.w, kf, gi)
         dots = qf @ kf.T
         absd = np.abs(qf) @ np.abs(kf).T
-        amb = np.abs(dots) <= 2e-3 * absd
+        amb = np.abs(dots) <= DOT_EPS * absd
         coef_abs = np.abs(row.w)[:, None] * np.abs(gi)[None, :]
         tol_q = 1e-5 * ((coef_abs * (dots > 0)) @ np.abs(kf)) + (coef_abs * amb) @ np.abs(kf) + 1e-12
         assert np.all(np.abs(dq[i] - q_ref) <= tol_q), float(np.max(np.abs(dq[i] - q_ref) - tol_q))
-        tol_w = 1e-5 * (np.maximum(dots, 0) @ np.abs(gi)) + (2e-3 * absd) @ np.abs(gi) + 1e-12
+        tol_w = 1e-5 * (np.maximum(dots, 0) @ np.abs(gi)) + (DOT_EPS * absd) @ np.abs(gi) + 1e-12
         assert np.all(np.abs(dw[i] - w_ref) <= tol_w)
         tol_k = 1e-5 * ((coef_abs * (dots > 0)).T @ np.abs(qf)) + (coef_abs * amb).T @ np.abs(qf) + 1e-12
         for s_ in range(n):
@@ -338,3 +343,44 @@ def test_dense_and_sparse_loss_agree_below_k(dsa):
         sm /= sm.sum()
         assert np.all(np.abs(g_s[i, : t + 1] - g_d[i, : t + 1]) <= 2e-3 * (sm + np.abs(g_d[i, : t + 1])) + 2e-7)
         print(f"[loss agree] row {r} (t = {t}): sparse {l_s[i]:.6f} dense {l_d[i]:.6f}", flush=True)
+
+
+def test_dense_rows_past_max_pos_untouched(dsa):
+    """A row at t > max_pos (still t < N) is not processed by the dense warm-up loss
+    or its backward: loss 0, a zero dscores row, no gradient, and no read of another
+    row's chunk partials (the row last, where such a read would pass the workspace's
+    end).  The row before it is still computed as the oracle says."""
+    cfg = di.CONFIGS["prefill8k"]
+    inp = dev_inputs("prefill8k")
+    host = HostInputs(cfg)
+    rows = [100, 1500]          # max_pos 200: one 1024-position chunk; row 1500 needs two
+    max_pos, ld = 200, 256
+    ridx = torch.tensor(rows, device="cuda")
+    seq, pos = inp.row_seq[ridx].contiguous(), inp.row_pos[ridx].contiguous()
+    rs = dsa.rows_struct(seq, pos, cfg.num_seqs, cfg.max_ctx, max_pos)
+    row = host.row(rows[0])
+    n = row.t + 1
+    sc = np.full((2, ld), np.nan, dtype=np.float32)
+    sc[0, :n] = host.scores(row).astype(np.float32)
+    sc[1, :] = 1.0
+    q = inp.q[ridx].contiguous()
+    loss, dsc = dsa.indexer_loss_dense(rs, q, inp.latent, cfg.scale, torch.from_numpy(sc).cuda())
+    g = torch.zeros(2, ld, device="cuda")
+    g[0, :n] = 1e-3
+    g[1, :] = 1.0
+    dq = torch.zeros(2, 64, 128, device="cuda")
+    dw = torch.zeros(2, 64, device="cuda")
+    dk = torch.zeros(cfg.num_seqs, cfg.max_ctx, 128, device="cuda")
+    dsa.indexer_backward_dense(rs, inp.q_idx[ridx].contiguous(), inp.q_scale[ridx].contiguous(),
+                               inp.w[ridx].contiguous(), inp.k_idx, inp.k_scale, g, dq, dw, dk)
+    torch.cuda.synchronize()
+    loss, dsc = loss.cpu().numpy(), dsc.cpu().numpy()
+    assert loss[1] == 0.0 and np.all(dsc[1] == 0.0)
+    assert bool((dq[1] == 0).all()) and bool((dw[1] == 0).all())
+    assert bool((dk[0, n:] == 0).all())           # only row 100's keys 0..100 are touched
+    ent = host.latent_rows(row.b, np.arange(n))
+    p = oracle.attention_target(oracle.decode_bf16(row.q), oracle.decode_bf16(ent), cfg.scale)
+    l_ref, _ = oracle.indexer_kl(p, sc[0, :n].astype(np.float64))
+    assert abs(loss[0] - l_ref) <= 1e-3 * abs(l_ref) + 1e-6, (loss[0], l_ref)
+    print(f"[past max_pos] row {rows[1]} untouched; row {rows[0]} loss {loss[0]:.6f} ref {l_ref:.6f}",
+          flush=True)
