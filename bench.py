@@ -1,14 +1,17 @@
 """Benchmark of the DSA hot path on one MI355X.
 
 A step is one pass of the whole path (indexer scores -> top-k -> sparse MLA
-attention) over one batch of synthetic input already resident in HBM.  The
-headline workload is decode at 32K context, batch 32 (one new token per
-sequence); 4 independent input sets are rotated so the 256 MB MALL cannot serve
-a step from the previous one.
+attention) over one batch of synthetic input already resident in HBM, issued as
+one dsa_forward call.  The headline workload is decode at 32K context, batch 32
+(one new token per sequence); 4 independent input sets are rotated so the 256 MB
+MALL cannot serve a step from the previous one.  The same line carries the other
+workloads of the metric: decode at 128K context (batch 8) and the 128K prefill
+(16 chunks of 8192 rows through dsa_forward), each with its own roofline object.
 
-Prints one JSON line.  Per-step kernel times come from HIP events recorded on the
-stream the library launches on, around each of the three C-ABI calls inside the
-timed region.
+Prints one JSON line.  Per-call kernel times come from a second pass that issues
+the path as its three C-ABI calls with HIP events recorded around each, on the
+stream the library launches on; graph replays of the dsa_forward call are timed
+beside the eager calls.
 
     python bench.py [--steps K] [--warmup W] [--workload decode32k] [--extra]
 """
@@ -87,9 +90,10 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--headline-only", action="store_true",
                    help="time only the headline step, so that a profiler run sees its kernels "
-                        "alone (no paged, training, projection or MHA sections)")
+                        "alone (no graph, paged, long-context, training, projection or MHA "
+                        "sections)")
     p.add_argument("--extra", action="store_true",
-                   help="also time decode128k, prefill8k and prefill128k")
+                   help="also time the 8K prefill")
     p.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                    help="only run an fp32 elementwise copy (x * 1) that reads and writes MIB MiB, "
                         "five times: the reference kernel of known traffic that scales the "
@@ -105,26 +109,38 @@ def _pairs(cfg):
     return cand, sel
 
 
-class Step:
-    """Device buffers and the three C-ABI calls of one input set."""
+class Workload:
+    """One input set of a workload in device memory and the buffers of its calls.
 
-    def __init__(self, dsa, di, cfg, set_id, r0=0, r1=None):
+    run() issues the path as three C-ABI calls per chunk of rows (indexer, top-k,
+    attention), optionally bracketing each with HIP events on the library's
+    stream; run_forward() issues the same work as one dsa_forward call."""
+
+    def __init__(self, dsa, di, cfg, set_id):
         import torch
 
         self.cfg = cfg
-        self.inp = di.make_inputs(cfg, set_id, device="cuda", rows=(r0, r1 or cfg.num_rows))
-        R = self.inp.row_pos.numel()
-        self.rows = dsa.rows_struct(self.inp.row_seq, self.inp.row_pos, cfg.num_seqs,
-                                    cfg.max_ctx, cfg.kv_len - 1)
+        self.dsa = dsa
+        self.inp = di.make_inputs(cfg, set_id, device="cuda")
+        R = cfg.num_rows
+        CH = cfg.chunk_rows if 0 < cfg.chunk_rows < R else R
+        self.chunk = CH if CH < R else 0
+        self.chunks = [(a, min(R, a + CH)) for a in range(0, R, CH)]
+        i = self.inp
+        self.rows = dsa.rows_struct(i.row_seq, i.row_pos, cfg.num_seqs, cfg.max_ctx, cfg.kv_len - 1)
+        self.sub = [dsa.rows_struct(i.row_seq[a:b], i.row_pos[a:b], cfg.num_seqs, cfg.max_ctx,
+                                    cfg.kv_len - 1) for a, b in self.chunks]
         self.dims = dsa.Dims.from_config(cfg)
         self.ld = (cfg.kv_len + 63) // 64 * 64
-        self.scores = torch.empty(R, self.ld, dtype=torch.float32, device="cuda")
-        self.idx = torch.empty(R, cfg.topk, dtype=torch.int32, device="cuda")
+        self.scores = torch.empty(CH, self.ld, dtype=torch.float32, device="cuda")
+        self.idx = torch.empty(CH, cfg.topk, dtype=torch.int32, device="cuda")
         self.out = torch.empty(R, cfg.n_heads, cfg.v_dim, dtype=torch.bfloat16, device="cuda")
         self.lse = torch.empty(R, cfg.n_heads, dtype=torch.float32, device="cuda")
-        need = dsa.sparse_mla_attn_workspace_size(self.rows, self.dims)
+        need = max(dsa.sparse_mla_attn_workspace_size(rs, self.dims) for rs in self.sub)
         self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
-        self.dsa = dsa
+        self.fws = torch.empty(max(dsa.forward_workspace_size(self.rows, self.dims, self.chunk), 1),
+                               dtype=torch.uint8, device="cuda")
+        self.graph = None
 
     def make_paged(self, P=64, seed=0):
         """Page pools holding this set's caches, pages scattered in a seeded order."""
@@ -154,83 +170,179 @@ class Step:
                                 self.cfg.scale, out=self.out, lse=self.lse, workspace=self.ws)
 
     def run(self, ev=None):
-        d, i = self.dsa, self.inp
-        if ev: ev[0].record()
-        d.indexer_scores(self.rows, self.dims, i.q_idx, i.q_scale, i.w, i.k_idx, i.k_scale,
-                         scores=self.scores)
-        if ev: ev[1].record()
-        d.topk(self.rows, self.cfg.topk, self.scores, indices=self.idx)
-        if ev: ev[2].record()
-        d.sparse_mla_attn(self.rows, self.dims, i.q, i.latent, self.idx, self.cfg.scale,
-                          out=self.out, lse=self.lse, workspace=self.ws)
-        if ev: ev[3].record()
+        """The three calls per chunk; ev, if given, is a list that receives one
+        (call, start event, end event) triple per call."""
+        import torch
+
+        d, i, c = self.dsa, self.inp, self.cfg
+
+        def mark(name, fn):
+            if ev is None:
+                fn()
+                return
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            ev.append((name, e0, e1))
+
+        for rs, (a, b) in zip(self.sub, self.chunks):
+            n = b - a
+            sc, ix = self.scores[:n], self.idx[:n]
+            mark("indexer", lambda: d.indexer_scores(rs, self.dims, i.q_idx[a:b], i.q_scale[a:b],
+                                                     i.w[a:b], i.k_idx, i.k_scale, scores=sc))
+            mark("topk", lambda: d.topk(rs, c.topk, sc, indices=ix))
+            mark("attention", lambda: d.sparse_mla_attn(rs, self.dims, i.q[a:b], i.latent, ix,
+                                                        c.scale, out=self.out[a:b],
+                                                        lse=self.lse[a:b], workspace=self.ws))
+
+    def run_forward(self):
+        i = self.inp
+        self.dsa.forward(self.rows, self.dims, i.q_idx, i.q_scale, i.w, i.k_idx, i.k_scale, i.q,
+                         i.latent, self.cfg.scale, out=self.out, lse=self.lse,
+                         chunk_rows=self.chunk, workspace=self.fws)
+
+    def capture(self):
+        """A HIP graph of one dsa_forward call (its kernels only: the library records
+        no memset or copy), checked bit for bit against the eager call."""
+        import torch
+
+        self.run_forward()
+        torch.cuda.synchronize()
+        ref = self.out.clone()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.run_forward()
+        torch.cuda.synchronize()
+        self.out.zero_()
+        for _ in range(2):
+            self.graph.replay()
+            torch.cuda.synchronize()
+            if not torch.equal(self.out, ref):
+                raise RuntimeError("graph replay differs from the eager dsa_forward call")
 
 
-def time_steps(steps, K, W):
-    """Times K steps twice: once bare (the throughput: nothing but the three calls
-    per step), then with HIP events around each call (per-call durations; the
-    markers add a little time of their own)."""
+def time_bare(fn_list, K, W):
+    """Wall time per step of K steps (fn_list rotated), after W warm-up steps, with a
+    device synchronisation on each side of the timed region."""
     import torch
 
     for i in range(W):
-        steps[i % len(steps)].run()
+        fn_list[i % len(fn_list)]()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        steps[i % len(steps)].run()
+        fn_list[i % len(fn_list)]()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
-    for i in range(K):
-        steps[i % len(steps)].run(evs[i])
-    torch.cuda.synchronize()
-    k_ms = [[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in evs]
-    avg = [sum(x[j] for x in k_ms) / K for j in range(3)]
-    return wall / K * 1e3, avg
+    return (time.perf_counter() - t0) / K * 1e3
 
 
-def time_workload(dsa, di, cfg, reps):
-    """Whole-path throughput of one more workload through dsa_forward (chunked like
-    the library's prefill loop), with MFMA/HBM fractions of its algorithmic work."""
+def time_calls(sets, K):
+    """Per-call event durations (ms per step, summed over a step's chunks) over K
+    steps with the sets rotated."""
     import torch
 
-    print(f"[bench] extra workload {cfg.name}", file=sys.stderr, flush=True)
-    inp = di.make_inputs(cfg, 0, device="cuda")
+    evs = []
+    for i in range(K):
+        ev = []
+        sets[i % len(sets)].run(ev)
+        evs.append(ev)
+    torch.cuda.synchronize()
+    tot = {}
+    for ev in evs:
+        for name, e0, e1 in ev:
+            tot[name] = tot.get(name, 0.0) + e0.elapsed_time(e1)
+    return {k: v / K for k, v in tot.items()}
+
+
+def kernel_table(cfg, k_ms):
+    """Per-call rates against each call's own bound from its algorithmic work."""
+    cand, sel = _pairs(cfg)
     R = cfg.num_rows
-    rows = dsa.rows_struct(inp.row_seq, inp.row_pos, cfg.num_seqs, cfg.max_ctx, cfg.kv_len - 1)
-    dims = dsa.Dims.from_config(cfg)
-    out = torch.empty(R, cfg.n_heads, cfg.v_dim, dtype=torch.bfloat16, device="cuda")
-    lse = torch.empty(R, cfg.n_heads, dtype=torch.float32, device="cuda")
-    chunk = cfg.chunk_rows if 0 < cfg.chunk_rows < R else 0
-    ws = torch.empty(max(dsa.forward_workspace_size(rows, dims, chunk), 1), dtype=torch.uint8,
-                     device="cuda")
-    run = lambda: dsa.forward(rows, dims, inp.q_idx, inp.q_scale, inp.w, inp.k_idx, inp.k_scale,
-                              inp.q, inp.latent, cfg.scale, out=out, lse=lse, chunk_rows=chunk,
-                              workspace=ws)
-    run()
+    idx_b, idx_f = cand * IDX_BYTES_PER_PAIR, cand * IDX_FLOP_PER_PAIR
+    topk_b = cand * TOPK_BYTES_PER_PAIR
+    att_b, att_f = sel * ATTN_BYTES_PER_ENTRY + R * ATTN_BYTES_PER_ROW, sel * ATTN_FLOP_PER_ENTRY
+    t = {"indexer": {"ms": k_ms["indexer"], "bytes": idx_b, "flop": idx_f},
+         "topk": {"ms": k_ms["topk"], "bytes": topk_b},
+         "attention": {"ms": k_ms["attention"], "bytes": att_b, "flop": att_f}}
+    for v in t.values():
+        v["gbs"] = v["bytes"] / v["ms"] / 1e6
+        if "flop" in v:
+            v["tflops"] = v["flop"] / v["ms"] / 1e9
+    t["indexer"]["fp8_frac"] = t["indexer"]["tflops"] / FP8_PEAK_TFLOPS
+    t["attention"]["bf16_frac"] = t["attention"]["tflops"] / BF16_PEAK_TFLOPS
+    return t
+
+
+def roofline_of(kernels, decode: bool):
+    """The roofline object of the dominant call: HBM-bound at decode (algorithmic
+    bytes over event time), MFMA-bound at prefill (fp8 peak for the indexer, bf16
+    for attention)."""
+    dom = max(kernels, key=lambda k: kernels[k]["ms"])
+    kd = kernels[dom]
+    if decode or dom == "topk":
+        return {"bound": "hbm", "kernel": dom, "achieved": kd["gbs"], "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": kd["gbs"] / HBM_PEAK_GBS,
+                "algorithmic_bytes": kd["bytes"], "launch_ms": kd["ms"]}
+    peak = FP8_PEAK_TFLOPS if dom == "indexer" else BF16_PEAK_TFLOPS
+    return {"bound": "mfma", "kernel": dom, "achieved": kd["tflops"], "peak": peak,
+            "unit": "TFLOP/s", "frac": kd["tflops"] / peak, "algorithmic_flop": kd["flop"],
+            "launch_ms": kd["ms"]}
+
+
+def time_decode(dsa, di, cfg, sets, K, W, graphs=True):
+    """A decode workload: bare dsa_forward steps (the throughput), HIP-graph replays
+    of the same call, and per-call event times."""
+    import torch
+
+    print(f"[bench] {cfg.name}: generating {sets} input sets", file=sys.stderr, flush=True)
+    ws = [Workload(dsa, di, cfg, s) for s in range(sets)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(reps):
-        run()
+    print(f"[bench] {cfg.name}: timing", file=sys.stderr, flush=True)
+    ms = time_bare([w.run_forward for w in ws], K, W)
+    calls_ms = time_bare([w.run for w in ws], K, W)
+    k_ms = time_calls(ws, K)
+    res = {"ms_per_step": ms, "tokens_per_s": cfg.num_rows / (ms * 1e-3),
+           "ms_per_step_three_calls": calls_ms}
+    if graphs:
+        try:
+            for w in ws:
+                w.capture()
+            gms = time_bare([w.graph.replay for w in ws], K, W)
+            res["graph"] = {"ms_per_step": gms, "tokens_per_s": cfg.num_rows / (gms * 1e-3)}
+        except Exception as e:  # capture unsupported: report and go on
+            res["graph"] = {"error": str(e)[:200]}
+    cand, sel = _pairs(cfg)
+    step_bytes = cand * IDX_BYTES_PER_PAIR + sel * ATTN_BYTES_PER_ENTRY + \
+        cfg.num_rows * ATTN_BYTES_PER_ROW
+    res["step_hbm_frac"] = step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS
+    res["kernels"] = kernel_table(cfg, k_ms)
+    res["roofline"] = roofline_of(res["kernels"], decode=True)
+    return res, ws
+
+
+def time_prefill(dsa, di, cfg, reps):
+    """A chunked prefill workload through dsa_forward (tokens/s), per-call event times
+    of the same chunks issued as separate calls, and time-weighted MFMA fractions."""
+    import torch
+
+    print(f"[bench] {cfg.name}: generating inputs", file=sys.stderr, flush=True)
+    w = Workload(dsa, di, cfg, 0)
     torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) / reps * 1e3
+    print(f"[bench] {cfg.name}: timing", file=sys.stderr, flush=True)
+    ms = time_bare([w.run_forward], reps, 1)
+    k_ms = time_calls([w], 1)
     cand, sel = _pairs(cfg)
     fp8_tf = cand * IDX_FLOP_PER_PAIR / 1e12
     bf16_tf = sel * ATTN_FLOP_PER_ENTRY / 1e12
-    hbm = (cand * IDX_BYTES_PER_PAIR + sel * ATTN_BYTES_PER_ENTRY + R * ATTN_BYTES_PER_ROW) / 1e9
     s = ms * 1e-3
-    res = {"tokens_per_s": R / s, "ms": ms, "rows": R, "reps": reps,
-           "fp8_tflop": fp8_tf, "bf16_tflop": bf16_tf,
+    kern = kernel_table(cfg, k_ms)
+    res = {"tokens_per_s": cfg.num_rows / s, "ms": ms, "rows": cfg.num_rows, "reps": reps,
+           "chunk_rows": w.chunk or cfg.num_rows, "fp8_tflop": fp8_tf, "bf16_tflop": bf16_tf,
            # time-weighted MFMA fraction: ideal time at both peaks over measured time
-           "mfma_frac": (fp8_tf / FP8_PEAK_TFLOPS + bf16_tf / BF16_PEAK_TFLOPS) / s}
-    if cfg.q_len == 1:
-        # decode: every algorithmic byte is an HBM byte (each row's keys and entries once)
-        res["hbm_frac"] = hbm / s / HBM_PEAK_GBS
-    else:
-        # prefill: rows of one sequence share keys and entries, which L2 / MALL serve;
-        # the algorithmic bytes over time are an effective rate through the caches
-        res["bytes_through_cache_tbps"] = hbm / s / 1e3
-    del inp, out, lse, ws
+           "mfma_frac": (fp8_tf / FP8_PEAK_TFLOPS + bf16_tf / BF16_PEAK_TFLOPS) / s,
+           "kernels": kern, "roofline": roofline_of(kern, decode=False)}
+    del w
     torch.cuda.empty_cache()
     return res
 
@@ -358,7 +470,7 @@ def time_mha(dsa, di, K):
 
     cfg = di.CONFIGS["prefill8k"]
     print("[bench] masked MHA mode prefill8k", file=sys.stderr, flush=True)
-    st = Step(dsa, di, cfg, 0)
+    st = Workload(dsa, di, cfg, 0)
     st.run()
     R, L = cfg.num_rows, cfg.kv_len
     mg = di.MhaGenerator(cfg.cfg_id, 0)
@@ -402,39 +514,91 @@ def time_mha(dsa, di, K):
     return res
 
 
-def cpu_baseline(di, cfg, budget_s=20.0):
-    """The float64 oracle on a bounded sample of the workload's rows, host cores."""
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(di, cfg, budget_s=20.0, single_budget_s=6.0):
+    """The float64 oracle on a bounded sample of the workload's rows on the host
+    cores (BLAS threads as configured), then the same rows on one thread."""
     import numpy as np
 
     import oracle
 
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
+        threadpool_limits = None
         threads = len(os.sched_getaffinity(0))
     g = di.Generator(cfg, 0)
     seq, pos = cfg.row_seq_pos()
     rows = di.sample_rows(cfg, 64)
-    done, spent = 0, 0.0
-    for r in rows:
-        b, t = int(seq[r]), int(pos[r])
-        qc, qs = g.q_idx(int(r), int(r) + 1)
-        kc, ks = g.k_idx(b, 0, t + 1)
-        qv = g.q(int(r), int(r) + 1)[0]
-        lat = g.latent(b, 0, t + 1)
-        args = (qc[0].numpy(), qs[0].numpy().astype(np.float64),
-                g.w(int(r), int(r) + 1)[0].numpy().astype(np.float64), kc.numpy(),
-                ks.numpy().astype(np.float64), di.bf16_bits(qv), di.bf16_bits(lat))
-        t0 = time.perf_counter()
-        oracle.dsa_row(*args, t, cfg.topk, cfg.scale, cfg.v_dim, quantised=True)
-        spent += time.perf_counter() - t0
-        done += 1
-        if spent >= budget_s:
-            break
-    return {"value": done / spent, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} of {cfg.num_rows} query rows of {cfg.name} (full indexer, top-k "
-                      f"and attention per row, float64 numpy), {spent:.1f} s"}
+
+    def run(budget):
+        done, spent = 0, 0.0
+        for r in rows:
+            b, t = int(seq[r]), int(pos[r])
+            qc, qs = g.q_idx(int(r), int(r) + 1)
+            kc, ks = g.k_idx(b, 0, t + 1)
+            qv = g.q(int(r), int(r) + 1)[0]
+            lat = g.latent(b, 0, t + 1)
+            args = (qc[0].numpy(), qs[0].numpy().astype(np.float64),
+                    g.w(int(r), int(r) + 1)[0].numpy().astype(np.float64), kc.numpy(),
+                    ks.numpy().astype(np.float64), di.bf16_bits(qv), di.bf16_bits(lat))
+            t0 = time.perf_counter()
+            oracle.dsa_row(*args, t, cfg.topk, cfg.scale, cfg.v_dim, quantised=True)
+            spent += time.perf_counter() - t0
+            done += 1
+            if spent >= budget:
+                break
+        return done, spent
+
+    done, spent = run(budget_s)
+    res = {"value": done / spent, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+           "cpu_model": _cpu_model(), "host_cpus": len(os.sched_getaffinity(0)),
+           "sample": f"{done} of {cfg.num_rows} query rows of {cfg.name} (full indexer, top-k "
+                     f"and attention per row, float64 numpy), {spent:.1f} s"}
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            d1, s1 = run(single_budget_s)
+        res["single_thread"] = {"value": d1 / s1, "unit": "tokens/s", "cores": 1,
+                                "sample": f"{d1} rows, {s1:.1f} s"}
+    return res
+
+
+def sclk_sample(busy_fn, seconds=1.5):
+    """The engine clock while the GPU runs busy_fn in a loop: rocm-smi is started,
+    the GPU kept busy until it returns, and its sclk line parsed (MHz; None if
+    rocm-smi is unavailable)."""
+    import re
+    import subprocess
+
+    import torch
+
+    try:
+        p = subprocess.Popen(["rocm-smi", "--showclocks"], stdout=subprocess.PIPE,
+                             stderr=subprocess.DEVNULL, text=True)
+    except OSError:
+        return None
+    t0 = time.perf_counter()
+    while p.poll() is None and time.perf_counter() - t0 < 10.0:
+        for _ in range(8):
+            busy_fn()
+        torch.cuda.synchronize()
+    try:
+        out, _ = p.communicate(timeout=10)
+    except subprocess.TimeoutExpired:
+        p.kill()
+        return None
+    m = re.search(r"sclk.*?\((\d+)\s*Mhz\)", out, re.I)
+    return int(m.group(1)) if m else None
 
 
 def main():
@@ -460,28 +624,15 @@ def main():
     import sparse_attention_fp8_amd as dsa
 
     cfg = di.CONFIGS[args.workload]
-    print(f"[bench] generating {args.sets} input sets of {cfg.name}", file=sys.stderr, flush=True)
-    steps = [Step(dsa, di, cfg, s) for s in range(args.sets)]
-    torch.cuda.synchronize()
-    print("[bench] timing", file=sys.stderr, flush=True)
-    ms, k_ms = time_steps(steps, args.steps, args.warmup)
-
-    cand, sel = _pairs(cfg)
+    head, sets = time_decode(dsa, di, cfg, args.sets, args.steps, args.warmup,
+                             graphs=not args.headline_only)
+    kernels = head["kernels"]
+    roof = dict(head["roofline"])
+    mt = measured_traffic(cfg.name, roof["kernel"])
+    roof["traffic"] = mt[0] if mt else None
+    roof["traffic_kernels"] = mt[1] if mt else None
+    ms = head["ms_per_step"]
     R = cfg.num_rows
-    idx_bytes = cand * IDX_BYTES_PER_PAIR
-    topk_bytes = cand * TOPK_BYTES_PER_PAIR
-    attn_bytes = sel * ATTN_BYTES_PER_ENTRY + R * ATTN_BYTES_PER_ROW
-    kernels = {
-        "indexer": {"ms": k_ms[0], "bytes": idx_bytes,
-                    "gbs": idx_bytes / k_ms[0] / 1e6, "tflops": cand * IDX_FLOP_PER_PAIR / k_ms[0] / 1e9},
-        "topk": {"ms": k_ms[1], "bytes": topk_bytes, "gbs": topk_bytes / k_ms[1] / 1e6},
-        "attention": {"ms": k_ms[2], "bytes": attn_bytes, "gbs": attn_bytes / k_ms[2] / 1e6,
-                      "tflops": sel * ATTN_FLOP_PER_ENTRY / k_ms[2] / 1e9},
-    }
-    dom = max(kernels, key=lambda k: kernels[k]["ms"])
-    kd = kernels[dom]
-    mt = measured_traffic(cfg.name, dom)
-    step_bytes = idx_bytes + attn_bytes
     line = {
         "metric": METRIC,
         "value": R / (ms * 1e-3),
@@ -496,41 +647,41 @@ def main():
         "dtype": "fp8e4m3+bf16",
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: {cfg.description}", "batch": cfg.num_seqs,
-                   "context": cfg.kv_len, "topk": cfg.topk, "input_sets": args.sets},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": kd["gbs"], "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": kd["gbs"] / HBM_PEAK_GBS,
-                     "traffic": mt[0] if mt else None,
-                     "traffic_kernels": mt[1] if mt else None,
-                     "algorithmic_bytes": kd["bytes"], "launch_ms": kd["ms"]},
-        "step_hbm_frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                   "context": cfg.kv_len, "topk": cfg.topk, "input_sets": args.sets,
+                   "timed_call": "dsa_forward, one call per step"},
+        "roofline": roof,
+        "step_hbm_frac": head["step_hbm_frac"],
         "kernels": kernels,
+        "ms_per_step_three_calls": head["ms_per_step_three_calls"],
     }
+    if "graph" in head:
+        line["graph"] = head["graph"]
     if not args.headline_only:
+        line["sclk_mhz"] = sclk_sample(sets[0].run_forward)
         # the same step over paged caches (64-entry pages in shuffled order)
         P = 64
-        for k, st in enumerate(steps):
+        for k, st in enumerate(sets):
             st.make_paged(P, seed=k)
-        for i in range(args.warmup):
-            steps[i % len(steps)].run_paged()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            steps[i % len(steps)].run_paged()
-        torch.cuda.synchronize()
-        pms = (time.perf_counter() - t0) / args.steps * 1e3
+        pms = time_bare([st.run_paged for st in sets], args.steps, args.warmup)
         line["paged"] = {"page_size": P, "ms_per_step": pms, "tokens_per_s": R / (pms * 1e-3),
-                         "vs_contiguous": ms / pms}
-        line["indexer_training"] = time_training(dsa, steps[0], args.steps)
-        del steps
+                         "vs_three_contiguous_calls": head["ms_per_step_three_calls"] / pms}
+        line["indexer_training"] = time_training(dsa, sets[0], args.steps)
+    del sets
+    torch.cuda.empty_cache()
+    if not args.headline_only:
+        # the other two headline workloads of the metric: long decode and 128K prefill
+        d128, s128 = time_decode(dsa, di, di.CONFIGS["decode128k"], 3, args.steps, args.warmup)
+        del s128
         torch.cuda.empty_cache()
+        line["decode128k"] = d128
+        line["prefill128k"] = time_prefill(dsa, di, di.CONFIGS["prefill128k"], 2)
+        line["prefill128k_tokens_per_s"] = line["prefill128k"]["tokens_per_s"]
         # the step before the path: projections and cache append of the new tokens
         line["projections"] = {name: time_projection(dsa, di, di.PROJ_CONFIGS[name], reps)
                                for name, reps in (("proj_decode32", 30), ("proj_prefill8k", 10))}
         line["mha_prefill8k"] = time_mha(dsa, di, max(2, args.steps // 4))
     if args.extra:
-        line["extra"] = {name: time_workload(dsa, di, di.CONFIGS[name], reps)
-                         for name, reps in (("decode128k", 20), ("prefill8k", 5),
-                                            ("prefill128k", 2))}
+        line["extra"] = {"prefill8k": time_prefill(dsa, di, di.CONFIGS["prefill8k"], 5)}
     if not args.no_cpu:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(di, cfg)
