@@ -181,6 +181,26 @@ dsa_status dsa_forward(const dsa_rows* rows, const dsa_dims* dims,
                        int32_t chunk_rows, void* workspace, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * dsa_forward without a workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, computation, kernels and results as dsa_forward;
+ * the scratch is a fixed 64 MiB device array inside the library (one per GPU,
+ * held until the process ends), so nothing is allocated.  A call whose
+ * dsa_forward_workspace_size exceeds 64 MiB returns DSA_E_WORKSPACE before
+ * anything is enqueued (decode batches fit: 32 rows at 32K context use 38 MB;
+ * prefill needs small chunk_rows).  Every call on one GPU shares that GPU's
+ * array: calls that overlap in time on one GPU (other streams or threads) race
+ * and must be serialised by the caller.  The array's previous contents are never
+ * read (no part of it needs to start at zero).
+ * ------------------------------------------------------------------------- */
+dsa_status dsa_forward_noalloc(const dsa_rows* rows, const dsa_dims* dims,
+                               const void* q_idx, const float* q_scale, const float* w,
+                               const void* k_idx, const float* k_scale,
+                               const void* q, const void* latent, float softmax_scale,
+                               void* out, float* lse, int32_t* indices_out,
+                               int32_t chunk_rows, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Step 0: projections of new tokens with fp8 quantisation and cache append.
  * The first step of the DSA workflow, before indexer scoring ("DeepSeek-V3.2开源技术
  * 报告", "DSA principle": query and key projection; DeepSeek-V3.2-Exp paper,

@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "LIB_PATH", "lib", "Dims", "PRODUCTION_DIMS", "rows_struct", "dims_struct",
-    "indexer_scores", "topk", "sparse_mla_attn", "forward",
+    "indexer_scores", "topk", "sparse_mla_attn", "forward", "forward_noalloc",
     "forward_workspace_size", "check_index_domain",
     "sparse_mla_attn_workspace_size", "project_append", "project_append_workspace_size",
     "pages_struct", "indexer_scores_paged", "sparse_mla_attn_paged", "forward_paged",
@@ -38,7 +38,8 @@ EXPORTED_SYMBOLS = [
     "dsa_indexer_loss_workspace_size", "dsa_indexer_loss", "dsa_indexer_backward",
     "dsa_indexer_loss_dense_workspace_size", "dsa_indexer_loss_dense", "dsa_indexer_backward_dense",
     "dsa_mha_prefill_workspace_size", "dsa_mha_prefill",
-    "dsa_check_index_domain", "dsa_status_string", "dsa_last_error", "dsa_api_version",
+    "dsa_forward_noalloc", "dsa_check_index_domain", "dsa_status_string", "dsa_last_error",
+    "dsa_api_version",
 ]
 
 
@@ -82,6 +83,7 @@ def _load() -> ctypes.CDLL:
     L.dsa_forward_workspace_size.argtypes = [R, D, i32]
     L.dsa_forward_workspace_size.restype = sz
     L.dsa_forward.argtypes = [R, D, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, i32, vp, sz, vp]
+    L.dsa_forward_noalloc.argtypes = [R, D, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, i32, vp]
     L.dsa_project_append_workspace_size.argtypes = [R, i32]
     L.dsa_project_append_workspace_size.restype = sz
     L.dsa_project_append.argtypes = [R, D, i32] + [vp] * 12 + [sz, vp]
@@ -106,7 +108,7 @@ def _load() -> ctypes.CDLL:
                  "dsa_project_append", "dsa_indexer_scores_paged", "dsa_sparse_mla_attn_paged",
                  "dsa_forward_paged", "dsa_project_append_paged", "dsa_indexer_loss",
                  "dsa_indexer_backward", "dsa_mha_prefill", "dsa_indexer_loss_dense",
-                 "dsa_indexer_backward_dense", "dsa_check_index_domain"):
+                 "dsa_indexer_backward_dense", "dsa_check_index_domain", "dsa_forward_noalloc"):
         getattr(L, name).restype = ctypes.c_int
     L.dsa_check_index_domain.argtypes = [ctypes.POINTER(ctypes.c_int32)]
     L.dsa_status_string.argtypes = [ctypes.c_int]
@@ -330,6 +332,22 @@ def forward(rows: _Rows, dims: Dims, q_idx, q_scale, w, k_idx, k_scale, q, laten
                            _ptr(w), _ptr(k_idx), _ptr(k_scale), _ptr(q), _ptr(latent),
                            float(softmax_scale), _ptr(out), _ptr(lse), _ptr(indices_out),
                            int(chunk_rows), _ptr(workspace), workspace.numel(), _stream()))
+    return out, lse, indices_out
+
+
+def forward_noalloc(rows: _Rows, dims: Dims, q_idx, q_scale, w, k_idx, k_scale, q, latent,
+                    softmax_scale: float, out, lse, indices_out=None, chunk_rows: int = 0):
+    """dsa_forward_noalloc: dsa_forward with the library's fixed scratch.  out and
+    lse must be given (nothing is allocated here either)."""
+    if out is None or lse is None:
+        raise ValueError("forward_noalloc writes into caller-provided out and lse")
+    _forward_outputs(rows, dims, q_idx, q_scale, w, k_idx, k_scale, q, latent, out, lse,
+                     indices_out)
+    ds = dims_struct(dims)
+    _check(lib.dsa_forward_noalloc(ctypes.byref(rows), ctypes.byref(ds), _ptr(q_idx),
+                                   _ptr(q_scale), _ptr(w), _ptr(k_idx), _ptr(k_scale), _ptr(q),
+                                   _ptr(latent), float(softmax_scale), _ptr(out), _ptr(lse),
+                                   _ptr(indices_out), int(chunk_rows), _stream()))
     return out, lse, indices_out
 
 

@@ -20,7 +20,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdsa.so")
 ARCH = "gfx950"
 
-SOURCES = ["indexer.hip", "topk.hip", "attention.hip", "project.hip", "train.hip", "mha.hip", "dsa_api.cpp"]
+SOURCES = ["indexer.hip", "topk.hip", "attention.hip", "project.hip", "train.hip", "mha.hip",
+           "noalloc.hip", "dsa_api.cpp"]
 # per-source code generation options
 EXTRA = {
     # keep MFMA results in VGPRs: the indexer epilogue reads every result with VALU

@@ -248,6 +248,18 @@ dsa_status project_impl(const dsa_rows* rows, const dsa_dims* dims, const dsa_pa
 
 }  // namespace
 
+namespace dsa {
+
+dsa_status set_error(dsa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+}  // namespace dsa
+
 extern "C" {
 
 int32_t dsa_api_version(void) { return DSA_API_VERSION; }

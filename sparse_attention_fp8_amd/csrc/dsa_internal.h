@@ -103,4 +103,7 @@ hipError_t launch_mha(const dsa_rows& rows, const void* q, const void* latent, c
                       const void* w_uv, const int32_t* indices, float softmax_scale, void* out,
                       float* lse, void* workspace, hipStream_t stream);
 
+// Sets the calling thread's dsa_last_error() text and returns st.
+dsa_status set_error(dsa_status st, const char* fmt, ...);
+
 }  // namespace dsa
