@@ -407,7 +407,7 @@ __global__ __launch_bounds__(KT) void indexer_kl_dense_kernel(
 // Backward into the indexer for 4 groups of 64 selected entries of one row per
 // block.  The
 // 64-head x 64-key dots come from the fp8 MFMA exactly as in the forward (exact
-// fp8 products, fp32 sums); each wave owns one 16-key tile, each lane 16 heads of
+// fp8 MFMA dots); each wave owns one 16-key tile, each lane 16 heads of
 // one key.  The coefficient matrices for dq and dk go through LDS; the two
 // 64 x 64 x 128 products run in fp32 on the VALU (each thread 4 heads or 4 keys
 // x 8 dims), and the results are added with atomics (dq over the row's blocks,

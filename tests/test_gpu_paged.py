@@ -168,7 +168,7 @@ def test_paged_multi_sequence_tiles(dsa):
     for r in (0, 1, 2, 3, 77, 127):
         row = host.row(int(src[r]))
         row.b, row.t = int(seq[r]), int(pos[r])
-        check_scores(got[r, : row.t + 1], host.scores(row), host.score_extra(row))
+        check_scores(got[r, : row.t + 1], host.scores(row))
 
 
 def test_paged_table_entries_out_of_range(dsa):

@@ -107,7 +107,7 @@ def test_indexer_parity(dsa, name):
         for i, r in enumerate(want):
             row = host.row(int(r))
             ref = host.scores(row)
-            worst = max(worst, check_scores(got[i, : row.t + 1], ref, host.score_extra(row)))
+            worst = max(worst, check_scores(got[i, : row.t + 1], ref))
             rel_row = max(rel_row, float(np.max(np.abs(got[i, : row.t + 1] - ref))
                                          / max(np.max(np.abs(ref)), 1e-30)))
     print(f"[indexer] {name}: worst error / allowed = {worst:.3e}, "

@@ -9,12 +9,12 @@ arithmetic:
 * target and softmax run in fp32 over 576-term bf16 dots and 2048-entry sums, so
   p and softmax carry relative errors near 1e-5: |d dI_i| <= 1e-3 (p_i +
   softmax_i) + 1e-7 and |d loss| <= 1e-3 |loss| + 1e-6;
-* the backward's dots are the forward's fp8 MFMA sums, whose error is at most
-  EPS_MAX_PRODUCT of the largest product (tests/test_gpu_fp8_accumulation.py)
-  plus the rounding of the result, so a ReLU mask may flip where a dot lies within
-  (EPS_MAX_PRODUCT + 2^-24) sum_d |q_d k_d| of zero.  Such a pair may add its
-  whole term, and it is allowed for.  The fp32 sums add 1e-5 of the absolute sum
-  of the terms.
+* the backward's dots are the forward's fp8 MFMA sums, off by at most
+  GROUP_EPS per unit of each 8-product group's largest product plus SUM_EPS of
+  sum_d |q_d k_d| (tests/test_gpu_fp8_accumulation.py), so a ReLU mask may flip
+  where a dot lies within (GROUP_EPS + SUM_EPS) sum_d |q_d k_d| of zero.  Such a
+  pair may add its whole term, and it is allowed for.  The fp32 sums add 1e-5 of
+  the absolute sum of the terms.
 A composed run (the GPU's own scores and selection) is held to C2 plus a bar on
 the loss that accounts for the indexer's own C1 error.
 """
@@ -26,12 +26,13 @@ import torch
 
 import dsa_inputs as di
 import oracle
-from dsa_check import EPS_MAX_PRODUCT, U32, HostInputs
+from dsa_check import GROUP_EPS, SUM_EPS, HostInputs
 
 pytestmark = pytest.mark.gpu
 
-# bound on |MFMA dot - exact dot| per unit of sum_d |q_d k_d| (>= the largest product)
-DOT_EPS = EPS_MAX_PRODUCT + U32
+# bound on |MFMA dot - exact dot| per unit of sum_d |q_d k_d| (each group's largest
+# product is at most the group's share of that sum)
+DOT_EPS = GROUP_EPS + SUM_EPS
 
 
 @pytest.fixture(scope="module")
