@@ -138,6 +138,8 @@ class Workload:
         self.lse = torch.empty(R, cfg.n_heads, dtype=torch.float32, device="cuda")
         need = max(dsa.sparse_mla_attn_workspace_size(rs, self.dims) for rs in self.sub)
         self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+        need = max(dsa.topk_workspace_size(rs, cfg.topk) for rs in self.sub)
+        self.tws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
         self.fws = torch.empty(max(dsa.forward_workspace_size(self.rows, self.dims, self.chunk), 1),
                                dtype=torch.uint8, device="cuda")
         self.graph = None
@@ -165,7 +167,7 @@ class Workload:
         d, i = self.dsa, self.inp
         d.indexer_scores_paged(self.rows, self.dims, self.pages, i.q_idx, i.q_scale, i.w,
                                self.k_pool, self.ks_pool, scores=self.scores)
-        d.topk(self.rows, self.cfg.topk, self.scores, indices=self.idx)
+        d.topk(self.rows, self.cfg.topk, self.scores, indices=self.idx, workspace=self.tws)
         d.sparse_mla_attn_paged(self.rows, self.dims, self.pages, i.q, self.lat_pool, self.idx,
                                 self.cfg.scale, out=self.out, lse=self.lse, workspace=self.ws)
 
@@ -191,7 +193,7 @@ class Workload:
             sc, ix = self.scores[:n], self.idx[:n]
             mark("indexer", lambda: d.indexer_scores(rs, self.dims, i.q_idx[a:b], i.q_scale[a:b],
                                                      i.w[a:b], i.k_idx, i.k_scale, scores=sc))
-            mark("topk", lambda: d.topk(rs, c.topk, sc, indices=ix))
+            mark("topk", lambda: d.topk(rs, c.topk, sc, indices=ix, workspace=self.tws))
             mark("attention", lambda: d.sparse_mla_attn(rs, self.dims, i.q[a:b], i.latent, ix,
                                                         c.scale, out=self.out[a:b],
                                                         lse=self.lse[a:b], workspace=self.ws))

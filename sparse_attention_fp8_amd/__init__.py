@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "LIB_PATH", "lib", "Dims", "PRODUCTION_DIMS", "rows_struct", "dims_struct",
-    "indexer_scores", "topk", "sparse_mla_attn", "forward", "forward_noalloc",
+    "indexer_scores", "topk", "topk_workspace_size", "sparse_mla_attn", "forward", "forward_noalloc",
     "forward_workspace_size", "check_index_domain",
     "sparse_mla_attn_workspace_size", "project_append", "project_append_workspace_size",
     "pages_struct", "indexer_scores_paged", "sparse_mla_attn_paged", "forward_paged",
@@ -31,7 +31,8 @@ DSA_OK, DSA_E_INVALID, DSA_E_UNSUPPORTED, DSA_E_WORKSPACE, DSA_E_HIP = range(5)
 DSA_F32, DSA_BF16, DSA_FP8_E4M3FN = range(3)
 
 EXPORTED_SYMBOLS = [
-    "dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_attn_workspace_size",
+    "dsa_indexer_scores", "dsa_topk_workspace_size", "dsa_topk",
+    "dsa_sparse_mla_attn_workspace_size",
     "dsa_sparse_mla_attn", "dsa_forward_workspace_size", "dsa_forward",
     "dsa_project_append_workspace_size", "dsa_project_append", "dsa_indexer_scores_paged",
     "dsa_sparse_mla_attn_paged", "dsa_forward_paged", "dsa_project_append_paged",
@@ -76,7 +77,9 @@ def _load() -> ctypes.CDLL:
                              ctypes.c_size_t)
     R, D = ctypes.POINTER(_Rows), ctypes.POINTER(_Dims)
     L.dsa_indexer_scores.argtypes = [R, D, vp, vp, vp, vp, vp, vp, i64, vp]
-    L.dsa_topk.argtypes = [R, i32, vp, i64, vp, vp]
+    L.dsa_topk_workspace_size.argtypes = [R, i32]
+    L.dsa_topk_workspace_size.restype = sz
+    L.dsa_topk.argtypes = [R, i32, vp, i64, vp, vp, sz, vp]
     L.dsa_sparse_mla_attn_workspace_size.argtypes = [R, D]
     L.dsa_sparse_mla_attn_workspace_size.restype = sz
     L.dsa_sparse_mla_attn.argtypes = [R, D, vp, vp, vp, f32, vp, vp, vp, sz, vp]
@@ -234,16 +237,26 @@ def indexer_scores(rows: _Rows, dims: Dims, q_idx, q_scale, w, k_idx, k_scale,
     return scores
 
 
+def topk_workspace_size(rows: _Rows, k: int) -> int:
+    return int(lib.dsa_topk_workspace_size(ctypes.byref(rows), int(k)))
+
+
 def topk(rows: _Rows, k: int, scores: torch.Tensor,
-         indices: Optional[torch.Tensor] = None) -> torch.Tensor:
+         indices: Optional[torch.Tensor] = None,
+         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """dsa_topk: returns indices [R, k] int32 (ascending, -1 padded)."""
     _dev(scores, torch.float32, "scores")
     if indices is None:
         indices = torch.empty(rows.num_rows, k, dtype=torch.int32, device=scores.device)
+    need = topk_workspace_size(rows, k)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
+    _dev(workspace, torch.uint8, "workspace")
     _dev(indices, torch.int32, "indices")
     _shape(scores, (rows.num_rows, None), "scores")
     _shape(indices, (rows.num_rows, k), "indices")
     _check(lib.dsa_topk(ctypes.byref(rows), k, _ptr(scores), scores.shape[1], _ptr(indices),
+                        _ptr(workspace), 0 if workspace is None else workspace.numel(),
                         _stream()))
     return indices
 

@@ -112,12 +112,12 @@ constexpr size_t kLatentRow = dsa::kQkDim * sizeof(uint16_t);  // bf16 latent en
 dsa_status run_indexer(const dsa_rows& rows, const dsa_dims& dims, const void* q_idx,
                        const float* q_scale, const float* w, const void* k_idx,
                        const float* k_scale, float* scores, int64_t ld, hipStream_t stream,
-                       const dsa::PageMap& pm) {
+                       const dsa::PageMap& pm, dsa::ClearWords clear = dsa::ClearWords()) {
   hipError_t err;
   if (dims.idx_dtype == DSA_FP8_E4M3FN)
     err = dsa::launch_indexer_fp8(rows, static_cast<const uint8_t*>(q_idx), q_scale, w,
                                   static_cast<const uint8_t*>(k_idx), k_scale, scores, ld, stream,
-                                  pm);
+                                  pm, clear);
   else
     err = dsa::launch_indexer_f32(rows, dims, static_cast<const float*>(q_idx), w,
                                   static_cast<const float*>(k_idx), scores, ld, stream);
@@ -125,8 +125,9 @@ dsa_status run_indexer(const dsa_rows& rows, const dsa_dims& dims, const void* q
 }
 
 dsa_status run_topk(const dsa_rows& rows, int topk, const float* scores, int64_t ld,
-                    int32_t* indices, hipStream_t stream) {
-  const hipError_t err = dsa::launch_topk(rows, topk, scores, ld, indices, stream);
+                    int32_t* indices, void* ws, hipStream_t stream, bool counts_cleared = false) {
+  const hipError_t err = dsa::launch_topk(rows, topk, scores, ld, indices, ws, stream,
+                                          counts_cleared);
   return err == hipSuccess ? DSA_OK : hip_fail(err, "top-k launch");
 }
 
@@ -146,6 +147,15 @@ dsa_status run_attn(const dsa_rows& rows, const dsa_dims& dims, const void* q,
 size_t elem_bytes(dsa_dtype t) { return t == DSA_FP8_E4M3FN ? 1 : (t == DSA_BF16 ? 2 : 4); }
 
 int64_t scores_ld(const dsa_rows& rows) { return (int64_t)align_up((size_t)rows.max_pos + 1, 64); }
+
+// top-k workspace of the forward's chunks: the largest over the chunk sizes it uses
+size_t forward_topk_ws(const dsa_rows& rows, int CH) {
+  dsa_rows a = rows, b = rows;
+  a.num_rows = CH;
+  b.num_rows = rows.num_rows - (rows.num_rows - 1) / CH * CH;
+  const size_t x = dsa::topk_workspace_bytes(a), y = dsa::topk_workspace_bytes(b);
+  return x > y ? x : y;
+}
 
 dsa_status forward_impl(const dsa_rows* rows, const dsa_dims* dims, const dsa_pages* pages,
                         const void* q_idx, const float* q_scale, const float* w, const void* k_idx,
@@ -179,6 +189,8 @@ dsa_status forward_impl(const dsa_rows* rows, const dsa_dims* dims, const dsa_pa
   ws += align_up((size_t)CH * ld * sizeof(float), 256);
   int32_t* idx_ws = reinterpret_cast<int32_t*>(ws);
   ws += align_up((size_t)CH * dims->topk * sizeof(int32_t), 256);
+  void* topk_ws = ws;
+  ws += align_up(forward_topk_ws(*rows, CH), 256);
   void* attn_ws = ws;
   const hipStream_t s = as_stream(stream);
 
@@ -193,11 +205,14 @@ dsa_status forward_impl(const dsa_rows* rows, const dsa_dims* dims, const dsa_pa
     sub.row_seq = rows->row_seq + r0;
     sub.row_pos = rows->row_pos + r0;
     int32_t* idx = indices_out ? indices_out + (size_t)r0 * dims->topk : idx_ws;
+    // the fp8 indexer clears the top-k launch's per-row counts, saving it a launch
+    const dsa::ClearWords clear = dims->idx_dtype == DSA_FP8_E4M3FN
+                                      ? dsa::topk_counts(sub, topk_ws) : dsa::ClearWords();
     st = run_indexer(sub, *dims, static_cast<const uint8_t*>(q_idx) + r0 * qi_row,
                      q_scale ? q_scale + r0 * hi : nullptr, w + r0 * hi, k_idx, k_scale, scores,
-                     ld, s, pm);
+                     ld, s, pm, clear);
     if (st != DSA_OK) return st;
-    st = run_topk(sub, dims->topk, scores, ld, idx, s);
+    st = run_topk(sub, dims->topk, scores, ld, idx, topk_ws, s, clear.ptr != nullptr);
     if (st != DSA_OK) return st;
     st = run_attn(sub, *dims, static_cast<const uint8_t*>(q) + r0 * q_row, latent, idx,
                   softmax_scale, static_cast<uint8_t*>(out) + r0 * o_row,
@@ -303,8 +318,13 @@ dsa_status dsa_indexer_scores(const dsa_rows* rows, const dsa_dims* dims, const 
                      as_stream(stream), dsa::PageMap());
 }
 
+size_t dsa_topk_workspace_size(const dsa_rows* rows, int32_t topk) {
+  if (check_rows(rows) != DSA_OK || topk < 1 || topk > 4096) return 0;
+  return dsa::topk_workspace_bytes(*rows);
+}
+
 dsa_status dsa_topk(const dsa_rows* rows, int32_t topk, const float* scores, int64_t ld_scores,
-                    int32_t* indices, void* stream) {
+                    int32_t* indices, void* workspace, size_t ws_bytes, void* stream) {
   dsa_status st = check_rows(rows);
   if (st != DSA_OK) return st;
   if (topk < 1 || topk > 4096) return fail(DSA_E_UNSUPPORTED, "topk must lie in [1, 4096]");
@@ -313,7 +333,10 @@ dsa_status dsa_topk(const dsa_rows* rows, int32_t topk, const float* scores, int
   if (!scores || !indices) return fail(DSA_E_INVALID, "NULL tensor pointer");
   if (ld_scores < (int64_t)rows->max_pos + 1)
     return fail(DSA_E_INVALID, "ld_scores < max_pos + 1");
-  return run_topk(*rows, topk, scores, ld_scores, indices, as_stream(stream));
+  const size_t need = dsa::topk_workspace_bytes(*rows);
+  if (need > 0 && (workspace == nullptr || ws_bytes < need))
+    return fail(DSA_E_WORKSPACE, "top-k needs %zu workspace bytes, got %zu", need, ws_bytes);
+  return run_topk(*rows, topk, scores, ld_scores, indices, workspace, as_stream(stream));
 }
 
 size_t dsa_sparse_mla_attn_workspace_size(const dsa_rows* rows, const dsa_dims* dims) {
@@ -346,6 +369,7 @@ size_t dsa_forward_workspace_size(const dsa_rows* rows, const dsa_dims* dims, in
   const int64_t ld = scores_ld(*rows);
   size_t bytes = align_up((size_t)CH * ld * sizeof(float), 256);
   bytes += align_up((size_t)CH * dims->topk * sizeof(int32_t), 256);
+  bytes += align_up(forward_topk_ws(*rows, CH), 256);
   // the last chunk may hold fewer rows and therefore use more attention splits
   const int last = R - (R - 1) / CH * CH;
   const size_t attn = dsa::attn_workspace_bytes(CH, *dims);

@@ -39,17 +39,32 @@ __host__ __device__ __forceinline__ uint32_t paged_row(const PageMap& pm, int b,
   return ((uint32_t)pg << pm.shift) | (uint32_t)(s & ((1 << pm.shift) - 1));
 }
 
+// Words the fp8 indexer launch sets to zero (from its first block) for the top-k
+// launch that follows it: the per-row counts of the many-blocks-per-row top-k.
+struct ClearWords {
+  uint32_t* ptr = nullptr;
+  int n = 0;
+};
+
 hipError_t launch_indexer_fp8(const dsa_rows& rows, const uint8_t* q_idx, const float* q_scale,
                               const float* w, const uint8_t* k_idx, const float* k_scale,
                               float* scores, int64_t ld, hipStream_t stream,
-                              const PageMap& pm = PageMap());
+                              const PageMap& pm = PageMap(), ClearWords clear = ClearWords());
 
 hipError_t launch_indexer_f32(const dsa_rows& rows, const dsa_dims& dims, const float* q_idx,
                               const float* w, const float* k_idx, float* scores, int64_t ld,
                               hipStream_t stream);
 
+// Workspace of the top-k launch for these rows (0 when one block per row runs).
+size_t topk_workspace_bytes(const dsa_rows& rows);
+// The words of that workspace that must be zero when the top-k launch starts
+// (none when one block per row runs).
+ClearWords topk_counts(const dsa_rows& rows, void* workspace);
+// counts_cleared: an earlier launch on the stream has zeroed topk_counts(rows, ws);
+// otherwise the launch zeroes them itself first.
 hipError_t launch_topk(const dsa_rows& rows, int topk, const float* scores, int64_t ld,
-                       int32_t* indices, hipStream_t stream);
+                       int32_t* indices, void* workspace, hipStream_t stream,
+                       bool counts_cleared = false);
 
 // Number of splits of each row's selected set used by the bf16 attention for R rows.
 int attn_num_splits(int num_rows, int topk);

@@ -108,7 +108,9 @@ __global__ __launch_bounds__(WAVES * 64) void indexer_fp8_decode_kernel(
     const float* __restrict__ w, const uint8_t* __restrict__ k_idx,
     const float* __restrict__ k_scale, const int32_t* __restrict__ row_seq,
     const int32_t* __restrict__ row_pos, int B, int N, int nkb, float* __restrict__ scores,
-    int64_t ld, PageMap pm) {
+    int64_t ld, PageMap pm, ClearWords clear) {
+  if (blockIdx.x == 0)  // words a following launch needs zeroed
+    for (int i = threadIdx.x; i < clear.n; i += WAVES * 64) clear.ptr[i] = 0u;
   const int r = blockIdx.x / nkb;
   const int kb0 = (blockIdx.x - r * nkb) * KPB;
   const int b = row_seq[r], t = row_pos[r];
@@ -286,8 +288,10 @@ void indexer_fp8_prefill_kernel(
     const float* __restrict__ w, const uint8_t* __restrict__ k_idx,
     const float* __restrict__ k_scale, const int32_t* __restrict__ row_seq,
     const int32_t* __restrict__ row_pos, int R, int B, int N, int ksplit,
-    float* __restrict__ scores, int64_t ld, PageMap pm) {
+    float* __restrict__ scores, int64_t ld, PageMap pm, ClearWords clear) {
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[PNBUF][PGB];
+  if (blockIdx.x == 0)  // words a following launch needs zeroed
+    for (int i = threadIdx.x; i < clear.n; i += PW * 64) clear.ptr[i] = 0u;
   __shared__ float ksbuf[PNBUF][PG];
   __shared__ __attribute__((aligned(16))) float sbuf[PROWS][PKPB];  // one key block's scores
   __shared__ int info[PW][3];
@@ -538,7 +542,8 @@ __global__ __launch_bounds__(256) void indexer_f32_kernel(
 
 hipError_t launch_indexer_fp8(const dsa_rows& rows, const uint8_t* q_idx, const float* q_scale,
                               const float* w, const uint8_t* k_idx, const float* k_scale,
-                              float* scores, int64_t ld, hipStream_t stream, const PageMap& pm) {
+                              float* scores, int64_t ld, hipStream_t stream, const PageMap& pm,
+                              ClearWords clear) {
   const bool paged = pm.table != nullptr;
   const int R = rows.num_rows;
   const int L = rows.max_pos + 1;
@@ -552,7 +557,7 @@ hipError_t launch_indexer_fp8(const dsa_rows& rows, const uint8_t* q_idx, const 
     auto kern = paged ? indexer_fp8_prefill_kernel<true> : indexer_fp8_prefill_kernel<false>;
     hipLaunchKernelGGL(kern, dim3(tiles * ksplit), dim3(PW * 64), 0, stream, q_idx, q_scale, w,
                        k_idx, k_scale, rows.row_seq, rows.row_pos, R, rows.num_seqs,
-                       rows.max_ctx, ksplit, scores, ld, pm);
+                       rows.max_ctx, ksplit, scores, ld, pm, clear);
   } else {
     constexpr int WAVES = 4, KPB = 1024, DEPTH = 3;
     const int nkb = (L + KPB - 1) / KPB;
@@ -560,7 +565,7 @@ hipError_t launch_indexer_fp8(const dsa_rows& rows, const uint8_t* q_idx, const 
                       : indexer_fp8_decode_kernel<WAVES, KPB, DEPTH, false>;
     hipLaunchKernelGGL(kern, dim3(R * nkb), dim3(WAVES * 64), 0, stream, q_idx, q_scale, w,
                        k_idx, k_scale, rows.row_seq, rows.row_pos, rows.num_seqs, rows.max_ctx,
-                       nkb, scores, ld, pm);
+                       nkb, scores, ld, pm, clear);
   }
   return hipGetLastError();
 }

@@ -470,24 +470,474 @@ __global__ __launch_bounds__(TK_T) void topk_kernel_any(const float* __restrict_
     topk_row<false, 4>(row, t, topk, vec_ok, orow, sh, sel, tie);
 }
 
+// ---------------------------------------------------------------------------
+// Few rows (decode): many blocks per row, one kernel.  Block (r, p) owns positions
+// [4096 p, 4096 p + 4096) of row r.
+//   1. Every block of the row derives the same lower bound tau of the threshold
+//      key from a fixed sample of the row (64 runs of 64 scores, evenly spaced): the
+//      sample's k'-th largest key, k' chosen so that about 1.5 n scores of the row
+//      lie above it, rounded down to a multiple of 2^8.  Rows of at most 8192
+//      positions use tau = 0: every position is a candidate.
+//   2. The block writes its positions whose key is >= tau, in position order, to
+//      its slot of the workspace (key and position), with device-scope stores, and
+//      their count.  Then it counts itself done (an atomic per row; no block waits
+//      for another).
+//   3. The last block of the row to finish selects exactly among the candidates,
+//      which are in position order: three radix levels (key bits 31..20, 19..8,
+//      7..0) find the threshold key; candidates above it are taken, and of those
+//      equal to it the first in position order.  If fewer than n positions reached
+//      tau (the sample misled), the same selection runs over the whole row.
+// The per-row counts must be zero when the kernel starts (topk_mb_zero_kernel).
+// ---------------------------------------------------------------------------
+constexpr int MB_CHUNK = 4 * TK_T;   // positions per block
+constexpr int MB_NBIN = 4096;        // radix bins per level (12 bits)
+constexpr int MB_SAMPLE = 4 * TK_T;  // sample size: 64 runs of 64 scores
+constexpr int MB_ALL = 8192;         // rows up to this long take every position
+constexpr int MB_CAP = 8192 + CMAX;  // candidates held in LDS, plus CMAX for a bin's members
+
+struct MbShared {
+  uint32_t hist[MB_NBIN];
+  uint32_t ckey[MB_CAP];
+  int cpos[MB_CAP];
+  uint32_t pref[kTopkMaxPositions / MB_CHUNK + 1];
+  uint32_t wtot[2][TK_W];
+  int misc[8];
+};
+
+// Whole block: the bin of hist[0..NB) holding the need-th largest element
+// (1 <= need <= total), counting from the top.  res[0] = bin, res[1] = count in
+// the bins above it.  The caller synchronises before reading res.
+template <int NB>
+__device__ __forceinline__ void find_desc_block(const uint32_t* hist, uint32_t need,
+                                                uint32_t* wtot, int* res) {
+  constexpr int PER = NB >= TK_T ? NB / TK_T : 1;
+  const int tid = threadIdx.x;
+  uint32_t c[PER];
+  uint32_t local = 0u;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = tid * PER + j;  // i-th bin from the top
+    c[j] = i < NB ? hist[NB - 1 - i] : 0u;
+    local += c[j];
+  }
+  const uint32_t incl = block_incl_scan(local, wtot);
+  const uint32_t excl = incl - local;
+  if (excl < need && need <= incl) {
+    uint32_t acc = excl;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      if (acc + c[j] >= need) {
+        res[0] = NB - 1 - (tid * PER + j);
+        res[1] = (int)acc;
+        break;
+      }
+      acc += c[j];
+    }
+  }
+}
+
+// four scores from position s (s % 4 == 0); past the row end and NaN read as -inf
+__device__ __forceinline__ f32x4 fetch4(const float* __restrict__ row, int s, int L, int vec_ok) {
+  f32x4 v;
+  if (vec_ok && s + 3 < L) {
+    v = *reinterpret_cast<const f32x4*>(row + s);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = s + e < L ? row[s + e] : -INFINITY;
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = (v[e] != v[e]) ? -INFINITY : v[e];
+  return v;
+}
+
+__device__ __forceinline__ void store_agent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t load_agent(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_agent2(uint2* p, uint32_t key, uint32_t pos) {
+  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p),
+                     ((unsigned long long)pos << 32) | key, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint2 load_agent2(const uint2* p) {
+  const unsigned long long x = __hip_atomic_load(
+      reinterpret_cast<unsigned long long*>(const_cast<uint2*>(p)), __ATOMIC_RELAXED,
+      __HIP_MEMORY_SCOPE_AGENT);
+  return make_uint2((uint32_t)x, (uint32_t)(x >> 32));
+}
+
+__global__ __launch_bounds__(256) void topk_mb_zero_kernel(uint32_t* __restrict__ counts, int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) counts[i] = 0u;
+}
+
+// Block-wide min and max of one key per thread.
+__device__ __forceinline__ uint2 block_minmax(uint32_t lo, uint32_t hi, MbShared& sh) {
+  lo = wave_reduce_bits(lo, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+  hi = wave_reduce_bits(hi, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+  const int wv = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane_id() == 0) {
+    sh.wtot[0][wv] = lo;
+    sh.wtot[1][wv] = hi;
+  }
+  __syncthreads();
+  uint32_t rlo = sh.wtot[0][0], rhi = sh.wtot[1][0];
+#pragma unroll
+  for (int w = 1; w < TK_W; ++w) {
+    rlo = min(rlo, sh.wtot[0][w]);
+    rhi = max(rhi, sh.wtot[1][w]);
+  }
+  __syncthreads();
+  return make_uint2(rlo, rhi);
+}
+
+// shift that maps key - lo for keys in [lo, hi] onto at most 4096 bins
+__device__ __forceinline__ int span_shift(uint32_t lo, uint32_t hi) {
+  const uint32_t span = hi - lo;
+  const int bits = span == 0u ? 0 : 32 - __clz(span);
+  return bits > 12 ? bits - 12 : 0;
+}
+
+// Exact selection of the n largest keys (ties to the lower position) among C
+// candidates given in position order by get(i) -> (key, pos), written ascending to
+// orow.  Whole block.  The keys are binned over their own range [lo, hi] (4096
+// bins), which finds the bin of the n-th largest; its members, typically a handful,
+// are ranked directly by (key desc, position asc).  A bin with more than CMAX
+// members (keys packed into a narrow range) is binned again over its own range, down
+// to a single key, whose members are ties taken in position order.
+template <typename Get>
+__device__ __forceinline__ void select_ordered(MbShared& sh, Get&& get, int C, int n,
+                                               int32_t* __restrict__ orow) {
+  const int tid = threadIdx.x;
+  uint32_t klo = 0xFFFFFFFFu, khi = 0u;
+  for (int i = tid; i < C; i += TK_T) {
+    const uint32_t k = get(i).x;
+    klo = min(klo, k);
+    khi = max(khi, k);
+  }
+  const uint2 mm = block_minmax(klo, khi, sh);
+  uint32_t lo = mm.x, hi = mm.y, need = (uint32_t)n;
+  uint32_t kstar = 0u, m_ties = 0u;
+  uint32_t* mk = sh.ckey + (MB_CAP - CMAX);  // the members of a bin
+  int* mp = sh.cpos + (MB_CAP - CMAX);
+#pragma unroll 1
+  for (;;) {
+    // the keys in [lo, hi] hold the remaining `need` winners; bin them
+    const int shift = span_shift(lo, hi);
+    for (int i = tid; i < MB_NBIN; i += TK_T) sh.hist[i] = 0u;
+    if (tid == 0) {
+      sh.misc[4] = 0;
+      sh.misc[6] = 0;
+    }
+    __syncthreads();
+    for (int i = tid; i < C; i += TK_T) {
+      const uint32_t k = get(i).x;
+      if (k >= lo && k <= hi) atomicAdd(&sh.hist[(k - lo) >> shift], 1u);
+    }
+    __syncthreads();
+    find_desc_block<MB_NBIN>(sh.hist, need, sh.wtot[0], sh.misc + 2);
+    __syncthreads();
+    const uint32_t tb = (uint32_t)sh.misc[2];
+    need -= (uint32_t)sh.misc[3];
+    const uint32_t m = sh.hist[tb];
+    const uint32_t blo = lo + (tb << shift);
+    const uint32_t bhi = shift == 0 ? blo : min(hi, blo + ((1u << shift) - 1u));
+    if (blo == bhi) {  // a single key: ties, taken in position order
+      kstar = blo;
+      m_ties = need;
+      break;
+    }
+    if (m > (uint32_t)CMAX) {  // refine over the bin's own range
+      lo = blo;
+      hi = bhi;
+      __syncthreads();
+      continue;
+    }
+    // collect the bin's members and rank them directly
+    for (int i = tid; i < C; i += TK_T) {
+      const uint2 kp = get(i);
+      if (kp.x >= blo && kp.x <= bhi) {
+        const int at = atomicAdd(&sh.misc[4], 1);
+        mk[at] = kp.x;
+        mp[at] = (int)kp.y;
+      }
+    }
+    __syncthreads();
+    // four threads per member, each over a quarter of the others: the member of
+    // rank need - 1 is the last winner; its key is kstar
+    for (int c0 = 0; c0 < (int)m; c0 += TK_T / 4) {
+      const int c = c0 + (tid >> 2), part = tid & 3;
+      uint32_t rank = 0u, k = 0u;
+      int pp = 0;
+      if (c < (int)m) {
+        k = mk[c];
+        pp = mp[c];
+        for (int u = part; u < (int)m; u += 4) {
+          const uint32_t ku = mk[u];
+          rank += (ku > k) || (ku == k && mp[u] < pp);
+        }
+      }
+      rank += dpp<kDppXor1>(rank);
+      rank += dpp<kDppXor2>(rank);
+      if (c < (int)m && part == 0 && rank == need - 1u) sh.misc[5] = (int)k;
+    }
+    __syncthreads();
+    kstar = (uint32_t)sh.misc[5];
+    // the winners equal to kstar (the first of them in position order)
+    for (int c = tid; c < (int)m; c += TK_T) {
+      if (mk[c] != kstar) continue;
+      uint32_t rank = 0u;
+      for (int u = 0; u < (int)m; ++u) rank += (mk[u] > kstar) || (mk[u] == kstar && mp[u] < mp[c]);
+      if (rank < need) atomicAdd(&sh.misc[6], 1);
+    }
+    __syncthreads();
+    m_ties = (uint32_t)sh.misc[6];
+    break;
+  }
+  __syncthreads();
+  // ordered output: the keys above kstar, and the first m_ties equal to it in
+  // position order; tiles of 4 candidates per thread
+  uint32_t sel_base = 0u, tie_base = 0u;
+  for (int c0 = 0; c0 < C; c0 += 4 * TK_T) {
+    uint32_t ksel = 0u, ktie = 0u;
+    int pos[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = c0 + 4 * tid + e;
+      uint2 kp = make_uint2(0u, 0u);
+      if (i < C) kp = get(i);
+      pos[e] = (int)kp.y;
+      ksel |= (i < C && kp.x > kstar ? 1u : 0u) << e;
+      ktie |= (i < C && kp.x == kstar ? 1u : 0u) << e;
+    }
+    __syncthreads();
+    const uint32_t ns = (uint32_t)__popc(ksel), nt = (uint32_t)__popc(ktie);
+    const uint32_t is = block_incl_scan(ns, sh.wtot[0]);
+    __syncthreads();
+    const uint32_t it = block_incl_scan(nt, sh.wtot[1]);
+    uint32_t S = sel_base + is - ns, E = tie_base + it - nt;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if ((ksel >> e) & 1u) {
+        const uint32_t at = S + min(E, m_ties);
+        if (at < (uint32_t)n) orow[at] = pos[e];
+        ++S;
+      } else if ((ktie >> e) & 1u) {
+        if (E < m_ties && S + E < (uint32_t)n) orow[S + E] = pos[e];
+        ++E;
+      }
+    }
+    uint32_t tot_s = 0u, tot_t = 0u;
+#pragma unroll
+    for (int w = 0; w < TK_W; ++w) {
+      tot_s += sh.wtot[0][w];
+      tot_t += sh.wtot[1][w];
+    }
+    sel_base += tot_s;
+    tie_base += tot_t;
+  }
+}
+
+__global__ __launch_bounds__(TK_T) void topk_mb_kernel(
+    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ row_pos,
+    int max_pos, int topk, int vec_ok, int32_t* __restrict__ out, uint2* __restrict__ cand,
+    uint32_t* __restrict__ ccount, uint32_t* __restrict__ done, int nchunk) {
+  __shared__ MbShared sh;
+  const int r = blockIdx.x / nchunk, p = blockIdx.x - r * nchunk;
+  const int tid = threadIdx.x;
+  const int t = row_pos[r];
+  int32_t* orow = out + (size_t)r * topk;
+  if (t < 0 || t > max_pos || (int64_t)t >= ld || t >= kTopkMaxPositions) {
+    if (p == 0)
+      for (int i = tid; i < topk; i += TK_T) orow[i] = -1;
+    return;
+  }
+  const int L = t + 1;
+  const int n = min(topk, L);
+  if (n == L) {  // every candidate is selected
+    if (p == 0)
+      for (int i = tid; i < topk; i += TK_T) orow[i] = i < L ? i : -1;
+    return;
+  }
+  const int P = (L + MB_CHUNK - 1) / MB_CHUNK;  // blocks of this row
+  if (p >= P) return;
+  const float* row = scores + (size_t)r * ld;
+  uint2* crow = cand + (size_t)r * nchunk * MB_CHUNK;
+  uint32_t* cnt = ccount + (size_t)r * nchunk;
+
+  // this block's scores, requested first
+  const int s0 = p * MB_CHUNK + 4 * tid;
+  const f32x4 v = fetch4(row, s0, L, vec_ok);
+
+  // ---- 1. tau from the sample
+  uint32_t tau = 0u;
+  if (L > MB_ALL) {
+    const int seg = (L / 64) & ~3;  // >= 128
+    const f32x4 sv = fetch4(row, (tid >> 4) * seg + 4 * (tid & 15), L, vec_ok);
+    // about 1.5 n of the row above the k'-th largest sample
+    const int ks = (int)(((int64_t)n * MB_SAMPLE + L - 1) / L);
+    const int kp = min(MB_SAMPLE, ks + ks / 4 + 4 * (int)ceilf(sqrtf((float)ks)) + 8);
+    uint32_t sk[4], slo = 0xFFFFFFFFu, shi = 0u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sk[e] = float_key(sv[e]);
+      slo = min(slo, sk[e]);
+      shi = max(shi, sk[e]);
+    }
+    const uint2 mm = block_minmax(slo, shi, sh);
+    const int shift = span_shift(mm.x, mm.y);
+    for (int i = tid; i < MB_NBIN; i += TK_T) sh.hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 4; ++e) atomicAdd(&sh.hist[(sk[e] - mm.x) >> shift], 1u);
+    __syncthreads();
+    find_desc_block<MB_NBIN>(sh.hist, (uint32_t)kp, sh.wtot[0], sh.misc + 2);
+    __syncthreads();
+    // the lower edge of the bin holding the k'-th largest sample key
+    tau = mm.x + ((uint32_t)sh.misc[2] << shift);
+    __syncthreads();
+  }
+
+  // ---- 2. this block's candidates, in position order
+  uint32_t key[4], flag = 0u;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    key[e] = float_key(v[e]);
+    flag |= (s0 + e < L && key[e] >= tau ? 1u : 0u) << e;
+  }
+  const uint32_t nc = (uint32_t)__popc(flag);
+  const uint32_t incl = block_incl_scan(nc, sh.wtot[0]);
+  uint32_t at = incl - nc;
+  uint2* cblk = crow + (size_t)p * MB_CHUNK;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if ((flag >> e) & 1u) store_agent2(cblk + at++, key[e], (uint32_t)(s0 + e));
+  if (tid == TK_T - 1) store_agent(cnt + p, incl);
+  // every store of this block has been performed before it counts itself done
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0)
+    sh.misc[0] = __hip_atomic_fetch_add(&done[r], 1u, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(P - 1) ? 1 : 0;
+  __syncthreads();
+  if (sh.misc[0] == 0) return;
+
+  // ---- 3. the last block: exact selection among the row's candidates
+  if (tid <= P) sh.pref[tid] = tid < P ? load_agent(cnt + tid) : 0u;
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t acc = 0u;
+    for (int i = 0; i <= P; ++i) {
+      const uint32_t c = sh.pref[i];
+      sh.pref[i] = acc;
+      acc += c;
+    }
+  }
+  __syncthreads();
+  const int C = (int)sh.pref[P];
+  // position-ordered candidate i: chunk q with pref[q] <= i < pref[q + 1]
+  auto cand_at = [&](int i) -> uint2 {
+    int q = 0;
+    while (q + 1 < P && sh.pref[q + 1] <= (uint32_t)i) ++q;
+    return load_agent2(crow + (size_t)q * MB_CHUNK + (i - (int)sh.pref[q]));
+  };
+  if (C < n) {
+    // the sample put tau too high: select over the whole row
+    select_ordered(sh, [&](int i) -> uint2 {
+      return make_uint2(float_key(fetch4(row, i & ~3, L, vec_ok)[i & 3]), (uint32_t)i);
+    }, L, n, orow);
+  } else if (C <= MB_CAP - CMAX) {
+    // gather chunk by chunk: each wave takes chunks in turn, every lane four
+    // candidates at a time with their loads in flight together
+    const int wv = tid >> 6, ln = lane_id();
+    for (int q = wv; q < P; q += TK_W) {
+      const int cq = (int)(sh.pref[q + 1] - sh.pref[q]);
+      const uint2* src = crow + (size_t)q * MB_CHUNK;
+      const int dst = (int)sh.pref[q];
+      for (int j0 = 0; j0 < cq; j0 += 256) {
+        uint2 kp[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = j0 + 64 * e + ln;
+          kp[e] = j < cq ? load_agent2(src + j) : make_uint2(0u, 0u);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = j0 + 64 * e + ln;
+          if (j < cq) {
+            sh.ckey[dst + j] = kp[e].x;
+            sh.cpos[dst + j] = (int)kp[e].y;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    select_ordered(sh, [&](int i) -> uint2 {
+      return make_uint2(sh.ckey[i], (uint32_t)sh.cpos[i]);
+    }, C, n, orow);
+  } else {
+    select_ordered(sh, cand_at, C, n, orow);
+  }
+  for (int i = n + tid; i < topk; i += TK_T) orow[i] = -1;
+}
+
 }  // namespace
 
+// The many-blocks-per-row path serves calls with too few rows to fill the GPU
+// with one block per row, when the rows are long enough to split.
+static bool topk_use_multi(const dsa_rows& rows) {
+  return rows.num_rows < 128 && rows.max_pos + 1 > MB_ALL;
+}
+
+static int topk_chunks(const dsa_rows& rows) { return (rows.max_pos + MB_CHUNK) / MB_CHUNK; }
+
+ClearWords topk_counts(const dsa_rows& rows, void* workspace) {
+  ClearWords c;
+  if (!topk_use_multi(rows) || workspace == nullptr) return c;
+  const size_t R = (size_t)rows.num_rows, P = (size_t)topk_chunks(rows);
+  c.ptr = reinterpret_cast<uint32_t*>(static_cast<uint2*>(workspace) + R * P * MB_CHUNK) + R * P;
+  c.n = (int)R;
+  return c;
+}
+
+size_t topk_workspace_bytes(const dsa_rows& rows) {
+  if (!topk_use_multi(rows)) return 0;
+  const size_t R = (size_t)rows.num_rows, P = (size_t)topk_chunks(rows);
+  // candidates [R, P, 4096] (key, position), their counts [R, P], done counts [R]
+  return R * P * MB_CHUNK * sizeof(uint2) + ((R * P + R) * sizeof(uint32_t) + 15) / 16 * 16;
+}
+
 hipError_t launch_topk(const dsa_rows& rows, int topk, const float* scores, int64_t ld,
-                       int32_t* indices, hipStream_t stream) {
+                       int32_t* indices, void* workspace, hipStream_t stream,
+                       bool counts_cleared) {
   const int R = rows.num_rows;
   const int L = rows.max_pos + 1;
   const int vec_ok = (ld % 4 == 0) && (reinterpret_cast<uintptr_t>(scores) % 16 == 0);
-  if (L <= 4 * TK_T * 2) {
+  if (L > BITMAP_POS) return hipErrorInvalidValue;  // refused on the host before this
+  if (topk_use_multi(rows)) {
+    const int nchunk = topk_chunks(rows);
+    uint2* cand = static_cast<uint2*>(workspace);
+    uint32_t* ccount = reinterpret_cast<uint32_t*>(cand + (size_t)R * nchunk * MB_CHUNK);
+    uint32_t* done = ccount + (size_t)R * nchunk;
+    if (!counts_cleared) {
+      hipLaunchKernelGGL(topk_mb_zero_kernel, dim3((R + 255) / 256), dim3(256), 0, stream, done, R);
+      const hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return err;
+    }
+    hipLaunchKernelGGL(topk_mb_kernel, dim3(R * nchunk), dim3(TK_T), 0, stream, scores, ld,
+                       rows.row_pos, rows.max_pos, topk, vec_ok, indices, cand, ccount, done,
+                       nchunk);
+  } else if (L <= 4 * TK_T * 2) {
     hipLaunchKernelGGL((topk_kernel<true, 2>), dim3(R), dim3(TK_T), 0, stream, scores, ld,
                        rows.row_pos, rows.max_pos, topk, vec_ok, indices);
   } else if (L <= kResidentMax) {
     hipLaunchKernelGGL((topk_kernel<true, 8>), dim3(R), dim3(TK_T), 0, stream, scores, ld,
                        rows.row_pos, rows.max_pos, topk, vec_ok, indices);
-  } else if (L <= BITMAP_POS) {
+  } else {
     hipLaunchKernelGGL(topk_kernel_any, dim3(R), dim3(TK_T), 0, stream, scores, ld, rows.row_pos,
                        rows.max_pos, topk, vec_ok, indices);
-  } else {
-    return hipErrorInvalidValue;  // rows longer than the bitmap capacity
   }
   return hipGetLastError();
 }

@@ -51,18 +51,18 @@ def test_invalid_arguments_rejected_on_host(m):
     r = _rows(m)
     p = ctypes.c_void_p(16)
     # NULL rows / dims
-    assert L.dsa_topk(None, 2048, p, 64, p, None) == m.DSA_E_INVALID
+    assert L.dsa_topk(None, 2048, p, 64, p, None, 0, None) == m.DSA_E_INVALID
     assert L.dsa_indexer_scores(ctypes.byref(r), None, p, p, p, p, p, p, 64, None) == m.DSA_E_INVALID
     # max_pos outside [0, N)
     bad = _rows(m, max_pos=64)
-    assert L.dsa_topk(ctypes.byref(bad), 2048, p, 64, p, None) == m.DSA_E_INVALID
+    assert L.dsa_topk(ctypes.byref(bad), 2048, p, 64, p, None, 0, None) == m.DSA_E_INVALID
     # ld too small
-    assert L.dsa_topk(ctypes.byref(r), 2048, p, 63, p, None) == m.DSA_E_INVALID
+    assert L.dsa_topk(ctypes.byref(r), 2048, p, 63, p, None, 0, None) == m.DSA_E_INVALID
     # topk out of range
-    assert L.dsa_topk(ctypes.byref(r), 0, p, 64, p, None) == m.DSA_E_UNSUPPORTED
-    assert L.dsa_topk(ctypes.byref(r), 5000, p, 64, p, None) == m.DSA_E_UNSUPPORTED
+    assert L.dsa_topk(ctypes.byref(r), 0, p, 64, p, None, 0, None) == m.DSA_E_UNSUPPORTED
+    assert L.dsa_topk(ctypes.byref(r), 5000, p, 64, p, None, 0, None) == m.DSA_E_UNSUPPORTED
     # NULL tensors
-    assert L.dsa_topk(ctypes.byref(r), 2048, None, 64, p, None) == m.DSA_E_INVALID
+    assert L.dsa_topk(ctypes.byref(r), 2048, None, 64, p, None, 0, None) == m.DSA_E_INVALID
     # fp8 indexer without scales
     assert L.dsa_indexer_scores(ctypes.byref(r), ctypes.byref(d), p, None, p, p, None, p, 64,
                                 None) == m.DSA_E_INVALID
@@ -81,7 +81,7 @@ def test_invalid_arguments_rejected_on_host(m):
                          None, 0, p, 16, None) == m.DSA_E_WORKSPACE
     # zero rows: nothing to do
     empty = _rows(m, R=0, seq=None, pos=None)
-    assert L.dsa_topk(ctypes.byref(empty), 2048, None, 64, None, None) == m.DSA_OK
+    assert L.dsa_topk(ctypes.byref(empty), 2048, None, 64, None, None, 0, None) == m.DSA_OK
 
 
 def test_workspace_sizes(m):
@@ -91,7 +91,17 @@ def test_workspace_sizes(m):
     attn = L.dsa_sparse_mla_attn_workspace_size(ctypes.byref(dec), ctypes.byref(d))
     assert attn == 32 * 8 * 128 * (512 * 2 + 4)   # 8 splits of bf16 partial outputs + fp32 lse
     fwd = L.dsa_forward_workspace_size(ctypes.byref(dec), ctypes.byref(d), 0)
-    assert fwd >= attn + 32 * 32768 * 4 + 32 * 2048 * 4
+    tk = L.dsa_topk_workspace_size(ctypes.byref(dec), 2048)
+    # candidates [32 rows, 8 chunks, 4096] of 8 bytes, their counts and the per-row counts
+    assert tk == 32 * 8 * 4096 * 8 + (32 * 8 * 4 + 32 * 4 + 15) // 16 * 16
+    assert fwd >= attn + tk + 32 * 32768 * 4 + 32 * 2048 * 4
+    # rows that fill the GPU one block each, or short rows: no top-k workspace
+    assert L.dsa_topk_workspace_size(ctypes.byref(_rows(m, R=8192, B=1, N=8192, max_pos=8191)),
+                                     2048) == 0
+    assert L.dsa_topk_workspace_size(ctypes.byref(_rows(m, R=32, B=32, N=8192, max_pos=8191)),
+                                     2048) == 0
+    p = ctypes.c_void_p(16)
+    assert L.dsa_topk(ctypes.byref(dec), 2048, p, 32768, p, p, tk - 1, None) == m.DSA_E_WORKSPACE
     pre = _rows(m, R=131072, B=1, N=131072, max_pos=131071)
     w = L.dsa_forward_workspace_size(ctypes.byref(pre), ctypes.byref(d), 8192)
     assert w >= 8192 * 131072 * 4 and w < 8192 * 131072 * 4 + 8192 * 2048 * 4 + (1 << 20)
@@ -215,10 +225,10 @@ def test_size_limits_rejected_before_enqueue(m):
     d = m.dims_struct(m.PRODUCTION_DIMS)
     p = ctypes.c_void_p(16)
     long_rows = _rows(m, R=1, B=1, N=262144, max_pos=131072)           # 131073 candidates
-    assert L.dsa_topk(ctypes.byref(long_rows), 2048, p, 131136, p, None) == m.DSA_E_UNSUPPORTED
+    assert L.dsa_topk(ctypes.byref(long_rows), 2048, p, 131136, p, None, 0, None) == m.DSA_E_UNSUPPORTED
     assert "131072" in L.dsa_last_error().decode()
     ok_rows = _rows(m, R=0, B=1, N=262144, max_pos=131071, seq=None, pos=None)
-    assert L.dsa_topk(ctypes.byref(ok_rows), 2048, None, 131072, None, None) == m.DSA_OK
+    assert L.dsa_topk(ctypes.byref(ok_rows), 2048, None, 131072, None, None, 0, None) == m.DSA_OK
     big = 1 << 30
     assert L.dsa_forward(ctypes.byref(long_rows), ctypes.byref(d), p, p, p, p, p, p, p, 0.1, p, p,
                          None, 0, p, big, None) == m.DSA_E_UNSUPPORTED

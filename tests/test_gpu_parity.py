@@ -142,11 +142,13 @@ def _synthetic_score_rows():
     return out
 
 
-@pytest.mark.parametrize("k", [2048, 64, 1])
-def test_topk_exact(dsa, k):
+@pytest.mark.parametrize("k,copies", [(2048, 1), (64, 1), (1, 1), (4096, 1), (2048, 6)])
+def test_topk_exact(dsa, k, copies):
     """Selection is integer work: the GPU set must equal the oracle's bit for bit
-    on the same float32 scores (synthetic rows, not produced by the HIP path)."""
-    rows = _synthetic_score_rows()
+    on the same float32 scores (synthetic rows, not produced by the HIP path).
+    One copy of the rows is few enough that each row is split over several
+    blocks; six copies (162 rows) run one block per row."""
+    rows = _synthetic_score_rows() * copies
     maxt = max(t for t, _ in rows)
     ld = maxt + 1
     R = len(rows)
