@@ -150,10 +150,11 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
   // product, so it must hold finite data, which an unused page need not.
   const int row0 = cache_row(0);
 
-  // Prologue, ordered so that three memory latencies do not add up: the first
+  // Prologue, ordered so that the memory latencies do not add up: the first
   // block's gather positions are read straight from the index row, the rest of the
-  // row and the queries are requested at the same time, and the first gather is
-  // issued as soon as its positions arrive, before the queries have.
+  // row and the rope queries are requested at the same time, the first gather is
+  // issued as soon as its positions arrive, and the latent queries (needed only by
+  // the first block's products) last.
   constexpr int MAXL = (LOADS + NWAVE - 1) / NWAVE;  // 5 direct loads per wave and block
   uint32_t off_first[MAXL];
 #pragma unroll
@@ -173,19 +174,6 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
     const int i = tid + NT * k;
     pv[k] = i < ES ? irow[i] : -1;
   }
-  // Contraction split: half hf owns latent dims [256 hf, 256 hf + 256) (k-steps
-  // 8 hf .. 8 hf + 7, queries in registers) and rope dims [512 + 32 hf, +32)
-  // (k-step 16 + hf, queries read from LDS).
-  // registers: queries of heads 32hg + 16nt + nn, dims 256hf + 32ks + 8g .. +7
-  i32x4 qr[2][KS_LAT];
-  {
-    const uint16_t* qrow = q + ((size_t)r * H + 32 * hg) * DK + 256 * hf;
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int ks = 0; ks < KS_LAT; ++ks)
-        qr[nt][ks] = *reinterpret_cast<const i32x4*>(qrow + (16 * nt + nn) * DK + 32 * ks + 8 * g);
-  }
   // rope queries of all 128 heads (8 chunks of 16 bytes per head), bound for LDS
   constexpr int QRC = H * (RD / 8) / NT;  // 2 chunks per thread
   i32x4 qrv[QRC];
@@ -200,6 +188,22 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
       const int i = wv + j * NWAVE;
       if (i < LOADS) gather16(lat_bytes, off_first[j], lds_addr(smem + i * 1024));
     }
+  }
+  // The latent queries are requested after the first gather and the rope queries:
+  // the barrier below waits for the rope queries (they go to LDS), and a memory
+  // counter that waited for them must not also wait for 128 KB of latent queries.
+  // Contraction split: half hf owns latent dims [256 hf, 256 hf + 256) (k-steps
+  // 8 hf .. 8 hf + 7, queries in registers) and rope dims [512 + 32 hf, +32)
+  // (k-step 16 + hf, queries read from LDS).
+  // registers: queries of heads 32hg + 16nt + nn, dims 256hf + 32ks + 8g .. +7
+  i32x4 qr[2][KS_LAT];
+  {
+    const uint16_t* qrow = q + ((size_t)r * H + 32 * hg) * DK + 256 * hf;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int ks = 0; ks < KS_LAT; ++ks)
+        qr[nt][ks] = *reinterpret_cast<const i32x4*>(qrow + (16 * nt + nn) * DK + 32 * ks + 8 * g);
   }
   // Causal rule: entries outside [0, t] are padding.  An entry past t (a future
   // position the selection cannot contain) also raises the index-domain flag.
@@ -453,41 +457,43 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
 #pragma unroll
       for (int dt = 0; dt < DT_HALF; ++dt) O[hm][dt][v] *= inv;
     }
+  // Output through LDS: each wave writes its 16-head half of the 32 x 256 output
+  // tile as bf16 into its own region of the (now free) stage buffers, then reads it
+  // back as 16-byte pieces, so that each store instruction writes whole 512-byte
+  // head rows.  (Straight from the MFMA layout every lane would store 2-byte values
+  // 32 bytes apart.)
+  constexpr int EP_PITCH = 256 * 2 + 16;  // bytes per head row in LDS (bank spread)
+  static_assert(NWAVE * 16 * EP_PITCH <= 2 * STAGE, "the epilogue tiles fit the stage buffers");
+  uint8_t* ep = smem + wv * 16 * EP_PITCH;
   const int head0 = 32 * hg;
-  const int col0 = 256 * hf + nn;
-  if (splits == 1) {
-    uint16_t* orow = out + (size_t)r * H * DV;
+  uint16_t* obase = splits == 1 ? out + (size_t)r * H * DV
+                                : o_part + ((size_t)r * splits + sp) * H * DV;
+  // every wave is done with the last stage buffer before any overwrites it
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
-    for (int hm = 0; hm < 2; ++hm)
+  for (int hm = 0; hm < 2; ++hm) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        uint16_t* oh = orow + (size_t)(head0 + 16 * hm + 4 * g + v) * DV + col0;
+    for (int v = 0; v < 4; ++v)
 #pragma unroll
-        for (int dt = 0; dt < DT_HALF; ++dt) oh[16 * dt] = bf16_bits(O[hm][dt][v]);
-      }
-    if (lse != nullptr && g == 0 && hf == 0) {
+      for (int dt = 0; dt < DT_HALF; ++dt)
+        *reinterpret_cast<uint16_t*>(ep + (4 * g + v) * EP_PITCH + 2 * (16 * dt + nn)) =
+            bf16_bits(O[hm][dt][v]);
+    // the wave reads back what it wrote (LDS operations of one wave are ordered)
+    uint16_t* orow = obase + (size_t)(head0 + 16 * hm) * DV + 256 * hf;
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-        lse[(size_t)r * H + head0 + 16 * nt + nn] =
-            l_tot[nt] > 0.f ? (m_run[nt] + __log2f(l_tot[nt])) * kLn2 : -INFINITY;
+    for (int k = 0; k < 8; ++k) {
+      const int c = l + 64 * k, hr = c >> 5, j = c & 31;  // head row hr, piece j
+      const i32x4 val = *reinterpret_cast<const i32x4*>(ep + hr * EP_PITCH + 16 * j);
+      *reinterpret_cast<i32x4*>(orow + (size_t)hr * DV + 8 * j) = val;
     }
-  } else {
-    // the split's normalised output, rounded to bf16 (its lse stays fp32)
-    uint16_t* prow = o_part + ((size_t)r * splits + sp) * H * DV;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next writes
+  }
+  float* lrow = splits == 1 ? lse : lse_part + ((size_t)r * splits + sp) * H - (size_t)r * H;
+  if (lrow != nullptr && g == 0 && hf == 0) {
 #pragma unroll
-    for (int hm = 0; hm < 2; ++hm)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        uint16_t* ph = prow + (size_t)(head0 + 16 * hm + 4 * g + v) * DV + col0;
-#pragma unroll
-        for (int dt = 0; dt < DT_HALF; ++dt) ph[16 * dt] = bf16_bits(O[hm][dt][v]);
-      }
-    if (g == 0 && hf == 0) {
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-        lse_part[((size_t)r * splits + sp) * H + head0 + 16 * nt + nn] =
-            l_tot[nt] > 0.f ? (m_run[nt] + __log2f(l_tot[nt])) * kLn2 : -INFINITY;
-    }
+    for (int nt = 0; nt < 2; ++nt)
+      lrow[(size_t)r * H + head0 + 16 * nt + nn] =
+          l_tot[nt] > 0.f ? (m_run[nt] + __log2f(l_tot[nt])) * kLn2 : -INFINITY;
   }
 }
 
