@@ -25,16 +25,6 @@ namespace {
 constexpr int IH = kIdxHeads;  // 64
 constexpr int ID = kIdxDim;    // 128
 
-// Fragment of one 128-byte fp8 row for lane group g in the "split" layout: bytes
-// [16 g, 16 g + 16) and [64 + 16 g, 64 + 16 g + 16).  The MFMA contracts over the
-// 128 bytes in any order as long as both operands use the same one; with this
-// order each 16-byte load of the 16 rows of a tile covers whole 64-byte sectors.
-__device__ __forceinline__ i32x8 load_frag_split(const uint8_t* row, int g) {
-  const i32x4 a = *reinterpret_cast<const i32x4*>(row + 16 * g);
-  const i32x4 b = *reinterpret_cast<const i32x4*>(row + 64 + 16 * g);
-  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
 __device__ __forceinline__ i32x8 load_frag32(const uint8_t* p) {
   const i32x4* v = reinterpret_cast<const i32x4*>(p);
   i32x4 a = v[0];
@@ -74,8 +64,8 @@ __device__ __forceinline__ float reduce_groups(float p0, float p1, float p2, flo
   return keep + xor16(send);
 }
 
-// SPLIT: the queries in the load_frag_split byte order (else contiguous 32 bytes)
-template <bool SPLIT = false>
+// The query row r as MFMA operands (lane: head 16 mt + (lane & 15), bytes
+// [32 g, 32 g + 32)) and the lane's 16 products head weight x query scale.
 __device__ __forceinline__ void load_query(const uint8_t* __restrict__ q_idx,
                                            const float* __restrict__ q_scale,
                                            const float* __restrict__ w, int r, i32x8 (&qa)[4],
@@ -83,9 +73,7 @@ __device__ __forceinline__ void load_query(const uint8_t* __restrict__ q_idx,
   const int l = lane_id(), g = l >> 4, n = l & 15;
   const uint8_t* qr = q_idx + (size_t)r * IH * ID;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-    qa[mt] = SPLIT ? load_frag_split(qr + (16 * mt + n) * ID, g)
-                   : load_frag32(qr + (16 * mt + n) * ID + 32 * g);
+  for (int mt = 0; mt < 4; ++mt) qa[mt] = load_frag32(qr + (16 * mt + n) * ID + 32 * g);
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -93,84 +81,6 @@ __device__ __forceinline__ void load_query(const uint8_t* __restrict__ q_idx,
       const int h = 16 * mt + 4 * g + v;
       wq[mt * 4 + v] = w[(size_t)r * IH + h] * q_scale[(size_t)r * IH + h];
     }
-}
-
-// ---------------------------------------------------------------------------
-// Decode tiling: one query row per block row, keys streamed from HBM.  Each wave
-// walks 64-key groups (interleaved across the block's waves) with the loads of the
-// next DEPTH - 1 groups in flight while the current one is multiplied; fragments
-// use the sector-aligned split byte order.
-// Grid: num_rows * key_blocks blocks (row-major), WAVES waves each.
-// ---------------------------------------------------------------------------
-template <int WAVES, int KPB, int DEPTH, bool PAGED>
-__global__ __launch_bounds__(WAVES * 64) void indexer_fp8_decode_kernel(
-    const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale,
-    const float* __restrict__ w, const uint8_t* __restrict__ k_idx,
-    const float* __restrict__ k_scale, const int32_t* __restrict__ row_seq,
-    const int32_t* __restrict__ row_pos, int B, int N, int nkb, float* __restrict__ scores,
-    int64_t ld, PageMap pm, ClearWords clear) {
-  if (blockIdx.x == 0)  // words a following launch needs zeroed
-    for (int i = threadIdx.x; i < clear.n; i += WAVES * 64) clear.ptr[i] = 0u;
-  const int r = blockIdx.x / nkb;
-  const int kb0 = (blockIdx.x - r * nkb) * KPB;
-  const int b = row_seq[r], t = row_pos[r];
-  if (b < 0 || b >= B || t < 0 || t >= N || (int64_t)t >= ld || kb0 > t) return;
-  const int kend = min(kb0 + KPB, t + 1);
-  const int l = lane_id(), wv = threadIdx.x >> 6, g = l >> 4, n = l & 15;
-
-  const int k0 = kb0 + 64 * wv;
-  if (k0 >= kend) return;
-
-  i32x8 qa[4];
-  float wq[16];
-  load_query<true>(q_idx, q_scale, w, r, qa, wq);
-
-  // paged: the pools; contiguous: this sequence's caches
-  const uint8_t* kc = PAGED ? k_idx : k_idx + (size_t)b * N * ID;
-  const float* ksc = PAGED ? k_scale : k_scale + (size_t)b * N;
-  float* out = scores + (size_t)r * ld;
-
-  // k is a multiple of 64 and a page holds at least 64 entries, so a group's keys
-  // are consecutive rows of one page
-  auto load_group = [&](int k, i32x8(&kb)[4], float& ks) {
-    if constexpr (PAGED) {
-      const uint32_t row0 = paged_row(pm, b, k);
-      const uint8_t* gb = kc + (size_t)row0 * ID;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-        kb[kt] = load_frag_split(gb + (size_t)(min(k + 16 * kt + n, t) - k) * ID, g);
-      ks = ksc[row0 + (min(k + l, t) - k)];
-    } else {
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-        kb[kt] = load_frag_split(kc + (size_t)min(k + 16 * kt + n, t) * ID, g);
-      ks = ksc[min(k + l, t)];
-    }
-  };
-  auto compute = [&](int k, const i32x8(&kb)[4], float ks) {
-    const float p0 = head_partial(qa, wq, kb[0]);
-    const float p1 = head_partial(qa, wq, kb[1]);
-    const float p2 = head_partial(qa, wq, kb[2]);
-    const float p3 = head_partial(qa, wq, kb[3]);
-    const float s = reduce_groups(p0, p1, p2, p3) * ks;
-    if (k + l < kend) out[k + l] = s;
-  };
-  constexpr int STEP = 64 * WAVES;
-  i32x8 kr[DEPTH][4];
-  float sr[DEPTH];
-#pragma unroll
-  for (int d = 0; d < DEPTH - 1; ++d)
-    if (k0 + d * STEP < kend) load_group(k0 + d * STEP, kr[d], sr[d]);
-  for (int it = 0;; it += DEPTH) {
-#pragma unroll
-    for (int d = 0; d < DEPTH; ++d) {
-      const int k = k0 + (it + d) * STEP;
-      if (k >= kend) return;
-      const int kn = k + (DEPTH - 1) * STEP;
-      if (kn < kend) load_group(kn, kr[(d + DEPTH - 1) % DEPTH], sr[(d + DEPTH - 1) % DEPTH]);
-      compute(k, kr[d], sr[d]);
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -195,7 +105,7 @@ __device__ __forceinline__ void prefill_rows(const uint8_t* __restrict__ q_idx,
 #pragma unroll
   for (int i = 0; i < NR; ++i) load_query(q_idx, q_scale, w, rr[i], qa[i], wq[i]);
   const int klast = kend - 1;
-  // k is a multiple of 64: one page per group (see the decode kernel)
+  // k is a multiple of 64 and a page holds at least 64 entries: one page per group
   auto load_group = [&](int k, i32x8(&kb)[4], float& ks) {
     if constexpr (PAGED) {
       const uint32_t row0 = paged_row(pm, b, k);
@@ -268,6 +178,143 @@ __device__ __forceinline__ void lds_dma4(const uint8_t* base, uint32_t off, uint
 __device__ __forceinline__ uint32_t lds_u32(const void* p) {
   return __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)(p));
+}
+
+// ---------------------------------------------------------------------------
+// Decode streaming tiling: one query row per block row, SKPB keys per block.  Each
+// wave owns a ring of SDEPTH groups of 64 keys in LDS and copies its groups (the
+// block's groups wv, wv + SW, ...) HBM -> LDS with contiguous 1 KB direct loads, plus
+// the group's 64 key scales; it reads its MFMA fragments from its own ring, so the
+// loop has no block barrier (a wave waits on its own loads only).  The query row
+// comes in by direct loads too, ahead of the first groups, so that its arrival is
+// awaited with the same counter instead of a wait for every load in flight.  Inside
+// a group the 16-byte chunk c of key e sits in slot e * 8 + (c ^ (e & 7)), which
+// spreads a fragment read over the LDS banks.  Scores are staged in LDS and written
+// once the block's keys are done, so the loop's memory counter counts only the
+// copies.  Grid: num_rows * key_blocks blocks (row-major), SW waves each.
+// ---------------------------------------------------------------------------
+constexpr int SW = 4;           // waves per block
+constexpr int SKPB = 4096;      // keys per block
+constexpr int SDEPTH = 3;       // groups in a wave's ring
+constexpr int SGK = 64;         // keys per group
+constexpr int SGB = SGK * ID;   // 8 KB per group
+constexpr int SLOADS = SGB / 1024 + 1;  // direct loads per group: 8 x 1 KB of keys + the scales
+
+template <bool PAGED>
+__global__ __launch_bounds__(SW * 64) void indexer_fp8_stream_kernel(
+    const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale,
+    const float* __restrict__ w, const uint8_t* __restrict__ k_idx,
+    const float* __restrict__ k_scale, const int32_t* __restrict__ row_seq,
+    const int32_t* __restrict__ row_pos, int B, int N, int nkb, float* __restrict__ scores,
+    int64_t ld, PageMap pm, ClearWords clear) {
+  __shared__ __attribute__((aligned(16))) uint8_t kring[SW][SDEPTH][SGB];
+  __shared__ __attribute__((aligned(16))) float sring[SW][SDEPTH][SGK];
+  __shared__ __attribute__((aligned(16))) float sout[SKPB];
+  __shared__ __attribute__((aligned(16))) uint8_t qlds[IH * ID];
+  __shared__ __attribute__((aligned(16))) float wlds[2][IH];  // head weights, query scales
+  static_assert(SW * 2048 == IH * ID, "each wave copies 2 KB of the query row");
+  if (blockIdx.x == 0)  // words a following launch needs zeroed
+    for (int i = threadIdx.x; i < clear.n; i += SW * 64) clear.ptr[i] = 0u;
+  const int r = blockIdx.x / nkb;
+  const int kb0 = (blockIdx.x - r * nkb) * SKPB;
+  const int b = row_seq[r], t = row_pos[r];
+  if (b < 0 || b >= B || t < 0 || t >= N || (int64_t)t >= ld || kb0 > t) return;
+  const int kend = min(kb0 + SKPB, t + 1);
+  const int ngroups = (kend - kb0 + SGK - 1) / SGK;
+  const int l = lane_id(), g = l >> 4, n = l & 15;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int mine = ngroups > wv ? (ngroups - wv + SW - 1) / SW : 0;  // groups wv, wv + SW, ...
+
+  // this wave's 2 KB of the query row; waves 0 and 1 also the head weights and scales
+  const uint8_t* qsrc = q_idx + (size_t)r * IH * ID;
+  lds_dma16(qsrc, (uint32_t)(2048 * wv + 16 * l), lds_u32(qlds + 2048 * wv));
+  lds_dma16(qsrc, (uint32_t)(2048 * wv + 1024 + 16 * l), lds_u32(qlds + 2048 * wv + 1024));
+  if (wv < 2)
+    lds_dma4(reinterpret_cast<const uint8_t*>((wv == 0 ? w : q_scale) + (size_t)r * IH),
+             (uint32_t)(4 * l), lds_u32(wlds[wv]));
+
+  // paged: offsets from the pool bases; contiguous: from this sequence's caches
+  const uint8_t* kc = PAGED ? k_idx : k_idx + (size_t)b * N * ID;
+  const uint8_t* ksc = reinterpret_cast<const uint8_t*>(PAGED ? k_scale : k_scale + (size_t)b * N);
+  // group j of this wave into ring slot j % SDEPTH: lane l of copy i fetches the
+  // chunk whose swizzled slot is 64 i + l.  Keys past kend read key kend - 1 (their
+  // scores are never written).  A group of 64 keys lies in one page.
+  auto issue = [&](int j) {
+    const int k0 = kb0 + SGK * (wv + SW * j);
+    uint32_t base = (uint32_t)k0;
+    if constexpr (PAGED) base = paged_row(pm, b, k0);
+    const int last = kend - 1 - k0;
+    uint8_t* dst = kring[wv][j % SDEPTH];
+#pragma unroll
+    for (int i = 0; i < SGB / 1024; ++i) {
+      const int P = 64 * i + l;
+      const int e = P >> 3;
+      const int c = (P & 7) ^ (e & 7);
+      lds_dma16(kc, (base + (uint32_t)min(e, last)) * (uint32_t)ID + (uint32_t)(16 * c),
+                lds_u32(dst + 1024 * i));
+    }
+    lds_dma4(ksc, (base + (uint32_t)min(l, last)) * 4u, lds_u32(sring[wv][j % SDEPTH]));
+  };
+  const int x = n & 7;  // key & 7 for every tile's key 16 kt + n
+  const int c0 = (2 * g) ^ x, c1 = (2 * g + 1) ^ x;
+  for (int j = 0; j < SDEPTH - 1 && j < mine; ++j) issue(j);
+  // the query copies are older than the group copies just issued: wait for them,
+  // then for the other waves' (one block barrier, outside the loop)
+  const int ahead = min(mine, SDEPTH - 1);
+  if (ahead == 2)
+    asm volatile("s_waitcnt vmcnt(18)\n\ts_barrier" ::: "memory");
+  else if (ahead == 1)
+    asm volatile("s_waitcnt vmcnt(9)\n\ts_barrier" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  i32x8 qa[4];
+  float wq[16];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const uint8_t* qrow = qlds + (16 * mt + n) * ID + 32 * g;
+    const i32x4 h0 = *reinterpret_cast<const i32x4*>(qrow);
+    const i32x4 h1 = *reinterpret_cast<const i32x4*>(qrow + 16);
+    qa[mt] = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int h = 16 * mt + 4 * g + v;
+      wq[mt * 4 + v] = wlds[0][h] * wlds[1][h];
+    }
+  }
+  for (int j = 0; j < mine; ++j) {
+    if (j + SDEPTH - 1 < mine) issue(j + SDEPTH - 1);
+    // group j is in: the copies of the (up to SDEPTH - 1) later groups may still fly
+    const int later = min(mine - 1 - j, SDEPTH - 1);
+    if (later == 2)
+      asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+    else if (later == 1)
+      asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    static_assert(SLOADS == 9 && SDEPTH == 3, "wait counts above");
+    const uint8_t* kg = kring[wv][j % SDEPTH];
+    float p[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const uint8_t* row = kg + (16 * kt + n) * ID;
+      const i32x4 a0 = *reinterpret_cast<const i32x4*>(row + 16 * c0);
+      const i32x4 a1 = *reinterpret_cast<const i32x4*>(row + 16 * c1);
+      p[kt] = head_partial(qa, wq, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+    sout[SGK * (wv + SW * j) + l] = reduce_groups(p[0], p[1], p[2], p[3]) * sring[wv][j % SDEPTH][l];
+  }
+  __syncthreads();
+  // the block's scores, keys [kb0, kend)
+  float* out = scores + (size_t)r * ld + kb0;
+  const int cnt = kend - kb0;
+  const bool vec = (reinterpret_cast<uintptr_t>(out) & 15u) == 0u;
+  for (int i = 4 * (int)threadIdx.x; i < cnt; i += 4 * SW * 64) {
+    if (vec && i + 3 < cnt) {
+      *reinterpret_cast<f32x4*>(out + i) = *reinterpret_cast<const f32x4*>(sout + i);
+    } else {
+      for (int e = 0; e < 4 && i + e < cnt; ++e) out[i + e] = sout[i + e];
+    }
+  }
 }
 
 // Prefill block: PW waves x PRW query rows (fp8 queries in registers) over PKPB keys.
@@ -559,13 +606,11 @@ hipError_t launch_indexer_fp8(const dsa_rows& rows, const uint8_t* q_idx, const 
                        k_idx, k_scale, rows.row_seq, rows.row_pos, R, rows.num_seqs,
                        rows.max_ctx, ksplit, scores, ld, pm, clear);
   } else {
-    constexpr int WAVES = 4, KPB = 1024, DEPTH = 3;
-    const int nkb = (L + KPB - 1) / KPB;
-    auto kern = paged ? indexer_fp8_decode_kernel<WAVES, KPB, DEPTH, true>
-                      : indexer_fp8_decode_kernel<WAVES, KPB, DEPTH, false>;
-    hipLaunchKernelGGL(kern, dim3(R * nkb), dim3(WAVES * 64), 0, stream, q_idx, q_scale, w,
-                       k_idx, k_scale, rows.row_seq, rows.row_pos, rows.num_seqs, rows.max_ctx,
-                       nkb, scores, ld, pm, clear);
+    const int nkb = (L + SKPB - 1) / SKPB;
+    auto kern = paged ? indexer_fp8_stream_kernel<true> : indexer_fp8_stream_kernel<false>;
+    hipLaunchKernelGGL(kern, dim3(R * nkb), dim3(SW * 64), 0, stream, q_idx, q_scale, w, k_idx,
+                       k_scale, rows.row_seq, rows.row_pos, rows.num_seqs, rows.max_ctx, nkb,
+                       scores, ld, pm, clear);
   }
   return hipGetLastError();
 }

@@ -20,8 +20,8 @@ so that a score is exactly ReLU(sum_i q8_i k8_i) as the MFMA formed it (the
 epilogue adds only exact zeros).  Rows come in pairs (q, -q), so every non-zero
 dot shows up positive in one of them.  Exact sums are integers after scaling by
 2^18 (every e4m3fn value is a multiple of 2^-9), computed with int64 on the host.
-Both indexer tilings are driven (they feed the instruction's slots in different
-byte orders; the groups are the same byte runs in both).
+Both indexer tilings are driven (they stage the keys by different routes and
+must form every dot the same way).
 """
 from __future__ import annotations
 
