@@ -41,6 +41,10 @@ def _flags():
     return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
             # packed fp32 VALU ops are kept out of every kernel
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # a register array indexed at run time must show up as scratch, not be
+            # moved to LDS behind the kernels' backs (that also reads the work-group
+            # size from the dispatch packet in host memory)
+            "-mllvm", "-disable-promote-alloca-to-lds",
             "-I", INCLUDE, "-I", CSRC, "-Wno-unused-command-line-argument"]
 
 

@@ -134,38 +134,25 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
   const int sp = rest % splits;
   const int r = (rest / splits) * 8 + xcd;
   if (r >= R) return;
-  const int b = row_seq[r], t = row_pos[r];
-  if (b < 0 || b >= B || t < 0 || t >= N) return;
 
   const int ES = topk / splits;  // positions of this split
   const int nblk = ES / BE;
   const int32_t* irow = indices + (size_t)r * topk + (size_t)sp * ES;
-  // paged: offsets from the pool base (pool rows from the block table); contiguous:
-  // from this sequence's cache
-  const uint16_t* lat = PAGED ? latent : latent + (size_t)b * N * DK;
-  const uint8_t* lat_bytes = reinterpret_cast<const uint8_t*>(lat);
-  auto cache_row = [&](int p) -> int { return PAGED ? (int)paged_row(pm, b, p) : p; };
-  // Padding slots gather the sequence's own entry 0 (present, since t >= 0) and are
-  // then masked: a masked row still meets a zero softmax weight in the value
-  // product, so it must hold finite data, which an unused page need not.
-  const int row0 = cache_row(0);
 
-  // Prologue, ordered so that the memory latencies do not add up: the first
-  // block's gather positions are read straight from the index row, the rest of the
-  // row and the rope queries are requested at the same time, the first gather is
-  // issued as soon as its positions arrive, and the latent queries (needed only by
-  // the first block's products) last.
+  // Prologue, ordered so that the memory latencies do not add up.  What needs only
+  // the row goes out first, before the row's sequence and position are known: the
+  // first block's gather positions (straight from the index row), the rest of the
+  // row and the rope queries.  The first gather is issued as soon as its positions
+  // and the sequence arrive, and the latent queries (needed only by the first
+  // block's products) last.
   constexpr int MAXL = (LOADS + NWAVE - 1) / NWAVE;  // 5 direct loads per wave and block
-  uint32_t off_first[MAXL];
+  int p_first[MAXL];
 #pragma unroll
   for (int j = 0; j < MAXL; ++j) {
     const int i = wv + j * NWAVE;
     const int P = (i < LOADS ? i : 0) * 64 + l;
     const int e = (P * 3641) >> 18;  // P / 72 for P < 2304
-    const int c = kswz(e, P - e * KCH);
-    const int p = nblk > 0 ? irow[e] : 0;
-    off_first[j] = __umul24((uint32_t)((p >= 0 && p <= t) ? cache_row(p) : row0), (uint32_t)KROW) +
-                   (uint32_t)(16 * c);
+    p_first[j] = nblk > 0 ? irow[e] : 0;
   }
   constexpr int IPT = kTopk / NT;  // selected positions per thread (at most)
   int pv[IPT];
@@ -181,6 +168,30 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
   for (int k = 0; k < QRC; ++k) {
     const int c = tid + NT * k, h = c >> 3, j = c & 7;
     qrv[k] = *reinterpret_cast<const i32x4*>(q + ((size_t)r * H + h) * DK + DV + 8 * j);
+  }
+
+  const int b = row_seq[r], t = row_pos[r];
+  if (b < 0 || b >= B || t < 0 || t >= N) return;
+  // paged: offsets from the pool base (pool rows from the block table); contiguous:
+  // from this sequence's cache
+  const uint16_t* lat = PAGED ? latent : latent + (size_t)b * N * DK;
+  const uint8_t* lat_bytes = reinterpret_cast<const uint8_t*>(lat);
+  auto cache_row = [&](int p) -> int { return PAGED ? (int)paged_row(pm, b, p) : p; };
+  // Padding slots gather the sequence's own entry 0 (present, since t >= 0) and are
+  // then masked: a masked row still meets a zero softmax weight in the value
+  // product, so it must hold finite data, which an unused page need not.
+  const int row0 = cache_row(0);
+
+  uint32_t off_first[MAXL];
+#pragma unroll
+  for (int j = 0; j < MAXL; ++j) {
+    const int i = wv + j * NWAVE;
+    const int P = (i < LOADS ? i : 0) * 64 + l;
+    const int e = (P * 3641) >> 18;  // P / 72 for P < 2304
+    const int c = kswz(e, P - e * KCH);
+    const int p = p_first[j];
+    off_first[j] = __umul24((uint32_t)((p >= 0 && p <= t) ? cache_row(p) : row0), (uint32_t)KROW) +
+                   (uint32_t)(16 * c);
   }
   if (nblk > 0) {
 #pragma unroll
@@ -516,8 +527,10 @@ __global__ __launch_bounds__(CMB_T * CMB_RH) void attn_combine_kernel(
   const float* lp = lse_part + (size_t)r * splits * H + h;
   const uint16_t* op = o_part + ((size_t)r * splits * H + h) * DV + 8 * c8;
   const size_t ostride = (size_t)H * DV;
+  // one pass over batches of B8 splits, every load of a batch in flight at once;
+  // the running max M rises per batch (a batch that raises it rescales what is
+  // summed so far), so up to B8 splits take a single round trip
   float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, lp[(size_t)s * H]);
   float den = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < splits; s0 += B8) {
@@ -528,6 +541,17 @@ __global__ __launch_bounds__(CMB_T * CMB_RH) void attn_combine_kernel(
       const int s = min(s0 + i, splits - 1);
       x[i] = s0 + i < splits ? lp[(size_t)s * H] : -INFINITY;
       v[i] = *reinterpret_cast<const uint4*>(op + (size_t)s * ostride);
+    }
+    float bm = M;
+#pragma unroll
+    for (int i = 0; i < B8; ++i) bm = fmaxf(bm, x[i]);
+    if (bm > M) {
+      // everything summed so far is zero while M is still -inf
+      const float c = (M == -INFINITY) ? 0.f : __expf(M - bm);
+      den *= c;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[k] *= c;
+      M = bm;
     }
 #pragma unroll
     for (int i = 0; i < B8; ++i) {
