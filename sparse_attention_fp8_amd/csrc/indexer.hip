@@ -188,10 +188,8 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p) {
 // loop has no block barrier (a wave waits on its own loads only).  The query row
 // comes in by direct loads too, ahead of the first groups, so that its arrival is
 // awaited with the same counter instead of a wait for every load in flight.  Inside
-// a group the 16-byte chunk c of key e sits in slot e * 8 + (c ^ ((e >> 1) & 7)): a
-// fragment read (16 keys, one chunk each) then covers 16 distinct 16-byte bank
-// groups (keys e and e + 8 share the bank half that e's parity selects, and the
-// swizzle separates them), so it is free of bank conflicts.  Scores are staged in LDS and written
+// a group the 16-byte chunk c of key e sits in slot e * 8 + (c ^ (e & 7)), which
+// spreads a fragment read over the LDS banks.  Scores are staged in LDS and written
 // once the block's keys are done, so the loop's memory counter counts only the
 // copies.  Grid: num_rows * key_blocks blocks (row-major), SW waves each.
 // ---------------------------------------------------------------------------
@@ -251,13 +249,13 @@ __global__ __launch_bounds__(SW * 64) void indexer_fp8_stream_kernel(
     for (int i = 0; i < SGB / 1024; ++i) {
       const int P = 64 * i + l;
       const int e = P >> 3;
-      const int c = (P & 7) ^ ((e >> 1) & 7);
+      const int c = (P & 7) ^ (e & 7);
       lds_dma16(kc, (base + (uint32_t)min(e, last)) * (uint32_t)ID + (uint32_t)(16 * c),
                 lds_u32(dst + 1024 * i));
     }
     lds_dma4(ksc, (base + (uint32_t)min(l, last)) * 4u, lds_u32(sring[wv][j % SDEPTH]));
   };
-  const int x = n >> 1;  // (key >> 1) & 7 for every tile's key 16 kt + n
+  const int x = n & 7;  // key & 7 for every tile's key 16 kt + n
   const int c0 = (2 * g) ^ x, c1 = (2 * g + 1) ^ x;
   for (int j = 0; j < SDEPTH - 1 && j < mine; ++j) issue(j);
   // the query copies are older than the group copies just issued: wait for them,
@@ -323,9 +321,8 @@ __global__ __launch_bounds__(SW * 64) void indexer_fp8_stream_kernel(
 // The keys are staged once per block, 64 at a time, HBM -> LDS by direct loads
 // into PNBUF buffers three groups ahead; every wave reads its MFMA fragments from
 // LDS, so the block fetches each key once instead of once per wave.  Inside a
-// group, the 16-byte chunk c of key e sits in slot e * 8 + (c ^ ((e >> 1) & 7)),
-// which makes the 16 rows of a fragment read free of bank conflicts (as in the
-// decode tiling).
+// group, the 16-byte chunk c of key e sits in slot e * 8 + (c ^ (e & 7)), which
+// spreads the 16 rows of a fragment read over the LDS banks.
 constexpr int PW = 8, PRW = 2, PROWS = PW * PRW, PKPB = 1024, PG = 128, PNBUF = 4;
 constexpr int PGB = PG * ID;  // 16 KB per group
 static_assert(PGB == PW * 2048, "two 1 KB direct loads per wave and group");
@@ -412,7 +409,7 @@ void indexer_fp8_prefill_kernel(
 
   // B fragment of key tile kt: row e = 16 kt + n, bytes [32 g, 32 g + 32) = chunks
   // 2 g and 2 g + 1, each at its swizzled slot
-  const int x = n >> 1;  // (e >> 1) & 7 for every tile
+  const int x = n & 7;  // e & 7 for every tile
   const int c0 = (2 * g) ^ x, c1 = (2 * g + 1) ^ x;
 
   for (int kb0 = ks * PKPB; kb0 <= Tmax; kb0 += ksplit * PKPB) {
@@ -440,7 +437,7 @@ void indexer_fp8_prefill_kernel(
       for (int h = 0; h < 2; ++h) {
         const int P = 64 * (2 * wv + h) + l;
         const int e = P >> 3;
-        const int c = (P & 7) ^ ((e >> 1) & 7);
+        const int c = (P & 7) ^ (e & 7);
         const uint32_t off = row(min(k0 + e, klast)) * (uint32_t)ID + (uint32_t)(16 * c);
         lds_dma16(kc, off, lds_u32(&kbuf[gi % PNBUF][1024 * (2 * wv + h)]));
       }
