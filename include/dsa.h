@@ -128,10 +128,11 @@ dsa_status dsa_indexer_scores(const dsa_rows* rows, const dsa_dims* dims,
  * indices[r, 0..n) hold them in ascending order, indices[r, n..topk) hold -1.
  * Supports topk in [1, 4096] and rows of up to 131072 candidates: max_pos + 1 >
  * 131072 returns DSA_E_UNSUPPORTED before anything is enqueued.  Scores must not be
- * NaN (a NaN row gives an unspecified but in-range selection).  Calls with few
- * rows split each row over several blocks and need a workspace of
- * dsa_topk_workspace_size bytes (per-row histograms and counts, cleared by the
- * call itself); otherwise the size is 0 and workspace may be NULL.
+ * NaN (a NaN row gives an unspecified but in-range selection).  Calls with fewer
+ * than 128 rows whose max_pos + 1 exceeds 32768 split each row over several
+ * blocks and need a workspace of dsa_topk_workspace_size bytes (candidates and
+ * per-row counts, cleared by the call itself); otherwise the size is 0 and
+ * workspace may be NULL.
  * ------------------------------------------------------------------------- */
 size_t dsa_topk_workspace_size(const dsa_rows* rows, int32_t topk);
 

@@ -91,17 +91,23 @@ def test_workspace_sizes(m):
     attn = L.dsa_sparse_mla_attn_workspace_size(ctypes.byref(dec), ctypes.byref(d))
     assert attn == 32 * 8 * 128 * (512 * 2 + 4)   # 8 splits of bf16 partial outputs + fp32 lse
     fwd = L.dsa_forward_workspace_size(ctypes.byref(dec), ctypes.byref(d), 0)
-    tk = L.dsa_topk_workspace_size(ctypes.byref(dec), 2048)
-    # candidates [32 rows, 8 chunks, 4096] of 8 bytes, their counts and the per-row counts
-    assert tk == 32 * 8 * 4096 * 8 + (32 * 8 * 4 + 32 * 4 + 15) // 16 * 16
-    assert fwd >= attn + tk + 32 * 32768 * 4 + 32 * 2048 * 4
-    # rows that fill the GPU one block each, or short rows: no top-k workspace
+    # rows of up to 32768 positions take one block each (their scores fit in the
+    # block's registers): no top-k workspace, also when few rows leave CUs idle
+    assert L.dsa_topk_workspace_size(ctypes.byref(dec), 2048) == 0
+    assert fwd >= attn + 32 * 32768 * 4 + 32 * 2048 * 4
     assert L.dsa_topk_workspace_size(ctypes.byref(_rows(m, R=8192, B=1, N=8192, max_pos=8191)),
                                      2048) == 0
     assert L.dsa_topk_workspace_size(ctypes.byref(_rows(m, R=32, B=32, N=8192, max_pos=8191)),
                                      2048) == 0
+    # few longer rows are split over several blocks each
+    d128 = _rows(m, R=8, B=8, N=131072, max_pos=131071)
+    tk = L.dsa_topk_workspace_size(ctypes.byref(d128), 2048)
+    # candidates [8 rows, 32 chunks, 4096] of 8 bytes, their counts and the per-row counts
+    assert tk == 8 * 32 * 4096 * 8 + (8 * 32 * 4 + 8 * 4 + 15) // 16 * 16
+    assert L.dsa_topk_workspace_size(ctypes.byref(_rows(m, R=128, B=128, N=131072,
+                                                        max_pos=131071)), 2048) == 0
     p = ctypes.c_void_p(16)
-    assert L.dsa_topk(ctypes.byref(dec), 2048, p, 32768, p, p, tk - 1, None) == m.DSA_E_WORKSPACE
+    assert L.dsa_topk(ctypes.byref(d128), 2048, p, 131072, p, p, tk - 1, None) == m.DSA_E_WORKSPACE
     pre = _rows(m, R=131072, B=1, N=131072, max_pos=131071)
     w = L.dsa_forward_workspace_size(ctypes.byref(pre), ctypes.byref(d), 8192)
     assert w >= 8192 * 131072 * 4 and w < 8192 * 131072 * 4 + 8192 * 2048 * 4 + (1 << 20)
