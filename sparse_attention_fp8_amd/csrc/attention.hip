@@ -495,7 +495,9 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(
     for (int k = 0; k < 8; ++k) {
       const int c = l + 64 * k, hr = c >> 5, j = c & 31;  // head row hr, piece j
       const i32x4 val = *reinterpret_cast<const i32x4*>(ep + hr * EP_PITCH + 16 * j);
-      *reinterpret_cast<i32x4*>(orow + (size_t)hr * DV + 8 * j) = val;
+      // streamed out: a split's partials are read once, by the combine, and the
+      // output by the caller's next step; neither is worth keeping in the caches
+      __builtin_nontemporal_store(val, reinterpret_cast<i32x4*>(orow + (size_t)hr * DV + 8 * j));
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next writes
   }
@@ -540,7 +542,8 @@ __global__ __launch_bounds__(CMB_T * CMB_RH) void attn_combine_kernel(
     for (int i = 0; i < B8; ++i) {
       const int s = min(s0 + i, splits - 1);
       x[i] = s0 + i < splits ? lp[(size_t)s * H] : -INFINITY;
-      v[i] = *reinterpret_cast<const uint4*>(op + (size_t)s * ostride);
+      const i32x4 raw = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(op + (size_t)s * ostride));
+      v[i] = make_uint4((uint32_t)raw[0], (uint32_t)raw[1], (uint32_t)raw[2], (uint32_t)raw[3]);
     }
     float bm = M;
 #pragma unroll

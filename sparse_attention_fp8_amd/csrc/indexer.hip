@@ -164,6 +164,19 @@ __device__ __forceinline__ void lds_dma16(const uint8_t* base, uint32_t off, uin
       : "v"(off), "s"(base), "s"(lds)
       : "memory");
 }
+// The same with the non-temporal hint, for bytes read once per call (a decode row's
+// keys): they stream through the caches without displacing what is reused.
+__device__ __forceinline__ void lds_dma16_nt(const uint8_t* base, uint32_t off, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "global_load_lds_dwordx4 %1, %2 nt\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off), "s"(base), "s"(lds)
+      : "memory");
+}
 __device__ __forceinline__ void lds_dma4(const uint8_t* base, uint32_t off, uint32_t lds) {
   uint32_t saved;
   asm volatile(
@@ -250,7 +263,7 @@ __global__ __launch_bounds__(SW * 64) void indexer_fp8_stream_kernel(
       const int P = 64 * i + l;
       const int e = P >> 3;
       const int c = (P & 7) ^ (e & 7);
-      lds_dma16(kc, (base + (uint32_t)min(e, last)) * (uint32_t)ID + (uint32_t)(16 * c),
+      lds_dma16_nt(kc, (base + (uint32_t)min(e, last)) * (uint32_t)ID + (uint32_t)(16 * c),
                 lds_u32(dst + 1024 * i));
     }
     lds_dma4(ksc, (base + (uint32_t)min(l, last)) * 4u, lds_u32(sring[wv][j % SDEPTH]));
