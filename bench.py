@@ -418,16 +418,22 @@ def time_training(dsa, st, K):
     i = st.inp
     fwd = lambda: dsa.indexer_loss(st.rows, i.q, i.latent, st.idx, st.lse, c.scale, st.scores,
                                    loss=loss, dscores=dsc, workspace=ws)
+    # one row per sequence: no key is selected twice, so the smallest backward
+    # workspace (no fixed-point accumulators) gives the deterministic result
+    ws_b = torch.empty(dsa.indexer_backward_workspace_size(st.rows, shared_keys=0),
+                       dtype=torch.uint8, device="cuda")
     bwd = lambda: dsa.indexer_backward(st.rows, i.q_idx, i.q_scale, i.w, i.k_idx, i.k_scale,
-                                       st.idx, dsc, dq, dw, dk)
+                                       st.idx, dsc, dq, dw, dk, workspace=ws_b)
     dsc_d = torch.empty_like(st.scores)
     ws_d = torch.empty(max(dsa.indexer_loss_dense_workspace_size(st.rows), 1), dtype=torch.uint8,
                        device="cuda")
     dense = lambda: dsa.indexer_loss_dense(st.rows, i.q, i.latent, c.scale, st.scores, loss=loss,
                                            dscores=dsc_d, workspace=ws_d)
     out = {}
+    ws_bd = torch.empty(dsa.indexer_backward_dense_workspace_size(st.rows, shared_keys=0),
+                        dtype=torch.uint8, device="cuda")
     bwd_d = lambda: dsa.indexer_backward_dense(st.rows, i.q_idx, i.q_scale, i.w, i.k_idx,
-                                               i.k_scale, dsc_d, dq, dw, dk)
+                                               i.k_scale, dsc_d, dq, dw, dk, workspace=ws_bd)
     for name, fn in (("loss", fwd), ("backward", bwd), ("loss_dense", dense),
                      ("backward_dense", bwd_d)):
         for _ in range(3):
@@ -459,7 +465,7 @@ def time_training(dsa, st, K):
     out["backward_dense"].update({"fp32_tflops": fl_bd / out["backward_dense"]["ms"] / 1e9,
                                   "frac_of_fp32_vector_peak": fl_bd / out["backward_dense"]["ms"]
                                   / 1e9 / 157.3})
-    del dk, dq, dw, ws, dsc, loss, dsc_d, ws_d
+    del dk, dq, dw, ws, dsc, loss, dsc_d, ws_d, ws_b, ws_bd
     torch.cuda.empty_cache()
     return out
 

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define DSA_API_VERSION 1
+#define DSA_API_VERSION 2
 
 typedef enum dsa_status {
   DSA_OK = 0,
@@ -320,10 +320,31 @@ dsa_status dsa_project_append_paged(const dsa_rows* rows, const dsa_dims* dims,
  *   dk[b,s_i,:]  += dscores[r,i] * w[r,j] * m * (q_scale q_idx[r,j,:])
  * i.e. the gradients of sum_i dscores[r,i] I[r,s_i] with respect to w and the
  * dequantised indexer queries and keys.  dq [R, H_I, d_I], dw [R, H_I] and
- * dk [B, N, d_I] are fp32 and ACCUMULATED (the caller zeroes them); the additions
- * are atomic, so their order, and the last bits, vary from run to run.  The dots
- * are the forward's (the fp8 MFMA's dots, see dsa_indexer_scores); the products
- * run in fp32.
+ * dk [B, N, d_I] are fp32 and ACCUMULATED (the caller zeroes them).  The dots are
+ * the forward's (the fp8 MFMA's dots, see dsa_indexer_scores); the products run in
+ * fp32.  Contiguous caches only.
+ *
+ * Every sum is formed in an order fixed by the call's shape, so the outputs are the
+ * same bits from run to run: dq and dw from per-chunk sums added in chunk order;
+ * dk of a key selected once in the call by its one writer; dk of a key selected
+ * more than once (rows of one sequence sharing keys, or an index list that repeats
+ * a position) as an exact 64-bit fixed-point sum, added into dk once.  The
+ * fixed-point step is 2^-s for the largest s with (largest selection count) x
+ * (bound on one contribution) < 2^62; the bound is max |dscores| over the call
+ * times the largest over rows of max_d sum_j |w[r,j]| |q_scale q_idx[r,j,d]|, so
+ * each contribution is rounded to within 2^-(s+1) and no sum overflows.
+ *
+ * Workspace (dsa_indexer_backward_workspace_size(rows, dims, shared_keys)): the
+ * selection counts of the B (max_pos + 1) keys, the per-chunk sums of dq and dw,
+ * and room for shared_keys fixed-point accumulators (1 KiB each); shared_keys = -1
+ * gives room for the most the call's shape allows, min(B (max_pos + 1), R k / 2).
+ * The call takes any ws_bytes from the size for shared_keys = 0 up, and uses what
+ * is left for accumulators.  Keys selected more than once beyond those
+ * accumulators, and all of them when the bound is not finite (inf or NaN inputs),
+ * are added into dk with fp32 atomics, whose order and last bits vary.  A call in
+ * which no key is selected twice (one row per sequence, as at decode) is exact and
+ * deterministic with shared_keys = 0.  Below that size: DSA_E_WORKSPACE.
+ * max_pos + 1 <= 131072 and num_seqs * (max_pos + 1) < 2^31, else DSA_E_UNSUPPORTED.
  * ------------------------------------------------------------------------- */
 size_t dsa_indexer_loss_workspace_size(const dsa_rows* rows, const dsa_dims* dims);
 
@@ -360,19 +381,27 @@ dsa_status dsa_indexer_loss_dense(const dsa_rows* rows, const dsa_dims* dims, co
  * indexed by position (the dscores of dsa_indexer_loss_dense):
  *   dw[r,j] += dscores[r,s] max(d, 0),  dq[r,j,:] += dscores[r,s] w[r,j] m k_s,
  *   dk[b,s,:] += dscores[r,s] w[r,j] m q_j          for all s <= t(r)
- * Same formats, accumulation (atomic, caller-zeroed) and arithmetic as
- * dsa_indexer_backward.  Contiguous caches; production dims. */
+ * Same formats, accumulation (caller-zeroed), summation order, workspace rules and
+ * arithmetic as dsa_indexer_backward, with t + 1 entries per row in place of k
+ * (shared_keys = -1 here means min(B (max_pos + 1), R (max_pos + 1) / 2)).
+ * Contiguous caches; production dims. */
+size_t dsa_indexer_backward_dense_workspace_size(const dsa_rows* rows, const dsa_dims* dims,
+                                                 int64_t shared_keys);
+
 dsa_status dsa_indexer_backward_dense(const dsa_rows* rows, const dsa_dims* dims, const void* q_idx,
                                       const float* q_scale, const float* w, const void* k_idx,
                                       const float* k_scale, const float* dscores,
                                       int64_t ld_dscores, float* dq, float* dw, float* dk,
-                                      void* stream);
+                                      void* workspace, size_t ws_bytes, void* stream);
+
+size_t dsa_indexer_backward_workspace_size(const dsa_rows* rows, const dsa_dims* dims,
+                                           int64_t shared_keys);
 
 dsa_status dsa_indexer_backward(const dsa_rows* rows, const dsa_dims* dims, const void* q_idx,
                                 const float* q_scale, const float* w, const void* k_idx,
                                 const float* k_scale, const int32_t* indices,
                                 const float* dscores, float* dq, float* dw, float* dk,
-                                void* stream);
+                                void* workspace, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Masked MHA mode for short prefill (DeepSeek-V3.2-Exp paper, section 3: short-

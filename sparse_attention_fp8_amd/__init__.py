@@ -21,6 +21,7 @@ __all__ = [
     "sparse_mla_attn_workspace_size", "project_append", "project_append_workspace_size",
     "pages_struct", "indexer_scores_paged", "sparse_mla_attn_paged", "forward_paged",
     "project_append_paged", "indexer_loss", "indexer_loss_workspace_size", "indexer_backward",
+    "indexer_backward_workspace_size", "indexer_backward_dense_workspace_size",
     "mha_prefill", "mha_prefill_workspace_size",
     "DSAError", "EXPORTED_SYMBOLS",
 ]
@@ -37,6 +38,7 @@ EXPORTED_SYMBOLS = [
     "dsa_project_append_workspace_size", "dsa_project_append", "dsa_indexer_scores_paged",
     "dsa_sparse_mla_attn_paged", "dsa_forward_paged", "dsa_project_append_paged",
     "dsa_indexer_loss_workspace_size", "dsa_indexer_loss", "dsa_indexer_backward",
+    "dsa_indexer_backward_workspace_size", "dsa_indexer_backward_dense_workspace_size",
     "dsa_indexer_loss_dense_workspace_size", "dsa_indexer_loss_dense", "dsa_indexer_backward_dense",
     "dsa_mha_prefill_workspace_size", "dsa_mha_prefill",
     "dsa_forward_noalloc", "dsa_check_index_domain", "dsa_status_string", "dsa_last_error",
@@ -99,11 +101,16 @@ def _load() -> ctypes.CDLL:
     L.dsa_indexer_loss_workspace_size.argtypes = [R, D]
     L.dsa_indexer_loss_workspace_size.restype = sz
     L.dsa_indexer_loss.argtypes = [R, D, vp, vp, vp, vp, f32, vp, i64, vp, vp, vp, sz, vp]
-    L.dsa_indexer_backward.argtypes = [R, D] + [vp] * 10 + [vp]
+    L.dsa_indexer_backward_workspace_size.argtypes = [R, D, i64]
+    L.dsa_indexer_backward_workspace_size.restype = sz
+    L.dsa_indexer_backward.argtypes = [R, D] + [vp] * 10 + [vp, sz, vp]
     L.dsa_indexer_loss_dense_workspace_size.argtypes = [R, D]
     L.dsa_indexer_loss_dense_workspace_size.restype = sz
     L.dsa_indexer_loss_dense.argtypes = [R, D, vp, vp, f32, vp, i64, vp, vp, vp, sz, vp]
-    L.dsa_indexer_backward_dense.argtypes = [R, D, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp]
+    L.dsa_indexer_backward_dense_workspace_size.argtypes = [R, D, i64]
+    L.dsa_indexer_backward_dense_workspace_size.restype = sz
+    L.dsa_indexer_backward_dense.argtypes = [R, D, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz,
+                                             vp]
     L.dsa_mha_prefill_workspace_size.argtypes = [R, D]
     L.dsa_mha_prefill_workspace_size.restype = sz
     L.dsa_mha_prefill.argtypes = [R, D, vp, vp, vp, vp, vp, f32, vp, vp, vp, sz, vp]
@@ -635,10 +642,32 @@ def indexer_loss_dense(rows: _Rows, q, latent, softmax_scale: float, scores,
     return loss, dscores
 
 
+def indexer_backward_workspace_size(rows: _Rows, dims: Dims = PRODUCTION_DIMS,
+                                    shared_keys: int = -1) -> int:
+    ds = dims_struct(dims)
+    return int(lib.dsa_indexer_backward_workspace_size(ctypes.byref(rows), ctypes.byref(ds),
+                                                       int(shared_keys)))
+
+
+def indexer_backward_dense_workspace_size(rows: _Rows, dims: Dims = PRODUCTION_DIMS,
+                                          shared_keys: int = -1) -> int:
+    ds = dims_struct(dims)
+    return int(lib.dsa_indexer_backward_dense_workspace_size(ctypes.byref(rows),
+                                                             ctypes.byref(ds), int(shared_keys)))
+
+
+def _bwd_workspace(workspace, need, device):
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    _dev(workspace, torch.uint8, "workspace")
+    return workspace
+
+
 def indexer_backward(rows: _Rows, q_idx, q_scale, w, k_idx, k_scale, indices, dscores, dq, dw,
-                     dk, dims: Dims = PRODUCTION_DIMS):
+                     dk, dims: Dims = PRODUCTION_DIMS, workspace: Optional[torch.Tensor] = None):
     """dsa_indexer_backward: adds the gradients into dq [R,H_I,d_I], dw [R,H_I] and
-    dk [B,N,d_I] (fp32, zeroed by the caller)."""
+    dk [B,N,d_I] (fp32, zeroed by the caller).  Without a workspace, one of the full
+    size (room for every key the call could select twice) is allocated."""
     R = rows.num_rows
     for t, dt, name in ((q_idx, torch.uint8, "q_idx"), (q_scale, torch.float32, "q_scale"),
                         (w, torch.float32, "w"), (k_idx, torch.uint8, "k_idx"),
@@ -653,18 +682,21 @@ def indexer_backward(rows: _Rows, q_idx, q_scale, w, k_idx, k_scale, indices, ds
     _shape(dscores, (R, dims.topk), "dscores")
     _caches(rows, dims, k_idx, k_scale)
     _shape(dk, (rows.num_seqs, rows.max_ctx, dims.idx_dim), "dk")
+    workspace = _bwd_workspace(workspace, indexer_backward_workspace_size(rows, dims), dq.device)
     ds = dims_struct(dims)
     _check(lib.dsa_indexer_backward(ctypes.byref(rows), ctypes.byref(ds), _ptr(q_idx),
                                     _ptr(q_scale), _ptr(w), _ptr(k_idx), _ptr(k_scale),
                                     _ptr(indices), _ptr(dscores), _ptr(dq), _ptr(dw), _ptr(dk),
-                                    _stream()))
+                                    _ptr(workspace), workspace.numel(), _stream()))
     return dq, dw, dk
 
 
 def indexer_backward_dense(rows: _Rows, q_idx, q_scale, w, k_idx, k_scale, dscores, dq, dw, dk,
-                           dims: Dims = PRODUCTION_DIMS):
+                           dims: Dims = PRODUCTION_DIMS,
+                           workspace: Optional[torch.Tensor] = None):
     """dsa_indexer_backward_dense: the dense warm-up loss's dscores [R, ld] (by position)
-    into dq, dw and dk (fp32, accumulated; zeroed by the caller)."""
+    into dq, dw and dk (fp32, accumulated; zeroed by the caller).  Without a
+    workspace, one of the full size is allocated."""
     R = rows.num_rows
     for t, dt, name in ((q_idx, torch.uint8, "q_idx"), (q_scale, torch.float32, "q_scale"),
                         (w, torch.float32, "w"), (k_idx, torch.uint8, "k_idx"),
@@ -678,11 +710,14 @@ def indexer_backward_dense(rows: _Rows, q_idx, q_scale, w, k_idx, k_scale, dscor
     _shape(dscores, (R, None), "dscores")
     _caches(rows, dims, k_idx, k_scale)
     _shape(dk, (rows.num_seqs, rows.max_ctx, dims.idx_dim), "dk")
+    workspace = _bwd_workspace(workspace, indexer_backward_dense_workspace_size(rows, dims),
+                               dq.device)
     ds = dims_struct(dims)
     _check(lib.dsa_indexer_backward_dense(ctypes.byref(rows), ctypes.byref(ds), _ptr(q_idx),
                                           _ptr(q_scale), _ptr(w), _ptr(k_idx), _ptr(k_scale),
                                           _ptr(dscores), dscores.shape[1], _ptr(dq), _ptr(dw),
-                                          _ptr(dk), _stream()))
+                                          _ptr(dk), _ptr(workspace), workspace.numel(),
+                                          _stream()))
     return dq, dw, dk
 
 

@@ -521,24 +521,54 @@ dsa_status dsa_indexer_loss_dense(const dsa_rows* rows, const dsa_dims* dims, co
   return err == hipSuccess ? DSA_OK : hip_fail(err, "dense indexer loss launch");
 }
 
-dsa_status dsa_indexer_backward_dense(const dsa_rows* rows, const dsa_dims* dims, const void* q_idx,
-                                      const float* q_scale, const float* w, const void* k_idx,
-                                      const float* k_scale, const float* dscores,
-                                      int64_t ld_dscores, float* dq, float* dw, float* dk,
-                                      void* stream) {
+namespace {
+// checks shared by the two backward calls
+dsa_status check_backward(const dsa_rows* rows, const dsa_dims* dims) {
   dsa_status st = check_rows(rows);
   if (st != DSA_OK) return st;
   if (dims == nullptr) return fail(DSA_E_INVALID, "dims is NULL");
   if (!is_production(*dims))
     return fail(DSA_E_UNSUPPORTED, "the indexer backward supports the production dims only");
+  if ((int64_t)rows->max_pos + 1 > dsa::kTopkMaxPositions)
+    return fail(DSA_E_UNSUPPORTED, "the indexer backward takes rows of up to %d positions",
+                dsa::kTopkMaxPositions);
+  if ((int64_t)rows->num_seqs * ((int64_t)rows->max_pos + 1) > INT32_MAX)
+    return fail(DSA_E_UNSUPPORTED, "the indexer backward needs num_seqs * (max_pos + 1) < 2^31");
+  return DSA_OK;
+}
+}  // namespace
+
+size_t dsa_indexer_backward_workspace_size(const dsa_rows* rows, const dsa_dims* dims,
+                                           int64_t shared_keys) {
+  if (check_rows(rows) != DSA_OK || dims == nullptr || !is_production(*dims)) return 0;
+  return dsa::indexer_backward_workspace_bytes(*rows, dims->topk, false, shared_keys);
+}
+
+size_t dsa_indexer_backward_dense_workspace_size(const dsa_rows* rows, const dsa_dims* dims,
+                                                 int64_t shared_keys) {
+  if (check_rows(rows) != DSA_OK || dims == nullptr || !is_production(*dims)) return 0;
+  return dsa::indexer_backward_workspace_bytes(*rows, dims->topk, true, shared_keys);
+}
+
+dsa_status dsa_indexer_backward_dense(const dsa_rows* rows, const dsa_dims* dims, const void* q_idx,
+                                      const float* q_scale, const float* w, const void* k_idx,
+                                      const float* k_scale, const float* dscores,
+                                      int64_t ld_dscores, float* dq, float* dw, float* dk,
+                                      void* workspace, size_t ws_bytes, void* stream) {
+  dsa_status st = check_backward(rows, dims);
+  if (st != DSA_OK) return st;
   if (rows->num_rows == 0) return DSA_OK;
   if (!q_idx || !q_scale || !w || !k_idx || !k_scale || !dscores || !dq || !dw || !dk)
     return fail(DSA_E_INVALID, "NULL tensor pointer");
   if (ld_dscores < (int64_t)rows->max_pos + 1)
     return fail(DSA_E_INVALID, "ld_dscores < max_pos + 1");
+  const size_t need = dsa::indexer_backward_workspace_bytes(*rows, dims->topk, true, 0);
+  if (workspace == nullptr || ws_bytes < need)
+    return fail(DSA_E_WORKSPACE, "the dense indexer backward needs at least %zu workspace bytes, got %zu",
+                need, ws_bytes);
   const hipError_t err = dsa::launch_indexer_backward_dense(
       *rows, static_cast<const uint8_t*>(q_idx), q_scale, w, static_cast<const uint8_t*>(k_idx),
-      k_scale, dscores, ld_dscores, dq, dw, dk, as_stream(stream));
+      k_scale, dscores, ld_dscores, dq, dw, dk, workspace, ws_bytes, as_stream(stream));
   return err == hipSuccess ? DSA_OK : hip_fail(err, "dense indexer backward launch");
 }
 
@@ -546,18 +576,19 @@ dsa_status dsa_indexer_backward(const dsa_rows* rows, const dsa_dims* dims, cons
                                 const float* q_scale, const float* w, const void* k_idx,
                                 const float* k_scale, const int32_t* indices,
                                 const float* dscores, float* dq, float* dw, float* dk,
-                                void* stream) {
-  dsa_status st = check_rows(rows);
+                                void* workspace, size_t ws_bytes, void* stream) {
+  dsa_status st = check_backward(rows, dims);
   if (st != DSA_OK) return st;
-  if (dims == nullptr) return fail(DSA_E_INVALID, "dims is NULL");
-  if (!is_production(*dims))
-    return fail(DSA_E_UNSUPPORTED, "the indexer backward supports the production dims only");
   if (rows->num_rows == 0) return DSA_OK;
   if (!q_idx || !q_scale || !w || !k_idx || !k_scale || !indices || !dscores || !dq || !dw || !dk)
     return fail(DSA_E_INVALID, "NULL tensor pointer");
+  const size_t need = dsa::indexer_backward_workspace_bytes(*rows, dims->topk, false, 0);
+  if (workspace == nullptr || ws_bytes < need)
+    return fail(DSA_E_WORKSPACE, "the indexer backward needs at least %zu workspace bytes, got %zu",
+                need, ws_bytes);
   const hipError_t err = dsa::launch_indexer_backward(
       *rows, static_cast<const uint8_t*>(q_idx), q_scale, w, static_cast<const uint8_t*>(k_idx),
-      k_scale, indices, dscores, dq, dw, dk, as_stream(stream));
+      k_scale, indices, dscores, dq, dw, dk, workspace, ws_bytes, as_stream(stream));
   return err == hipSuccess ? DSA_OK : hip_fail(err, "indexer backward launch");
 }
 

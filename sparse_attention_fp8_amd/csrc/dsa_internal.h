@@ -92,10 +92,15 @@ hipError_t launch_project(const dsa_rows& rows, int d_model, const uint16_t* h, 
 
 size_t indexer_loss_workspace_bytes(int num_rows, int topk);
 size_t indexer_loss_dense_workspace_bytes(int num_rows, int max_pos);
+// Backward workspace: shared_keys accumulators for keys selected more than once
+// (-1: the most the call's shape allows).
+size_t indexer_backward_workspace_bytes(const dsa_rows& rows, int topk, bool dense,
+                                        int64_t shared_keys);
 hipError_t launch_indexer_backward_dense(const dsa_rows& rows, const uint8_t* q_idx,
                                          const float* q_scale, const float* w, const uint8_t* k_idx,
                                          const float* k_scale, const float* dscores, int64_t ld,
-                                         float* dq, float* dw, float* dk, hipStream_t stream);
+                                         float* dq, float* dw, float* dk, void* workspace,
+                                         size_t ws_bytes, hipStream_t stream);
 hipError_t launch_indexer_loss_dense(const dsa_rows& rows, const void* q, const void* latent,
                                      float softmax_scale, const float* scores, int64_t ld,
                                      float* loss, float* dscores, void* workspace,
@@ -110,7 +115,7 @@ hipError_t launch_indexer_backward(const dsa_rows& rows, const uint8_t* q_idx,
                                    const float* q_scale, const float* w, const uint8_t* k_idx,
                                    const float* k_scale, const int32_t* indices,
                                    const float* dscores, float* dq, float* dw, float* dk,
-                                   hipStream_t stream, const PageMap& pm = PageMap());
+                                   void* workspace, size_t ws_bytes, hipStream_t stream);
 
 size_t mha_workspace_bytes(int num_rows, int num_seqs, int max_pos);
 

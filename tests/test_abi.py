@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol(m):
 
 
 def test_status_strings_and_version(m):
-    assert m.lib.dsa_api_version() == 1
+    assert m.lib.dsa_api_version() == 2
     for st in range(5):
         assert m.lib.dsa_status_string(st).decode().startswith("DSA_")
 
@@ -114,6 +114,27 @@ def test_workspace_sizes(m):
     f32 = m.dims_struct(m.Dims(4, 32, 16, 80, 64, 64, True))
     tiny = _rows(m, R=256, B=1, N=256, max_pos=255)
     assert L.dsa_sparse_mla_attn_workspace_size(ctypes.byref(tiny), ctypes.byref(f32)) == 0
+    # backward: header, per-row flags, key counts and accumulator slots of the B (max_pos + 1) keys,
+    # chunk sums of dq and dw (R rows x E chunks x (64 x 128 + 64) floats, E > 1), then
+    # the accumulators (4 + 1024 bytes each)
+    a256 = lambda x: (x + 255) // 256 * 256
+    def bwd_size(R, B, P, E, cap):
+        base = 256 + a256(R * 4) + a256((B * P + 3) // 4 * 16) + a256(B * P * 4) + \
+            (a256(R * E * 8256 * 4) if E > 1 else 0)
+        return base + a256(cap * 4) + cap * 1024
+    sz = lambda rows, k: L.dsa_indexer_backward_workspace_size(ctypes.byref(rows), ctypes.byref(d), k)
+    szd = lambda rows, k: L.dsa_indexer_backward_dense_workspace_size(ctypes.byref(rows),
+                                                                      ctypes.byref(d), k)
+    # decode 32K: 8 chunks of 256 entries per row; at most R k / 2 keys selected twice
+    assert sz(dec, 0) == bwd_size(32, 32, 32768, 8, 0)
+    assert sz(dec, -1) == bwd_size(32, 32, 32768, 8, 32 * 2048 // 2)
+    assert sz(dec, 100) == bwd_size(32, 32, 32768, 8, 100)
+    assert szd(dec, -1) == bwd_size(32, 32, 32768, 8, 32 * 32768 // 2)
+    # prefill 8K chunk: one chunk per row (no chunk sums); at most B (max_pos + 1) keys
+    pre8 = _rows(m, R=8192, B=1, N=8192, max_pos=8191)
+    assert sz(pre8, -1) == bwd_size(8192, 1, 8192, 1, 8192)
+    assert sz(pre8, 1 << 40) == sz(pre8, -1)
+    assert L.dsa_indexer_backward_workspace_size(ctypes.byref(dec), ctypes.byref(f32), -1) == 0
 
 
 def test_project_append_host_checks(m):
@@ -204,10 +225,29 @@ def test_training_and_mha_host_checks(m):
     assert L.dsa_indexer_loss_dense(ctypes.byref(dec), ctypes.byref(d), None, p, 0.1, p, 32768, p,
                                     p, p, need, None) == m.DSA_E_INVALID
     # dense backward
-    bwd = lambda ld, dq: L.dsa_indexer_backward_dense(ctypes.byref(dec), ctypes.byref(d), p, p, p, p,
-                                                      p, p, ld, dq, p, p, None)
-    assert bwd(32767, p) == m.DSA_E_INVALID
-    assert bwd(32768, None) == m.DSA_E_INVALID
+    nbd = L.dsa_indexer_backward_dense_workspace_size(ctypes.byref(dec), ctypes.byref(d), 0)
+    bwd = lambda ld, dq, ws, n: L.dsa_indexer_backward_dense(ctypes.byref(dec), ctypes.byref(d), p,
+                                                             p, p, p, p, p, ld, dq, p, p, ws, n, None)
+    assert bwd(32767, p, p, nbd) == m.DSA_E_INVALID
+    assert bwd(32768, None, p, nbd) == m.DSA_E_INVALID
+    assert bwd(32768, p, p, nbd - 1) == m.DSA_E_WORKSPACE
+    assert bwd(32768, p, None, nbd) == m.DSA_E_WORKSPACE
+    # sparse backward
+    nb = L.dsa_indexer_backward_workspace_size(ctypes.byref(dec), ctypes.byref(d), 0)
+    sb = lambda rows, dims, ws, n: L.dsa_indexer_backward(ctypes.byref(rows), dims, p, p, p, p, p,
+                                                          p, p, p, p, p, ws, n, None)
+    assert sb(dec, ctypes.byref(f32), p, nb) == m.DSA_E_UNSUPPORTED
+    assert sb(dec, None, p, nb) == m.DSA_E_INVALID
+    assert sb(dec, ctypes.byref(d), p, nb - 1) == m.DSA_E_WORKSPACE
+    assert sb(dec, ctypes.byref(d), None, nb) == m.DSA_E_WORKSPACE
+    assert L.dsa_indexer_backward(ctypes.byref(dec), ctypes.byref(d), p, p, p, p, p, None, p, p, p,
+                                  p, p, nb, None) == m.DSA_E_INVALID
+    # key counts of num_seqs * (max_pos + 1) >= 2^31 are refused
+    big = _rows(m, R=32, B=32768, N=65536, max_pos=65535)
+    assert sb(big, ctypes.byref(d), p, 1 << 50) == m.DSA_E_UNSUPPORTED
+    # and rows longer than 131072 positions
+    long_rows = _rows(m, R=1, B=1, N=262144, max_pos=131072)
+    assert sb(long_rows, ctypes.byref(d), p, 1 << 50) == m.DSA_E_UNSUPPORTED
     # masked MHA mode: short prefill only, production dims, workspace
     pre = _rows(m, R=8192, B=1, N=8192, max_pos=8191)
     need = L.dsa_mha_prefill_workspace_size(ctypes.byref(pre), ctypes.byref(d))

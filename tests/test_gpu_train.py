@@ -177,15 +177,22 @@ def test_indexer_loss_composed(dsa):
         assert abs(loss[r] - l_ref) <= 0.05 * l_ref + 1e-4, (r, loss[r], l_ref)
 
 
-@pytest.mark.parametrize("name,rows", [("decode32k", [0, 13, 31]),
-                                       ("prefill8k", list(range(4000, 4016)))])
-def test_indexer_backward_parity(dsa, name, rows):
+@pytest.mark.parametrize("name,rows,mode", [("decode32k", [0, 13, 31], "full"),
+                                            ("decode32k", [0, 13, 31], "dup"),
+                                            ("prefill8k", list(range(4000, 4016)), "full"),
+                                            ("prefill8k", list(range(4000, 4016)), "min"),
+                                            ("prefill8k", list(range(4000, 4016)), "few")])
+def test_indexer_backward_parity(dsa, name, rows, mode):
     """Seeded dscores on the oracle's selections; for the prefill rows the key
-    gradients of rows that select the same key add up."""
+    gradients of rows that select the same key add up.  Modes: "full" workspace
+    (every key selected more than once is summed in fixed point); "min" (no
+    accumulators: such keys are added with fp32 atomics); "few" (7 accumulators, the
+    rest atomics); "dup" (each row's index list holds its first 1024 selected
+    positions twice, so keys repeat within a row)."""
     cfg = di.CONFIGS[name]
     inp = dev_inputs(name)
     host = HostInputs(cfg)
-    print(f"[backward] {name} rows {rows[0]}..{rows[-1]}", flush=True)
+    print(f"[backward] {name} rows {rows[0]}..{rows[-1]} mode {mode}", flush=True)
     setup = _oracle_setup(cfg, host, rows)
     R = len(rows)
     ridx = torch.tensor(rows, device="cuda")
@@ -194,19 +201,27 @@ def test_indexer_backward_parity(dsa, name, rows):
     rng = np.random.default_rng(77)
     idx = np.full((R, cfg.topk), -1, dtype=np.int32)
     g = np.zeros((R, cfg.topk), dtype=np.float32)
+    ents = []
     for i, (row, I, S) in enumerate(setup):
-        idx[i, : S.size] = S
-        g[i, : S.size] = (rng.standard_normal(S.size) * 1e-3).astype(np.float32)
+        ent = np.concatenate([S[:1024], S[:1024]]) if mode == "dup" else S
+        ents.append(ent)
+        idx[i, : ent.size] = ent
+        g[i, : ent.size] = (rng.standard_normal(ent.size) * 1e-3).astype(np.float32)
     dq = torch.zeros(R, 64, 128, dtype=torch.float32, device="cuda")
     dw = torch.zeros(R, 64, dtype=torch.float32, device="cuda")
     dk = torch.zeros(cfg.num_seqs, cfg.max_ctx, 128, dtype=torch.float32, device="cuda")
+    nacc = {"full": -1, "dup": -1, "min": 0, "few": 7}[mode]
+    ws = torch.empty(dsa.indexer_backward_workspace_size(rs, shared_keys=nacc),
+                     dtype=torch.uint8, device="cuda")
     dsa.indexer_backward(rs, inp.q_idx[ridx].contiguous(), inp.q_scale[ridx].contiguous(),
                          inp.w[ridx].contiguous(), inp.k_idx, inp.k_scale,
-                         torch.from_numpy(idx).cuda(), torch.from_numpy(g).cuda(), dq, dw, dk)
+                         torch.from_numpy(idx).cuda(), torch.from_numpy(g).cuda(), dq, dw, dk,
+                         workspace=ws)
     torch.cuda.synchronize()
     dq, dw = dq.cpu().numpy(), dw.cpu().numpy()
-    dk_ref, dk_tol, keys_of = {}, {}, {}
+    dk_ref, dk_tol = {}, {}
     for i, (row, I, S) in enumerate(setup):
+        S = ents[i]
         qf = oracle.decode_e4m3fn(row.q_idx) * row.q_scale[:, None]
         codes, ksc = host.keys(row.b, row.t + 1)
         kf = oracle.decode_e4m3fn(codes[S]) * ksc[S][:, None]
@@ -235,12 +250,13 @@ def test_indexer_backward_parity(dsa, name, rows):
     tol = np.stack([dk_tol[k] for k in keys])
     assert np.all(np.abs(got - ref) <= tol + 1e-12), float(np.max(np.abs(got - ref) - tol))
     count = {}
-    for row, I, S in setup:
-        for s_ in S.tolist():
+    for (row, I, S), ent in zip(setup, ents):
+        for s_ in ent.tolist():
             count[(row.b, s_)] = count.get((row.b, s_), 0) + 1
     shared = sum(1 for k in keys if count[k] > 1)
-    print(f"[backward] {name}: dq, dw, dk within bars; {len(keys)} keys, {shared} selected by "
-          f"several rows", flush=True)
+    assert mode not in ("dup", "few") or shared > 7
+    print(f"[backward] {name} {mode}: dq, dw, dk within bars; {len(keys)} keys, "
+          f"{shared} selected more than once", flush=True)
     # nothing outside the selected keys is written
     mask = torch.zeros(cfg.num_seqs, cfg.max_ctx, dtype=torch.bool, device="cuda")
     mask[bt, st] = True
@@ -384,4 +400,59 @@ def test_dense_rows_past_max_pos_untouched(dsa):
     l_ref, _ = oracle.indexer_kl(p, sc[0, :n].astype(np.float64))
     assert abs(loss[0] - l_ref) <= 1e-3 * abs(l_ref) + 1e-6, (loss[0], l_ref)
     print(f"[past max_pos] row {rows[1]} untouched; row {rows[0]} loss {loss[0]:.6f} ref {l_ref:.6f}",
+          flush=True)
+
+
+@pytest.mark.parametrize("case", ["decode32k", "prefill8k", "decode32k_dense", "prefill8k_dense"])
+def test_indexer_backward_deterministic(dsa, case):
+    """The backward's outputs are the same bits from run to run, whatever the
+    workspace held before (it is filled with 0xFF bytes before each run): decode
+    rows (one per sequence: every key has one writer) with the smallest workspace
+    and with the full one, which must also agree bit for bit; prefill rows that
+    share most of their keys (fixed-point sums) with the full workspace."""
+    name = case.split("_")[0]
+    dense = case.endswith("_dense")
+    cfg = di.CONFIGS[name]
+    inp = dev_inputs(name)
+    rows = list(range(cfg.num_rows)) if name == "decode32k" else \
+        list(range(3000, 3016)) if dense else list(range(4000, 4064))
+    R = len(rows)
+    ridx = torch.tensor(rows, device="cuda")
+    seq, pos = inp.row_seq[ridx].contiguous(), inp.row_pos[ridx].contiguous()
+    rs = dsa.rows_struct(seq, pos, cfg.num_seqs, cfg.max_ctx, cfg.kv_len - 1)
+    dims = dsa.Dims.from_config(cfg)
+    q_idx, q_scale, w = (x[ridx].contiguous() for x in (inp.q_idx, inp.q_scale, inp.w))
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    if dense:
+        ld = (cfg.kv_len + 63) // 64 * 64
+        g = torch.randn(R, ld, generator=gen, device="cuda") * 1e-4
+        size = dsa.indexer_backward_dense_workspace_size
+        call = lambda dq, dw, dk, ws: dsa.indexer_backward_dense(
+            rs, q_idx, q_scale, w, inp.k_idx, inp.k_scale, g, dq, dw, dk, workspace=ws)
+    else:
+        sc = dsa.indexer_scores(rs, dims, q_idx, q_scale, w, inp.k_idx, inp.k_scale)
+        idx = dsa.topk(rs, cfg.topk, sc)
+        g = torch.randn(R, cfg.topk, generator=gen, device="cuda") * 1e-3
+        size = dsa.indexer_backward_workspace_size
+        call = lambda dq, dw, dk, ws: dsa.indexer_backward(
+            rs, q_idx, q_scale, w, inp.k_idx, inp.k_scale, idx, g, dq, dw, dk, workspace=ws)
+    modes = ((0, -1) if name == "decode32k" else (-1,))
+    first = None
+    for nacc in modes:
+        ws = torch.empty(size(rs, shared_keys=nacc), dtype=torch.uint8, device="cuda")
+        for run in range(3):
+            ws.fill_(255)
+            dq = torch.zeros(R, 64, 128, device="cuda")
+            dw = torch.zeros(R, 64, device="cuda")
+            dk = torch.zeros(cfg.num_seqs, cfg.max_ctx, 128, device="cuda")
+            call(dq, dw, dk, ws)
+            torch.cuda.synchronize()
+            if first is None:
+                first = (dq, dw, dk)
+                assert bool(dk.abs().sum() > 0) and bool(dq.abs().sum() > 0)
+                continue
+            for a, b_, nm in zip(first, (dq, dw, dk), ("dq", "dw", "dk")):
+                assert torch.equal(a, b_), (case, nacc, run, nm)
+        del ws
+    print(f"[backward determinism] {case}: {R} rows, workspaces {modes}: identical bits",
           flush=True)
