@@ -470,17 +470,17 @@ def time_training(dsa, st, K):
     return out
 
 
-def time_mha(dsa, di, K):
-    """The masked MHA mode on the 8K prefill (one sequence, 8192 rows, the library's
-    own selections), against the MQA mode's sparse attention on the same selection.
-    Both are timed with HIP events over K calls."""
+def time_mha(dsa, di, K, name="prefill8k"):
+    """The masked MHA mode on a prefill workload (the library's own selections),
+    against the MQA mode's sparse attention on the same selection.  Both are timed
+    with HIP events over K calls."""
     import torch
 
-    cfg = di.CONFIGS["prefill8k"]
-    print("[bench] masked MHA mode prefill8k", file=sys.stderr, flush=True)
+    cfg = di.CONFIGS[name]
+    print(f"[bench] masked MHA mode {name}", file=sys.stderr, flush=True)
     st = Workload(dsa, di, cfg, 0)
     st.run()
-    R, L = cfg.num_rows, cfg.kv_len
+    R = cfg.num_rows
     mg = di.MhaGenerator(cfg.cfg_id, 0)
     q = mg.q(0, R, device="cuda")
     w_uk, w_uv = mg.weights(device="cuda")
@@ -493,8 +493,8 @@ def time_mha(dsa, di, K):
                                   dims=st.dims, out=out, lse=lse, workspace=ws)
     mqa = lambda: dsa.sparse_mla_attn(st.rows, st.dims, i.q, i.latent, st.idx, cfg.scale,
                                       out=st.out, lse=st.lse, workspace=st.ws)
-    res = {}
-    for name, fn in (("mha", mha), ("mqa", mqa)):
+    res = {"workload": f"{cfg.name}: {cfg.description}"}
+    for nm, fn in (("mha", mha), ("mqa", mqa)):
         for _ in range(2):
             fn()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -504,19 +504,20 @@ def time_mha(dsa, di, K):
             fn()
         e1.record()
         torch.cuda.synchronize()
-        res[name + "_ms"] = e0.elapsed_time(e1) / K
-    _, sel = _pairs(cfg)
-    # MHA mode: decompression GEMM (L positions x 32768 x 512) and, per head, the
-    # attention over the causal positions (the mask cuts the selection out of them):
-    # 192-wide q.k and 128-wide p.v per (row, position)
-    causal = R * (R + 1) // 2
-    dec_tf = L * 2 * 16384 * 512 * 2 / 1e12
+        res[nm + "_ms"] = e0.elapsed_time(e1) / K
+    causal, sel = _pairs(cfg)
+    # MHA mode: decompression GEMM (each sequence's positions x 32768 x 512) and,
+    # per head, the attention over the causal positions (the mask cuts the
+    # selection out of them): 192-wide q.k and 128-wide p.v per (row, position)
+    dec_tf = cfg.num_seqs * cfg.kv_len * 2 * 16384 * 512 * 2 / 1e12
     att_tf = causal * cfg.n_heads * 2 * (192 + 128) / 1e12
-    res.update({"rows": R, "mha_tflop": dec_tf + att_tf,
+    res.update({"rows": R, "selected_entries": sel, "causal_pairs": causal,
+                "mha_tflop": dec_tf + att_tf,
                 "mha_bf16_frac": (dec_tf + att_tf) / (res["mha_ms"] * 1e-3) / BF16_PEAK_TFLOPS,
                 "mqa_tflop": sel * ATTN_FLOP_PER_ENTRY / 1e12,
                 "mqa_bf16_frac": sel * ATTN_FLOP_PER_ENTRY / 1e12 / (res["mqa_ms"] * 1e-3)
-                / BF16_PEAK_TFLOPS})
+                / BF16_PEAK_TFLOPS,
+                "mha_speedup": res["mqa_ms"] / res["mha_ms"]})
     del st, q, w_uk, w_uv, out, lse, ws
     torch.cuda.empty_cache()
     return res
@@ -687,7 +688,10 @@ def main():
         # the step before the path: projections and cache append of the new tokens
         line["projections"] = {name: time_projection(dsa, di, di.PROJ_CONFIGS[name], reps)
                                for name, reps in (("proj_decode32", 30), ("proj_prefill8k", 10))}
-        line["mha_prefill8k"] = time_mha(dsa, di, max(2, args.steps // 4))
+        # the masked MHA mode beside the MQA mode: short prefill (every causal set
+        # fits in k, where the mode is meant to win) and 8K
+        line["mha_prefill2k"] = time_mha(dsa, di, max(2, args.steps // 4), "prefill2k")
+        line["mha_prefill8k"] = time_mha(dsa, di, max(2, args.steps // 4), "prefill8k")
     if args.extra:
         line["extra"] = {"prefill8k": time_prefill(dsa, di, di.CONFIGS["prefill8k"], 5)}
     if not args.no_cpu:

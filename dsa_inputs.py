@@ -218,6 +218,9 @@ CONFIGS: Dict[str, Config] = {
         Config("prefill128k", 5, 1, 131072, 131072, 131072, 8192, 64, 128, 128, 576, 512,
                2048, 1.0 / math.sqrt(192.0), False, False,
                "causal prefill of one 131072-token sequence in 8192-row chunks"),
+        Config("prefill2k", 8, 4, 2048, 2048, 2048, 8192, 64, 128, 128, 576, 512, 2048,
+               1.0 / math.sqrt(192.0), False, False,
+               "short causal prefill, 4 sequences of 2048 tokens (every causal set fits in k)"),
     ]
 }
 

@@ -177,12 +177,18 @@ __device__ __forceinline__ float sum4g(float v) {
 }
 
 constexpr int AW = 8;            // waves
-constexpr int AR = 16 * AW;      // rows per block
-constexpr int AKS = 32;          // keys per stage
+constexpr int RT = 2;            // 16-row tiles per wave
+constexpr int AR = 16 * RT * AW; // rows per block (256)
+constexpr int AKS = 64;          // keys per stage
 constexpr int KST = DQ + 8;      // key tile row stride (bf16), padded
 constexpr int VST = AKS + 8;     // value tile row stride (bf16), padded
 
-__global__ __launch_bounds__(AW * 64, 4) void mha_attn_kernel(
+// Position of key k (0..31 within a 32-key half) in a value row of the tile: the
+// keys 16 a + 4 g + v that lane group g holds for the value product (a, v = 0..3)
+// sit together at 8 g + 4 a + v, so a lane's A operand is one 16-byte read.
+__device__ __forceinline__ int vperm(int k) { return 8 * ((k >> 2) & 3) + 4 * (k >> 4) + (k & 3); }
+
+__global__ __launch_bounds__(AW * 64) void mha_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ latent,
     const uint16_t* __restrict__ kdec, const uint16_t* __restrict__ vtdec,
     const uint32_t* __restrict__ mask, const int32_t* __restrict__ row_seq,
@@ -199,22 +205,31 @@ __global__ __launch_bounds__(AW * 64, 4) void mha_attn_kernel(
   const int xcd = blockIdx.x & 7, within = blockIdx.x >> 3;
   const int h = 8 * (within / nrb) + xcd;
   const int r0 = (nrb - 1 - within % nrb) * AR;
-  const int tid = threadIdx.x, l = lane_id(), wv = tid >> 6, g = l >> 4, n = l & 15;
+  const int tid = threadIdx.x, l = lane_id(), g = l >> 4, n = l & 15;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int W = L / 32;
 
-  // this lane's row (B operand column n of the S^T tiles) and its sequence
-  const int r = r0 + 16 * wv + n;
-  const bool rv = r < R;
-  const int b = rv ? row_seq[r] : -1, t = rv ? row_pos[r] : -1;
-  const bool valid = rv && b >= 0 && b < B && t >= 0 && t < Lc;
-  const uint32_t* mrow = mask + (size_t)(rv ? r : 0) * W;
+  // this lane's rows (B operand column n of the S^T tiles of tile i) and sequences
+  int rr[RT], bb[RT], tt[RT];
+  bool valid[RT];
+#pragma unroll
+  for (int i = 0; i < RT; ++i) {
+    rr[i] = r0 + 16 * (RT * wv + i) + n;
+    const bool rv = rr[i] < R;
+    bb[i] = rv ? row_seq[rr[i]] : -1;
+    tt[i] = rv ? row_pos[rr[i]] : -1;
+    valid[i] = rv && bb[i] >= 0 && bb[i] < B && tt[i] >= 0 && tt[i] < Lc;
+  }
 
   // One pass over the keys per distinct sequence among the block's rows, in
   // ascending sequence order: a single pass when the rows are grouped by sequence.
   int bdone = -1;
   for (;;) {
     // the next sequence: the smallest above bdone among the block's valid rows
-    int bn = valid && b > bdone ? b : INT_MAX;
+    int bn = INT_MAX;
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+      if (valid[i] && bb[i] > bdone) bn = min(bn, bb[i]);
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) bn = min(bn, __shfl_xor(bn, o));
     if (l == 0) seq_s[wv] = bn;
@@ -224,8 +239,13 @@ __global__ __launch_bounds__(AW * 64, 4) void mha_attn_kernel(
     for (int i = 0; i < AW; ++i) bseq = min(bseq, seq_s[i]);
     if (bseq == INT_MAX) break;  // the same for every thread of the block
     bdone = bseq;
-    const bool ok = valid && b == bseq;
-    int tw = ok ? t : -1;
+    bool ok[RT];
+    int tw = -1;
+#pragma unroll
+    for (int i = 0; i < RT; ++i) {
+      ok[i] = valid[i] && bb[i] == bseq;
+      if (ok[i]) tw = max(tw, tt[i]);
+    }
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) tw = max(tw, __shfl_xor(tw, o));
     if (l == 0) tmax_s[wv] = tw;
@@ -236,117 +256,173 @@ __global__ __launch_bounds__(AW * 64, 4) void mha_attn_kernel(
     const uint16_t* kseq = kdec + (size_t)bseq * L * KCOLS + (size_t)h * DH;
     const uint16_t* vseq = vtdec + ((size_t)bseq * KCOLS + (size_t)h * DH) * L;
     const uint16_t* lseq = latent + (size_t)bseq * N * kQkDim;
-    // queries of this lane's row, contraction step s: dims [32 s + 8 g, +8)
-    i32x4 qr[DQ / 32];
-    {
-      const uint16_t* qp = q + ((size_t)(rv ? r : 0) * H + h) * DQ + 8 * g;
+    // queries of this lane's rows, contraction step s: dims [32 s + 8 g, +8)
+    i32x4 qr[RT][DQ / 32];
 #pragma unroll
-      for (int s = 0; s < DQ / 32; ++s) qr[s] = *reinterpret_cast<const i32x4*>(qp + 32 * s);
+    for (int i = 0; i < RT; ++i) {
+      const uint16_t* qp = q + ((size_t)(rr[i] < R ? rr[i] : 0) * H + h) * DQ + 8 * g;
+#pragma unroll
+      for (int s2 = 0; s2 < DQ / 32; ++s2) qr[i][s2] = *reinterpret_cast<const i32x4*>(qp + 32 * s2);
     }
 
-    f32x4 acc[DH / 16];
+    f32x4 acc[RT][DH / 16];
 #pragma unroll
-    for (int i = 0; i < DH / 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.f;
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+      for (int d = 0; d < DH / 16; ++d) acc[i][d] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run[RT], l_run[RT];
+#pragma unroll
+    for (int i = 0; i < RT; ++i) {
+      m_run[i] = -INFINITY;
+      l_run[i] = 0.f;
+    }
 
     // Stage k0's tiles are fetched into registers one stage ahead (the loads are in
-    // flight while the previous stage computes): key chunks tid and tid + 512 (the
-    // latter for tid < 256) of 32 keys x 24 chunks, value chunk tid of 128 dims x 4,
-    // and this lane's mask word.
-    static_assert(AKS * (DQ / 8) == AW * 64 + AW * 32 && DH * (AKS / 8) == AW * 64, "chunk counts");
-    i32x4 pf_k0, pf_k1 = {0, 0, 0, 0}, pf_v;
-    uint32_t pf_m;
-    auto key_src = [&](int k0, int c) {
-      const int e = c / (DQ / 8), d8 = c - e * (DQ / 8);
-      const int s = min(k0 + e, L - 1);
-      return d8 < DH / 8 ? kseq + (size_t)s * KCOLS + 8 * d8
-                         : lseq + (size_t)min(s, Lc - 1) * kQkDim + DL + 8 * (d8 - DH / 8);
-    };
+    // flight while the previous stage computes): key chunks tid + 512 j (64 keys x
+    // 24 chunks), value chunks tid + 512 j (128 dims x 8 chunks of 8 keys), and the
+    // two mask words of each of this lane's rows.
+    static_assert(AKS * (DQ / 8) == 3 * AW * 64 && DH * (AKS / 8) == 2 * AW * 64, "chunk counts");
+    i32x4 pf_k[3], pf_v[2];
+    uint2 pf_m[RT];
+    // a stage's two mask words of row r0 + 32 wv + 16 i + n, in 8-byte units (W is
+    // even, and the stage's words start at an even word): a wave-uniform base plus
+    // one lane offset shared by the tiles
+    const uint2* mask2 = reinterpret_cast<const uint2*>(mask) + (size_t)(r0 + 32 * wv) * (W / 2);
+    const int mlane = n * (W / 2);
     auto fetch = [&](int k0) {
-      pf_k0 = *reinterpret_cast<const i32x4*>(key_src(k0, tid));
-      if (tid < AW * 32) pf_k1 = *reinterpret_cast<const i32x4*>(key_src(k0, tid + AW * 64));
-      const int d = tid / (AKS / 8), k8 = tid - d * (AKS / 8);
-      const int s = k0 + 8 * k8;
-      pf_v = s + 8 <= L ? *reinterpret_cast<const i32x4*>(vseq + (size_t)d * L + s) : i32x4{0, 0, 0, 0};
-      pf_m = ok ? mrow[k0 >> 5] : 0u;
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        const int c = tid + AW * 64 * j, e = c / (DQ / 8), d8 = c - e * (DQ / 8);
+        const int s2 = min(k0 + e, L - 1);
+        const uint16_t* src = d8 < DH / 8
+                                  ? kseq + (size_t)s2 * KCOLS + 8 * d8
+                                  : lseq + (size_t)min(s2, Lc - 1) * kQkDim + DL + 8 * (d8 - DH / 8);
+        pf_k[j] = *reinterpret_cast<const i32x4*>(src);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int c = tid + AW * 64 * j, d = c / (AKS / 8), k8 = c - d * (AKS / 8);
+        pf_v[j] = *reinterpret_cast<const i32x4*>(vseq + (size_t)d * L + k0 + 8 * k8);
+      }
+#pragma unroll
+      for (int i = 0; i < RT; ++i)
+        pf_m[i] = ok[i] ? mask2[16 * i * (W / 2) + (k0 >> 6) + mlane] : make_uint2(0u, 0u);
     };
     auto stash = [&]() {
-      {
-        const int e = tid / (DQ / 8), d8 = tid - e * (DQ / 8);
-        *reinterpret_cast<i32x4*>(&kt[e][8 * d8]) = pf_k0;
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        const int c = tid + AW * 64 * j, e = c / (DQ / 8), d8 = c - e * (DQ / 8);
+        *reinterpret_cast<i32x4*>(&kt[e][8 * d8]) = pf_k[j];
       }
-      if (tid < AW * 32) {
-        const int c = tid + AW * 64, e = c / (DQ / 8), d8 = c - e * (DQ / 8);
-        *reinterpret_cast<i32x4*>(&kt[e][8 * d8]) = pf_k1;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int c = tid + AW * 64 * j, d = c / (AKS / 8), k8 = c - d * (AKS / 8);
+        const int base = 32 * (k8 >> 2) + vperm(8 * (k8 & 3));  // keys 8 k8 .. + 3
+        *reinterpret_cast<uint2*>(&vt[d][base]) = make_uint2((uint32_t)pf_v[j][0], (uint32_t)pf_v[j][1]);
+        *reinterpret_cast<uint2*>(&vt[d][base + 8]) = make_uint2((uint32_t)pf_v[j][2], (uint32_t)pf_v[j][3]);
       }
-      const int d = tid / (AKS / 8), k8 = tid - d * (AKS / 8);
-      *reinterpret_cast<i32x4*>(&vt[d][8 * k8]) = pf_v;
     };
     if (tmax >= 0) fetch(0);
     for (int k0 = 0; k0 <= tmax; k0 += AKS) {
       __syncthreads();  // previous stage's tile reads are done
       stash();
-      const uint32_t mw = pf_m;
+      uint32_t mw[RT][2];
+#pragma unroll
+      for (int i = 0; i < RT; ++i) {
+        mw[i][0] = pf_m[i].x;
+        mw[i][1] = pf_m[i].y;
+      }
       __syncthreads();
       if (k0 + AKS <= tmax) fetch(k0 + AKS);
-      // S^T = K Q^T: keys 16 mt + 4 g + v (mt = 0, 1) of this lane's row
-      f32x4 st[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      // the stage's two 32-key halves in turn: S^T = K Q^T (lane holds keys
+      // 32 hf + 16 a + 4 g + v of row n of each tile), the online softmax, O^T += V^T P^T
 #pragma unroll
-      for (int s = 0; s < DQ / 32; ++s)
+      for (int hf = 0; hf < 2; ++hf) {
+        f32x4 st[RT][2];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const bf16x8 ka = as_bf16x8(*reinterpret_cast<const i32x4*>(&kt[16 * mt + n][32 * s + 8 * g]));
-          st[mt] = mfma_bf16_16x16x32(ka, as_bf16x8(qr[s]), st[mt]);
-        }
-      float x[8];
-      float mx = -INFINITY;
+        for (int i = 0; i < RT; ++i) st[i][0] = st[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+        for (int s2 = 0; s2 < DQ / 32; ++s2)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int e = 16 * mt + 4 * g + v;
-          const float z = ((mw >> e) & 1u) ? st[mt][v] * scale_log2 : -INFINITY;
-          x[4 * mt + v] = z;
-          mx = fmaxf(mx, z);
-        }
-      mx = max4g(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
-      float psum = 0.f;
-      float pv[8];
+          for (int a2 = 0; a2 < 2; ++a2) {
+            const bf16x8 ka = as_bf16x8(
+                *reinterpret_cast<const i32x4*>(&kt[32 * hf + 16 * a2 + n][32 * s2 + 8 * g]));
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        pv[i] = x[i] == -INFINITY ? 0.f : exp2f(x[i] - m_new);
-        psum += pv[i];
-      }
-      psum = sum4g(psum);
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-      // P^T operand: keys {4g..4g+3, 16+4g..16+4g+3} of this lane's row, as bf16
-      const i32x4 pb = {(int)pack_bf16x2(pv[0], pv[1]), (int)pack_bf16x2(pv[2], pv[3]),
+            for (int i = 0; i < RT; ++i) st[i][a2] = mfma_bf16_16x16x32(ka, as_bf16x8(qr[i][s2]), st[i][a2]);
+          }
+        i32x4 pb[RT];
+        float alpha[RT];
+        bool rescale[RT];
+#pragma unroll
+        for (int i = 0; i < RT; ++i) {
+          // masked raw scores; a wave whose rows see every key of the half skips
+          // the mask tests
+          float sm[8];
+          const uint32_t m0 = mw[i][hf];
+          if (__all(m0 == 0xffffffffu)) {
+#pragma unroll
+            for (int a2 = 0; a2 < 2; ++a2)
+#pragma unroll
+              for (int v = 0; v < 4; ++v) sm[4 * a2 + v] = st[i][a2][v];
+          } else {
+#pragma unroll
+            for (int a2 = 0; a2 < 2; ++a2)
+#pragma unroll
+              for (int v = 0; v < 4; ++v)
+                sm[4 * a2 + v] = ((m0 >> (16 * a2 + 4 * g + v)) & 1u) ? st[i][a2][v] : -INFINITY;
+          }
+          float mx = sm[0];
+#pragma unroll
+          for (int k = 1; k < 8; ++k) mx = fmaxf(mx, sm[k]);
+          mx = max4g(mx);
+          // running max in log2 units (the scale is positive, so it commutes with max);
+          // exp2 of -inf is 0, which covers masked keys and the first stage
+          const float m_new = fmaxf(m_run[i], mx * scale_log2);
+          const float m_use = m_new == -INFINITY ? 0.f : m_new;
+          alpha[i] = exp2f(m_run[i] - m_use);
+          rescale[i] = !__all(alpha[i] == 1.f);
+          float psum = 0.f;
+          float pv[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            pv[k] = exp2f(fmaf(sm[k], scale_log2, -m_use));
+            psum += pv[k];
+          }
+          psum = sum4g(psum);
+          l_run[i] = l_run[i] * alpha[i] + psum;
+          m_run[i] = m_new;
+          pb[i] = i32x4{(int)pack_bf16x2(pv[0], pv[1]), (int)pack_bf16x2(pv[2], pv[3]),
                         (int)pack_bf16x2(pv[4], pv[5]), (int)pack_bf16x2(pv[6], pv[7])};
+        }
 #pragma unroll
-      for (int dt = 0; dt < DH / 16; ++dt) {
+        for (int i = 0; i < RT; ++i)
+          if (rescale[i])  // (uniform over the wave)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[dt][v] *= alpha;
-        const uint16_t* vr = &vt[16 * dt + n][0];
-        const uint2 lo = *reinterpret_cast<const uint2*>(vr + 4 * g);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16 + 4 * g);
-        const i32x4 va = {(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
-        acc[dt] = mfma_bf16_16x16x32(as_bf16x8(va), as_bf16x8(pb), acc[dt]);
+            for (int dt = 0; dt < DH / 16; ++dt)
+#pragma unroll
+              for (int v = 0; v < 4; ++v) acc[i][dt][v] *= alpha[i];
+#pragma unroll
+        for (int dt = 0; dt < DH / 16; ++dt) {
+          const bf16x8 va = as_bf16x8(*reinterpret_cast<const i32x4*>(&vt[16 * dt + n][32 * hf + 8 * g]));
+#pragma unroll
+          for (int i = 0; i < RT; ++i) acc[i][dt] = mfma_bf16_16x16x32(va, as_bf16x8(pb[i]), acc[i][dt]);
+        }
       }
     }
-    // lane holds dims 16 dt + 4 g + v of its row
-    if (ok) {
-      const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-      uint16_t* orow = out + ((size_t)r * H + h) * DH;
+    // lane holds dims 16 dt + 4 g + v of row n of each tile
+#pragma unroll
+    for (int i = 0; i < RT; ++i) {
+      if (!ok[i]) continue;
+      const float inv = l_run[i] > 0.f ? 1.f / l_run[i] : 0.f;
+      uint16_t* orow = out + ((size_t)rr[i] * H + h) * DH;
 #pragma unroll
       for (int dt = 0; dt < DH / 16; ++dt)
         *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * g) =
-            make_uint2(pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv),
-                       pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv));
+            make_uint2(pack_bf16x2(acc[i][dt][0] * inv, acc[i][dt][1] * inv),
+                       pack_bf16x2(acc[i][dt][2] * inv, acc[i][dt][3] * inv));
       if (lse != nullptr && g == 0)
-        lse[(size_t)r * H + h] = l_run > 0.f ? (m_run + log2f(l_run)) * 0.69314718055994530942f : -INFINITY;
+        lse[(size_t)rr[i] * H + h] =
+            l_run[i] > 0.f ? (m_run[i] + log2f(l_run[i])) * 0.69314718055994530942f : -INFINITY;
     }
     __syncthreads();  // the pass's LDS reads are done before the next pass writes
   }
