@@ -101,6 +101,42 @@ def test_mha_prefill8k_masked(dsa):
                lse[t].cpu().numpy().astype(np.float64), lse_ref, f"8K row {t}")
 
 
+def test_mha_prefill2k_batch(dsa):
+    """The short-prefill workload the bench times: 4 sequences of 2048 tokens, rows
+    grouped by sequence, each row selecting its whole causal set (t + 1 <= k, as
+    the indexer's top-k does there); sampled rows of every sequence against the
+    MQA-mode oracle with the absorbed query."""
+    cfg = di.CONFIGS["prefill2k"]
+    dev = torch.device("cuda")
+    inp = di.make_inputs(cfg, 0, device=dev)
+    R, L = cfg.num_rows, cfg.kv_len
+    mg = di.MhaGenerator(cfg.cfg_id, 0)
+    q = mg.q(0, R, device=dev)
+    w_uk, w_uv = mg.weights(device=dev)
+    seq, pos = cfg.row_seq_pos()
+    idx = np.full((R, cfg.topk), -1, dtype=np.int32)
+    for i, t in enumerate(pos):
+        idx[i, : t + 1] = np.arange(t + 1)
+    rs = dsa.rows_struct(inp.row_seq, inp.row_pos, cfg.num_seqs, cfg.max_ctx, L - 1)
+    dims = dsa.Dims.from_config(cfg)
+    out, lse = dsa.mha_prefill(rs, q, inp.latent, w_uk, w_uv, torch.from_numpy(idx).to(dev),
+                               cfg.scale, dims=dims)
+    torch.cuda.synchronize()
+    g = di.Generator(cfg, 0)
+    wuk, wuv = (oracle.decode_bf16(di.bf16_bits(x)) for x in mg.weights())
+    for b in range(cfg.num_seqs):
+        for t in (0, 63, 64, 1000, 2047):
+            i = b * L + t
+            S = np.arange(t + 1)
+            ent = oracle.decode_bf16(di.bf16_bits(g.latent_rows(b, torch.from_numpy(S.astype(np.int64)))))
+            qh = oracle.decode_bf16(di.bf16_bits(mg.q(i, i + 1)))[0]
+            q_abs = np.concatenate([np.einsum("hdc,hd->hc", wuk, qh[:, :128]), qh[:, 128:]], axis=1)
+            o_lat, lse_ref = oracle.sparse_attention(q_abs, ent, cfg.scale, cfg.v_dim)
+            o_ref = np.einsum("hdc,hc->hd", wuv, o_lat)
+            _check(out[i].float().cpu().numpy().astype(np.float64), o_ref,
+                   lse[i].cpu().numpy().astype(np.float64), lse_ref, f"2K seq {b} row {t}")
+
+
 def test_mha_interleaved_sequences(dsa):
     """Three sequences of 100, 250 and 180 tokens whose rows are interleaved (row
     order by position, then sequence), so every 128-row tile holds rows of all three;

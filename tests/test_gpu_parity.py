@@ -18,7 +18,7 @@ from dsa_check import (HostInputs, attn_errors, check_attention, check_scores,
 
 pytestmark = pytest.mark.gpu
 
-CFGS = ["tiny", "decode32k", "prefill8k", "decode128k", "prefill128k"]
+CFGS = ["tiny", "decode32k", "prefill8k", "decode128k", "prefill128k", "prefill2k"]
 
 
 @pytest.fixture(scope="module")
@@ -43,7 +43,7 @@ def dev_inputs(name: str, set_id: int = 0) -> di.Inputs:
 
 
 def sample(cfg: di.Config) -> np.ndarray:
-    if cfg.name == "prefill8k":
+    if cfg.name in ("prefill8k", "prefill2k"):
         return di.sample_rows(cfg, 64)
     return di.sample_rows(cfg, 256)
 
