@@ -94,6 +94,9 @@ def parse():
                         "sections)")
     p.add_argument("--extra", action="store_true",
                    help="also time the 8K prefill")
+    p.add_argument("--mha-only", action="store_true",
+                   help="only time the masked MHA mode beside the MQA mode (short prefill and "
+                        "8K), so that a profiler run sees those kernels alone")
     p.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                    help="only run an fp32 elementwise copy (x * 1) that reads and writes MIB MiB, "
                         "five times: the reference kernel of known traffic that scales the "
@@ -633,6 +636,12 @@ def main():
 
     import dsa_inputs as di
     import sparse_attention_fp8_amd as dsa
+
+    if args.mha_only:
+        K = max(2, args.steps // 4)
+        print(json.dumps({name: time_mha(dsa, di, K, name) for name in ("prefill2k", "prefill8k")}),
+              flush=True)
+        return
 
     cfg = di.CONFIGS[args.workload]
     head, sets = time_decode(dsa, di, cfg, args.sets, args.steps, args.warmup,
