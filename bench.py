@@ -242,6 +242,23 @@ def time_bare(fn_list, K, W):
     return (time.perf_counter() - t0) / K * 1e3
 
 
+def step_percentiles(fn_list, K):
+    """Per-step durations from HIP events recorded between K back-to-back steps (fn_list
+    rotated): p10, median and p90 in ms."""
+    import torch
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(K):
+        fn_list[i % len(fn_list)]()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    d = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(K))
+    pick = lambda q: d[min(K - 1, int(q * (K - 1) + 0.5))]
+    return {"p10": pick(0.1), "median": pick(0.5), "p90": pick(0.9), "steps": K}
+
+
 def time_calls(sets, K):
     """Per-call event durations (ms per step, summed over a step's chunks) over K
     steps with the sets rotated."""
@@ -308,7 +325,11 @@ def time_decode(dsa, di, cfg, sets, K, W, graphs=True):
     calls_ms = time_bare([w.run for w in ws], K, W)
     k_ms = time_calls(ws, K)
     res = {"ms_per_step": ms, "tokens_per_s": cfg.num_rows / (ms * 1e-3),
-           "ms_per_step_three_calls": calls_ms}
+           "ms_per_step_three_calls": calls_ms,
+           # the step's spread (events between steps, input sets rotated: MALL-cold) and
+           # the same step repeated on one input set (MALL-warm)
+           "step_ms_events": step_percentiles([w.run_forward for w in ws], K),
+           "ms_per_step_warm": time_bare([ws[0].run_forward], K, W)}
     if graphs:
         try:
             for w in ws:
@@ -673,6 +694,8 @@ def main():
         "step_hbm_frac": head["step_hbm_frac"],
         "kernels": kernels,
         "ms_per_step_three_calls": head["ms_per_step_three_calls"],
+        "step_ms_events": head["step_ms_events"],
+        "ms_per_step_warm": head["ms_per_step_warm"],
     }
     if "graph" in head:
         line["graph"] = head["graph"]
