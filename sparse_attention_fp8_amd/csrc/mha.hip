@@ -278,11 +278,12 @@ __global__ __launch_bounds__(AW * 64) void mha_attn_kernel(
     }
 
     // Stage k0's tiles are fetched into registers one stage ahead (the loads are in
-    // flight while the previous stage computes): key chunks tid + 512 j (64 keys x
-    // 24 chunks), value chunks tid + 512 j (128 dims x 8 chunks of 8 keys), and the
+    // flight while the previous stage computes): key chunks tid + 64 AW j (64 keys x
+    // 24 chunks), value chunks tid + 64 AW j (128 dims x 8 chunks of 8 keys), and the
     // two mask words of each of this lane's rows.
-    static_assert(AKS * (DQ / 8) == 3 * AW * 64 && DH * (AKS / 8) == 2 * AW * 64, "chunk counts");
-    i32x4 pf_k[3], pf_v[2];
+    constexpr int KCH = AKS * (DQ / 8) / (AW * 64), VCH = DH * (AKS / 8) / (AW * 64);
+    static_assert(KCH * AW * 64 == AKS * (DQ / 8) && VCH * AW * 64 == DH * (AKS / 8), "chunk counts");
+    i32x4 pf_k[KCH], pf_v[VCH];
     uint2 pf_m[RT];
     // a stage's two mask words of row r0 + 32 wv + 16 i + n, in 8-byte units (W is
     // even, and the stage's words start at an even word): a wave-uniform base plus
@@ -291,7 +292,7 @@ __global__ __launch_bounds__(AW * 64) void mha_attn_kernel(
     const int mlane = n * (W / 2);
     auto fetch = [&](int k0) {
 #pragma unroll
-      for (int j = 0; j < 3; ++j) {
+      for (int j = 0; j < KCH; ++j) {
         const int c = tid + AW * 64 * j, e = c / (DQ / 8), d8 = c - e * (DQ / 8);
         const int s2 = min(k0 + e, L - 1);
         const uint16_t* src = d8 < DH / 8
@@ -300,7 +301,7 @@ __global__ __launch_bounds__(AW * 64) void mha_attn_kernel(
         pf_k[j] = *reinterpret_cast<const i32x4*>(src);
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < VCH; ++j) {
         const int c = tid + AW * 64 * j, d = c / (AKS / 8), k8 = c - d * (AKS / 8);
         pf_v[j] = *reinterpret_cast<const i32x4*>(vseq + (size_t)d * L + k0 + 8 * k8);
       }
@@ -310,12 +311,12 @@ __global__ __launch_bounds__(AW * 64) void mha_attn_kernel(
     };
     auto stash = [&]() {
 #pragma unroll
-      for (int j = 0; j < 3; ++j) {
+      for (int j = 0; j < KCH; ++j) {
         const int c = tid + AW * 64 * j, e = c / (DQ / 8), d8 = c - e * (DQ / 8);
         *reinterpret_cast<i32x4*>(&kt[e][8 * d8]) = pf_k[j];
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < VCH; ++j) {
         const int c = tid + AW * 64 * j, d = c / (AKS / 8), k8 = c - d * (AKS / 8);
         const int base = 32 * (k8 >> 2) + vperm(8 * (k8 & 3));  // keys 8 k8 .. + 3
         *reinterpret_cast<uint2*>(&vt[d][base]) = make_uint2((uint32_t)pf_v[j][0], (uint32_t)pf_v[j][1]);
