@@ -321,8 +321,10 @@ dsa_status dsa_project_append_paged(const dsa_rows* rows, const dsa_dims* dims,
  * i.e. the gradients of sum_i dscores[r,i] I[r,s_i] with respect to w and the
  * dequantised indexer queries and keys.  dq [R, H_I, d_I], dw [R, H_I] and
  * dk [B, N, d_I] are fp32 and ACCUMULATED (the caller zeroes them).  The dots are
- * the forward's (the fp8 MFMA's dots, see dsa_indexer_scores); the products run in
- * fp32.  Contiguous caches only.
+ * the forward's (the fp8 MFMA's dots, see dsa_indexer_scores).  The two products
+ * run on the bf16 MFMA with fp32 accumulation: the fp8 codes are bf16 values
+ * exactly, and each fp32 coefficient enters as three bf16 parts that sum to it (to
+ * within 2^-25 of it).  Contiguous caches only.
  *
  * Every sum is formed in an order fixed by the call's shape, so the outputs are the
  * same bits from run to run: dq and dw from per-chunk sums added in chunk order;
@@ -342,8 +344,9 @@ dsa_status dsa_project_append_paged(const dsa_rows* rows, const dsa_dims* dims,
  * is left for accumulators.  Keys selected more than once beyond those
  * accumulators, and all of them when the bound is not finite (inf or NaN inputs),
  * are added into dk with fp32 atomics, whose order and last bits vary.  A call in
- * which no key is selected twice (one row per sequence, as at decode) is exact and
- * deterministic with shared_keys = 0.  Below that size: DSA_E_WORKSPACE.
+ * which no key is selected twice (one row per sequence, as at decode) needs no
+ * accumulators: shared_keys = 0 keeps it deterministic.  Below that size:
+ * DSA_E_WORKSPACE.
  * max_pos + 1 <= 131072 and num_seqs * (max_pos + 1) < 2^31, else DSA_E_UNSUPPORTED.
  * ------------------------------------------------------------------------- */
 size_t dsa_indexer_loss_workspace_size(const dsa_rows* rows, const dsa_dims* dims);
