@@ -90,6 +90,10 @@ def test_workspace_sizes(m):
     dec = _rows(m, R=32, B=32, N=32768, max_pos=32767)
     attn = L.dsa_sparse_mla_attn_workspace_size(ctypes.byref(dec), ctypes.byref(d))
     assert attn == 32 * 8 * 128 * (512 * 2 + 4)   # 8 splits of bf16 partial outputs + fp32 lse
+    # 8 rows (decode 128K): 16 splits of 4 stages rather than 32 of 2
+    r8 = _rows(m, R=8, B=8, N=131072, max_pos=131071)
+    assert L.dsa_sparse_mla_attn_workspace_size(ctypes.byref(r8), ctypes.byref(d)) == \
+        8 * 16 * 128 * (512 * 2 + 4)
     fwd = L.dsa_forward_workspace_size(ctypes.byref(dec), ctypes.byref(d), 0)
     # rows of up to 32768 positions take one block each (their scores fit in the
     # block's registers): no top-k workspace, also when few rows leave CUs idle
