@@ -331,7 +331,7 @@ __global__ __launch_bounds__(SW * 64) void indexer_fp8_stream_kernel(
 }
 
 // Prefill block: PW waves x PRW query rows (fp8 queries in registers) over PKPB keys.
-// The keys are staged once per block, 64 at a time, HBM -> LDS by direct loads
+// The keys are staged once per block, 128 at a time, HBM -> LDS by direct loads
 // into PNBUF buffers three groups ahead; every wave reads its MFMA fragments from
 // LDS, so the block fetches each key once instead of once per wave.  Inside a
 // group, the 16-byte chunk c of key e sits in slot e * 8 + (c ^ (e & 7)), which
@@ -419,6 +419,9 @@ void indexer_fp8_prefill_kernel(
   float wq[PRW][16];
 #pragma unroll
   for (int i = 0; i < PRW; ++i) load_query(q_idx, q_scale, w, rr[i], qa[i], wq[i]);
+  // the queries are in before the key loop (s_waitcnt vmcnt(0), as a builtin the
+  // compiler's wait bookkeeping sees): the loop's vmcnt counts only the key copies
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 
   // B fragment of key tile kt: row e = 16 kt + n, bytes [32 g, 32 g + 32) = chunks
   // 2 g and 2 g + 1, each at its swizzled slot
@@ -474,73 +477,56 @@ void indexer_fp8_prefill_kernel(
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
       if (gi + 3 < ngroups) issue_group(gi + 3);
       const uint8_t* kg = kbuf[gi % PNBUF];
-      // fragments of the 64-key half u (key tiles 4 u .. 4 u + 3)
-      auto read_half = [&](int u, i32x8 (&kf)[4]) {
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          const uint8_t* row = kg + (64 * u + 16 * kt + n) * ID;
-          const i32x4 a = *reinterpret_cast<const i32x4*>(row + 16 * c0);
-          const i32x4 b = *reinterpret_cast<const i32x4*>(row + 16 * c1);
-          kf[kt] = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
+      const float* ksg = ksbuf[gi % PNBUF];
+      // The group as one pipeline of 64 MFMAs: m = 4 v + mt, unit v = (half u,
+      // key tile kt, row i) with v = 8 u + 2 kt + i, head tile mt.  Step m issues
+      // MFMA m and the epilogue of MFMA m - LAG (ReLU and 4 weighted head terms,
+      // 8 VALU ops, into head chain mt of its unit); a scheduling fence closes
+      // every step, so the matrix pipe and the VALU always have independent work
+      // (left to itself the compiler consumes each MFMA's result right after it
+      // and waits out its latency).  Fragment f = 4 u + kt (B operand of key tile
+      // kt of half u) is read from LDS when the group starts (f < 4) or once
+      // fragment f - 4 has issued its last MFMA.  Rows past their last position
+      // are computed too; such scores are never written out.
+      static_assert(PRW == 2 && PG == 128, "unit order v = 8 u + 2 kt + i");
+      constexpr int LAG = 2, NM = 64;
+      i32x8 kf[8];
+      auto read_frag = [&](int f) {
+        const uint8_t* row = kg + (64 * (f >> 2) + 16 * (f & 3) + n) * ID;
+        const i32x4 a = *reinterpret_cast<const i32x4*>(row + 16 * c0);
+        const i32x4 b = *reinterpret_cast<const i32x4*>(row + 16 * c1);
+        kf[f] = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
       };
-      // One 64-key half: 8 units (row i, key tile kt), each 4 MFMAs (the 64 heads)
-      // and 32 VALU ops of epilogue (ReLU and the weighted head sum of 4 values
-      // per head tile).  The MFMAs of unit v + 1 are issued among the epilogue of
-      // unit v, so the matrix pipe and the VALU work at the same time (in this
-      // kernel the epilogue costs about as much as the MFMAs).  Both rows are
-      // computed even when a row ends before this half; such scores are never
-      // written out.
-      auto compute_half = [&](int u, const i32x8 (&kf)[4]) {
-        const int k = kb0 + gi * PG + 64 * u;
-        const float ksv = ksbuf[gi % PNBUF][64 * u + l];
-        constexpr int NU = PRW * 4;
-        f32x4 acc[2][4];
-        float p[PRW][4];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-          acc[0][mt] = mfma_fp8_16x16x128(qa[0][mt], kf[0], f32x4{0.f, 0.f, 0.f, 0.f});
+      for (int f = 0; f < 4; ++f) read_frag(f);
+      const float ks0 = ksg[l], ks1 = ksg[64 + l];
+      f32x4 acc[LAG + 1];
+      float a[4], p[PRW][4];
 #pragma unroll
-        for (int v = 0; v < NU; ++v) {
-          const int i = v >> 2, kt = v & 3;
-          if (v + 1 < NU) {
-            const int i1 = (v + 1) >> 2, kt1 = (v + 1) & 3;
+      for (int m = 0; m < NM + LAG; ++m) {
+        if (m < NM) {
+          const int v = m >> 2, mt = m & 3, f = v >> 1, i = v & 1;
+          acc[m % (LAG + 1)] = mfma_fp8_16x16x128(qa[i][mt], kf[f], f32x4{0.f, 0.f, 0.f, 0.f});
+          if (mt == 3 && i == 1 && f + 4 < 8) read_frag(f + 4);
+        }
+        if (m >= LAG) {
+          const int e = m - LAG, v = e >> 2, mt = e & 3, i = v & 1, kt = (v >> 1) & 3;
+          const f32x4 x = acc[e % (LAG + 1)];
+          float c = wq[i][mt * 4] * relu_bits(x[0]);
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-              acc[(v + 1) & 1][mt] =
-                  mfma_fp8_16x16x128(qa[i1][mt], kf[kt1], f32x4{0.f, 0.f, 0.f, 0.f});
-          }
-          // four independent accumulation chains (one per head tile), so the
-          // FMAs do not wait on each other
-          float a[4];
+          for (int j = 1; j < 4; ++j) c = fmaf(wq[i][mt * 4 + j], relu_bits(x[j]), c);
+          a[mt] = c;
+          if (mt == 3) p[i][kt] = (a[0] + a[1]) + (a[2] + a[3]);
+          if ((e & 31) == 31) {  // both rows of half e >> 5 are complete
+            const int u = e >> 5;
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt) {
-            a[mt] = wq[i][mt * 4] * relu_bits(acc[v & 1][mt][0]);
-#pragma unroll
-            for (int e = 1; e < 4; ++e)
-              a[mt] = fmaf(wq[i][mt * 4 + e], relu_bits(acc[v & 1][mt][e]), a[mt]);
-          }
-          p[i][kt] = (a[0] + a[1]) + (a[2] + a[3]);
-          if (v + 1 < NU) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA of unit v + 1
-              __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // then 8 epilogue ops
-            }
+            for (int r = 0; r < PRW; ++r)
+              sbuf[wv * PRW + r][gi * PG + 64 * u + l] =
+                  reduce_groups(p[r][0], p[r][1], p[r][2], p[r][3]) * (u ? ks1 : ks0);
           }
         }
-#pragma unroll
-        for (int i = 0; i < PRW; ++i)
-          if (k <= tt[i])  // wave-uniform
-            sbuf[wv * PRW + i][gi * PG + 64 * u + l] =
-                reduce_groups(p[i][0], p[i][1], p[i][2], p[i][3]) * ksv;
-      };
-      // the second half's fragments are read while the first half is multiplied
-      i32x8 kfa[4], kfb[4];
-      read_half(0, kfa);
-      read_half(1, kfb);
-      compute_half(0, kfa);
-      compute_half(1, kfb);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     // The key block's scores leave LDS after its loop, so that no vector-memory
     // store sits between the direct loads whose completion the loop counts with
