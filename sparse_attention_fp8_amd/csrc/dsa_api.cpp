@@ -112,12 +112,13 @@ constexpr size_t kLatentRow = dsa::kQkDim * sizeof(uint16_t);  // bf16 latent en
 dsa_status run_indexer(const dsa_rows& rows, const dsa_dims& dims, const void* q_idx,
                        const float* q_scale, const float* w, const void* k_idx,
                        const float* k_scale, float* scores, int64_t ld, hipStream_t stream,
-                       const dsa::PageMap& pm, dsa::ClearWords clear = dsa::ClearWords()) {
+                       const dsa::PageMap& pm, dsa::ClearWords clear = dsa::ClearWords(),
+                       uint32_t* rowmm = nullptr) {
   hipError_t err;
   if (dims.idx_dtype == DSA_FP8_E4M3FN)
     err = dsa::launch_indexer_fp8(rows, static_cast<const uint8_t*>(q_idx), q_scale, w,
                                   static_cast<const uint8_t*>(k_idx), k_scale, scores, ld, stream,
-                                  pm, clear);
+                                  pm, clear, rowmm);
   else
     err = dsa::launch_indexer_f32(rows, dims, static_cast<const float*>(q_idx), w,
                                   static_cast<const float*>(k_idx), scores, ld, stream);
@@ -125,9 +126,10 @@ dsa_status run_indexer(const dsa_rows& rows, const dsa_dims& dims, const void* q
 }
 
 dsa_status run_topk(const dsa_rows& rows, int topk, const float* scores, int64_t ld,
-                    int32_t* indices, void* ws, hipStream_t stream, bool counts_cleared = false) {
+                    int32_t* indices, void* ws, hipStream_t stream, bool counts_cleared = false,
+                    uint32_t* rowmm = nullptr) {
   const hipError_t err = dsa::launch_topk(rows, topk, scores, ld, indices, ws, stream,
-                                          counts_cleared);
+                                          counts_cleared, rowmm);
   return err == hipSuccess ? DSA_OK : hip_fail(err, "top-k launch");
 }
 
@@ -155,6 +157,22 @@ size_t forward_topk_ws(const dsa_rows& rows, int CH) {
   b.num_rows = rows.num_rows - (rows.num_rows - 1) / CH * CH;
   const size_t x = dsa::topk_workspace_bytes(a), y = dsa::topk_workspace_bytes(b);
   return x > y ? x : y;
+}
+
+// A chunk whose fp8 indexer runs the tiled kernel and whose top-k streams its rows
+// passes each row's score extremes from the one to the other (two words per row),
+// so the top-k skips its min / max pass over the scores.
+bool forward_fuses_extremes(const dsa_rows& sub, const dsa_dims& dims) {
+  return dims.idx_dtype == DSA_FP8_E4M3FN && dsa::indexer_uses_tiles(sub) &&
+         dsa::topk_streams_rows(sub);
+}
+
+size_t forward_extremes_bytes(const dsa_rows& rows, const dsa_dims& dims, int CH) {
+  dsa_rows a = rows, b = rows;
+  a.num_rows = CH;
+  b.num_rows = rows.num_rows - (rows.num_rows - 1) / CH * CH;
+  if (!forward_fuses_extremes(a, dims) && !forward_fuses_extremes(b, dims)) return 0;
+  return (size_t)CH * 2 * sizeof(uint32_t);
 }
 
 dsa_status forward_impl(const dsa_rows* rows, const dsa_dims* dims, const dsa_pages* pages,
@@ -191,6 +209,9 @@ dsa_status forward_impl(const dsa_rows* rows, const dsa_dims* dims, const dsa_pa
   ws += align_up((size_t)CH * dims->topk * sizeof(int32_t), 256);
   void* topk_ws = ws;
   ws += align_up(forward_topk_ws(*rows, CH), 256);
+  uint32_t* rowmm = reinterpret_cast<uint32_t*>(ws);
+  ws += align_up(forward_extremes_bytes(*rows, *dims, CH), 256);
+  bool rowmm_zero = false;  // every top-k launch leaves the words it read at zero
   void* attn_ws = ws;
   const hipStream_t s = as_stream(stream);
 
@@ -208,11 +229,18 @@ dsa_status forward_impl(const dsa_rows* rows, const dsa_dims* dims, const dsa_pa
     // the fp8 indexer clears the top-k launch's per-row counts, saving it a launch
     const dsa::ClearWords clear = dims->idx_dtype == DSA_FP8_E4M3FN
                                       ? dsa::topk_counts(sub, topk_ws) : dsa::ClearWords();
+    const bool fuse = forward_fuses_extremes(sub, *dims);
+    if (fuse && !rowmm_zero) {
+      const hipError_t err = dsa::launch_zero_words(rowmm, 2 * CH, s);
+      if (err != hipSuccess) return hip_fail(err, "workspace clear");
+      rowmm_zero = true;
+    }
     st = run_indexer(sub, *dims, static_cast<const uint8_t*>(q_idx) + r0 * qi_row,
                      q_scale ? q_scale + r0 * hi : nullptr, w + r0 * hi, k_idx, k_scale, scores,
-                     ld, s, pm, clear);
+                     ld, s, pm, clear, fuse ? rowmm : nullptr);
     if (st != DSA_OK) return st;
-    st = run_topk(sub, dims->topk, scores, ld, idx, topk_ws, s, clear.ptr != nullptr);
+    st = run_topk(sub, dims->topk, scores, ld, idx, topk_ws, s, clear.ptr != nullptr,
+                  fuse ? rowmm : nullptr);
     if (st != DSA_OK) return st;
     st = run_attn(sub, *dims, static_cast<const uint8_t*>(q) + r0 * q_row, latent, idx,
                   softmax_scale, static_cast<uint8_t*>(out) + r0 * o_row,
@@ -370,6 +398,7 @@ size_t dsa_forward_workspace_size(const dsa_rows* rows, const dsa_dims* dims, in
   size_t bytes = align_up((size_t)CH * ld * sizeof(float), 256);
   bytes += align_up((size_t)CH * dims->topk * sizeof(int32_t), 256);
   bytes += align_up(forward_topk_ws(*rows, CH), 256);
+  bytes += align_up(forward_extremes_bytes(*rows, *dims, CH), 256);
   // the last chunk may hold fewer rows and therefore use more attention splits
   const int last = R - (R - 1) / CH * CH;
   const size_t attn = dsa::attn_workspace_bytes(CH, *dims);

@@ -49,7 +49,13 @@ struct ClearWords {
 hipError_t launch_indexer_fp8(const dsa_rows& rows, const uint8_t* q_idx, const float* q_scale,
                               const float* w, const uint8_t* k_idx, const float* k_scale,
                               float* scores, int64_t ld, hipStream_t stream,
-                              const PageMap& pm = PageMap(), ClearWords clear = ClearWords());
+                              const PageMap& pm = PageMap(), ClearWords clear = ClearWords(),
+                              uint32_t* rowmm = nullptr);
+// Whether launch_indexer_fp8 runs the tiled (prefill) kernel for these rows.  Only that
+// kernel accepts rowmm: two words per row (2 r: max, 2 r + 1: ~min, as order-preserving
+// float keys) that must start at zero and that it raises with atomic maxima to the
+// extremes of the row's non-NaN scores at positions <= its own.
+bool indexer_uses_tiles(const dsa_rows& rows);
 
 hipError_t launch_indexer_f32(const dsa_rows& rows, const dsa_dims& dims, const float* q_idx,
                               const float* w, const float* k_idx, float* scores, int64_t ld,
@@ -62,9 +68,16 @@ size_t topk_workspace_bytes(const dsa_rows& rows);
 ClearWords topk_counts(const dsa_rows& rows, void* workspace);
 // counts_cleared: an earlier launch on the stream has zeroed topk_counts(rows, ws);
 // otherwise the launch zeroes them itself first.
+// rowmm (only when topk_streams_rows): the extremes the tiled indexer left for these
+// rows (see indexer_uses_tiles); the launch reads them and sets them back to zero.
 hipError_t launch_topk(const dsa_rows& rows, int topk, const float* scores, int64_t ld,
                        int32_t* indices, void* workspace, hipStream_t stream,
-                       bool counts_cleared = false);
+                       bool counts_cleared = false, uint32_t* rowmm = nullptr);
+// Whether launch_topk runs one block per row with rows longer than its registers hold
+// (streamed from memory once per pass).
+bool topk_streams_rows(const dsa_rows& rows);
+// Sets n words to zero (a fill kernel, so a captured stream records no memset node).
+hipError_t launch_zero_words(uint32_t* p, int n, hipStream_t stream);
 
 // Number of splits of each row's selected set used by the bf16 attention for R rows.
 int attn_num_splits(int num_rows, int topk);

@@ -98,7 +98,7 @@ __device__ __forceinline__ void prefill_rows(const uint8_t* __restrict__ q_idx,
                                              const float* __restrict__ ksc, const int* rr,
                                              const int* tt, int kb0, int kend,
                                              float* __restrict__ scores, int64_t ld,
-                                             const PageMap& pm, int b) {
+                                             const PageMap& pm, int b, float* mx, float* mn) {
   const int l = lane_id(), g = l >> 4, n = l & 15;
   i32x8 qa[NR][4];
   float wq[NR][16];
@@ -130,7 +130,11 @@ __device__ __forceinline__ void prefill_rows(const uint8_t* __restrict__ q_idx,
       const float p2 = head_partial(qa[i], wq[i], kb[2]);
       const float p3 = head_partial(qa[i], wq[i], kb[3]);
       const float s = reduce_groups(p0, p1, p2, p3) * ks;
-      if (k + l <= tt[i]) scores[(size_t)rr[i] * ld + k + l] = s;
+      if (k + l <= tt[i]) {
+        scores[(size_t)rr[i] * ld + k + l] = s;
+        mx[i] = fmaxf(mx[i], s);  // a NaN score leaves both unchanged
+        mn[i] = fminf(mn[i], s);
+      }
     }
   };
   i32x8 ka[4], kb[4];
@@ -348,7 +352,8 @@ void indexer_fp8_prefill_kernel(
     const float* __restrict__ w, const uint8_t* __restrict__ k_idx,
     const float* __restrict__ k_scale, const int32_t* __restrict__ row_seq,
     const int32_t* __restrict__ row_pos, int R, int B, int N, int ksplit,
-    float* __restrict__ scores, int64_t ld, PageMap pm, ClearWords clear) {
+    float* __restrict__ scores, int64_t ld, PageMap pm, ClearWords clear,
+    uint32_t* __restrict__ rowmm) {
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[PNBUF][PGB];
   if (blockIdx.x == 0)  // words a following launch needs zeroed
     for (int i = threadIdx.x; i < clear.n; i += PW * 64) clear.ptr[i] = 0u;
@@ -399,6 +404,12 @@ void indexer_fp8_prefill_kernel(
 
   if (Bmin != Bmax) {
     // rows of several sequences: each wave walks its own rows' keys from global memory
+    float mx[PRW], mn[PRW];
+#pragma unroll
+    for (int i = 0; i < PRW; ++i) {
+      mx[i] = -INFINITY;
+      mn[i] = INFINITY;
+    }
     for (int kb0 = ks * PKPB; kb0 <= Tmax; kb0 += ksplit * PKPB) {
 #pragma unroll
       for (int i = 0; i < PRW; ++i) {
@@ -406,7 +417,17 @@ void indexer_fp8_prefill_kernel(
         const int kend = min(kb0 + PKPB, tt[i] + 1);
         prefill_rows<1, PAGED>(q_idx, q_scale, w, PAGED ? k_idx : k_idx + (size_t)bs[i] * N * ID,
                                PAGED ? k_scale : k_scale + (size_t)bs[i] * N, &rr[i], &tt[i],
-                               kb0, kend, scores, ld, pm, bs[i]);
+                               kb0, kend, scores, ld, pm, bs[i], &mx[i], &mn[i]);
+      }
+    }
+    if (rowmm != nullptr) {
+#pragma unroll
+      for (int i = 0; i < PRW; ++i) {
+        const float a = wave_max(mx[i]), c = wave_min(mn[i]);
+        if (l == 0 && tt[i] >= 0) {
+          atomicMax(&rowmm[2 * rr[i]], float_key(a));
+          atomicMax(&rowmm[2 * rr[i] + 1], ~float_key(c));
+        }
       }
     }
     return;
@@ -428,6 +449,16 @@ void indexer_fp8_prefill_kernel(
   const int x = n & 7;  // e & 7 for every tile
   const int c0 = (2 * g) ^ x, c1 = (2 * g + 1) ^ x;
 
+  // extremes of the scores this thread writes out, per write-out step (one row each)
+  constexpr int V4 = PKPB / 4;
+  constexpr int WJ = PROWS * V4 / (PW * 64);  // write-out steps per thread
+  static_assert(V4 % 64 == 0 && PROWS * V4 == WJ * PW * 64, "one row per wave and step");
+  float wmx[WJ], wmn[WJ];
+#pragma unroll
+  for (int j = 0; j < WJ; ++j) {
+    wmx[j] = -INFINITY;
+    wmn[j] = INFINITY;
+  }
   for (int kb0 = ks * PKPB; kb0 <= Tmax; kb0 += ksplit * PKPB) {
     const int kend = min(kb0 + PKPB, Tmax + 1);
     const int ngroups = (kend - kb0 + PG - 1) / PG;
@@ -532,24 +563,52 @@ void indexer_fp8_prefill_kernel(
     // store sits between the direct loads whose completion the loop counts with
     // vmcnt.  Each valid row writes keys [kb0, kend) (entries past its own
     // position are left unspecified, as the interface allows).
+    // Write-out step j of a thread covers row (threadIdx.x + 512 j) / V4, the same
+    // row in every key block; the scores at positions <= the row's own also update
+    // the step's extremes (fmaxf / fminf pass over a NaN).
     __syncthreads();
-    constexpr int V4 = PKPB / 4;
     const int nv4 = (kend - kb0 + 3) / 4;
-    for (int idx = threadIdx.x; idx < PROWS * V4; idx += PW * 64) {
-      const int row = idx / V4, c4 = idx - row * V4;
-      const int r = tile * PROWS + row;
-      if (c4 >= nv4 || r >= R) continue;
-      const int t = row_pos[r];
-      const int s0 = kb0 + 4 * c4;
-      if (t < s0) continue;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(&sbuf[row][4 * c4]);
-      float* dst = scores + (size_t)r * ld + s0;
-      if (s0 + 4 <= kend && ((reinterpret_cast<uintptr_t>(dst) & 15) == 0)) {
-        *reinterpret_cast<f32x4*>(dst) = v;
-      } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (s0 + e < kend) dst[e] = v[e];
+    for (int j = 0; j < WJ; ++j) {
+      const int idx = threadIdx.x + j * PW * 64;
+      const int row = idx / V4, c4 = idx - row * V4;  // row is wave-uniform
+      const int r = tile * PROWS + row;
+      if (c4 < nv4 && r < R) {
+        const int t = row_pos[r];
+        const int s0 = kb0 + 4 * c4;
+        if (t >= s0) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(&sbuf[row][4 * c4]);
+          float* dst = scores + (size_t)r * ld + s0;
+          if (s0 + 4 <= kend && ((reinterpret_cast<uintptr_t>(dst) & 15) == 0)) {
+            *reinterpret_cast<f32x4*>(dst) = v;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (s0 + e < kend) dst[e] = v[e];
+          }
+          if (s0 + 3 <= t) {
+            wmx[j] = fmaxf(wmx[j], fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+            wmn[j] = fminf(wmn[j], fminf(fminf(v[0], v[1]), fminf(v[2], v[3])));
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (s0 + e <= t) {
+                wmx[j] = fmaxf(wmx[j], v[e]);
+                wmn[j] = fminf(wmn[j], v[e]);
+              }
+          }
+        }
+      }
+    }
+  }
+  if (rowmm != nullptr) {  // block-uniform
+#pragma unroll
+    for (int j = 0; j < WJ; ++j) {
+      const int r = tile * PROWS + ((int)threadIdx.x + j * PW * 64) / V4;
+      const float a = wave_max(wmx[j]), c = wave_min(wmn[j]);
+      if (l == 0 && r < R) {
+        atomicMax(&rowmm[2 * r], float_key(a));
+        atomicMax(&rowmm[2 * r + 1], ~float_key(c));
       }
     }
   }
@@ -586,14 +645,18 @@ __global__ __launch_bounds__(256) void indexer_f32_kernel(
 
 }  // namespace
 
+bool indexer_uses_tiles(const dsa_rows& rows) {
+  return rows.num_rows >= 8 && rows.num_rows >= 4 * rows.num_seqs;
+}
+
 hipError_t launch_indexer_fp8(const dsa_rows& rows, const uint8_t* q_idx, const float* q_scale,
                               const float* w, const uint8_t* k_idx, const float* k_scale,
                               float* scores, int64_t ld, hipStream_t stream, const PageMap& pm,
-                              ClearWords clear) {
+                              ClearWords clear, uint32_t* rowmm) {
   const bool paged = pm.table != nullptr;
   const int R = rows.num_rows;
   const int L = rows.max_pos + 1;
-  if (R >= 8 && R >= 4 * rows.num_seqs) {
+  if (indexer_uses_tiles(rows)) {
     // key blocks are split over ksplit blocks per row tile (enough blocks to fill
     // the GPU several times over); each block loops over its share
     const int nkb = (L + PKPB - 1) / PKPB;
@@ -603,8 +666,9 @@ hipError_t launch_indexer_fp8(const dsa_rows& rows, const uint8_t* q_idx, const 
     auto kern = paged ? indexer_fp8_prefill_kernel<true> : indexer_fp8_prefill_kernel<false>;
     hipLaunchKernelGGL(kern, dim3(tiles * ksplit), dim3(PW * 64), 0, stream, q_idx, q_scale, w,
                        k_idx, k_scale, rows.row_seq, rows.row_pos, R, rows.num_seqs,
-                       rows.max_ctx, ksplit, scores, ld, pm, clear);
+                       rows.max_ctx, ksplit, scores, ld, pm, clear, rowmm);
   } else {
+    if (rowmm != nullptr) return hipErrorInvalidValue;  // only the tiled kernel keeps extremes
     const int nkb = (L + SKPB - 1) / SKPB;
     auto kern = paged ? indexer_fp8_stream_kernel<true> : indexer_fp8_stream_kernel<false>;
     hipLaunchKernelGGL(kern, dim3(R * nkb), dim3(SW * 64), 0, stream, q_idx, q_scale, w, k_idx,

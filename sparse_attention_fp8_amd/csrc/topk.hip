@@ -126,11 +126,17 @@ __device__ __forceinline__ uint2 block_scan2(uint32_t* a, uint32_t* b, int M,
 constexpr int kResidentMax = 32768;  // longest row staged in LDS (128 KB)
 
 // One row at position t (0 <= t < CAP): row = its scores, orow = its k outputs.
-// sel / tie are LDS bitmaps covering CAP positions.
+// sel / tie are LDS bitmaps covering CAP positions.  A streamed row whose score
+// extremes are known (have_mm: lo / hi over its non-NaN scores) skips the min / max
+// pass.  Any lo < hi gives the same selection (the bins only need to be the same in
+// every pass: a score below lo, or a NaN read as -inf, lands in bin 0); lo >= hi
+// (all scores equal, or none known) takes the pass, which reads NaN as -inf.
 template <bool RESIDENT, int JV>
 __device__ __forceinline__ void topk_row(const float* __restrict__ row, int t, int topk,
                                          int vec_ok, int32_t* __restrict__ orow,
-                                         TopkShared& sh, uint32_t* sel, uint32_t* tie) {
+                                         TopkShared& sh, uint32_t* sel, uint32_t* tie,
+                                         bool have_mm = false, float mm_lo = 0.f,
+                                         float mm_hi = 0.f) {
   constexpr int CH = 4 * TK_T * JV;
   constexpr int CAP = RESIDENT ? CH : BITMAP_POS;  // positions the bitmaps cover
   constexpr int BM_WORDS = CAP / 32;
@@ -164,7 +170,8 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ row, int t, i
   //      stays in rv for every later pass: thread tid holds groups j * 1024 + tid.
   f32x4 rv[RESIDENT ? JV : 1];
   float mn = INFINITY, mx = -INFINITY;
-  for (int c = 0; c < nchunks; ++c) {
+  const bool pass1 = RESIDENT || !have_mm || !(mm_hi > mm_lo);  // block-uniform
+  for (int c = 0; pass1 && c < nchunks; ++c) {
     f32x4 v[JV];
 #pragma unroll
     for (int j = 0; j < JV; ++j) {
@@ -196,20 +203,27 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ row, int t, i
       if (RESIDENT) rv[j] = s < L ? v[j] : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     }
   }
-  mn = wave_min(mn);
-  mx = wave_max(mx);
-  if (l == 0) {
-    sh.fred[0][wv] = mn;
-    sh.fred[1][wv] = mx;
+  if (pass1) {
+    mn = wave_min(mn);
+    mx = wave_max(mx);
+    if (l == 0) {
+      sh.fred[0][wv] = mn;
+      sh.fred[1][wv] = mx;
+    }
   }
   for (int i = tid; i < NBIN; i += TK_T) sh.hist[i] = 0u;
   __syncthreads();
-  mn = sh.fred[0][0];
-  mx = sh.fred[1][0];
+  if (pass1) {
+    mn = sh.fred[0][0];
+    mx = sh.fred[1][0];
 #pragma unroll
-  for (int i = 1; i < TK_W; ++i) {
-    mn = fminf(mn, sh.fred[0][i]);
-    mx = fmaxf(mx, sh.fred[1][i]);
+    for (int i = 1; i < TK_W; ++i) {
+      mn = fminf(mn, sh.fred[0][i]);
+      mx = fmaxf(mx, sh.fred[1][i]);
+    }
+  } else {
+    mn = mm_lo;
+    mx = mm_hi;
   }
   if (!(mx > mn)) {  // all candidates equal: the n lowest positions
     for (int i = tid; i < topk; i += TK_T) orow[i] = i < n ? i : -1;
@@ -444,19 +458,39 @@ __global__ __launch_bounds__(TK_T) void topk_kernel(const float* __restrict__ sc
   topk_row<RESIDENT, JV>(scores + (size_t)r * ld, t, topk, vec_ok, orow, sh, sel, tie);
 }
 
+// float of an order-preserving key (inverse of float_key; +0.0 for either zero)
+__device__ __forceinline__ float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
 // Rows of any length up to BITMAP_POS, chosen per row: a row of at most
 // kResidentMax positions is held in registers, a longer one is streamed.  Used when
 // the host bound on the positions is above kResidentMax, since a looser bound (a
 // chunk of a long prefill, say) says nothing about each row's own length.
+// rowmm (optional): the score extremes of every row, two words per row as the
+// tiled indexer leaves them (2 r: max key, 2 r + 1: ~min key, over the non-NaN
+// scores); a streamed row uses them instead of its min / max pass, and every row's
+// block sets its two words back to zero for the next indexer launch.
 __global__ __launch_bounds__(TK_T) void topk_kernel_any(const float* __restrict__ scores,
                                                         int64_t ld,
                                                         const int32_t* __restrict__ row_pos,
                                                         int max_pos, int topk, int vec_ok,
-                                                        int32_t* __restrict__ out) {
+                                                        int32_t* __restrict__ out,
+                                                        uint32_t* __restrict__ rowmm) {
   __shared__ TopkShared sh;
   __shared__ uint32_t sel[BITMAP_POS / 32];
   __shared__ uint32_t tie[BITMAP_POS / 32];
+  __shared__ uint32_t mmw[2];
   const int r = blockIdx.x;
+  if (rowmm != nullptr) {  // block-uniform
+    if (threadIdx.x == 0) {
+      mmw[0] = rowmm[2 * r];
+      mmw[1] = rowmm[2 * r + 1];
+      rowmm[2 * r] = 0u;
+      rowmm[2 * r + 1] = 0u;
+    }
+    __syncthreads();
+  }
   const int t = row_pos[r];
   int32_t* orow = out + (size_t)r * topk;
   if (t < 0 || t > max_pos || (int64_t)t >= ld || t >= BITMAP_POS) {
@@ -467,7 +501,8 @@ __global__ __launch_bounds__(TK_T) void topk_kernel_any(const float* __restrict_
   if (t < kResidentMax)  // block-uniform
     topk_row<true, kResidentMax / (4 * TK_T)>(row, t, topk, vec_ok, orow, sh, sel, tie);
   else
-    topk_row<false, 4>(row, t, topk, vec_ok, orow, sh, sel, tie);
+    topk_row<false, 4>(row, t, topk, vec_ok, orow, sh, sel, tie, rowmm != nullptr,
+                       key_float(~mmw[1]), key_float(mmw[0]));
 }
 
 // ---------------------------------------------------------------------------
@@ -911,13 +946,24 @@ size_t topk_workspace_bytes(const dsa_rows& rows) {
   return R * P * MB_CHUNK * sizeof(uint2) + ((R * P + R) * sizeof(uint32_t) + 15) / 16 * 16;
 }
 
+hipError_t launch_zero_words(uint32_t* p, int n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(topk_mb_zero_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
+}
+
+bool topk_streams_rows(const dsa_rows& rows) {
+  return !topk_use_multi(rows) && rows.max_pos + 1 > kResidentMax;
+}
+
 hipError_t launch_topk(const dsa_rows& rows, int topk, const float* scores, int64_t ld,
                        int32_t* indices, void* workspace, hipStream_t stream,
-                       bool counts_cleared) {
+                       bool counts_cleared, uint32_t* rowmm) {
   const int R = rows.num_rows;
   const int L = rows.max_pos + 1;
   const int vec_ok = (ld % 4 == 0) && (reinterpret_cast<uintptr_t>(scores) % 16 == 0);
   if (L > BITMAP_POS) return hipErrorInvalidValue;  // refused on the host before this
+  if (rowmm != nullptr && !topk_streams_rows(rows)) return hipErrorInvalidValue;
   if (topk_use_multi(rows)) {
     const int nchunk = topk_chunks(rows);
     uint2* cand = static_cast<uint2*>(workspace);
@@ -939,7 +985,7 @@ hipError_t launch_topk(const dsa_rows& rows, int topk, const float* scores, int6
                        rows.row_pos, rows.max_pos, topk, vec_ok, indices);
   } else {
     hipLaunchKernelGGL(topk_kernel_any, dim3(R), dim3(TK_T), 0, stream, scores, ld, rows.row_pos,
-                       rows.max_pos, topk, vec_ok, indices);
+                       rows.max_pos, topk, vec_ok, indices, rowmm);
   }
   return hipGetLastError();
 }

@@ -461,6 +461,56 @@ def test_forward_ragged_decode(dsa):
         check_attention(o_all[i], o_ref)
 
 
+def test_forward_long_rows_match_separate_calls(dsa):
+    """Long-context chunks pass each row's score extremes from the tiled indexer to
+    the streamed top-k, which then skips its min / max pass.  The selections must be
+    the same bits as the separate indexer and top-k calls on the same rows: two
+    chunks of 128 rows (the second reuses the words the first left at zero), tiles
+    spanning two sequences (the indexer's per-row path) and tiles of one sequence,
+    rows shorter and longer than the top-k's register-resident length."""
+    cfg = di.CONFIGS["decode128k"]
+    inp = dev_inputs("decode128k")
+    R, CH = 256, 128
+    seq = np.zeros(R, dtype=np.int32)
+    pos = np.zeros(R, dtype=np.int32)
+    for i in range(CH):                      # chunk 0: sequences 0 and 1 alternate
+        seq[i] = i & 1
+        pos[i] = 40000 + 7 * i if i & 1 == 0 else 131071 - 11 * i
+    pos[5], pos[9], pos[12] = 1000, 0, 32768
+    for i in range(CH, R):                   # chunk 1: 16-row tiles of sequences 2 / 3
+        j = i - CH
+        seq[i] = 2 + ((j >> 4) & 1)
+        pos[i] = 70000 + 13 * j if seq[i] == 2 else 100000 + 3 * j
+    pos[CH + 3], pos[CH + 20] = 32767, 32768
+    seq_t, pos_t = torch.from_numpy(seq).cuda(), torch.from_numpy(pos).cuda()
+    rs = dsa.rows_struct(seq_t, pos_t, cfg.num_seqs, cfg.max_ctx, cfg.kv_len - 1)
+    qsel = torch.arange(R, device="cuda") % cfg.num_rows
+    q_idx, q_scale = inp.q_idx[qsel].contiguous(), inp.q_scale[qsel].contiguous()
+    w, q = inp.w[qsel].contiguous(), inp.q[qsel].contiguous()
+    dims = dsa.Dims.from_config(cfg)
+    # second pass: NaN key codes give NaN scores (read as -inf by the top-k) in rows of
+    # both chunks
+    k_nan = inp.k_idx.clone()
+    k_nan[0, 5000:5040, 0] = 0x7F
+    k_nan[1, 90000:90100, 7] = 0x7F
+    k_nan[3, 40000:40064, 1] = 0xFF
+    for k_idx, what in ((inp.k_idx, "finite"), (k_nan, "NaN keys")):
+        idx_f = torch.empty(R, cfg.topk, dtype=torch.int32, device="cuda")
+        dsa.forward(rs, dims, q_idx, q_scale, w, k_idx, inp.k_scale, q, inp.latent, cfg.scale,
+                    indices_out=idx_f, chunk_rows=CH)
+        for a in range(0, R, CH):
+            rc = dsa.rows_struct(seq_t[a:a + CH], pos_t[a:a + CH], cfg.num_seqs, cfg.max_ctx,
+                                 cfg.kv_len - 1)
+            sc = dsa.indexer_scores(rc, dims, q_idx[a:a + CH], q_scale[a:a + CH], w[a:a + CH],
+                                    k_idx, inp.k_scale, ld=cfg.kv_len)
+            idx_s = dsa.topk(rc, cfg.topk, sc)
+            torch.cuda.synchronize()
+            same = (idx_f[a:a + CH] == idx_s).all(dim=1).cpu().numpy()
+            assert same.all(), f"{what}, chunk at {a}: rows {np.nonzero(~same)[0][:8]} differ"
+        print(f"[forward] long rows ({what}): fused extremes give the separate calls' "
+              f"selections", flush=True)
+
+
 def test_forward_deterministic(dsa):
     """Two runs give bitwise-identical outputs, and a NaN-filled workspace does not
     leak into them (catches races and reads of uninitialised scratch)."""
