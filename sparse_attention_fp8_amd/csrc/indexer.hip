@@ -310,13 +310,31 @@ __global__ __launch_bounds__(SW * 64) void indexer_fp8_stream_kernel(
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     static_assert(SLOADS == 9 && SDEPTH == 3, "wait counts above");
     const uint8_t* kg = kring[wv][j % SDEPTH];
-    float p[4];
+    i32x8 kf[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       const uint8_t* row = kg + (16 * kt + n) * ID;
       const i32x4 a0 = *reinterpret_cast<const i32x4*>(row + 16 * c0);
       const i32x4 a1 = *reinterpret_cast<const i32x4*>(row + 16 * c1);
-      p[kt] = head_partial(qa, wq, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+      kf[kt] = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    // 16 MFMAs (key tile kt = m >> 2, head tile mt = m & 3); step m issues MFMA m and
+    // the epilogue of MFMA m - 2, a scheduling fence closing each step
+    float p[4], hp[4];
+    f32x4 acc[3];
+#pragma unroll
+    for (int m = 0; m < 18; ++m) {
+      if (m < 16) acc[m % 3] = mfma_fp8_16x16x128(qa[m & 3], kf[m >> 2], f32x4{0.f, 0.f, 0.f, 0.f});
+      if (m >= 2) {
+        const int e = m - 2, mt = e & 3;
+        const f32x4 x = acc[e % 3];
+        float c = wq[mt * 4] * relu_bits(x[0]);
+#pragma unroll
+        for (int v = 1; v < 4; ++v) c = fmaf(wq[mt * 4 + v], relu_bits(x[v]), c);
+        hp[mt] = c;
+        if (mt == 3) p[e >> 2] = (hp[0] + hp[1]) + (hp[2] + hp[3]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     sout[SGK * (wv + SW * j) + l] = reduce_groups(p[0], p[1], p[2], p[3]) * sring[wv][j % SDEPTH][l];
   }
