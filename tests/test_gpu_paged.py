@@ -171,6 +171,42 @@ def test_paged_multi_sequence_tiles(dsa):
         check_scores(got[r, : row.t + 1], host.scores(row))
 
 
+def test_paged_long_rows_forward(dsa):
+    """Rows longer than the top-k's register-resident length in chunks of 128: the
+    paged forward (whose tiled indexer passes each row's score extremes to the
+    top-k) equals the contiguous forward bit for bit, on tiles spanning two
+    sequences and tiles of one sequence."""
+    cfg = di.CONFIGS["decode128k"]
+    inp = dev_inputs("decode128k")
+    pages, k_pool, ks_pool, lat_pool = make_pools(dsa, inp, 64, extra=5, seed=11)
+    R, CH = 256, 128
+    seq = np.zeros(R, dtype=np.int32)
+    pos = np.zeros(R, dtype=np.int32)
+    for i in range(CH):
+        seq[i] = i & 1
+        pos[i] = 40000 + 7 * i if i & 1 == 0 else 131071 - 11 * i
+    for i in range(CH, R):
+        j = i - CH
+        seq[i] = 2 + ((j >> 4) & 1)
+        pos[i] = 70000 + 13 * j if seq[i] == 2 else 100000 + 3 * j
+    pos[7], pos[CH + 1] = 500, 32768
+    rs = dsa.rows_struct(torch.from_numpy(seq).cuda(), torch.from_numpy(pos).cuda(),
+                         cfg.num_seqs, cfg.max_ctx, cfg.kv_len - 1)
+    sel = torch.arange(R, device="cuda") % cfg.num_rows
+    q_idx, q_scale, w, q = (inp.q_idx[sel].contiguous(), inp.q_scale[sel].contiguous(),
+                            inp.w[sel].contiguous(), inp.q[sel].contiguous())
+    dims = dsa.Dims.from_config(cfg)
+    i_c = torch.empty(R, cfg.topk, dtype=torch.int32, device="cuda")
+    i_p = torch.empty_like(i_c)
+    o_c, _, _ = dsa.forward(rs, dims, q_idx, q_scale, w, inp.k_idx, inp.k_scale, q, inp.latent,
+                            cfg.scale, indices_out=i_c, chunk_rows=CH)
+    o_p, _, _ = dsa.forward_paged(rs, dims, pages, q_idx, q_scale, w, k_pool, ks_pool, q,
+                                  lat_pool, cfg.scale, indices_out=i_p, chunk_rows=CH)
+    torch.cuda.synchronize()
+    assert torch.equal(i_c, i_p), "paged selection differs"
+    assert torch.equal(o_c, o_p), "paged output differs"
+
+
 def test_paged_table_entries_out_of_range(dsa):
     """Block-table entries outside the pool are read as page 0: the call completes
     and every score stays finite (its value is unspecified)."""
