@@ -511,6 +511,49 @@ def test_forward_long_rows_match_separate_calls(dsa):
               f"selections", flush=True)
 
 
+def test_forward_long_rows_graph_replays(dsa):
+    """The long-row forward (a fill kernel clears the extremes words, every top-k
+    block clears its row's words again) captured in a HIP graph: three replays, with
+    eager calls of the same forward between them, each give the eager call's bits."""
+    cfg = di.CONFIGS["decode128k"]
+    inp = dev_inputs("decode128k")
+    R, CH = 256, 128
+    pos = torch.tensor([40000 + 97 * i for i in range(R)], dtype=torch.int32, device="cuda")
+    pos[3], pos[200] = 20000, 0
+    seq = (torch.arange(R, device="cuda") // 64).to(torch.int32)
+    rs = dsa.rows_struct(seq, pos, cfg.num_seqs, cfg.max_ctx, cfg.kv_len - 1)
+    sel = torch.arange(R, device="cuda") % cfg.num_rows
+    q_idx, q_scale = inp.q_idx[sel].contiguous(), inp.q_scale[sel].contiguous()
+    w, q = inp.w[sel].contiguous(), inp.q[sel].contiguous()
+    dims = dsa.Dims.from_config(cfg)
+    out = torch.empty(R, cfg.n_heads, cfg.v_dim, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(R, cfg.n_heads, dtype=torch.float32, device="cuda")
+    idx = torch.empty(R, cfg.topk, dtype=torch.int32, device="cuda")
+    ws = torch.empty(dsa.forward_workspace_size(rs, dims, CH), dtype=torch.uint8, device="cuda")
+
+    def run():
+        dsa.forward(rs, dims, q_idx, q_scale, w, inp.k_idx, inp.k_scale, q, inp.latent,
+                    cfg.scale, out=out, lse=lse, indices_out=idx, chunk_rows=CH, workspace=ws)
+
+    run()
+    torch.cuda.synchronize()
+    ref = (out.clone(), lse.clone(), idx.clone())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.zero_(); idx.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1]) and torch.equal(idx, ref[2]), \
+            f"replay {rep} differs from the eager call"
+        run()  # eager work between the replays
+        torch.cuda.synchronize()
+        assert torch.equal(idx, ref[2]), f"eager call after replay {rep} differs"
+    print("[forward] long rows: graph replays equal the eager call", flush=True)
+
+
 def test_forward_deterministic(dsa):
     """Two runs give bitwise-identical outputs, and a NaN-filled workspace does not
     leak into them (catches races and reads of uninitialised scratch)."""
